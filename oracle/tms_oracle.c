@@ -1,0 +1,499 @@
+/*
+ * Plain CPU oracle for the trie-constrained sparse decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product links, loads or calls this
+ * file; only the tests, the smoke check and the bench's CPU-baseline leg do.
+ * It shares no code with the HIP library (its own trie build, its own state,
+ * its own arithmetic) and is written to be checked by eye, not to be fast:
+ * scalar loops, fp64 arithmetic, no blocking and no reordering.
+ *
+ * What it computes (sources: "Constraint made cheaper than no constraint",
+ * sections "The grammar as a trie over tokens", "Masked sampling inside the
+ * sampler" and "The sparse output layer"; "Constrained decoding with weighted
+ * automata", the definition of the next-token mask; "Understanding inference
+ * for systems engineers", section 3.8 on the greedy tie rule):
+ *
+ *   A catalog C is K distinct non-empty token strings over [0,V) without the
+ *   separator id sep and the stop id stop.  The answer language is
+ *       L_k(C) = { c_p1 sep c_p2 sep ... sep c_pk stop : p an injection [k]->[K] },
+ *   i.e. exactly k pointers, none repeated.  After an emitted prefix u the legal
+ *   set is Mask(u) = { v : some w makes u v w a string of L_k(C) }.  Each step the
+ *   decoder takes the legal token with the largest logit <h_t, E_v>, ties to
+ *   the lower token id, and stops after the stop token.
+ *
+ * The trie form of that definition (token-id trie in CSR, sentinel children for
+ * the two control edges, per-edge live counts decremented along a completed
+ * pointer's path, a per-terminal spent flag) is written out below in the
+ * order the first page describes it.  Readings where the pages are silent:
+ *   - control edges are ordinary edges of a terminal's range, labelled sep and
+ *     stop, with sentinel children -1 (sep) and -2 (stop);
+ *   - the live count of a content edge starts at the number of entries whose
+ *     string passes through it (the entry ending at its child included);
+ *   - completing a pointer decrements every content edge on its root path and
+ *     sets the spent flag of its terminal, which removes both control edges of
+ *     that terminal only;
+ *   - sep is legal at an unspent terminal iff done+1 < k, stop iff done+1 == k;
+ *   - logits are fp64 sums of exact products in index order, never rounded to
+ *     bf16 before the argmax; no scale, temperature or softcap.
+ *
+ * Planted mistakes (negative controls) are selected by orc_set_mutant(); the
+ * default 0 is the oracle proper.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* status codes, same numbering as the library's public header */
+enum {
+  ORC_OK = 0,
+  ORC_ERR_INVALID_ARG = 1,
+  ORC_ERR_CATALOG = 2,
+  ORC_ERR_FANOUT = 3,
+  ORC_ERR_K = 4,
+  ORC_ERR_EMPTY_MASK = 5,
+  ORC_ERR_NOT_WALKABLE = 6,
+  ORC_ERR_NOT_DONE = 7,
+};
+
+#define CHILD_SEP (-1)
+#define CHILD_STOP (-2)
+
+/* planted mistakes for negative-control tests */
+enum {
+  MUT_NONE = 0,
+  MUT_TIE_HIGHER_ID = 1,    /* ties go to the higher token id */
+  MUT_NO_LIVE_DECREMENT = 2,/* completing a pointer does not touch live counts */
+  MUT_NO_SPENT_FLAG = 3,    /* finished terminals keep their control edges */
+  MUT_ROW_OFF_BY_ONE = 4,   /* logit of token v is read from row v+1 */
+  MUT_SEP_STOP_SWAPPED = 5, /* sep when the last pointer is due, stop otherwise */
+  MUT_DROP_LAST_TERM = 6,   /* dot product skips the last hidden element */
+};
+static int g_mutant = 0;
+void orc_set_mutant(int m) { g_mutant = m; }
+
+/* ------------------------------------------------------------------------- */
+/* Trie build                                                                 */
+/* ------------------------------------------------------------------------- */
+
+/* pointer-style build trie: each node keeps an unsorted child list */
+typedef struct {
+  int32_t *ctok, *cnode; /* child tokens and child build-node ids */
+  int32_t nchild, capchild;
+  int32_t entry;         /* catalog index ending here, or -1 */
+} bnode;
+
+typedef struct {
+  int32_t n_nodes, n_edges, n_entries, cap, max_depth, sep, stop, vocab;
+  int32_t *begin;  /* [n_nodes+1] edge range of each node */
+  int32_t *entry;  /* [n_nodes] catalog index ending at the node, or -1 */
+  int32_t *tok;    /* [n_edges] edge label */
+  int32_t *child;  /* [n_edges] child node, or -1 (sep) / -2 (stop) */
+  int32_t *live0;  /* [n_edges] entries below a content edge; 0 for control */
+} orc_trie;
+
+static int32_t bnode_find(const bnode* n, int32_t t) {
+  for (int32_t i = 0; i < n->nchild; ++i)
+    if (n->ctok[i] == t) return n->cnode[i];
+  return -1;
+}
+
+static void bnode_add(bnode* n, int32_t t, int32_t id) {
+  if (n->nchild == n->capchild) {
+    n->capchild = n->capchild ? 2 * n->capchild : 4;
+    n->ctok = (int32_t*)realloc(n->ctok, sizeof(int32_t) * n->capchild);
+    n->cnode = (int32_t*)realloc(n->cnode, sizeof(int32_t) * n->capchild);
+  }
+  n->ctok[n->nchild] = t;
+  n->cnode[n->nchild] = id;
+  n->nchild++;
+}
+
+/* insertion sort of a node's children by token (fan-outs are small) */
+static void bnode_sort(bnode* n) {
+  for (int32_t i = 1; i < n->nchild; ++i) {
+    int32_t t = n->ctok[i], c = n->cnode[i], j = i - 1;
+    while (j >= 0 && n->ctok[j] > t) {
+      n->ctok[j + 1] = n->ctok[j];
+      n->cnode[j + 1] = n->cnode[j];
+      --j;
+    }
+    n->ctok[j + 1] = t;
+    n->cnode[j + 1] = c;
+  }
+}
+
+/* number of entries ending at or below build node b (iterative post-order) */
+static void count_terminals(const bnode* nodes, int32_t nb, int32_t* below) {
+  /* children always get larger build ids than their parent (they are created
+   * after it), so a reverse sweep over ids visits children first */
+  for (int32_t b = nb - 1; b >= 0; --b) {
+    int32_t s = nodes[b].entry >= 0 ? 1 : 0;
+    for (int32_t i = 0; i < nodes[b].nchild; ++i) s += below[nodes[b].cnode[i]];
+    below[b] = s;
+  }
+}
+
+void orc_trie_free(orc_trie* t) {
+  if (!t) return;
+  free(t->begin); free(t->entry); free(t->tok); free(t->child); free(t->live0);
+  free(t);
+}
+
+/* Validate the catalog and build the canonical CSR: nodes numbered breadth
+ * first from root 0 with children in ascending token order; a node's range
+ * holds its content edges and, when it is terminal, the sep and stop edges,
+ * all in ascending token order. */
+int orc_trie_build(const int32_t* tokens, const int64_t* offsets, int32_t K, int32_t vocab,
+                   int32_t sep, int32_t stop, orc_trie** out) {
+  *out = NULL;
+  if (K < 1 || vocab < 2 || sep < 0 || sep >= vocab || stop < 0 || stop >= vocab || sep == stop)
+    return ORC_ERR_INVALID_ARG;
+  if (offsets[0] != 0) return ORC_ERR_CATALOG;
+  for (int32_t i = 0; i < K; ++i) {
+    if (offsets[i + 1] <= offsets[i]) return ORC_ERR_CATALOG; /* empty entry */
+    for (int64_t j = offsets[i]; j < offsets[i + 1]; ++j) {
+      int32_t t = tokens[j];
+      if (t < 0 || t >= vocab || t == sep || t == stop) return ORC_ERR_CATALOG;
+    }
+  }
+
+  int64_t total = offsets[K];
+  int32_t capn = (int32_t)(total + 1);
+  bnode* nodes = (bnode*)calloc((size_t)capn, sizeof(bnode));
+  int32_t nb = 1;
+  nodes[0].entry = -1;
+  int32_t max_depth = 0;
+  int rc = ORC_OK;
+  for (int32_t i = 0; i < K && rc == ORC_OK; ++i) {
+    int32_t cur = 0;
+    int32_t len = (int32_t)(offsets[i + 1] - offsets[i]);
+    if (len > max_depth) max_depth = len;
+    for (int64_t j = offsets[i]; j < offsets[i + 1]; ++j) {
+      int32_t nxt = bnode_find(&nodes[cur], tokens[j]);
+      if (nxt < 0) {
+        nxt = nb++;
+        nodes[nxt].entry = -1;
+        bnode_add(&nodes[cur], tokens[j], nxt);
+      }
+      cur = nxt;
+    }
+    if (nodes[cur].entry >= 0) rc = ORC_ERR_CATALOG; /* duplicate entry */
+    else nodes[cur].entry = i;
+  }
+  if (rc != ORC_OK) {
+    for (int32_t b = 0; b < nb; ++b) { free(nodes[b].ctok); free(nodes[b].cnode); }
+    free(nodes);
+    return rc;
+  }
+
+  int32_t* below = (int32_t*)malloc(sizeof(int32_t) * nb);
+  count_terminals(nodes, nb, below);
+
+  /* breadth-first numbering */
+  int32_t* order = (int32_t*)malloc(sizeof(int32_t) * nb); /* bfs id -> build id */
+  int32_t* bfs_of = (int32_t*)malloc(sizeof(int32_t) * nb); /* build id -> bfs id */
+  int32_t head = 0, tail = 0;
+  order[tail++] = 0;
+  while (head < tail) {
+    int32_t b = order[head++];
+    bnode_sort(&nodes[b]);
+    for (int32_t i = 0; i < nodes[b].nchild; ++i) order[tail++] = nodes[b].cnode[i];
+  }
+  for (int32_t i = 0; i < nb; ++i) bfs_of[order[i]] = i;
+
+  orc_trie* t = (orc_trie*)calloc(1, sizeof(orc_trie));
+  t->n_nodes = nb;
+  t->n_entries = K;
+  t->sep = sep;
+  t->stop = stop;
+  t->vocab = vocab;
+  t->max_depth = max_depth;
+  int32_t n_edges = 0;
+  for (int32_t b = 0; b < nb; ++b) n_edges += nodes[b].nchild + (nodes[b].entry >= 0 ? 2 : 0);
+  t->n_edges = n_edges;
+  t->begin = (int32_t*)malloc(sizeof(int32_t) * (nb + 1));
+  t->entry = (int32_t*)malloc(sizeof(int32_t) * nb);
+  t->tok = (int32_t*)malloc(sizeof(int32_t) * (n_edges ? n_edges : 1));
+  t->child = (int32_t*)malloc(sizeof(int32_t) * (n_edges ? n_edges : 1));
+  t->live0 = (int32_t*)malloc(sizeof(int32_t) * (n_edges ? n_edges : 1));
+
+  int32_t e = 0, cap = 0;
+  for (int32_t id = 0; id < nb; ++id) {
+    const bnode* n = &nodes[order[id]];
+    t->begin[id] = e;
+    t->entry[id] = n->entry;
+    /* merge the sorted content edges with the (sorted) control edges */
+    int32_t ctl_tok[2], ctl_child[2], nctl = 0;
+    if (n->entry >= 0) {
+      if (sep < stop) {
+        ctl_tok[0] = sep; ctl_child[0] = CHILD_SEP; ctl_tok[1] = stop; ctl_child[1] = CHILD_STOP;
+      } else {
+        ctl_tok[0] = stop; ctl_child[0] = CHILD_STOP; ctl_tok[1] = sep; ctl_child[1] = CHILD_SEP;
+      }
+      nctl = 2;
+    }
+    int32_t i = 0, c = 0;
+    while (i < n->nchild || c < nctl) {
+      if (c >= nctl || (i < n->nchild && n->ctok[i] < ctl_tok[c])) {
+        t->tok[e] = n->ctok[i];
+        t->child[e] = bfs_of[n->cnode[i]];
+        t->live0[e] = below[n->cnode[i]];
+        ++i;
+      } else {
+        t->tok[e] = ctl_tok[c];
+        t->child[e] = ctl_child[c];
+        t->live0[e] = 0;
+        ++c;
+      }
+      ++e;
+    }
+    if (e - t->begin[id] > cap) cap = e - t->begin[id];
+  }
+  t->begin[nb] = e;
+  t->cap = cap;
+
+  for (int32_t b = 0; b < nb; ++b) { free(nodes[b].ctok); free(nodes[b].cnode); }
+  free(nodes); free(below); free(order); free(bfs_of);
+  *out = t;
+  return ORC_OK;
+}
+
+/* info: n_nodes, n_edges, n_entries, cap, max_depth, sep, stop, vocab */
+void orc_trie_info(const orc_trie* t, int32_t* info) {
+  info[0] = t->n_nodes; info[1] = t->n_edges; info[2] = t->n_entries; info[3] = t->cap;
+  info[4] = t->max_depth; info[5] = t->sep; info[6] = t->stop; info[7] = t->vocab;
+}
+
+void orc_trie_csr(const orc_trie* t, int32_t* begin, int32_t* entry, int32_t* tok,
+                  int32_t* child, int32_t* live0) {
+  memcpy(begin, t->begin, sizeof(int32_t) * (t->n_nodes + 1));
+  memcpy(entry, t->entry, sizeof(int32_t) * t->n_nodes);
+  memcpy(tok, t->tok, sizeof(int32_t) * t->n_edges);
+  memcpy(child, t->child, sizeof(int32_t) * t->n_edges);
+  memcpy(live0, t->live0, sizeof(int32_t) * t->n_edges);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Decode state of one sequence                                               */
+/* ------------------------------------------------------------------------- */
+
+typedef struct {
+  const orc_trie* t;
+  int32_t k;
+  int32_t node, depth, done, finished, status, n_emitted;
+  int32_t* path;     /* [max_depth] content edges from the root */
+  int32_t* live;     /* [n_edges] */
+  unsigned char* spent; /* [n_entries] */
+  int32_t* entries;  /* [k] catalog indices of completed pointers */
+} orc_state;
+
+orc_state* orc_state_new(const orc_trie* t, int32_t k) {
+  orc_state* s = (orc_state*)calloc(1, sizeof(orc_state));
+  s->t = t;
+  s->k = k;
+  s->path = (int32_t*)calloc((size_t)t->max_depth + 1, sizeof(int32_t));
+  s->live = (int32_t*)malloc(sizeof(int32_t) * (t->n_edges ? t->n_edges : 1));
+  memcpy(s->live, t->live0, sizeof(int32_t) * t->n_edges);
+  s->spent = (unsigned char*)calloc((size_t)t->n_entries, 1);
+  s->entries = (int32_t*)malloc(sizeof(int32_t) * (k > 0 ? k : 1));
+  for (int32_t i = 0; i < k; ++i) s->entries[i] = -1;
+  return s;
+}
+
+void orc_state_free(orc_state* s) {
+  if (!s) return;
+  free(s->path); free(s->live); free(s->spent); free(s->entries); free(s);
+}
+
+/* is edge e of the current node legal for this sequence? */
+static int edge_legal(const orc_state* s, int32_t e) {
+  const orc_trie* t = s->t;
+  int32_t c = t->child[e];
+  if (c >= 0) return s->live[e] > 0;
+  int32_t ent = t->entry[s->node];
+  if (ent < 0) return 0;
+  if (s->spent[ent] && g_mutant != MUT_NO_SPENT_FLAG) return 0;
+  int more = s->done + 1 < s->k;
+  if (g_mutant == MUT_SEP_STOP_SWAPPED) more = !more;
+  return c == CHILD_SEP ? more : !more;
+}
+
+/* legal tokens (and their edges) at the current node, ascending token order;
+ * returns the count, or -1 when the sequence is finished or in error */
+int32_t orc_state_legal(const orc_state* s, int32_t* toks, int32_t* edges) {
+  if (s->finished || s->status != ORC_OK) return -1;
+  const orc_trie* t = s->t;
+  int32_t n = 0;
+  for (int32_t e = t->begin[s->node]; e < t->begin[s->node + 1]; ++e) {
+    if (edge_legal(s, e)) {
+      if (toks) toks[n] = t->tok[e];
+      if (edges) edges[n] = e;
+      ++n;
+    }
+  }
+  return n;
+}
+
+/* take token `tok` at the current node; returns the sequence status */
+int32_t orc_state_advance(orc_state* s, int32_t tok) {
+  if (s->finished || s->status != ORC_OK) return s->status != ORC_OK ? s->status : ORC_ERR_INVALID_ARG;
+  const orc_trie* t = s->t;
+  int32_t e = -1;
+  for (int32_t i = t->begin[s->node]; i < t->begin[s->node + 1]; ++i)
+    if (t->tok[i] == tok) { e = i; break; }
+  if (e < 0 || !edge_legal(s, e)) {
+    s->status = ORC_ERR_NOT_WALKABLE;
+    return s->status;
+  }
+  s->n_emitted++;
+  int32_t c = t->child[e];
+  if (c >= 0) {
+    s->path[s->depth++] = e;
+    s->node = c;
+    return ORC_OK;
+  }
+  /* a pointer completes: spend its terminal, release its path */
+  int32_t ent = t->entry[s->node];
+  s->spent[ent] = 1;
+  if (g_mutant != MUT_NO_LIVE_DECREMENT)
+    for (int32_t i = 0; i < s->depth; ++i) s->live[s->path[i]] -= 1;
+  s->depth = 0;
+  s->entries[s->done] = ent;
+  s->done++;
+  if (c == CHILD_SEP) s->node = 0;
+  else s->finished = 1;
+  return ORC_OK;
+}
+
+/* node, depth, done, finished, status, n_emitted */
+void orc_state_info(const orc_state* s, int32_t* info) {
+  info[0] = s->node; info[1] = s->depth; info[2] = s->done;
+  info[3] = s->finished; info[4] = s->status; info[5] = s->n_emitted;
+}
+
+void orc_state_live(const orc_state* s, int32_t* live) {
+  memcpy(live, s->live, sizeof(int32_t) * s->t->n_edges);
+}
+
+void orc_state_entries(const orc_state* s, int32_t* entries) {
+  memcpy(entries, s->entries, sizeof(int32_t) * s->k);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Logits                                                                      */
+/* ------------------------------------------------------------------------- */
+
+/* element i of a row stored as fp32 (dtype 0) or as bf16 bit patterns (1),
+ * widened exactly to double */
+static double elem(const void* base, int dtype, int64_t i) {
+  if (dtype == 0) return (double)((const float*)base)[i];
+  uint32_t bits = (uint32_t)((const uint16_t*)base)[i] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/* logit of token v: sum over i of h[i] * E[v][i] in index order, in fp64.
+ * Every product is exact in fp64 (bf16 and fp32 significands are 8 and 24
+ * bits).  *sumabs receives sum |h[i] E[v][i]| for error bounds. */
+double orc_logit(const void* emb, int dtype, int32_t H, int32_t v, const void* h, double* sumabs) {
+  int64_t row = (int64_t)(g_mutant == MUT_ROW_OFF_BY_ONE ? v + 1 : v) * H;
+  int32_t n = g_mutant == MUT_DROP_LAST_TERM ? H - 1 : H;
+  double acc = 0.0, a = 0.0;
+  for (int32_t i = 0; i < n; ++i) {
+    double p = elem(h, dtype, i) * elem(emb, dtype, row + i);
+    acc += p;
+    a += fabs(p);
+  }
+  if (sumabs) *sumabs = a;
+  return acc;
+}
+
+/* all V logits of one hidden vector (the dense head) */
+void orc_dense_logits(const void* emb, int dtype, int32_t V, int32_t H, const void* h, double* out) {
+  for (int32_t v = 0; v < V; ++v) {
+    int32_t vv = (g_mutant == MUT_ROW_OFF_BY_ONE && v == V - 1) ? V - 2 : v; /* keep in range */
+    out[v] = orc_logit(emb, dtype, H, vv, h, NULL);
+  }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Greedy decode                                                               */
+/* ------------------------------------------------------------------------- */
+
+/* One greedy step: legal set, logits, first maximum in ascending token order
+ * (ties to the lower id), advance.  Records the winner's logit, the top-two
+ * margin (+inf with one candidate), the larger sum|p| of the top two, and the
+ * size of the legal set.  Returns the token, or -1 when nothing was emitted. */
+static int32_t greedy_step(orc_state* s, const void* emb, int dtype, int32_t H, const void* h,
+                           int32_t* scratch_tok, double* best_out, double* margin_out,
+                           double* sumabs_out, int32_t* nlegal_out) {
+  int32_t n = orc_state_legal(s, scratch_tok, NULL);
+  if (nlegal_out) *nlegal_out = n < 0 ? 0 : n;
+  if (n < 0) return -1;
+  if (n == 0) {
+    s->status = ORC_ERR_EMPTY_MASK;
+    return -1;
+  }
+  int32_t win = -1;
+  double best = 0.0, second = -INFINITY, best_abs = 0.0, second_abs = 0.0;
+  for (int32_t j = 0; j < n; ++j) {
+    double a;
+    double l = orc_logit(emb, dtype, H, scratch_tok[j], h, &a);
+    int better = (win < 0) || (g_mutant == MUT_TIE_HIGHER_ID ? l >= best : l > best);
+    if (better) {
+      if (win >= 0) { second = best; second_abs = best_abs; }
+      win = scratch_tok[j];
+      best = l;
+      best_abs = a;
+    } else if (l > second || (l == second && second_abs < a)) {
+      second = l;
+      second_abs = a;
+    }
+  }
+  if (best_out) *best_out = best;
+  if (margin_out) *margin_out = n > 1 ? best - second : INFINITY;
+  if (sumabs_out) *sumabs_out = n > 1 && second_abs > best_abs ? second_abs : best_abs;
+  orc_state_advance(s, win);
+  return win;
+}
+
+/* Greedy decode of B independent sequences over T steps.
+ * hidden: [T][B][H] (fp32 or bf16 bits, same dtype as emb).
+ * Outputs (any may be NULL): tokens [B][T] (-1 padded), len [B], entries [B][k],
+ * status [B] (NOT_DONE when no stop was emitted within T steps), and per step
+ * best logit, top-two margin, sum|p| and legal-set size, each [B][T].
+ * Sequences are decoded one after another; nothing is shared between them. */
+int orc_decode(const orc_trie* t, int32_t k, const void* emb, int dtype, int32_t V, int32_t H,
+               const void* hidden, int32_t B, int32_t T, int32_t* tokens, int32_t* len,
+               int32_t* entries, int32_t* status, double* best, double* margin, double* sumabs,
+               int32_t* nlegal) {
+  if (k < 1 || k > t->n_entries) return ORC_ERR_K;
+  if (V != t->vocab || H < 1 || B < 1 || T < 0) return ORC_ERR_INVALID_ARG;
+  size_t esz = dtype == 0 ? 4 : 2;
+  int32_t* scratch = (int32_t*)malloc(sizeof(int32_t) * (t->cap ? t->cap : 1));
+  for (int32_t b = 0; b < B; ++b) {
+    orc_state* s = orc_state_new(t, k);
+    for (int32_t step = 0; step < T; ++step) {
+      const void* h = (const char*)hidden + ((size_t)step * B + b) * (size_t)H * esz;
+      int64_t o = (int64_t)b * T + step;
+      int32_t tok = greedy_step(s, emb, dtype, H, h, scratch, best ? &best[o] : NULL,
+                                margin ? &margin[o] : NULL, sumabs ? &sumabs[o] : NULL,
+                                nlegal ? &nlegal[o] : NULL);
+      if (tokens) tokens[o] = tok;
+      if (tok < 0) {
+        if (best) best[o] = NAN;
+        if (margin) margin[o] = NAN;
+        if (sumabs) sumabs[o] = NAN;
+      }
+    }
+    if (s->status == ORC_OK && !s->finished) s->status = ORC_ERR_NOT_DONE;
+    if (len) len[b] = s->n_emitted;
+    if (entries) memcpy(&entries[(int64_t)b * k], s->entries, sizeof(int32_t) * k);
+    if (status) status[b] = s->status;
+    orc_state_free(s);
+  }
+  free(scratch);
+  return ORC_OK;
+}
