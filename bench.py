@@ -1,0 +1,358 @@
+"""Benchmark of the trie-constrained sparse decode on one MI355X.
+
+One bench step = one whole answer for one batch of the product-scale workload
+(V=151936, H=2048 bf16 tied embedding, 42-tool catalog, k=3, B=1): reset the
+decode state, then the device-resident loop (a replayed hipGraph of step
+kernels) until every sequence has emitted exactly k pointers.  value = decode
+steps per second (lockstep steps that emitted a token), over K timed steps
+after W warmup steps, bracketed by device synchronisations.
+
+Also reported on the same line: the step kernel's roofline (algorithmic bytes
+per launch / its average duration, timed with HIP events on the launch
+stream), the batch-64 workloads, the gather-GEMV bandwidth stress shape
+(64 x 256 distinct rows per launch cycling through 9 disjoint row sets, 604 MB
+of the 622 MB table), the dense+mask step, and the CPU oracle timed on this
+host (cpu_baseline leg, the only place the oracle is used here).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "constrained decode steps/sec (sparse head) at B=1/64; achieved HBM GB/s"
+
+
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _kernel_hash():
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "kernels.h"):
+        with open(os.path.join(ROOT, "trie_masked_sparse_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+class Workload:
+    """Device copies of one seeded workload plus a state for it."""
+
+    def __init__(self, cid, B=None):
+        import numpy as np
+        import torch
+
+        import trie_masked_sparse_amd as tms
+        from synth import CONFIGS, catalog, embedding, hidden_states
+        self.c = c = CONFIGS[cid]
+        self.cid = cid
+        self.B = c.batch if B is None else B
+        cat = catalog(cid)
+        self.trie = tms.Trie(cat, c.vocab, c.sep, c.stop)
+        self.info = self.trie.info
+        self.T = c.k * (self.info["max_depth"] + 1)
+        self.emb_np = embedding(cid)
+        self.emb = _to_dev(self.emb_np)
+        self.hid_np = hidden_states(cid, self.T, self.B)
+        self.hid = _to_dev(self.hid_np)
+        self.state = tms.State(self.trie, self.B, c.k, self.emb)
+        self.tokens = torch.empty((self.B, self.T), dtype=torch.int32, device="cuda")
+        self.len = torch.empty(self.B, dtype=torch.int32, device="cuda")
+        self.entries = torch.empty((self.B, c.k), dtype=torch.int32, device="cuda")
+        self.esz = 2 if c.dtype == "bf16" else 4
+        self.np = np
+
+    def decode(self):
+        import trie_masked_sparse_amd as tms
+        self.state.reset()
+        tms.decode_k_pointers(self.state.h, self.hid, self.tokens, self.len, self.entries)
+
+    def legal_profile(self):
+        """Per step: legal-set sizes and unique rows, from the library's own
+        materialiser, along the decode's own path (host-driven steps)."""
+        import torch
+
+        import trie_masked_sparse_amd as tms
+        np = self.np
+        cap = self.info["cap"]
+        legal = torch.empty((self.B, cap), dtype=torch.int32, device="cuda")
+        nleg = torch.empty(self.B, dtype=torch.int32, device="cuda")
+        tok = torch.empty(self.B, dtype=torch.int32, device="cuda")
+        self.state.reset()
+        n_rows, n_active, n_unique = [], [], []
+        for t in range(self.T):
+            tms.legal_set(self.state.h, legal, nleg)
+            lg, nl = legal.cpu().numpy(), nleg.cpu().numpy()
+            act = nl >= 0
+            n_active.append(int(act.sum()))
+            n_rows.append(int(nl[act].sum()))
+            u = set()
+            for b in np.nonzero(act)[0]:
+                u.update(lg[b, :nl[b]].tolist())
+            n_unique.append(len(u))
+            tms.decode_step_sparse(self.state.h, self.hid[t], tok)
+        torch.cuda.synchronize()
+        return np.array(n_rows), np.array(n_active), np.array(n_unique)
+
+    def step_durations(self, reps):
+        """Average duration of each step-kernel launch (HIP events around each
+        launch on the launch stream), host-driven loop."""
+        import torch
+
+        import trie_masked_sparse_amd as tms
+        tok = torch.empty(self.B, dtype=torch.int32, device="cuda")
+        durs = []
+        for _ in range(reps):
+            self.state.reset()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(self.T)]
+            for t in range(self.T):
+                evs[t][0].record()
+                tms.decode_step_sparse(self.state.h, self.hid[t], tok)
+                evs[t][1].record()
+            torch.cuda.synchronize()
+            durs.append([a.elapsed_time(b) * 1e3 for a, b in evs])  # us
+        return self.np.array(durs).mean(axis=0)
+
+    def close(self):
+        self.state.close()
+        self.trie.close()
+
+
+def _to_dev(a):
+    import numpy as np
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def time_decode(w: Workload, steps: int, warmup: int):
+    import torch
+    for _ in range(warmup):
+        w.decode()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        w.decode()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    ln = w.len.cpu().numpy()
+    assert (w.state.status() == 0).all(), "decode reported a device error"
+    steps_per_call = int(ln.max())  # lockstep steps that emitted a token
+    tokens_per_call = int(ln.sum())
+    return {
+        "wall_s": wall, "gpu_ms": gpu_ms, "ms_per_call": wall * 1e3 / steps,
+        "steps_per_s": steps_per_call * steps / wall, "tokens_per_s": tokens_per_call * steps / wall,
+        "steps_per_call": steps_per_call, "tokens_per_call": tokens_per_call, "launches_per_call": w.T,
+    }
+
+
+def step_roofline(w: Workload, reps: int):
+    np = w.np
+    n_rows, n_act, n_uni = w.legal_profile()
+    durs = w.step_durations(reps)
+    H, esz = w.c.hidden, w.esz
+    gathered = (n_rows + n_act) * H * esz          # rows + hidden vectors, per launch
+    unique = (n_uni + n_act) * H * esz
+    return {
+        "avg_launch_us": float(durs.mean()),
+        "alg_bytes_per_launch": float(gathered.mean()),
+        "unique_bytes_per_launch": float(unique.mean()),
+        "achieved_GBps": float(gathered.sum() / (durs.sum() * 1e-6) / 1e9),
+        "unique_GBps": float(unique.sum() / (durs.sum() * 1e-6) / 1e9),
+        "per_step_us": [round(float(x), 2) for x in durs],
+        "per_step_rows": [int(x) for x in n_rows],
+    }
+
+
+def stress_gemv(steps: int, warmup: int, emb, emb_np):
+    """64 sequences x 256 distinct rows per launch, 9 disjoint row sets."""
+    import numpy as np
+    import torch
+
+    import trie_masked_sparse_amd as tms
+    from synth import bf16_bits_from_f32, stress_rows
+    V, H = emb_np.shape
+    B, R, S = 64, 256, 9
+    sets = [_to_dev(np.ascontiguousarray(s)) for s in stress_rows(V, B, R, S)]
+    rng = np.random.Generator(np.random.PCG64(5))
+    hid = _to_dev(bf16_bits_from_f32(rng.standard_normal((B, H), dtype=np.float32)))
+    n = torch.full((B,), R, dtype=torch.int32, device="cuda")
+    out = torch.empty((B, R), dtype=torch.float32, device="cuda")
+    for i in range(warmup * S):
+        tms.gather_gemv(emb, hid, sets[i % S], n, out)
+    torch.cuda.synchronize()
+    iters = max(steps, 1) * S
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for i in range(iters):
+        evs[i][0].record()
+        tms.gather_gemv(emb, hid, sets[i % S], n, out)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    durs = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    nbytes = B * R * H * 2 + B * H * 2
+    return {"shape": "64 seq x 256 distinct rows, H=2048 bf16, 9 disjoint sets (604 MB)",
+            "avg_launch_us": float(durs.mean()), "alg_bytes_per_launch": nbytes,
+            "achieved_GBps": nbytes / (durs.mean() * 1e-6) / 1e9,
+            "frac_of_8TBps": nbytes / (durs.mean() * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+
+
+def stream_read_GBps():
+    """Reference: torch's sum over 2 GiB of bf16 (a plain streaming read)."""
+    import torch
+    x = torch.ones(1 << 30, dtype=torch.bfloat16, device="cuda")
+    for _ in range(3):
+        x.sum()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        x.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 10 * x.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del x
+    return gbps
+
+
+def dense_step_us(w: Workload, reps=5):
+    import torch
+
+    import trie_masked_sparse_amd as tms
+    tok = torch.empty(w.B, dtype=torch.int32, device="cuda")
+    w.state.reset()
+    tms.decode_step_dense_masked(w.state.h, w.hid[0], tok)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w.state.reset()
+    e0.record()
+    n = min(reps, w.T)
+    for t in range(n):
+        tms.decode_step_dense_masked(w.state.h, w.hid[t], tok)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    table = w.c.vocab * w.c.hidden * w.esz
+    return {"B": w.B, "us_per_step": us, "table_GBps": table / (us * 1e-6) / 1e9}
+
+
+def cpu_baseline(w: Workload, min_seconds: float):
+    """The oracle (plain C, fp64, one thread) decoding the same batch, repeated."""
+    import oracle
+    otr = oracle.Trie(__import__("synth").catalog(w.cid), w.c.vocab, w.c.sep, w.c.stop)
+    reps, t0 = 0, time.perf_counter()
+    steps = 0
+    while True:
+        out = oracle.decode(otr, w.c.k, w.emb_np, w.hid_np)
+        reps += 1
+        steps += int(out["len"].max())
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    return {"value": steps / el, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} repetitions of the full {w.cid} decode (B={w.B}, {int(out['len'].max())} steps, "
+                      f"{int(out['len'].sum())} tokens each), {el:.1f} s, single thread, gcc -O2 fp64"}
+
+
+def _pmc_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken with the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        d = json.load(fh)
+    if d.get("kernel_sources_sha256_16") != _kernel_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--only", default="", help="comma list: headline,b64,stress,dense,cpu (default all)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+              "Sequences shard across GPUs with no per-step exchange; run one process per GPU.", file=sys.stderr)
+        sys.exit(2)
+    only = set(filter(None, args.only.split(",")))
+
+    def want(x):
+        return not only or x in only
+
+    import torch
+
+    import trie_masked_sparse_amd as tms
+    tms.lib()
+    torch.cuda.init()
+    _log(f"device {torch.cuda.get_device_name(0)}")
+
+    line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    also = {}
+    _log("product-scale workload")
+    w = Workload("product")
+    if want("headline"):
+        r = time_decode(w, args.steps, args.warmup)
+        line.update({"value": r["steps_per_s"], "unit": "steps/s", "ms_per_step": r["ms_per_call"],
+                     "tokens_per_s": r["tokens_per_s"]})
+        line["config"] = {
+            "workload": "product-scale: V=151936, H=2048 bf16 tied embedding (622 MB), 42-tool catalog "
+                        f"({w.info['n_nodes']} trie nodes, cap {w.info['cap']}), k=3, B=1; one bench step = "
+                        "state reset + device-loop graph of "
+                        f"{w.T} step kernels; bf16 inputs, fp32 accumulation",
+            "path": "fast" if w.info["path"] == tms.PATH_FAST else "global",
+            "steps_per_call": r["steps_per_call"], "tokens_per_call": r["tokens_per_call"],
+            "launches_per_call": r["launches_per_call"], "split": tms.state_get_launch(w.state.h)[0]}
+        _log(f"headline {r}")
+        rf = step_roofline(w, reps=max(3, args.steps // 5))
+        line["roofline"] = {"bound": "hbm", "kernel": "step_sparse_kernel", "achieved": rf["achieved_GBps"],
+                            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": rf["achieved_GBps"] / HBM_PEAK_GBPS,
+                            "traffic": _pmc_traffic("step_sparse", "product"),
+                            "alg_bytes_per_launch": rf["alg_bytes_per_launch"],
+                            "avg_launch_us": rf["avg_launch_us"]}
+        also["product_step_detail"] = rf
+    if want("dense"):
+        also["dense_masked_product_B1"] = dense_step_us(w)
+        _log(f"dense {also['dense_masked_product_B1']}")
+    if want("stress"):
+        also["gather_gemv_stress"] = stress_gemv(max(3, args.steps // 5), 2, w.emb, w.emb_np)
+        _log(f"stress {also['gather_gemv_stress']}")
+        also["stream_read_GBps"] = stream_read_GBps()
+    if want("b64"):
+        for cid in ("structured", "unstructured"):
+            _log(f"{cid} workload")
+            wb = Workload(cid)
+            rb = time_decode(wb, max(5, args.steps // 2), args.warmup)
+            rfb = step_roofline(wb, reps=3)
+            also[f"{cid}_B64"] = {"steps_per_s": rb["steps_per_s"], "tokens_per_s": rb["tokens_per_s"],
+                                  "ms_per_call": rb["ms_per_call"], "steps_per_call": rb["steps_per_call"],
+                                  "path": "fast" if wb.info["path"] == tms.PATH_FAST else "global",
+                                  "step_kernel": {k: v for k, v in rfb.items() if k not in ("per_step_rows",)}}
+            _log(f"{cid} {also[f'{cid}_B64']['steps_per_s']:.0f} steps/s")
+            wb.close()
+    if want("cpu"):
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        _log(f"cpu {line['cpu_baseline']}")
+    line["also"] = also
+    w.close()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,214 @@
+/*
+ * tms.h - trie-constrained sparse decode step for finite-set outputs (tool
+ * catalogs), MI355X (gfx950) HIP library with a plain C ABI.
+ *
+ * The method (web page "Constraint made cheaper than no constraint"):
+ *   - section "The grammar as a trie over tokens": a catalog of token-id
+ *     strings is compiled into a trie in CSR form with sentinel children for a
+ *     separator edge and a stop edge;
+ *   - section "Masked sampling inside the sampler": each step builds the legal
+ *     set at the current node, takes the argmax with ties to the lower token
+ *     id, fails loudly on an empty mask or an unwalkable winner, and advances;
+ *     exactly k pointers come out because sep is legal only while another
+ *     pointer is owed and stop only when none is; live counts per edge,
+ *     decremented along a completed pointer's path, keep pointers from
+ *     repeating; a per-terminal spent flag handles entries that are prefixes
+ *     of other entries;
+ *   - section "The sparse output layer": the head computes one dot product per
+ *     legal token against the tied embedding instead of all V logits; the
+ *     dense head stays as a cross-check with the same tie rule and transitions;
+ *   - section "The whole loop on the device": the decode loop runs without the
+ *     host between steps.
+ * The mask semantics are Mask(u) = {v : some w makes u v w an answer} (page
+ * "Constrained decoding with weighted automata", the next-token mask), and the
+ * greedy tie rule is the one of page "Understanding inference for systems
+ * engineers", section 3.8.
+ *
+ * Conventions for every call:
+ *   - Every function returns a tms_status and never throws.  On failure
+ *     tms_last_error() gives a thread-local message.
+ *   - "dev" pointers are device memory owned by the caller (for example
+ *     torch.Tensor.data_ptr()); "host" pointers are host memory owned by the
+ *     caller.  The library never frees caller memory.
+ *   - stream is a hipStream_t (NULL = the legacy default stream).  Decode
+ *     calls only enqueue work on it and return; they allocate nothing.
+ *   - Device-detected errors (EMPTY_MASK, NOT_WALKABLE, NOT_DONE) are recorded
+ *     per sequence and are sticky: that sequence stops, the others continue.
+ *     tms_state_sync_status() synchronises the stream and reports them.
+ *   - Element type of the embedding and of every hidden-state buffer: fp32, or
+ *     bf16 as raw 16-bit patterns.  Products and sums are fp32.
+ *   - Rows must be 16-byte aligned: H*elem_size % 16 == 0 and the embedding and
+ *     hidden base pointers 16-byte aligned.  H <= 8192 (bf16) or 4096 (fp32).
+ */
+#ifndef TMS_H
+#define TMS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TMS_OK = 0,
+  TMS_ERR_INVALID_ARG = 1,  /* bad pointer, size, alignment or dtype */
+  TMS_ERR_CATALOG = 2,      /* empty entry, token outside [0,V), control token inside an entry, duplicate */
+  TMS_ERR_FANOUT = 3,       /* fast path forced on a trie whose widest node has more than 256 edges */
+  TMS_ERR_K = 4,            /* k outside [1, K] */
+  TMS_ERR_EMPTY_MASK = 5,   /* device: a step found no legal token */
+  TMS_ERR_NOT_WALKABLE = 6, /* device: the chosen or forced token is not a live edge of the node */
+  TMS_ERR_NOT_DONE = 7,     /* device: no stop token within the steps given */
+  TMS_ERR_BUSY = 8,         /* trie freed while states still use it */
+  TMS_ERR_OOM = 9,          /* device allocation failed */
+  TMS_ERR_HIP = 10          /* any other HIP runtime failure (no device, launch failure, ...) */
+} tms_status;
+
+typedef enum { TMS_F32 = 0, TMS_BF16 = 1 } tms_dtype;
+
+/* Trie store path.  FAST: every node has at most 256 edges and the hot CSR
+ * arrays (begin, tok, child) fit in 64 KiB; the step reads edge records with
+ * wave-uniform scalar loads (the MI355X stand-in for the constant-memory trie of
+ * section "The grammar as a trie over tokens").  GLOBAL: any fan-out; edge records are
+ * read with per-lane vector loads in batches of 64 per wavefront.  AUTO picks
+ * FAST when both FAST conditions hold.  Both paths give bit-identical results. */
+typedef enum { TMS_PATH_AUTO = 0, TMS_PATH_FAST = 1, TMS_PATH_GLOBAL = 2 } tms_path;
+
+typedef struct tms_trie tms_trie;
+typedef struct tms_state tms_state;
+
+typedef struct {
+  int32_t n_nodes, n_edges, n_entries;
+  int32_t cap;        /* widest node's edge count, control edges included */
+  int32_t max_depth;  /* longest entry, in tokens */
+  int32_t sep, stop, vocab;
+  int32_t path;       /* TMS_PATH_FAST or TMS_PATH_GLOBAL once uploaded, TMS_PATH_AUTO for a host-only trie */
+  int64_t device_bytes;
+} tms_trie_info;
+
+/* ---------------------------------------------------------------- tries -- */
+
+/* Compile a catalog on the host only (no device memory; usable without a GPU).
+ * tokens: host int32 [offsets[K]]; offsets: host int64 [K+1], offsets[0] = 0,
+ * entry i is tokens[offsets[i] .. offsets[i+1]).  sep and stop are two distinct
+ * ids in [0, vocab) that no entry may contain.  Errors: INVALID_ARG, CATALOG.
+ * Canonical CSR: nodes numbered breadth first from root 0, children in
+ * ascending token order; a node's edge range holds its content edges and, for
+ * a terminal, the sep and stop edges, all in ascending token order; control
+ * edges have child -1 (sep) or -2 (stop); live0 of a content edge is the
+ * number of entries whose string passes through it, 0 for control edges. */
+tms_status tms_trie_build(const int32_t* tokens, const int64_t* offsets, int32_t K, int32_t vocab,
+                          int32_t sep, int32_t stop, tms_trie** out);
+
+/* tms_trie_build plus a device copy owned by the handle (allocated and copied
+ * on `stream`, which is synchronised before returning).  path selects the
+ * store layout; FAST on a trie with cap > 256 is TMS_ERR_FANOUT. */
+tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_t K, int32_t vocab,
+                           int32_t sep, int32_t stop, tms_path path, void* stream, tms_trie** out);
+
+tms_status tms_trie_info_get(const tms_trie* trie, tms_trie_info* info);
+
+/* Copy the canonical CSR to host arrays sized from tms_trie_info:
+ * begin [n_nodes+1], entry [n_nodes], tok/child/live0 [n_edges].  NULL skips. */
+tms_status tms_trie_export_csr(const tms_trie* trie, int32_t* begin, int32_t* entry, int32_t* tok,
+                               int32_t* child, int32_t* live0);
+
+/* Free a trie.  TMS_ERR_BUSY (and nothing freed) while a state uses it. */
+tms_status tms_trie_free(tms_trie* trie);
+
+/* --------------------------------------------------------------- states -- */
+
+/* Decode state for B sequences that each must emit exactly k distinct
+ * catalog entries.  emb: dev [V][H] tied embedding (V = trie vocab), dtype
+ * fp32 or bf16, kept by pointer (caller keeps it alive).  Allocates all device
+ * memory the decode calls will need (per-sequence live counts [B][E], spent
+ * flags, path stack, argmax slots) and leaves the state reset.
+ * Errors: INVALID_ARG (upload-less trie, bad sizes, alignment), K, OOM, HIP. */
+tms_status tms_state_create(tms_trie* trie, int32_t B, int32_t k, const void* emb, tms_dtype dtype,
+                            int32_t H, void* stream, tms_state** out);
+
+/* Every sequence back to the root: live = live0, spent cleared, no pointers
+ * done, status OK, nothing emitted.  Enqueued on stream (kernels, no memset). */
+tms_status tms_state_reset(tms_state* st, void* stream);
+
+/* Synchronise stream, copy per-sequence status to host_status [B] (may be
+ * NULL) and return the status of the lowest-numbered sequence in error, or
+ * TMS_OK. */
+tms_status tms_state_sync_status(tms_state* st, int32_t* host_status, void* stream);
+
+/* Copy the state to host arrays after synchronising stream (tests/debug).
+ * node, depth, done, status, finished, n_emitted: [B]; entries: [B][k] (-1 for
+ * pointers not yet done); live: [B][n_edges] (may be NULL). */
+tms_status tms_state_export(tms_state* st, int32_t* node, int32_t* depth, int32_t* done,
+                            int32_t* status, int32_t* finished, int32_t* n_emitted,
+                            int32_t* entries, int32_t* live, void* stream);
+
+tms_status tms_state_free(tms_state* st);
+
+/* --------------------------------------------------------------- decode -- */
+
+/* One decode step for all B sequences (section "The sparse output layer").
+ * hidden: dev [B][H] (state dtype).  For each active sequence s: legal set at
+ * its node, logit = sum_i hidden[s][i]*emb[v][i] in fp32 for each legal v,
+ * argmax with ties to the lower token id, advance.  Outputs: tok dev int32 [B]
+ * (the emitted token, -1 if s was inactive or failed), logit dev fp32 [B] or
+ * NULL (the winner's logit, NaN when nothing was emitted).
+ * One fused kernel; fixed grid per state, so it can be graph-captured. */
+tms_status tms_decode_step_sparse(tms_state* st, const void* hidden, int32_t* tok, float* logit,
+                                  void* stream);
+
+/* The same step computed the post-logit way (cross-check): all V logits,
+ * illegal tokens masked out, full-vocabulary argmax with the same tie rule,
+ * same advance.  full_logits: dev fp32 [B][V] or NULL (written unmasked). */
+tms_status tms_decode_step_dense_masked(tms_state* st, const void* hidden, int32_t* tok, float* logit,
+                                        float* full_logits, void* stream);
+
+/* The device-resident loop (section "The whole loop on the device"): T sparse
+ * steps from the current state with no host work in between, replayed from a
+ * hipGraph built on the first call for these pointers.  hidden_seq: dev
+ * [T][B][H], step t uses hidden_seq[t].  Outputs: tokens dev int32 [B][T]
+ * (token of step t, -1 where a sequence was inactive), len dev int32 [B]
+ * (tokens emitted since the last reset), entries dev int32 [B][k] (catalog
+ * index of each completed pointer, -1 if missing).  Sequences still unfinished
+ * after T steps get NOT_DONE.  T must be >= k*(max_depth+1) (INVALID_ARG).
+ * Bit-identical to T calls of tms_decode_step_sparse. */
+tms_status tms_decode_k_pointers(tms_state* st, const void* hidden_seq, int32_t T, int32_t* tokens,
+                                 int32_t* len, int32_t* entries, void* stream);
+
+/* Teacher forcing: advance sequence s by token tok[s] (dev int32 [B]); tok[s] <
+ * 0 leaves s unchanged.  A token that is not a legal edge of the current node
+ * sets NOT_WALKABLE for that sequence. */
+tms_status tms_advance_forced(tms_state* st, const int32_t* tok, void* stream);
+
+/* The legal set of every sequence at its current node (the materialiser on
+ * its own).  legal_tok: dev int32 [B][cap] (cap from tms_trie_info), ascending
+ * token order; n_legal: dev int32 [B], -1 for an inactive sequence. */
+tms_status tms_legal_set(tms_state* st, int32_t* legal_tok, int32_t* n_legal, void* stream);
+
+/* The sparse head on its own (a gather-GEMV over explicit row lists, as for a
+ * restricted vocabulary projection): out[s][j] = sum_i hidden[s][i] *
+ * emb[rows[s][j]][i] for j < min(n_rows[s], cap), same fp32 arithmetic and
+ * summation order as the decode step.  emb dev [V][H]; hidden dev [B][H];
+ * rows dev int32 [B][cap]; n_rows dev int32 [B]; out dev fp32 [B][cap].  Row
+ * ids outside [0, V) give NaN and are not read.  Slots j >= n_rows[s] are not
+ * written. */
+tms_status tms_gather_gemv(const void* emb, tms_dtype dtype, int32_t V, int32_t H, const void* hidden,
+                           const int32_t* rows, const int32_t* n_rows, int32_t B, int32_t cap,
+                           float* out, void* stream);
+
+/* Negative tests: set live[s][edge] = value on the device. */
+tms_status tms_debug_set_live(tms_state* st, int32_t s, int32_t edge, int32_t value, void* stream);
+
+/* Tuning knob (also read from the TMS_SPLIT environment variable at create):
+ * workgroups per sequence in the fused step; 0 restores the default. */
+tms_status tms_state_set_split(tms_state* st, int32_t split);
+
+/* Workgroups per sequence used by the fused step, and its grid size. */
+tms_status tms_state_get_launch(const tms_state* st, int32_t* split, int32_t* grid);
+
+const char* tms_status_str(tms_status s);
+const char* tms_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TMS_H */

@@ -1,0 +1,435 @@
+"""GPU parity: the HIP library against the CPU oracle on the same seeded inputs.
+
+Tokens must be identical (bit-exact) except at steps the oracle's own top-two
+margin explains (see tests/gpu_util.py); logits within 2e-3 relative plus the
+fp32 summation bound.  Paths of the library itself (graph loop vs host loop,
+fast vs global trie store, any workgroup split, any batch order, dense+mask vs
+sparse) must agree bit for bit.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import trie_masked_sparse_amd as tms
+from gpu_util import compare, config_case, dev_embedding, gamma, oracle_trie, run_k_pointers, run_step_loop, to_dev
+from synth import CONFIGS, bf16_bits_from_f32, catalog, embedding, random_catalog, stress_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu(oracle_lib):
+    assert torch.cuda.is_available(), "the GPU tests need a GPU"
+    tms.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _rand_table(rng, V, H, dtype, scale=0.02):
+    x = rng.standard_normal((V, H), dtype=np.float32) * np.float32(scale)
+    return bf16_bits_from_f32(x) if dtype == "bf16" else x
+
+
+def _rand_hidden(rng, T, B, H, dtype):
+    x = rng.standard_normal((T, B, H), dtype=np.float32)
+    return bf16_bits_from_f32(x) if dtype == "bf16" else x
+
+
+# ---------------------------------------------------------------------------
+# The five workloads
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cid", ["tiny", "product", "product_deep", "structured", "unstructured"])
+def test_config_parity(cid):
+    c, otr, T, hid = config_case(cid)
+    trie = tms.Trie(catalog(cid), c.vocab, c.sep, c.stop)
+    st = tms.State(trie, c.batch, c.k, dev_embedding(cid))
+    hd = to_dev(hid)
+    tok_g, len_g, ent_g = run_k_pointers(st, hd)
+    assert (st.status() == 0).all()
+    ref = oracle.decode(otr, c.k, embedding(cid), hid)
+    assert (ref["status"] == 0).all()
+    flips = compare(tok_g, ref, c.hidden, None, len_g, ent_g, where=cid)
+    # the host-driven loop: identical tokens, logits within tolerance
+    st.reset()
+    tok_h, lg_h = run_step_loop(st, hd)
+    assert np.array_equal(tok_h, tok_g)
+    compare(tok_h, ref, c.hidden, lg_h, where=cid + "/host")
+    print(f"{cid}: path={trie.info['path']} nodes={trie.info['n_nodes']} tie flips={flips}")
+    st.close()
+    trie.close()
+
+
+def test_large_parity_sampled():
+    """Large workload at full size (B=256, H=4096, 100k entries, global path);
+    the oracle decodes a seeded sample of 24 sequences."""
+    cid = "large"
+    c, otr, T, hid = config_case(cid)
+    trie = tms.Trie(catalog(cid), c.vocab, c.sep, c.stop)
+    assert trie.info["path"] == tms.PATH_GLOBAL
+    st = tms.State(trie, c.batch, c.k, dev_embedding(cid))
+    hd = to_dev(hid)
+    tok_g, len_g, ent_g = run_k_pointers(st, hd)
+    assert (st.status() == 0).all()
+    idx = np.sort(np.random.Generator(np.random.PCG64(77)).choice(c.batch, 24, replace=False))
+    ref = oracle.decode(otr, c.k, embedding(cid), np.ascontiguousarray(hid[:, idx, :]))
+    flips = compare(tok_g[idx], ref, c.hidden, None, len_g[idx], ent_g[idx], where=cid)
+    # every sequence, sampled or not: a valid answer (exactly k distinct entries)
+    for b in range(c.batch):
+        e = ent_g[b]
+        assert len(set(e.tolist())) == c.k and (e >= 0).all()
+    print(f"large: tie flips={flips}")
+    st.close()
+    trie.close()
+
+
+# ---------------------------------------------------------------------------
+# Small random cases: ragged hidden sizes, both store paths, prefix pairs
+# ---------------------------------------------------------------------------
+
+CASES = [("f32", 100), ("f32", 256), ("f32", 300), ("f32", 4096), ("bf16", 8), ("bf16", 520), ("bf16", 1000),
+         ("bf16", 2048), ("bf16", 4096), ("bf16", 8192)]
+
+
+@pytest.mark.parametrize("dtype,H", CASES)
+@pytest.mark.parametrize("path", [tms.PATH_FAST, tms.PATH_GLOBAL])
+def test_random_catalog_parity(dtype, H, path):
+    rng = np.random.Generator(np.random.PCG64(H * 7 + path))
+    V = 700
+    sep, stop = (V - 2, V - 1) if (H // 4) % 2 == 0 else (3, 500)
+    ids = [v for v in range(V) if v not in (sep, stop)]
+    # small id range -> heavy prefix sharing and prefix pairs
+    cat = [[ids[t] for t in e] for e in random_catalog(H + path, 60, 6, 24)]
+    B, k = 7, 4
+    otr = oracle.Trie(cat, V, sep, stop)
+    T = k * (otr.max_depth + 1)
+    emb = _rand_table(rng, V, H, dtype)
+    hid = _rand_hidden(rng, T, B, H, dtype)
+    trie = tms.Trie(cat, V, sep, stop, path=path)
+    st = tms.State(trie, B, k, to_dev(emb))
+    hd = to_dev(hid)
+    tok_g, len_g, ent_g = run_k_pointers(st, hd)
+    ref = oracle.decode(otr, k, emb, hid)
+    compare(tok_g, ref, H, None, len_g, ent_g, where=f"{dtype}/{H}/{path}")
+    st.reset()
+    tok_h, lg_h = run_step_loop(st, hd)
+    assert np.array_equal(tok_h, tok_g)
+    compare(tok_h, ref, H, lg_h, where=f"{dtype}/{H}/{path}/host")
+
+
+@pytest.mark.parametrize("fan,path", [(250, tms.PATH_FAST), (250, tms.PATH_GLOBAL), (650, tms.PATH_GLOBAL)])
+def test_wide_nodes(fan, path):
+    """A root with hundreds of edges (several edge batches per wavefront)."""
+    rng = np.random.Generator(np.random.PCG64(fan))
+    V, H, B, k = 1024, 512, 9, 3
+    firsts = rng.choice(V - 2, size=fan, replace=False)
+    cat = [[int(f)] + [int(x) for x in rng.integers(0, V - 2, size=int(rng.integers(0, 3)))] for f in firsts]
+    otr = oracle.Trie(cat, V, V - 2, V - 1)
+    T = k * (otr.max_depth + 1)
+    emb = _rand_table(rng, V, H, "bf16")
+    hid = _rand_hidden(rng, T, B, H, "bf16")
+    trie = tms.Trie(cat, V, V - 2, V - 1, path=path)
+    st = tms.State(trie, B, k, to_dev(emb))
+    tok_h, lg_h = run_step_loop(st, to_dev(hid))
+    compare(tok_h, oracle.decode(otr, k, emb, hid), H, lg_h, where=f"wide{fan}")
+
+
+def test_exact_ties_lower_id_wins():
+    """Legal tokens with identical rows tie exactly; the lower id must win."""
+    rng = np.random.Generator(np.random.PCG64(3))
+    V, H = 512, 256
+    emb = _rand_table(rng, V, H, "bf16")
+    toks = sorted(rng.choice(V - 2, size=40, replace=False).tolist())
+    for a in (5, 9, 17):
+        emb[toks[a]] = emb[toks[30]]
+    cat = [[t] for t in toks]
+    k = 4
+    h = emb[toks[30]].copy()
+    hid = np.broadcast_to(h, (2 * k, 2, H)).copy()
+    for path in (tms.PATH_FAST, tms.PATH_GLOBAL):
+        trie = tms.Trie(cat, V, V - 2, V - 1, path=path)
+        st = tms.State(trie, 2, k, to_dev(emb))
+        tok, ln, ent = run_k_pointers(st, to_dev(hid))
+        for b in range(2):
+            assert list(tok[b][::2]) == [toks[5], toks[9], toks[17], toks[30]]
+    ref = oracle.decode(oracle.Trie(cat, V, V - 2, V - 1), k, emb, hid)
+    compare(tok, ref, H, where="ties")
+
+
+def test_zero_hidden_lexicographic():
+    """h = 0: every logit is +0, so the answer is the lexicographic minimum."""
+    cid = "structured"
+    c, otr, T, hid = config_case(cid, B=4)
+    zero = np.zeros_like(hid)
+    trie = tms.Trie(catalog(cid), c.vocab, c.sep, c.stop)
+    st = tms.State(trie, 4, c.k, dev_embedding(cid))
+    tok, lg = run_step_loop(st, to_dev(zero))
+    ref = oracle.decode(otr, c.k, embedding(cid), zero)
+    assert np.array_equal(tok, ref["tokens"])
+    live = lg[tok >= 0]
+    assert np.all(live == 0.0) and not np.any(np.signbit(live))
+
+
+# ---------------------------------------------------------------------------
+# Bit identity between the library's own paths
+# ---------------------------------------------------------------------------
+
+def test_paths_splits_graph_and_shuffle_identical():
+    cid = "structured"
+    c, otr, T, hid = config_case(cid, B=16)
+    hd = to_dev(hid)
+    emb = dev_embedding(cid)
+    base = None
+    for path in (tms.PATH_FAST, tms.PATH_GLOBAL):
+        trie = tms.Trie(catalog(cid), c.vocab, c.sep, c.stop, path=path)
+        st = tms.State(trie, 16, c.k, emb)
+        for split in (1, 2, 3, 8, 0):
+            tms.state_set_split(st.h, split)
+            st.reset()
+            tok, lg = run_step_loop(st, hd)
+            if base is None:
+                base = (tok, lg)
+            assert np.array_equal(tok, base[0]), (path, split)
+            assert np.array_equal(lg, base[1], equal_nan=True), (path, split)
+            # graph replays, with eager work and syncs in between
+            for rep in range(3):
+                st.reset()
+                torch.cuda.synchronize()
+                g_tok, g_len, g_ent = run_k_pointers(st, hd)
+                assert np.array_equal(g_tok, base[0]), (path, split, rep)
+        st.close()
+        trie.close()
+    # batch shuffle: permuting the sequences permutes the outputs, nothing else
+    perm = np.random.Generator(np.random.PCG64(1)).permutation(16)
+    trie = tms.Trie(catalog(cid), c.vocab, c.sep, c.stop)
+    st = tms.State(trie, 16, c.k, emb)
+    tok, lg = run_step_loop(st, to_dev(np.ascontiguousarray(hid[:, perm, :])))
+    assert np.array_equal(tok, base[0][perm])
+    assert np.array_equal(lg, base[1][perm], equal_nan=True)
+
+
+def test_two_tries_no_contamination():
+    """Interleaved steps on two tries and two states give the same results as
+    running each alone (each grammar owns its store)."""
+    outs = {}
+    for cid in ("product", "structured"):
+        c, otr, T, hid = config_case(cid, B=4)
+        trie = tms.Trie(catalog(cid), c.vocab, c.sep, c.stop)
+        st = tms.State(trie, 4, c.k, dev_embedding(cid))
+        outs[cid] = (run_step_loop(st, to_dev(hid)), trie, st, to_dev(hid), T)
+    (pa, ta, sa, ha, Ta), (pb, tb, sb, hb, Tb) = outs["product"], outs["structured"]
+    sa.reset()
+    sb.reset()
+    toks = {n: torch.empty((T, 4), dtype=torch.int32, device="cuda") for n, T in (("a", Ta), ("b", Tb))}
+    for t in range(max(Ta, Tb)):
+        if t < Ta:
+            tms.decode_step_sparse(sa.h, ha[t], toks["a"][t])
+        if t < Tb:
+            tms.decode_step_sparse(sb.h, hb[t], toks["b"][t])
+    torch.cuda.synchronize()
+    assert np.array_equal(toks["a"].cpu().numpy().T, pa[0])
+    assert np.array_equal(toks["b"].cpu().numpy().T, pb[0])
+
+
+# ---------------------------------------------------------------------------
+# Dense + mask cross-check
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cid,B", [("tiny", 1), ("product", 1), ("structured", 8), ("unstructured", 4)])
+def test_dense_masked_matches_sparse(cid, B):
+    c, otr, T, hid = config_case(cid, B=B)
+    trie = tms.Trie(catalog(cid), c.vocab, c.sep, c.stop)
+    st = tms.State(trie, B, c.k, dev_embedding(cid))
+    hd = to_dev(hid)
+    s_tok, s_lg = run_step_loop(st, hd)
+    st.reset()
+    full = torch.zeros((T, B, c.vocab), dtype=torch.float32, device="cuda") if B == 1 else None
+    d_tok, d_lg = run_step_loop(st, hd, dense=True, full=full)
+    # same per-row arithmetic: identical tokens and identical logits
+    assert np.array_equal(d_tok, s_tok)
+    assert np.array_equal(d_lg, s_lg, equal_nan=True)
+    ref = oracle.decode(otr, c.k, embedding(cid), hid)
+    compare(d_tok, ref, c.hidden, d_lg, where=cid + "/dense")
+    if full is not None:
+        fl = full.cpu().numpy()
+        emb_np = embedding(cid)
+        rng = np.random.Generator(np.random.PCG64(9))
+        for t in (0, 1, T // 2):
+            rows = np.arange(c.vocab) if c.vocab <= 8192 else rng.choice(c.vocab, 2048, replace=False)
+            for v in rows:
+                want, sa = oracle.logit(emb_np, int(v), hid[t, 0])
+                tol = 2e-3 * abs(want) + gamma(c.hidden + 1) * sa
+                assert abs(float(fl[t, 0, v]) - want) <= tol, (cid, t, v)
+
+
+# ---------------------------------------------------------------------------
+# Materialiser, advance and state against the oracle under teacher forcing
+# ---------------------------------------------------------------------------
+
+def _forced_walk(cat, V, sep, stop, k, B, path, seed, check_live=True):
+    otr = oracle.Trie(cat, V, sep, stop)
+    trie = tms.Trie(cat, V, sep, stop, path=path)
+    emb = torch.zeros((V, 8), dtype=torch.float32, device="cuda")
+    st = tms.State(trie, B, k, emb)
+    orefs = [oracle.State(otr, k) for _ in range(B)]
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cap = trie.info["cap"]
+    legal = torch.zeros((B, cap), dtype=torch.int32, device="cuda")
+    nleg = torch.zeros(B, dtype=torch.int32, device="cuda")
+    forced = torch.zeros(B, dtype=torch.int32, device="cuda")
+    T = k * (otr.max_depth + 1)
+    for step in range(T + 1):
+        tms.legal_set(st.h, legal, nleg)
+        torch.cuda.synchronize()
+        lg, nl = legal.cpu().numpy(), nleg.cpu().numpy()
+        choice = np.full(B, -1, np.int32)
+        for b in range(B):
+            want = orefs[b].legal()
+            if want is None:
+                assert nl[b] == -1, (step, b)
+                continue
+            assert list(lg[b, :nl[b]]) == list(want[0]), (step, b)
+            choice[b] = int(want[0][rng.integers(0, len(want[0]))])
+        if (choice < 0).all():
+            break
+        forced.copy_(torch.from_numpy(choice))
+        tms.advance_forced(st.h, forced)
+        for b in range(B):
+            if choice[b] >= 0:
+                assert orefs[b].advance(int(choice[b])) == oracle.OK
+        ex = st.export(live=check_live)
+        for b in range(B):
+            oi = orefs[b].info()
+            got = (ex["node"][b], ex["depth"][b], ex["done"][b], ex["finished"][b], ex["status"][b], ex["n_emitted"][b])
+            assert got == (oi["node"], oi["depth"], oi["done"], oi["finished"], oi["status"], oi["n_emitted"]), (step, b)
+            assert list(ex["entries"][b]) == list(orefs[b].entries())
+            if check_live:
+                assert np.array_equal(ex["live"][b], orefs[b].live()), (step, b)
+    assert all(o.info()["finished"] for o in orefs)
+
+
+@pytest.mark.parametrize("path", [tms.PATH_FAST, tms.PATH_GLOBAL])
+def test_teacher_forced_small(path):
+    cases = [([[1], [1, 2], [1, 2, 3], [4]], 16, 14, 15, 3), ([[3, 3], [3], [3, 3, 3]], 16, 0, 15, 3),
+             ([[5, 6], [5], [7], [5, 6, 7]], 16, 15, 1, 4)]
+    for seed in range(12):
+        cat = random_catalog(seed, 12, 4, 6)
+        cases.append((cat, 16, 14, 15, 1 + seed % 4))
+    for i, (cat, V, sep, stop, k) in enumerate(cases):
+        _forced_walk(cat, V, sep, stop, min(k, len(cat)), 6, path, i)
+
+
+def test_teacher_forced_structured():
+    c = CONFIGS["structured"]
+    _forced_walk(catalog("structured"), c.vocab, c.sep, c.stop, c.k, 16, tms.PATH_AUTO, 5)
+
+
+# ---------------------------------------------------------------------------
+# Fail loudly
+# ---------------------------------------------------------------------------
+
+def test_device_errors_are_sticky_and_isolated():
+    c, otr, T, hid = config_case("tiny", B=3)
+    trie = tms.Trie(catalog("tiny"), c.vocab, c.sep, c.stop)
+    st = tms.State(trie, 3, c.k, dev_embedding("tiny"))
+    csr = trie.csr()
+    # empty mask for sequence 1: no live pointer below any root edge
+    for e in range(csr["begin"][0], csr["begin"][1]):
+        tms.debug_set_live(st.h, 1, e, 0)
+    tok, lg = run_step_loop(st, to_dev(hid))
+    status = st.status()
+    assert list(status) == [0, tms.ERR_EMPTY_MASK, 0]
+    assert (tok[1] == -1).all() and np.isnan(lg[1]).all()
+    ref = oracle.decode(otr, c.k, embedding("tiny"), hid[:, [0, 2], :])
+    compare(tok[[0, 2]], ref, c.hidden, lg[[0, 2]], where="isolated")
+    with pytest.raises(tms.TmsError) as ei:
+        tms.state_sync_status(st.h, 3, check=True)
+    assert ei.value.code == tms.ERR_EMPTY_MASK
+    # unwalkable forced token
+    st.reset()
+    forced = torch.tensor([c.stop, -1, c.sep], dtype=torch.int32, device="cuda")
+    tms.advance_forced(st.h, forced)
+    assert list(st.status()) == [tms.ERR_NOT_WALKABLE, 0, tms.ERR_NOT_WALKABLE]
+    # the trie cannot be freed while a state uses it
+    with pytest.raises(tms.TmsError) as ei:
+        tms.trie_free(trie.h)
+    assert ei.value.code == tms.ERR_BUSY
+    st.close()
+    trie.close()
+
+
+def test_host_side_errors():
+    c = CONFIGS["unstructured"]
+    emb = dev_embedding("unstructured")
+    with pytest.raises(tms.TmsError) as ei:
+        tms.Trie(catalog("unstructured"), c.vocab, c.sep, c.stop, path=tms.PATH_FAST)
+    assert ei.value.code == tms.ERR_FANOUT
+    trie = tms.Trie(catalog("unstructured"), c.vocab, c.sep, c.stop)
+    assert trie.info["path"] == tms.PATH_GLOBAL
+    with pytest.raises(tms.TmsError) as ei:
+        tms.State(trie, 2, 1001, emb)
+    assert ei.value.code == tms.ERR_K
+    with pytest.raises(tms.TmsError) as ei:
+        tms.State(trie, 2, 2, emb.reshape(-1)[: c.vocab * 2044].view(c.vocab, 2044))
+    assert ei.value.code in (tms.ERR_INVALID_ARG,)
+    st = tms.State(trie, 2, 2, emb)
+    short = torch.zeros((3, 2, c.hidden), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(tms.TmsError) as ei:
+        tms.decode_k_pointers(st.h, short, torch.zeros((2, 3), dtype=torch.int32, device="cuda"))
+    assert ei.value.code == tms.ERR_INVALID_ARG
+    st.close()
+    trie.close()
+
+
+# ---------------------------------------------------------------------------
+# The sparse head on its own
+# ---------------------------------------------------------------------------
+
+def test_gather_gemv_rows():
+    cid = "product"
+    emb_np, emb = embedding(cid), dev_embedding(cid)
+    V, H = emb_np.shape
+    rng = np.random.Generator(np.random.PCG64(21))
+    B, cap = 6, 300
+    n_rows = np.array([0, 1, 150, 300, 37, 299], np.int32)
+    rows = rng.integers(0, V, size=(B, cap)).astype(np.int32)
+    rows[2, 10] = -5
+    rows[3, 7] = V + 3
+    rows[4, 3] = rows[4, 30]  # duplicate row -> identical logit
+    hid = bf16_bits_from_f32(rng.standard_normal((B, H), dtype=np.float32))
+    out = torch.full((B, cap), 1234.5, dtype=torch.float32, device="cuda")
+    tms.gather_gemv(emb, to_dev(hid), to_dev(rows), to_dev(n_rows), out)
+    o = out.cpu().numpy()
+    for b in range(B):
+        assert (o[b, n_rows[b]:] == 1234.5).all()
+        for j in range(n_rows[b]):
+            r = rows[b, j]
+            if r < 0 or r >= V:
+                assert math.isnan(o[b, j])
+                continue
+            want, sa = oracle.logit(emb_np, int(r), hid[b])
+            assert abs(float(o[b, j]) - want) <= 2e-3 * abs(want) + gamma(H + 1) * sa, (b, j)
+    assert o[4, 3] == o[4, 30]
+
+
+def test_gather_gemv_stress_shape_sampled():
+    """The bandwidth stress shape (64 sequences x 256 distinct rows), sampled."""
+    cid = "product"
+    emb_np, emb = embedding(cid), dev_embedding(cid)
+    V, H = emb_np.shape
+    sets = stress_rows(V, 64, 256, 9)
+    rng = np.random.Generator(np.random.PCG64(8))
+    hid = bf16_bits_from_f32(rng.standard_normal((64, H), dtype=np.float32))
+    out = torch.zeros((64, 256), dtype=torch.float32, device="cuda")
+    hd = to_dev(hid)
+    n = torch.full((64,), 256, dtype=torch.int32, device="cuda")
+    for si in (0, 8):
+        tms.gather_gemv(emb, hd, to_dev(np.ascontiguousarray(sets[si])), n, out)
+        o = out.cpu().numpy()
+        for _ in range(300):
+            b, j = int(rng.integers(0, 64)), int(rng.integers(0, 256))
+            want, sa = oracle.logit(emb_np, int(sets[si, b, j]), hid[b])
+            assert abs(float(o[b, j]) - want) <= 2e-3 * abs(want) + gamma(H + 1) * sa

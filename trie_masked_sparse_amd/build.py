@@ -1,0 +1,49 @@
+"""Compile the HIP library in-tree: trie_masked_sparse_amd/libtms.so (gfx950).
+
+Run as ``python -m trie_masked_sparse_amd.build``.  Needs hipcc, no GPU.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libtms.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+# Packed fp32 instructions are disabled for all device code.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{os.path.join(ROOT, 'include')}"]
+
+
+def _run(cmd):
+    print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+
+
+def build(verbose: bool = True) -> str:
+    objdir = os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    for src, lang in (("kernels.hip", "hip"), ("api.cpp", "c++"), ("trie_build.cpp", "c++")):
+        obj = os.path.join(objdir, src + ".o")
+        cmd = [HIPCC, f"--offload-arch={ARCH}", *COMMON, "-c", "-x", lang, os.path.join(CSRC, src), "-o", obj]
+        if lang == "hip":
+            cmd[1:1] = DEVICE_FLAGS
+        else:
+            cmd[1:1] = ["-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"]
+        _run(cmd)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build()
+    sys.exit(0)

@@ -1,0 +1,521 @@
+// C ABI of the trie-constrained sparse decode library (declared in include/tms.h).
+// Handles own their device memory; decode calls only enqueue kernels on the
+// caller's stream.  The device loop is a hipGraph of T step kernels captured on
+// a private stream and replayed on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/tms.h"
+#include "kernels.h"
+#include "trie_build.h"
+
+struct tms_trie {
+  tms::HostTrie host;
+  int path = TMS_PATH_AUTO;  // FAST or GLOBAL once uploaded
+  int device = -1;
+  void* dmem = nullptr;
+  size_t dbytes = 0;
+  tms::DevTrie dev{};
+  int refs = 0;
+};
+
+struct tms_state {
+  tms_trie* trie = nullptr;
+  int B = 0, k = 0, H = 0, dtype = 0, device = -1;
+  const void* emb = nullptr;
+  void* dmem = nullptr;
+  size_t dbytes = 0;
+  tms::DevState dev{};
+  int split = 1, split_default = 1;
+  bool fast = false;
+  bool use_graph = true;
+  hipStream_t capture = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t gexec = nullptr;
+  const void* g_hidden = nullptr;
+  int32_t g_T = 0;
+  int32_t *g_tokens = nullptr, *g_len = nullptr, *g_entries = nullptr;
+  std::vector<int32_t> host_status;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+tms_status fail(tms_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+tms_status hip_fail(hipError_t e, const char* what) {
+  g_err = std::string(what) + ": " + hipGetErrorString(e);
+  return e == hipErrorOutOfMemory ? TMS_ERR_OOM : TMS_ERR_HIP;
+}
+
+#define TMS_HIP(call, what)                       \
+  do {                                            \
+    hipError_t e_ = (call);                       \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Carve typed sub-buffers out of one allocation.
+struct Carve {
+  size_t off = 0;
+  template <typename T>
+  size_t take(size_t n) {
+    const size_t o = off;
+    off = align256(off + sizeof(T) * std::max<size_t>(n, 1));
+    return o;
+  }
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_size(int dtype) { return dtype == TMS_F32 ? 4 : 2; }
+
+int default_split(int B, int cap) {
+  const int target_waves = 4096;
+  int s = (target_waves + 4 * B - 1) / (4 * B);
+  const int by_cap = std::max(1, (cap + 3) / 4);
+  s = std::min(s, by_cap);
+  return std::max(1, s);
+}
+
+void destroy_graph(tms_state* st) {
+  if (st->gexec) (void)hipGraphExecDestroy(st->gexec);
+  if (st->graph) (void)hipGraphDestroy(st->graph);
+  st->gexec = nullptr;
+  st->graph = nullptr;
+  st->g_hidden = nullptr;
+}
+
+tms::StepIO make_io(const tms_state* st, const void* hidden) {
+  tms::StepIO io{};
+  io.emb = st->emb;
+  io.hidden = hidden;
+  io.H = st->H;
+  io.V = st->trie->host.vocab;
+  return io;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tms_status_str(tms_status s) {
+  switch (s) {
+    case TMS_OK: return "ok";
+    case TMS_ERR_INVALID_ARG: return "invalid argument";
+    case TMS_ERR_CATALOG: return "invalid catalog";
+    case TMS_ERR_FANOUT: return "node fan-out above 256 on the fast path";
+    case TMS_ERR_K: return "k outside [1, K]";
+    case TMS_ERR_EMPTY_MASK: return "empty mask";
+    case TMS_ERR_NOT_WALKABLE: return "token not walkable";
+    case TMS_ERR_NOT_DONE: return "sequence not done";
+    case TMS_ERR_BUSY: return "trie still in use";
+    case TMS_ERR_OOM: return "out of device memory";
+    case TMS_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* tms_last_error(void) { return g_err.c_str(); }
+
+tms_status tms_trie_build(const int32_t* tokens, const int64_t* offsets, int32_t K, int32_t vocab, int32_t sep,
+                          int32_t stop, tms_trie** out) {
+  if (!out) return fail(TMS_ERR_INVALID_ARG, "out is null");
+  *out = nullptr;
+  tms_trie* t = new tms_trie();
+  std::string err;
+  const int rc = tms::build_trie(tokens, offsets, K, vocab, sep, stop, &t->host, &err);
+  if (rc != 0) {
+    delete t;
+    return fail(static_cast<tms_status>(rc), err);
+  }
+  *out = t;
+  return TMS_OK;
+}
+
+tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_t K, int32_t vocab, int32_t sep,
+                           int32_t stop, tms_path path, void* stream, tms_trie** out) {
+  if (path != TMS_PATH_AUTO && path != TMS_PATH_FAST && path != TMS_PATH_GLOBAL)
+    return fail(TMS_ERR_INVALID_ARG, "unknown path");
+  tms_trie* t = nullptr;
+  tms_status rc = tms_trie_build(tokens, offsets, K, vocab, sep, stop, &t);
+  if (rc != TMS_OK) return rc;
+  const tms::HostTrie& h = t->host;
+  // hot CSR bytes read by the step: begin, tok, child
+  const int64_t hot = 4ll * (h.n_nodes + 1) + 8ll * h.n_edges;
+  const bool fast_ok = h.cap <= 256 && hot <= 65536;
+  if (path == TMS_PATH_FAST && h.cap > 256) {
+    delete t;
+    return fail(TMS_ERR_FANOUT, "fast path needs every node to have at most 256 edges; widest has " +
+                                    std::to_string(h.cap));
+  }
+  t->path = path == TMS_PATH_GLOBAL ? TMS_PATH_GLOBAL
+            : path == TMS_PATH_FAST ? TMS_PATH_FAST
+            : (fast_ok ? TMS_PATH_FAST : TMS_PATH_GLOBAL);
+  const int32_t live_stride = (h.n_edges + 3) & ~3;
+  Carve c;
+  const size_t o_begin = c.take<int32_t>(h.n_nodes + 1);
+  const size_t o_entry = c.take<int32_t>(h.n_nodes);
+  const size_t o_tok = c.take<int32_t>(h.n_edges);
+  const size_t o_child = c.take<int32_t>(h.n_edges);
+  const size_t o_live0 = c.take<int32_t>(live_stride);
+  hipError_t e = hipGetDevice(&t->device);
+  if (e == hipSuccess) e = hipMalloc(&t->dmem, c.off);
+  if (e != hipSuccess) {
+    delete t;
+    return hip_fail(e, "trie upload");
+  }
+  t->dbytes = c.off;
+  char* base = static_cast<char*>(t->dmem);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::vector<int32_t> live0(live_stride, 0);
+  std::copy(h.live0.begin(), h.live0.end(), live0.begin());
+  e = hipMemcpyAsync(base + o_begin, h.begin.data(), 4 * h.begin.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(base + o_entry, h.entry.data(), 4 * h.entry.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(base + o_tok, h.tok.data(), 4 * h.tok.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(base + o_child, h.child.data(), 4 * h.child.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(base + o_live0, live0.data(), 4 * live0.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    (void)hipFree(t->dmem);
+    delete t;
+    return hip_fail(e, "trie upload copy");
+  }
+  tms::DevTrie& d = t->dev;
+  d.begin = reinterpret_cast<const int32_t*>(base + o_begin);
+  d.entry = reinterpret_cast<const int32_t*>(base + o_entry);
+  d.tok = reinterpret_cast<const int32_t*>(base + o_tok);
+  d.child = reinterpret_cast<const int32_t*>(base + o_child);
+  d.live0 = reinterpret_cast<const int32_t*>(base + o_live0);
+  d.n_nodes = h.n_nodes;
+  d.n_edges = h.n_edges;
+  d.n_entries = h.n_entries;
+  d.cap = h.cap;
+  d.max_depth = h.max_depth;
+  d.sep = h.sep;
+  d.stop = h.stop;
+  d.vocab = h.vocab;
+  d.live_stride = live_stride;
+  *out = t;
+  return TMS_OK;
+}
+
+tms_status tms_trie_info_get(const tms_trie* t, tms_trie_info* info) {
+  if (!t || !info) return fail(TMS_ERR_INVALID_ARG, "null argument");
+  const tms::HostTrie& h = t->host;
+  info->n_nodes = h.n_nodes;
+  info->n_edges = h.n_edges;
+  info->n_entries = h.n_entries;
+  info->cap = h.cap;
+  info->max_depth = h.max_depth;
+  info->sep = h.sep;
+  info->stop = h.stop;
+  info->vocab = h.vocab;
+  info->path = t->path;
+  info->device_bytes = static_cast<int64_t>(t->dbytes);
+  return TMS_OK;
+}
+
+tms_status tms_trie_export_csr(const tms_trie* t, int32_t* begin, int32_t* entry, int32_t* tok, int32_t* child,
+                               int32_t* live0) {
+  if (!t) return fail(TMS_ERR_INVALID_ARG, "null trie");
+  const tms::HostTrie& h = t->host;
+  if (begin) std::memcpy(begin, h.begin.data(), 4 * h.begin.size());
+  if (entry) std::memcpy(entry, h.entry.data(), 4 * h.entry.size());
+  if (tok) std::memcpy(tok, h.tok.data(), 4 * h.tok.size());
+  if (child) std::memcpy(child, h.child.data(), 4 * h.child.size());
+  if (live0) std::memcpy(live0, h.live0.data(), 4 * h.live0.size());
+  return TMS_OK;
+}
+
+tms_status tms_trie_free(tms_trie* t) {
+  if (!t) return TMS_OK;
+  if (t->refs > 0) return fail(TMS_ERR_BUSY, std::to_string(t->refs) + " state(s) still use this trie");
+  if (t->dmem) (void)hipFree(t->dmem);
+  delete t;
+  return TMS_OK;
+}
+
+tms_status tms_state_create(tms_trie* trie, int32_t B, int32_t k, const void* emb, tms_dtype dtype, int32_t H,
+                            void* stream, tms_state** out) {
+  if (!out) return fail(TMS_ERR_INVALID_ARG, "out is null");
+  *out = nullptr;
+  if (!trie || !trie->dmem) return fail(TMS_ERR_INVALID_ARG, "trie has no device copy (use tms_trie_upload)");
+  if (B < 1 || B > 65535) return fail(TMS_ERR_INVALID_ARG, "B must be in [1, 65535]");
+  if (k < 1 || k > trie->host.n_entries)
+    return fail(TMS_ERR_K, "k = " + std::to_string(k) + " outside [1, " + std::to_string(trie->host.n_entries) + "]");
+  if (dtype != TMS_F32 && dtype != TMS_BF16) return fail(TMS_ERR_INVALID_ARG, "dtype must be fp32 or bf16");
+  if (!emb || !aligned16(emb)) return fail(TMS_ERR_INVALID_ARG, "embedding pointer null or not 16-byte aligned");
+  if (tms::chunks_for(dtype, H) == 0)
+    return fail(TMS_ERR_INVALID_ARG, "H must be a positive multiple of " + std::to_string(16 / elem_size(dtype)) +
+                                         " and at most " + std::to_string(dtype == TMS_F32 ? 4096 : 8192));
+  int dev = -1;
+  TMS_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev != trie->device) return fail(TMS_ERR_INVALID_ARG, "trie was uploaded on another device");
+
+  tms_state* st = new tms_state();
+  st->trie = trie;
+  st->B = B;
+  st->k = k;
+  st->H = H;
+  st->dtype = dtype;
+  st->emb = emb;
+  st->device = dev;
+  st->fast = trie->path == TMS_PATH_FAST;
+  const tms::HostTrie& h = trie->host;
+  const int32_t path_stride = std::max(1, h.max_depth);
+  const int32_t spent_words = (h.n_entries + 31) / 32;
+  const int32_t mask_words = (h.vocab + 31) / 32;
+  const int64_t live_stride = trie->dev.live_stride;
+  Carve c;
+  const size_t o_node = c.take<int32_t>(B), o_depth = c.take<int32_t>(B), o_done = c.take<int32_t>(B);
+  const size_t o_status = c.take<int32_t>(B), o_fin = c.take<int32_t>(B), o_nemit = c.take<int32_t>(B);
+  const size_t o_path = c.take<int32_t>(size_t(B) * path_stride);
+  const size_t o_entries = c.take<int32_t>(size_t(B) * k);
+  const size_t o_key = c.take<unsigned long long>(B);
+  const size_t o_arrive = c.take<uint32_t>(B);
+  const size_t o_live = c.take<int32_t>(size_t(B) * live_stride);
+  const size_t o_spent = c.take<uint32_t>(size_t(B) * spent_words);
+  const size_t o_mask = c.take<uint32_t>(size_t(B) * mask_words);
+  hipError_t e = hipMalloc(&st->dmem, c.off);
+  if (e != hipSuccess) {
+    delete st;
+    return hip_fail(e, "state allocation");
+  }
+  st->dbytes = c.off;
+  char* base = static_cast<char*>(st->dmem);
+  tms::DevState& d = st->dev;
+  d.B = B;
+  d.k = k;
+  d.path_stride = path_stride;
+  d.spent_words = spent_words;
+  d.mask_words = mask_words;
+  d.node = reinterpret_cast<int32_t*>(base + o_node);
+  d.depth = reinterpret_cast<int32_t*>(base + o_depth);
+  d.done = reinterpret_cast<int32_t*>(base + o_done);
+  d.status = reinterpret_cast<int32_t*>(base + o_status);
+  d.finished = reinterpret_cast<int32_t*>(base + o_fin);
+  d.nemit = reinterpret_cast<int32_t*>(base + o_nemit);
+  d.path = reinterpret_cast<int32_t*>(base + o_path);
+  d.entries = reinterpret_cast<int32_t*>(base + o_entries);
+  d.key = reinterpret_cast<unsigned long long*>(base + o_key);
+  d.arrive = reinterpret_cast<uint32_t*>(base + o_arrive);
+  d.live = reinterpret_cast<int32_t*>(base + o_live);
+  d.spent = reinterpret_cast<uint32_t*>(base + o_spent);
+  d.mask = reinterpret_cast<uint32_t*>(base + o_mask);
+  st->split_default = default_split(B, h.cap);
+  st->split = st->split_default;
+  if (const char* env = std::getenv("TMS_SPLIT")) {
+    const int v = std::atoi(env);
+    if (v > 0) st->split = v;
+  }
+  if (const char* env = std::getenv("TMS_GRAPH")) st->use_graph = std::atoi(env) != 0;
+  st->host_status.assign(B, 0);
+  e = hipStreamCreateWithFlags(&st->capture, hipStreamNonBlocking);
+  if (e != hipSuccess) {
+    (void)hipFree(st->dmem);
+    delete st;
+    return hip_fail(e, "capture stream");
+  }
+  trie->refs++;
+  *out = st;
+  tms_status rc = tms_state_reset(st, stream);
+  if (rc != TMS_OK) {
+    tms_state_free(st);
+    *out = nullptr;
+    return rc;
+  }
+  return TMS_OK;
+}
+
+tms_status tms_state_reset(tms_state* st, void* stream) {
+  if (!st) return fail(TMS_ERR_INVALID_ARG, "null state");
+  TMS_HIP(tms::launch_reset(st->trie->dev, st->dev, static_cast<hipStream_t>(stream)), "reset launch");
+  return TMS_OK;
+}
+
+tms_status tms_state_sync_status(tms_state* st, int32_t* host_status, void* stream) {
+  if (!st) return fail(TMS_ERR_INVALID_ARG, "null state");
+  TMS_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "stream synchronize");
+  TMS_HIP(hipMemcpy(st->host_status.data(), st->dev.status, 4 * st->B, hipMemcpyDeviceToHost), "status copy");
+  if (host_status) std::memcpy(host_status, st->host_status.data(), 4 * st->B);
+  for (int s = 0; s < st->B; ++s) {
+    if (st->host_status[s] != 0) {
+      g_err = "sequence " + std::to_string(s) + ": " + tms_status_str(static_cast<tms_status>(st->host_status[s]));
+      return static_cast<tms_status>(st->host_status[s]);
+    }
+  }
+  return TMS_OK;
+}
+
+tms_status tms_state_export(tms_state* st, int32_t* node, int32_t* depth, int32_t* done, int32_t* status,
+                            int32_t* finished, int32_t* n_emitted, int32_t* entries, int32_t* live, void* stream) {
+  if (!st) return fail(TMS_ERR_INVALID_ARG, "null state");
+  TMS_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "stream synchronize");
+  const size_t b4 = 4 * size_t(st->B);
+  const tms::DevState& d = st->dev;
+  if (node) TMS_HIP(hipMemcpy(node, d.node, b4, hipMemcpyDeviceToHost), "export");
+  if (depth) TMS_HIP(hipMemcpy(depth, d.depth, b4, hipMemcpyDeviceToHost), "export");
+  if (done) TMS_HIP(hipMemcpy(done, d.done, b4, hipMemcpyDeviceToHost), "export");
+  if (status) TMS_HIP(hipMemcpy(status, d.status, b4, hipMemcpyDeviceToHost), "export");
+  if (finished) TMS_HIP(hipMemcpy(finished, d.finished, b4, hipMemcpyDeviceToHost), "export");
+  if (n_emitted) TMS_HIP(hipMemcpy(n_emitted, d.nemit, b4, hipMemcpyDeviceToHost), "export");
+  if (entries) TMS_HIP(hipMemcpy(entries, d.entries, b4 * st->k, hipMemcpyDeviceToHost), "export");
+  if (live) {
+    const int E = st->trie->host.n_edges;
+    const int64_t ls = st->trie->dev.live_stride;
+    TMS_HIP(hipMemcpy2D(live, 4 * size_t(E), d.live, 4 * size_t(ls), 4 * size_t(E), st->B, hipMemcpyDeviceToHost),
+            "export live");
+  }
+  return TMS_OK;
+}
+
+tms_status tms_state_free(tms_state* st) {
+  if (!st) return TMS_OK;
+  destroy_graph(st);
+  if (st->capture) (void)hipStreamDestroy(st->capture);
+  if (st->dmem) (void)hipFree(st->dmem);
+  if (st->trie) st->trie->refs--;
+  delete st;
+  return TMS_OK;
+}
+
+tms_status tms_decode_step_sparse(tms_state* st, const void* hidden, int32_t* tok, float* logit, void* stream) {
+  if (!st) return fail(TMS_ERR_INVALID_ARG, "null state");
+  if (!hidden || !aligned16(hidden)) return fail(TMS_ERR_INVALID_ARG, "hidden null or not 16-byte aligned");
+  tms::StepIO io = make_io(st, hidden);
+  io.out_tok = tok;
+  io.out_logit = logit;
+  TMS_HIP(tms::launch_step_sparse(st->trie->dev, st->dev, io, st->dtype, st->fast, st->split,
+                                  static_cast<hipStream_t>(stream)),
+          "sparse step launch");
+  return TMS_OK;
+}
+
+tms_status tms_decode_step_dense_masked(tms_state* st, const void* hidden, int32_t* tok, float* logit,
+                                        float* full_logits, void* stream) {
+  if (!st) return fail(TMS_ERR_INVALID_ARG, "null state");
+  if (!hidden || !aligned16(hidden)) return fail(TMS_ERR_INVALID_ARG, "hidden null or not 16-byte aligned");
+  if (size_t(st->dev.mask_words) * 4 > 65536) return fail(TMS_ERR_INVALID_ARG, "vocabulary too large for the dense mask");
+  tms::StepIO io = make_io(st, hidden);
+  io.out_tok = tok;
+  io.out_logit = logit;
+  TMS_HIP(tms::launch_dense_step(st->trie->dev, st->dev, io, st->dtype, full_logits, 1024,
+                                 static_cast<hipStream_t>(stream)),
+          "dense step launch");
+  return TMS_OK;
+}
+
+tms_status tms_decode_k_pointers(tms_state* st, const void* hidden_seq, int32_t T, int32_t* tokens, int32_t* len,
+                                 int32_t* entries, void* stream) {
+  if (!st) return fail(TMS_ERR_INVALID_ARG, "null state");
+  if (!hidden_seq || !aligned16(hidden_seq) || !tokens)
+    return fail(TMS_ERR_INVALID_ARG, "hidden_seq or tokens null, or hidden_seq not 16-byte aligned");
+  const int32_t need = st->k * (st->trie->host.max_depth + 1);
+  if (T < need)
+    return fail(TMS_ERR_INVALID_ARG, "T = " + std::to_string(T) + " < k*(max_depth+1) = " + std::to_string(need));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t step_bytes = size_t(st->B) * st->H * elem_size(st->dtype);
+  auto enqueue = [&](hipStream_t q) -> hipError_t {
+    for (int32_t t = 0; t < T; ++t) {
+      tms::StepIO io = make_io(st, static_cast<const char*>(hidden_seq) + step_bytes * t);
+      io.tokens_bt = tokens;
+      io.T = T;
+      io.t = t;
+      hipError_t e = tms::launch_step_sparse(st->trie->dev, st->dev, io, st->dtype, st->fast, st->split, q);
+      if (e != hipSuccess) return e;
+    }
+    return tms::launch_finalize(st->dev, len, entries, q);
+  };
+  if (!st->use_graph) {
+    TMS_HIP(enqueue(s), "step loop launch");
+    return TMS_OK;
+  }
+  const bool same = st->gexec && st->g_hidden == hidden_seq && st->g_T == T && st->g_tokens == tokens &&
+                    st->g_len == len && st->g_entries == entries;
+  if (!same) {
+    destroy_graph(st);
+    TMS_HIP(hipStreamBeginCapture(st->capture, hipStreamCaptureModeRelaxed), "begin capture");
+    const hipError_t le = enqueue(st->capture);
+    hipGraph_t g = nullptr;
+    const hipError_t ce = hipStreamEndCapture(st->capture, &g);
+    if (le != hipSuccess) {
+      if (g) (void)hipGraphDestroy(g);
+      return hip_fail(le, "capture launch");
+    }
+    TMS_HIP(ce, "end capture");
+    st->graph = g;
+    TMS_HIP(hipGraphInstantiate(&st->gexec, g, nullptr, nullptr, 0), "graph instantiate");
+    st->g_hidden = hidden_seq;
+    st->g_T = T;
+    st->g_tokens = tokens;
+    st->g_len = len;
+    st->g_entries = entries;
+  }
+  TMS_HIP(hipGraphLaunch(st->gexec, s), "graph launch");
+  return TMS_OK;
+}
+
+tms_status tms_advance_forced(tms_state* st, const int32_t* tok, void* stream) {
+  if (!st || !tok) return fail(TMS_ERR_INVALID_ARG, "null argument");
+  TMS_HIP(tms::launch_forced(st->trie->dev, st->dev, tok, static_cast<hipStream_t>(stream)), "forced launch");
+  return TMS_OK;
+}
+
+tms_status tms_legal_set(tms_state* st, int32_t* legal_tok, int32_t* n_legal, void* stream) {
+  if (!st || !legal_tok || !n_legal) return fail(TMS_ERR_INVALID_ARG, "null argument");
+  TMS_HIP(tms::launch_legal_set(st->trie->dev, st->dev, legal_tok, n_legal, static_cast<hipStream_t>(stream)),
+          "legal set launch");
+  return TMS_OK;
+}
+
+tms_status tms_gather_gemv(const void* emb, tms_dtype dtype, int32_t V, int32_t H, const void* hidden,
+                           const int32_t* rows, const int32_t* n_rows, int32_t B, int32_t cap, float* out,
+                           void* stream) {
+  if (!emb || !hidden || !rows || !n_rows || !out) return fail(TMS_ERR_INVALID_ARG, "null argument");
+  if (!aligned16(emb) || !aligned16(hidden)) return fail(TMS_ERR_INVALID_ARG, "emb/hidden not 16-byte aligned");
+  if (dtype != TMS_F32 && dtype != TMS_BF16) return fail(TMS_ERR_INVALID_ARG, "dtype must be fp32 or bf16");
+  if (V < 1 || B < 1 || cap < 1 || B > (1 << 24)) return fail(TMS_ERR_INVALID_ARG, "bad sizes");
+  if (tms::chunks_for(dtype, H) == 0) return fail(TMS_ERR_INVALID_ARG, "unsupported H");
+  const int split = default_split(B, cap);
+  if (int64_t(B) * split > (int64_t(1) << 31) - 1) return fail(TMS_ERR_INVALID_ARG, "grid too large");
+  TMS_HIP(tms::launch_gather_gemv(emb, dtype, V, H, hidden, rows, n_rows, B, cap, out, split,
+                                  static_cast<hipStream_t>(stream)),
+          "gather gemv launch");
+  return TMS_OK;
+}
+
+tms_status tms_debug_set_live(tms_state* st, int32_t s, int32_t edge, int32_t value, void* stream) {
+  if (!st) return fail(TMS_ERR_INVALID_ARG, "null state");
+  if (s < 0 || s >= st->B || edge < 0 || edge >= st->trie->host.n_edges)
+    return fail(TMS_ERR_INVALID_ARG, "sequence or edge out of range");
+  TMS_HIP(tms::launch_set_live(st->trie->dev, st->dev, s, edge, value, static_cast<hipStream_t>(stream)),
+          "set live launch");
+  return TMS_OK;
+}
+
+tms_status tms_state_set_split(tms_state* st, int32_t split) {
+  if (!st || split < 0 || split > 4096) return fail(TMS_ERR_INVALID_ARG, "split must be in [0, 4096]");
+  st->split = split == 0 ? st->split_default : split;
+  destroy_graph(st);
+  return TMS_OK;
+}
+
+tms_status tms_state_get_launch(const tms_state* st, int32_t* split, int32_t* grid) {
+  if (!st) return fail(TMS_ERR_INVALID_ARG, "null state");
+  if (split) *split = st->split;
+  if (grid) *grid = st->B * st->split;
+  return TMS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// Plain views of device buffers shared by the host API and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace tms {
+
+// Sequence status codes written by the device (same values as tms_status).
+enum : int32_t { kSeqOk = 0, kSeqEmptyMask = 5, kSeqNotWalkable = 6, kSeqNotDone = 7 };
+enum : int32_t { kChildSep = -1, kChildStop = -2 };
+
+struct DevTrie {
+  const int32_t* begin;  // [n_nodes+1]
+  const int32_t* entry;  // [n_nodes]
+  const int32_t* tok;    // [n_edges]
+  const int32_t* child;  // [n_edges]
+  const int32_t* live0;  // [live_stride], zero padded past n_edges
+  int32_t n_nodes, n_edges, n_entries, cap, max_depth, sep, stop, vocab;
+  int32_t live_stride;   // n_edges rounded up to a multiple of 4
+};
+
+// Struct-of-arrays decode state for B sequences.
+struct DevState {
+  int32_t B, k;
+  int32_t path_stride;   // >= max_depth
+  int32_t spent_words;   // ceil(n_entries / 32)
+  int32_t mask_words;    // ceil(vocab / 32)
+  int32_t* node;         // [B] current trie node
+  int32_t* depth;        // [B] content edges on the current pointer's path
+  int32_t* done;         // [B] pointers completed
+  int32_t* status;       // [B] kSeq* code, sticky
+  int32_t* finished;     // [B] 1 after stop
+  int32_t* nemit;        // [B] tokens emitted since reset
+  int32_t* path;         // [B][path_stride] edge ids root -> node
+  int32_t* entries;      // [B][k] completed catalog indices, -1 unused
+  unsigned long long* key;  // [B] packed (logit, id) argmax slot, 0 = empty
+  uint32_t* arrive;      // [B] workgroups of the current step that finished
+  int32_t* live;         // [B][live_stride]
+  uint32_t* spent;       // [B][spent_words] one bit per catalog entry
+  uint32_t* mask;        // [B][mask_words] dense-path vocabulary bitmask
+};
+
+// Per-step inputs and outputs.
+struct StepIO {
+  const void* emb;       // [V][H]
+  const void* hidden;    // [B][H] for this step
+  int32_t H, V;
+  int32_t* out_tok;      // [B] or null
+  float* out_logit;      // [B] or null
+  int32_t* tokens_bt;    // [B][T] or null: column t receives this step's token
+  int32_t T, t;
+};
+
+// dtype: 0 fp32, 1 bf16.  Every launcher returns hipGetLastError().
+hipError_t launch_reset(const DevTrie& tr, const DevState& st, hipStream_t s);
+hipError_t launch_step_sparse(const DevTrie& tr, const DevState& st, const StepIO& io, int dtype,
+                              bool fast, int split, hipStream_t s);
+hipError_t launch_dense_step(const DevTrie& tr, const DevState& st, const StepIO& io, int dtype,
+                             float* full_logits, int grid, hipStream_t s);
+hipError_t launch_forced(const DevTrie& tr, const DevState& st, const int32_t* forced, hipStream_t s);
+hipError_t launch_legal_set(const DevTrie& tr, const DevState& st, int32_t* legal_tok,
+                            int32_t* n_legal, hipStream_t s);
+hipError_t launch_gather_gemv(const void* emb, int dtype, int32_t V, int32_t H, const void* hidden,
+                              const int32_t* rows, const int32_t* n_rows, int32_t B, int32_t cap,
+                              float* out, int split, hipStream_t s);
+hipError_t launch_finalize(const DevState& st, int32_t* len, int32_t* entries, hipStream_t s);
+hipError_t launch_set_live(const DevTrie& tr, const DevState& st, int32_t seq, int32_t edge,
+                           int32_t value, hipStream_t s);
+
+// Chunks of 16 bytes per lane needed for a row of H elements (0 if too wide).
+int chunks_for(int dtype, int H);
+
+}  // namespace tms

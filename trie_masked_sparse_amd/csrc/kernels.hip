@@ -1,0 +1,652 @@
+// HIP kernels for gfx950 (CDNA4, 64-wide wavefronts): the trie-constrained
+// sparse decode step and its dense-plus-mask cross-check.
+//
+// Sources (web page "Constraint made cheaper than no constraint"):
+//   section "The grammar as a trie over tokens"  - CSR trie, sentinel children;
+//   section "Masked sampling inside the sampler" - filter the node's edges,
+//     argmax with ties to the lower token id, fail loudly on an empty mask or
+//     an unwalkable winner, exactly-k rule, live counts decremented along the
+//     completed pointer's path, per-terminal spent flag;
+//   section "The sparse output layer" - one dot product per legal token against
+//     the tied embedding on a fixed grid; the dense head kept as a cross-check
+//     with the same tie rule and transitions;
+//   section "The whole loop on the device" - step kernels that read token,
+//     node and no-repeat state from device memory.
+// Dense-plus-mask semantics: page "Constrained decoding with weighted
+// automata" (mask the logits, then take the argmax) and page "Understanding
+// inference for systems engineers", section 7 (the post-logit bitmask pipeline).
+//
+// Arithmetic contract (identical in every kernel that produces a logit):
+//   lane l of a wavefront owns 16-byte chunks c = 0,1,.. of a row, i.e. the
+//   elements [c*CH + l*EL, c*CH + l*EL + EL) with EL = 4 (fp32) or 8 (bf16) and
+//   CH = 64*EL; it accumulates h[i]*E[v][i] in fp32 with fused multiply-adds in
+//   ascending element order; the 64 partial sums are then combined by an
+//   xor butterfly (lane distance 32, 16, 8, 4, 2, 1).  The order depends only on
+//   H, never on the workgroup, slot, batch size or path, so equal rows give
+//   equal logits and every path gives bit-identical logits.
+//
+// Argmax: a 64-bit key (order-preserving fp32 bits, -0 folded into +0, in the
+// high word; 0xFFFFFFFF - id in the low word) so that an unsigned max picks
+// the largest logit and, among equal logits, the lowest id.  Unsigned max is
+// associative and commutative, so combining per-wavefront and per-workgroup
+// maxima with atomics gives the same result in any order.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "kernels.h"
+
+namespace tms {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+// scalar-load views: wave-uniform addresses read through the scalar cache
+typedef const __attribute__((address_space(4))) int32_t* cint_p;
+typedef const __attribute__((address_space(4))) uint32_t* cuint_p;
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
+
+__host__ __device__ constexpr int rows_per_pass(int nc) { return nc <= 4 ? 4 : (nc == 8 ? 2 : 1); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// acc += h . e over one 16-byte chunk, ascending element order
+template <int DT>
+__device__ __forceinline__ float fma_chunk(const uint4& h, const uint4& e, float acc) {
+  if constexpr (DT == 0) {
+    acc = fmaf(__uint_as_float(h.x), __uint_as_float(e.x), acc);
+    acc = fmaf(__uint_as_float(h.y), __uint_as_float(e.y), acc);
+    acc = fmaf(__uint_as_float(h.z), __uint_as_float(e.z), acc);
+    acc = fmaf(__uint_as_float(h.w), __uint_as_float(e.w), acc);
+  } else {
+    acc = fmaf(bf16_lo(h.x), bf16_lo(e.x), acc);
+    acc = fmaf(bf16_hi(h.x), bf16_hi(e.x), acc);
+    acc = fmaf(bf16_lo(h.y), bf16_lo(e.y), acc);
+    acc = fmaf(bf16_hi(h.y), bf16_hi(e.y), acc);
+    acc = fmaf(bf16_lo(h.z), bf16_lo(e.z), acc);
+    acc = fmaf(bf16_hi(h.z), bf16_hi(e.z), acc);
+    acc = fmaf(bf16_lo(h.w), bf16_lo(e.w), acc);
+    acc = fmaf(bf16_hi(h.w), bf16_hi(e.w), acc);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Dot products of up to U rows with the hidden chunks hq held by this lane.
+// rows[u] < 0 skips row u.  All loads are issued before any arithmetic.
+template <int DT, int NC, int U>
+__device__ __forceinline__ void dot_rows(const uint4* __restrict__ emb, int nq, const int (&rows)[U],
+                                         const uint4 (&hq)[NC], float (&out)[U], int lane) {
+  uint4 raw[U][NC];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (rows[u] >= 0) {
+      const uint4* p = emb + (int64_t)rows[u] * nq + lane;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) raw[u][c] = (c * kWave + lane < nq) ? p[c * kWave] : make_uint4(0, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float acc = 0.0f;
+    if (rows[u] >= 0) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        if (c * kWave + lane < nq) acc = fma_chunk<DT>(hq[c], raw[u][c], acc);
+    }
+    out[u] = wave_sum(acc);
+  }
+}
+
+template <int NC>
+__device__ __forceinline__ void load_hidden(const uint4* __restrict__ h, int nq, uint4 (&hq)[NC], int lane) {
+#pragma unroll
+  for (int c = 0; c < NC; ++c) hq[c] = (c * kWave + lane < nq) ? h[c * kWave + lane] : make_uint4(0, 0, 0, 0);
+}
+
+__device__ __forceinline__ unsigned long long pack_key(float x, uint32_t id) {
+  uint32_t b = __float_as_uint(x);
+  if (x == 0.0f) b = 0u;  // -0 and +0 are the same logit
+  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((unsigned long long)o << 32) | (unsigned long long)(0xFFFFFFFFu - id);
+}
+__device__ __forceinline__ float key_logit(unsigned long long k) {
+  const uint32_t o = (uint32_t)(k >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+__device__ __forceinline__ uint32_t key_id(unsigned long long k) { return 0xFFFFFFFFu - (uint32_t)k; }
+
+// Per-sequence view at the start of a step.
+struct Seq {
+  int node, depth, done, b0, b1;
+  bool sep_ok, stop_ok;  // control edges of the current node (terminal, not spent, exactly-k rule)
+};
+
+// Reads the sequence record with scalar loads; false when s is finished or in
+// error.  Section "Masked sampling inside the sampler": sep is legal at an
+// unspent terminal only while another pointer is owed, stop only when none is.
+__device__ __forceinline__ bool load_seq(const DevTrie& tr, const DevState& st, int s, Seq& q) {
+  if (((cint_p)st.status)[s] != kSeqOk || ((cint_p)st.finished)[s] != 0) return false;
+  q.node = ((cint_p)st.node)[s];
+  q.depth = ((cint_p)st.depth)[s];
+  q.done = ((cint_p)st.done)[s];
+  q.b0 = ((cint_p)tr.begin)[q.node];
+  q.b1 = ((cint_p)tr.begin)[q.node + 1];
+  const int ent = ((cint_p)tr.entry)[q.node];
+  bool ctl = false;
+  if (ent >= 0) {
+    const uint32_t w = ((cuint_p)st.spent)[(int64_t)s * st.spent_words + (ent >> 5)];
+    ctl = ((w >> (ent & 31)) & 1u) == 0u;
+  }
+  const bool more = q.done + 1 < st.k;
+  q.sep_ok = ctl && more;
+  q.stop_ok = ctl && !more;
+  return true;
+}
+
+__device__ __forceinline__ bool edge_ok(int child, int live, const Seq& q) {
+  return child >= 0 ? live > 0 : (child == kChildSep ? q.sep_ok : q.stop_ok);
+}
+
+__device__ __forceinline__ void write_step_out(const StepIO& io, int s, int tok, float logit) {
+  if (io.out_tok) io.out_tok[s] = tok;
+  if (io.out_logit) io.out_logit[s] = tok >= 0 ? logit : NAN;
+  if (io.tokens_bt) io.tokens_bt[(int64_t)s * io.T + io.t] = tok;
+}
+
+// Advance sequence s along edge e (executed by one whole wavefront).
+// e == -2: the mask was empty.  e outside the node's range or not legal:
+// the winner is not walkable.  Both set a sticky error and stop the sequence.
+// Completing a pointer: its terminal is marked spent, every content edge on
+// its path loses one live pointer, and the catalog index is recorded.
+__device__ void advance(const DevTrie& tr, const DevState& st, const StepIO* io, int s, const Seq& q, int e,
+                        float logit, int lane) {
+  int status = kSeqOk, tok = -1;
+  int32_t* live = st.live + (int64_t)s * tr.live_stride;
+  if (e == -2) {
+    status = kSeqEmptyMask;
+  } else {
+    bool ok = e >= q.b0 && e < q.b1;
+    int c = 0;
+    if (ok) {
+      c = tr.child[e];
+      ok = edge_ok(c, c >= 0 ? live[e] : 0, q);
+    }
+    if (!ok) {
+      status = kSeqNotWalkable;
+    } else {
+      tok = tr.tok[e];
+      if (c >= 0) {
+        if (lane == 0) {
+          st.path[(int64_t)s * st.path_stride + q.depth] = e;
+          st.depth[s] = q.depth + 1;
+          st.node[s] = c;
+        }
+      } else {
+        const int ent = tr.entry[q.node];
+        const int32_t* path = st.path + (int64_t)s * st.path_stride;
+        for (int i = lane; i < q.depth; i += kWave) live[path[i]] -= 1;  // distinct edges
+        if (lane == 0) {
+          st.spent[(int64_t)s * st.spent_words + (ent >> 5)] |= 1u << (ent & 31);
+          st.entries[(int64_t)s * st.k + q.done] = ent;
+          st.done[s] = q.done + 1;
+          st.depth[s] = 0;
+          if (c == kChildStop) st.finished[s] = 1;
+          else st.node[s] = 0;
+        }
+      }
+      if (lane == 0) st.nemit[s] = st.nemit[s] + 1;
+    }
+  }
+  if (lane == 0) {
+    if (status != kSeqOk) st.status[s] = status;
+    if (io) write_step_out(*io, s, tok, logit);
+  }
+}
+
+// First edge of the node's range labelled tok, or -1 (one wavefront).
+__device__ __forceinline__ int find_edge(const DevTrie& tr, const Seq& q, int tok, int lane) {
+  for (int base = q.b0; base < q.b1; base += kWave) {
+    const int e = base + lane;
+    const unsigned long long m = __ballot(e < q.b1 && tr.tok[e] == tok);
+    if (m) return base + (int)__builtin_ctzll(m);
+  }
+  return -1;
+}
+
+// ---------------------------------------------------------------------------
+// Fused sparse step: materialise the legal set, gather-GEMV, argmax, advance.
+// Grid: B * split workgroups of 256 threads; workgroup g serves sequence
+// g / split.  Wavefront wv of the sequence's W = 4*split wavefronts takes the
+// edges b0+wv, b0+wv+W, ... of the current node.  The last workgroup of a
+// sequence to finish (arrival counter) reads the combined key and advances.
+// FAST: edge records through wave-uniform scalar loads, U edges per pass.
+// GLOBAL: 64 edges per pass through per-lane vector loads, legal ones
+// compacted with a ballot, U rows in flight.
+// ---------------------------------------------------------------------------
+template <int DT, int NC, bool FAST>
+__global__ __launch_bounds__(kBlock) void step_sparse_kernel(DevTrie tr, DevState st, StepIO io, int split) {
+  constexpr int U = rows_per_pass(NC);
+  constexpr int EL = DT == 0 ? 4 : 8;
+  const int g = blockIdx.x;
+  const int s = g / split;
+  const int w = g - s * split;
+  const int lane = __lane_id();
+  const int wv = w * kWavesPerBlock + wave_id();
+  const int W = split * kWavesPerBlock;
+  Seq q;
+  if (!load_seq(tr, st, s, q)) {
+    if (w == 0 && threadIdx.x == 0) write_step_out(io, s, -1, NAN);
+    return;
+  }
+  const int nq = io.H / EL;
+  uint4 hq[NC];
+  load_hidden<NC>((const uint4*)io.hidden + (int64_t)s * nq, nq, hq, lane);
+  const uint4* emb = (const uint4*)io.emb;
+  const int32_t* live = st.live + (int64_t)s * tr.live_stride;
+  unsigned long long best = 0;
+
+  if constexpr (FAST) {
+    const cint_p ctok = (cint_p)tr.tok;
+    const cint_p cchild = (cint_p)tr.child;
+    const cint_p clive = (cint_p)live;
+    for (int e0 = q.b0 + wv; e0 < q.b1; e0 += U * W) {
+      int rows[U], edges[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + u * W;
+        edges[u] = e;
+        rows[u] = -1;
+        if (e < q.b1) {
+          const int c = cchild[e];
+          if (edge_ok(c, c >= 0 ? clive[e] : 0, q)) rows[u] = ctok[e];
+        }
+      }
+      float l[U];
+      dot_rows<DT, NC, U>(emb, nq, rows, hq, l, lane);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (rows[u] >= 0) best = max(best, pack_key(l[u], (uint32_t)edges[u]));
+    }
+  } else {
+    for (int base = q.b0 + wv; base < q.b1; base += kWave * W) {
+      const int e = base + lane * W;
+      int tk = -1;
+      if (e < q.b1) {
+        const int c = tr.child[e];
+        if (edge_ok(c, c >= 0 ? live[e] : 0, q)) tk = tr.tok[e];
+      }
+      unsigned long long m = __ballot(tk >= 0);
+      while (m) {
+        int rows[U], edges[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (m) {
+            const int j = (int)__builtin_ctzll(m);
+            m &= m - 1;
+            rows[u] = __builtin_amdgcn_readlane(tk, j);
+            edges[u] = base + j * W;
+          } else {
+            rows[u] = -1;
+            edges[u] = 0;
+          }
+        }
+        float l[U];
+        dot_rows<DT, NC, U>(emb, nq, rows, hq, l, lane);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (rows[u] >= 0) best = max(best, pack_key(l[u], (uint32_t)edges[u]));
+      }
+    }
+  }
+
+  __shared__ unsigned long long s_best[kWavesPerBlock];
+  __shared__ unsigned long long s_key;
+  __shared__ int s_last;
+  if (lane == 0) s_best[wave_id()] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long b = s_best[0];
+#pragma unroll
+    for (int i = 1; i < kWavesPerBlock; ++i) b = max(b, s_best[i]);
+    if (split == 1) {
+      s_last = 1;
+      s_key = b;
+    } else {
+      if (b) __hip_atomic_fetch_max(&st.key[s], b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t prev = __hip_atomic_fetch_add(&st.arrive[s], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = prev == (uint32_t)(split - 1);
+      s_last = last;
+      if (last) s_key = __hip_atomic_load(&st.key[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+  if (!s_last || threadIdx.x >= kWave) return;
+  const unsigned long long key = s_key;
+  advance(tr, st, &io, s, q, key ? (int)key_id(key) : -2, key ? key_logit(key) : NAN, lane);
+  if (lane == 0 && split > 1) {
+    __hip_atomic_store(&st.key[s], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&st.arrive[s], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dense cross-check: vocabulary bitmask, all-V head, masked argmax, advance.
+// ---------------------------------------------------------------------------
+
+// One workgroup per sequence builds its V-bit mask in LDS, then stores it.
+__global__ __launch_bounds__(kBlock) void dense_mask_kernel(DevTrie tr, DevState st) {
+  extern __shared__ uint32_t smask[];
+  const int s = blockIdx.x;
+  const int mw = st.mask_words;
+  for (int i = threadIdx.x; i < mw; i += kBlock) smask[i] = 0u;
+  __syncthreads();
+  Seq q;
+  if (load_seq(tr, st, s, q)) {
+    const int32_t* live = st.live + (int64_t)s * tr.live_stride;
+    for (int e = q.b0 + threadIdx.x; e < q.b1; e += kBlock) {
+      const int c = tr.child[e];
+      if (edge_ok(c, c >= 0 ? live[e] : 0, q)) {
+        const int t = tr.tok[e];
+        atomicOr(&smask[t >> 5], 1u << (t & 31));
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t* dst = st.mask + (int64_t)s * mw;
+  for (int i = threadIdx.x; i < mw; i += kBlock) dst[i] = smask[i];
+}
+
+// Every logit of every sequence; masked-in ones feed the per-sequence key.
+// Grid-stride over groups of U consecutive rows per wavefront.
+template <int DT, int NC>
+__global__ __launch_bounds__(kBlock) void dense_head_kernel(DevState st, StepIO io, float* full_logits) {
+  constexpr int U = rows_per_pass(NC);
+  constexpr int EL = DT == 0 ? 4 : 8;
+  const int lane = __lane_id();
+  const int gw = blockIdx.x * kWavesPerBlock + wave_id();
+  const int nw = gridDim.x * kWavesPerBlock;
+  const int nq = io.H / EL;
+  const int V = io.V;
+  const uint4* emb = (const uint4*)io.emb;
+  const cuint_p cmask = (cuint_p)st.mask;
+  uint4 hq[NC];
+  if (st.B == 1) load_hidden<NC>((const uint4*)io.hidden, nq, hq, lane);
+  for (int v0 = gw * U; v0 < V; v0 += nw * U) {
+    int rows[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) rows[u] = v0 + u < V ? v0 + u : -1;
+    for (int b = 0; b < st.B; ++b) {
+      if (st.B > 1) load_hidden<NC>((const uint4*)io.hidden + (int64_t)b * nq, nq, hq, lane);
+      float l[U];
+      dot_rows<DT, NC, U>(emb, nq, rows, hq, l, lane);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (rows[u] < 0) continue;
+        const int v = rows[u];
+        if (full_logits && lane == u) full_logits[(int64_t)b * V + v] = l[u];
+        const uint32_t word = cmask[(int64_t)b * st.mask_words + (v >> 5)];
+        if (((word >> (v & 31)) & 1u) && lane == 0)
+          __hip_atomic_fetch_max(&st.key[b], pack_key(l[u], (uint32_t)v), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+}
+
+// One wavefront per sequence: winner token from the key, its edge, advance.
+__global__ __launch_bounds__(kWave) void dense_advance_kernel(DevTrie tr, DevState st, StepIO io) {
+  const int s = blockIdx.x;
+  const int lane = __lane_id();
+  Seq q;
+  if (!load_seq(tr, st, s, q)) {
+    if (lane == 0) write_step_out(io, s, -1, NAN);
+    return;
+  }
+  const unsigned long long key = st.key[s];
+  int e = -2;
+  float lg = NAN;
+  if (key) {
+    e = find_edge(tr, q, (int)key_id(key), lane);
+    lg = key_logit(key);
+  }
+  advance(tr, st, &io, s, q, e, lg, lane);
+  if (lane == 0) st.key[s] = 0ull;
+}
+
+// Teacher forcing: one wavefront per sequence.
+__global__ __launch_bounds__(kWave) void forced_kernel(DevTrie tr, DevState st, const int32_t* forced) {
+  const int s = blockIdx.x;
+  const int lane = __lane_id();
+  const int t = forced[s];
+  Seq q;
+  if (t < 0 || !load_seq(tr, st, s, q)) return;
+  advance(tr, st, nullptr, s, q, find_edge(tr, q, t, lane), NAN, lane);
+}
+
+// The legal set alone, compacted in ascending token order (one wavefront per sequence).
+__global__ __launch_bounds__(kWave) void legal_set_kernel(DevTrie tr, DevState st, int32_t* legal_tok,
+                                                          int32_t* n_legal) {
+  const int s = blockIdx.x;
+  const int lane = __lane_id();
+  Seq q;
+  if (!load_seq(tr, st, s, q)) {
+    if (lane == 0) n_legal[s] = -1;
+    return;
+  }
+  const int32_t* live = st.live + (int64_t)s * tr.live_stride;
+  int cnt = 0;
+  for (int base = q.b0; base < q.b1; base += kWave) {
+    const int e = base + lane;
+    bool ok = false;
+    int t = 0;
+    if (e < q.b1) {
+      const int c = tr.child[e];
+      ok = edge_ok(c, c >= 0 ? live[e] : 0, q);
+      t = tr.tok[e];
+    }
+    const unsigned long long m = __ballot(ok);
+    if (ok) legal_tok[(int64_t)s * tr.cap + cnt + __popcll(m & ((1ull << lane) - 1ull))] = t;
+    cnt += __popcll(m);
+  }
+  if (lane == 0) n_legal[s] = cnt;
+}
+
+// The sparse head alone over explicit row lists (same arithmetic as the step).
+template <int DT, int NC>
+__global__ __launch_bounds__(kBlock) void gather_gemv_kernel(const uint4* __restrict__ emb, int V, int H,
+                                                             const uint4* __restrict__ hidden,
+                                                             const int32_t* rows_in, const int32_t* n_rows,
+                                                             int cap, float* out, int split) {
+  constexpr int U = rows_per_pass(NC);
+  constexpr int EL = DT == 0 ? 4 : 8;
+  const int g = blockIdx.x;
+  const int s = g / split;
+  const int w = g - s * split;
+  const int lane = __lane_id();
+  const int wv = w * kWavesPerBlock + wave_id();
+  const int W = split * kWavesPerBlock;
+  const int n = min(((cint_p)n_rows)[s], cap);
+  if (n <= 0) return;
+  const int nq = H / EL;
+  uint4 hq[NC];
+  load_hidden<NC>(hidden + (int64_t)s * nq, nq, hq, lane);
+  const cint_p crow = (cint_p)(rows_in + (int64_t)s * cap);
+  float* o = out + (int64_t)s * cap;
+  for (int j0 = wv; j0 < n; j0 += U * W) {
+    int rows[U];
+    bool bad[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * W;
+      const int r = j < n ? crow[j] : -1;
+      const bool valid = r >= 0 && r < V;
+      bad[u] = j < n && !valid;
+      rows[u] = valid ? r : -1;
+    }
+    float l[U];
+    dot_rows<DT, NC, U>(emb, nq, rows, hq, l, lane);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * W;
+      if (lane == u && j < n) o[j] = bad[u] ? NAN : l[u];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// State maintenance
+// ---------------------------------------------------------------------------
+
+// grid (x, B): row s = blockIdx.y; live row copied from live0 with 16-byte stores.
+__global__ __launch_bounds__(kBlock) void reset_kernel(DevTrie tr, DevState st) {
+  const int s = blockIdx.y;
+  const int q4 = tr.live_stride / 4;
+  const int4* src = (const int4*)tr.live0;
+  int4* dst = (int4*)(st.live + (int64_t)s * tr.live_stride);
+  for (int i = blockIdx.x * kBlock + threadIdx.x; i < q4; i += gridDim.x * kBlock) dst[i] = src[i];
+  uint32_t* sp = st.spent + (int64_t)s * st.spent_words;
+  for (int i = blockIdx.x * kBlock + threadIdx.x; i < st.spent_words; i += gridDim.x * kBlock) sp[i] = 0u;
+  if (blockIdx.x == 0) {
+    for (int i = threadIdx.x; i < st.k; i += kBlock) st.entries[(int64_t)s * st.k + i] = -1;
+    if (threadIdx.x == 0) {
+      st.node[s] = 0;
+      st.depth[s] = 0;
+      st.done[s] = 0;
+      st.status[s] = kSeqOk;
+      st.finished[s] = 0;
+      st.nemit[s] = 0;
+      st.key[s] = 0ull;
+      st.arrive[s] = 0u;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void finalize_kernel(DevState st, int32_t* len, int32_t* entries) {
+  const int s = blockIdx.x * kBlock + threadIdx.x;
+  if (s >= st.B) return;
+  if (st.status[s] == kSeqOk && st.finished[s] == 0) st.status[s] = kSeqNotDone;
+  if (len) len[s] = st.nemit[s];
+  if (entries)
+    for (int j = 0; j < st.k; ++j) entries[(int64_t)s * st.k + j] = st.entries[(int64_t)s * st.k + j];
+}
+
+__global__ void set_live_kernel(DevTrie tr, DevState st, int32_t s, int32_t e, int32_t v) {
+  if (threadIdx.x == 0) st.live[(int64_t)s * tr.live_stride + e] = v;
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch on (dtype, chunks per lane)
+// ---------------------------------------------------------------------------
+template <template <int, int> class F, typename... A>
+hipError_t dispatch(int dtype, int nc, A&&... a) {
+#define TMS_CASE(D, N) \
+  if (dtype == D && nc == N) return F<D, N>::run(static_cast<A&&>(a)...);
+  TMS_CASE(0, 1) TMS_CASE(0, 2) TMS_CASE(0, 4) TMS_CASE(0, 8) TMS_CASE(0, 16)
+  TMS_CASE(1, 1) TMS_CASE(1, 2) TMS_CASE(1, 4) TMS_CASE(1, 8) TMS_CASE(1, 16)
+#undef TMS_CASE
+  return hipErrorInvalidValue;
+}
+
+template <int DT, int NC>
+struct StepLaunch {
+  static hipError_t run(const DevTrie& tr, const DevState& st, const StepIO& io, bool fast, int split,
+                        hipStream_t s) {
+    const dim3 grid((unsigned)(st.B * split)), block(kBlock);
+    if (fast) hipLaunchKernelGGL((step_sparse_kernel<DT, NC, true>), grid, block, 0, s, tr, st, io, split);
+    else hipLaunchKernelGGL((step_sparse_kernel<DT, NC, false>), grid, block, 0, s, tr, st, io, split);
+    return hipGetLastError();
+  }
+};
+
+template <int DT, int NC>
+struct DenseLaunch {
+  static hipError_t run(const DevState& st, const StepIO& io, float* full, int grid, hipStream_t s) {
+    hipLaunchKernelGGL((dense_head_kernel<DT, NC>), dim3(grid), dim3(kBlock), 0, s, st, io, full);
+    return hipGetLastError();
+  }
+};
+
+template <int DT, int NC>
+struct GemvLaunch {
+  static hipError_t run(const void* emb, int V, int H, const void* hidden, const int32_t* rows,
+                        const int32_t* n_rows, int B, int cap, float* out, int split, hipStream_t s) {
+    hipLaunchKernelGGL((gather_gemv_kernel<DT, NC>), dim3((unsigned)(B * split)), dim3(kBlock), 0, s,
+                       (const uint4*)emb, V, H, (const uint4*)hidden, rows, n_rows, cap, out, split);
+    return hipGetLastError();
+  }
+};
+
+}  // namespace
+
+int chunks_for(int dtype, int H) {
+  const int el = dtype == 0 ? 4 : 8;
+  if (H <= 0 || H % el) return 0;
+  const int need = (H / el + kWave - 1) / kWave;
+  for (int nc = 1; nc <= 16; nc *= 2)
+    if (need <= nc) return nc;
+  return 0;
+}
+
+hipError_t launch_reset(const DevTrie& tr, const DevState& st, hipStream_t s) {
+  const int q4 = tr.live_stride / 4;
+  int gx = (q4 + kBlock * 8 - 1) / (kBlock * 8);
+  gx = gx < 1 ? 1 : (gx > 256 ? 256 : gx);
+  hipLaunchKernelGGL(reset_kernel, dim3(gx, st.B), dim3(kBlock), 0, s, tr, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_step_sparse(const DevTrie& tr, const DevState& st, const StepIO& io, int dtype, bool fast,
+                              int split, hipStream_t s) {
+  return dispatch<StepLaunch>(dtype, chunks_for(dtype, io.H), tr, st, io, fast, split, s);
+}
+
+hipError_t launch_dense_step(const DevTrie& tr, const DevState& st, const StepIO& io, int dtype, float* full,
+                             int grid, hipStream_t s) {
+  hipLaunchKernelGGL(dense_mask_kernel, dim3(st.B), dim3(kBlock), st.mask_words * sizeof(uint32_t), s, tr, st);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  err = dispatch<DenseLaunch>(dtype, chunks_for(dtype, io.H), st, io, full, grid, s);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(dense_advance_kernel, dim3(st.B), dim3(kWave), 0, s, tr, st, io);
+  return hipGetLastError();
+}
+
+hipError_t launch_forced(const DevTrie& tr, const DevState& st, const int32_t* forced, hipStream_t s) {
+  hipLaunchKernelGGL(forced_kernel, dim3(st.B), dim3(kWave), 0, s, tr, st, forced);
+  return hipGetLastError();
+}
+
+hipError_t launch_legal_set(const DevTrie& tr, const DevState& st, int32_t* legal_tok, int32_t* n_legal,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(legal_set_kernel, dim3(st.B), dim3(kWave), 0, s, tr, st, legal_tok, n_legal);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_gemv(const void* emb, int dtype, int32_t V, int32_t H, const void* hidden,
+                              const int32_t* rows, const int32_t* n_rows, int32_t B, int32_t cap, float* out,
+                              int split, hipStream_t s) {
+  return dispatch<GemvLaunch>(dtype, chunks_for(dtype, H), emb, V, H, hidden, rows, n_rows, B, cap, out, split,
+                              s);
+}
+
+hipError_t launch_finalize(const DevState& st, int32_t* len, int32_t* entries, hipStream_t s) {
+  hipLaunchKernelGGL(finalize_kernel, dim3((st.B + kBlock - 1) / kBlock), dim3(kBlock), 0, s, st, len, entries);
+  return hipGetLastError();
+}
+
+hipError_t launch_set_live(const DevTrie& tr, const DevState& st, int32_t seq, int32_t edge, int32_t value,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(set_live_kernel, dim3(1), dim3(kWave), 0, s, tr, st, seq, edge, value);
+  return hipGetLastError();
+}
+
+}  // namespace tms
