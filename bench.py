@@ -2,14 +2,15 @@
 
 One bench step = one whole answer for one batch of the product-scale workload
 (V=151936, H=2048 bf16 tied embedding, 42-tool catalog, k=3, B=1): reset the
-decode state, then the device-resident loop (a replayed hipGraph of step
-kernels) until every sequence has emitted exactly k pointers.  value = decode
+decode state, then the device-resident loop (one kernel, one workgroup per
+sequence) until every sequence has emitted exactly k pointers.  value = decode
 steps per second (lockstep steps that emitted a token), over K timed steps
 after W warmup steps, bracketed by device synchronisations.
 
-Also reported on the same line: the step kernel's roofline (algorithmic bytes
-per launch / its average duration, timed with HIP events on the launch
-stream), the batch-64 workloads, the gather-GEMV bandwidth stress shape
+Also reported on the same line: the loop kernel's roofline (algorithmic bytes
+of one answer / that launch's duration, timed with HIP events on the launch
+stream), the same answers through the hipGraph of per-step kernels, the
+batch-64 workloads, the gather-GEMV bandwidth stress shape
 (64 x 256 distinct rows per launch cycling through 9 disjoint row sets, 604 MB
 of the 622 MB table), the dense+mask step, and the CPU oracle timed on this
 host (cpu_baseline leg, the only place the oracle is used here).
@@ -101,25 +102,6 @@ class Workload:
         torch.cuda.synchronize()
         return np.array(n_rows), np.array(n_active), np.array(n_unique)
 
-    def step_durations(self, reps):
-        """Average duration of each step-kernel launch (HIP events around each
-        launch on the launch stream), host-driven loop."""
-        import torch
-
-        import trie_masked_sparse_amd as tms
-        tok = torch.empty(self.B, dtype=torch.int32, device="cuda")
-        durs = []
-        for _ in range(reps):
-            self.state.reset()
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(self.T)]
-            for t in range(self.T):
-                evs[t][0].record()
-                tms.decode_step_sparse(self.state.h, self.hid[t], tok)
-                evs[t][1].record()
-            torch.cuda.synchronize()
-            durs.append([a.elapsed_time(b) * 1e3 for a, b in evs])  # us
-        return self.np.array(durs).mean(axis=0)
-
     def close(self):
         self.state.close()
         self.trie.close()
@@ -158,22 +140,44 @@ def time_decode(w: Workload, steps: int, warmup: int):
     }
 
 
-def step_roofline(w: Workload, reps: int):
-    np = w.np
+def reset_us(w: Workload, n: int = 50):
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n):
+        w.state.reset()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
+def loop_roofline(w: Workload, timed: dict, steps: int):
+    """Algorithmic bytes of one whole answer (the resident loop kernel's launch)
+    over that launch's duration: the event-timed region divided by the number
+    of answers, minus the separately timed state reset."""
     n_rows, n_act, n_uni = w.legal_profile()
-    durs = w.step_durations(reps)
     H, esz = w.c.hidden, w.esz
-    gathered = (n_rows + n_act) * H * esz          # rows + hidden vectors, per launch
-    unique = (n_uni + n_act) * H * esz
+    gathered = float(((n_rows + n_act) * H * esz).sum())   # legal rows + hidden vectors
+    unique = float(((n_uni + n_act) * H * esz).sum())
+    r_us = reset_us(w)
+    launch_us = timed["gpu_ms"] * 1e3 / steps - r_us
     return {
-        "avg_launch_us": float(durs.mean()),
-        "alg_bytes_per_launch": float(gathered.mean()),
-        "unique_bytes_per_launch": float(unique.mean()),
-        "achieved_GBps": float(gathered.sum() / (durs.sum() * 1e-6) / 1e9),
-        "unique_GBps": float(unique.sum() / (durs.sum() * 1e-6) / 1e9),
-        "per_step_us": [round(float(x), 2) for x in durs],
-        "per_step_rows": [int(x) for x in n_rows],
+        "kernel": "loop_kernel", "avg_launch_us": launch_us, "reset_us": r_us,
+        "alg_bytes_per_launch": gathered, "unique_bytes_per_launch": unique,
+        "achieved_GBps": gathered / (launch_us * 1e-6) / 1e9, "unique_GBps": unique / (launch_us * 1e-6) / 1e9,
+        "rows_per_step": [int(x) for x in n_rows],
     }
+
+
+def graph_mode(w: Workload, steps: int, warmup: int):
+    """The same answers through the hipGraph of per-step kernels."""
+    import trie_masked_sparse_amd as tms
+    tms.state_set_loop(w.state.h, tms.LOOP_GRAPH)
+    r = time_decode(w, steps, warmup)
+    tms.state_set_loop(w.state.h, tms.LOOP_RESIDENT)
+    return {"steps_per_s": r["steps_per_s"], "ms_per_call": r["ms_per_call"],
+            "step_kernel_launches_per_call": w.T}
 
 
 def stress_gemv(steps: int, warmup: int, emb, emb_np):
@@ -194,13 +198,13 @@ def stress_gemv(steps: int, warmup: int, emb, emb_np):
         tms.gather_gemv(emb, hid, sets[i % S], n, out)
     torch.cuda.synchronize()
     iters = max(steps, 1) * S
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
     for i in range(iters):
-        evs[i][0].record()
         tms.gather_gemv(emb, hid, sets[i % S], n, out)
-        evs[i][1].record()
+    e1.record()
     torch.cuda.synchronize()
-    durs = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    durs = np.array([e0.elapsed_time(e1) * 1e3 / iters])  # back-to-back launches, us each
     nbytes = B * R * H * 2 + B * H * 2
     return {"shape": "64 seq x 256 distinct rows, H=2048 bf16, 9 disjoint sets (604 MB)",
             "avg_launch_us": float(durs.mean()), "alg_bytes_per_launch": nbytes,
@@ -314,19 +318,20 @@ def main():
         line["config"] = {
             "workload": "product-scale: V=151936, H=2048 bf16 tied embedding (622 MB), 42-tool catalog "
                         f"({w.info['n_nodes']} trie nodes, cap {w.info['cap']}), k=3, B=1; one bench step = "
-                        "state reset + device-loop graph of "
-                        f"{w.T} step kernels; bf16 inputs, fp32 accumulation",
+                        "state reset + one whole answer from the resident device loop "
+                        f"(up to {w.T} steps); bf16 inputs, fp32 accumulation",
             "path": "fast" if w.info["path"] == tms.PATH_FAST else "global",
-            "steps_per_call": r["steps_per_call"], "tokens_per_call": r["tokens_per_call"],
-            "launches_per_call": r["launches_per_call"], "split": tms.state_get_launch(w.state.h)[0]}
+            "steps_per_call": r["steps_per_call"], "tokens_per_call": r["tokens_per_call"]}
         _log(f"headline {r}")
-        rf = step_roofline(w, reps=max(3, args.steps // 5))
-        line["roofline"] = {"bound": "hbm", "kernel": "step_sparse_kernel", "achieved": rf["achieved_GBps"],
+        rf = loop_roofline(w, r, args.steps)
+        line["roofline"] = {"bound": "hbm", "kernel": rf["kernel"], "achieved": rf["achieved_GBps"],
                             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": rf["achieved_GBps"] / HBM_PEAK_GBPS,
-                            "traffic": _pmc_traffic("step_sparse", "product"),
+                            "traffic": _pmc_traffic("loop", "product"),
                             "alg_bytes_per_launch": rf["alg_bytes_per_launch"],
                             "avg_launch_us": rf["avg_launch_us"]}
-        also["product_step_detail"] = rf
+        also["product_loop_detail"] = rf
+        also["product_graph_mode"] = graph_mode(w, args.steps, args.warmup)
+        _log(f"roofline {line['roofline']}; graph {also['product_graph_mode']}")
     if want("dense"):
         also["dense_masked_product_B1"] = dense_step_us(w)
         _log(f"dense {also['dense_masked_product_B1']}")
@@ -338,12 +343,14 @@ def main():
         for cid in ("structured", "unstructured"):
             _log(f"{cid} workload")
             wb = Workload(cid)
-            rb = time_decode(wb, max(5, args.steps // 2), args.warmup)
-            rfb = step_roofline(wb, reps=3)
+            nb = max(5, args.steps // 2)
+            rb = time_decode(wb, nb, args.warmup)
+            rfb = loop_roofline(wb, rb, nb)
             also[f"{cid}_B64"] = {"steps_per_s": rb["steps_per_s"], "tokens_per_s": rb["tokens_per_s"],
                                   "ms_per_call": rb["ms_per_call"], "steps_per_call": rb["steps_per_call"],
                                   "path": "fast" if wb.info["path"] == tms.PATH_FAST else "global",
-                                  "step_kernel": {k: v for k, v in rfb.items() if k not in ("per_step_rows",)}}
+                                  "loop_kernel": {k: v for k, v in rfb.items() if k != "rows_per_step"},
+                                  "graph_mode": graph_mode(wb, nb, args.warmup)}
             _log(f"{cid} {also[f'{cid}_B64']['steps_per_s']:.0f} steps/s")
             wb.close()
     if want("cpu"):

@@ -163,8 +163,9 @@ tms_status tms_decode_step_dense_masked(tms_state* st, const void* hidden, int32
                                         float* full_logits, void* stream);
 
 /* The device-resident loop (section "The whole loop on the device"): T sparse
- * steps from the current state with no host work in between, replayed from a
- * hipGraph built on the first call for these pointers.  hidden_seq: dev
+ * steps from the current state with no host work in between.  By default one
+ * kernel runs the whole loop with one workgroup per sequence (state kept on
+ * chip between steps); see tms_state_set_loop for the other forms.  hidden_seq: dev
  * [T][B][H], step t uses hidden_seq[t].  Outputs: tokens dev int32 [B][T]
  * (token of step t, -1 where a sequence was inactive), len dev int32 [B]
  * (tokens emitted since the last reset), entries dev int32 [B][k] (catalog
@@ -201,6 +202,15 @@ tms_status tms_debug_set_live(tms_state* st, int32_t s, int32_t edge, int32_t va
 /* Tuning knob (also read from the TMS_SPLIT environment variable at create):
  * workgroups per sequence in the fused step; 0 restores the default. */
 tms_status tms_state_set_split(tms_state* st, int32_t split);
+
+/* How tms_decode_k_pointers runs its T steps (all bit-identical):
+ * RESIDENT: one launch, one workgroup per sequence loops over the steps;
+ * GRAPH: a hipGraph of T step kernels (as tms_decode_step_sparse), built on
+ *   the first call for a given set of pointers and replayed afterwards;
+ * STREAM: the same T step kernels launched directly on the stream.
+ * Also read from the TMS_LOOP environment variable (0, 1, 2) at create. */
+typedef enum { TMS_LOOP_RESIDENT = 0, TMS_LOOP_GRAPH = 1, TMS_LOOP_STREAM = 2 } tms_loop_mode;
+tms_status tms_state_set_loop(tms_state* st, int32_t mode);
 
 /* Workgroups per sequence used by the fused step, and its grid size. */
 tms_status tms_state_get_launch(const tms_state* st, int32_t* split, int32_t* grid);

@@ -194,12 +194,20 @@ def test_paths_splits_graph_and_shuffle_identical():
                 base = (tok, lg)
             assert np.array_equal(tok, base[0]), (path, split)
             assert np.array_equal(lg, base[1], equal_nan=True), (path, split)
-            # graph replays, with eager work and syncs in between
-            for rep in range(3):
-                st.reset()
-                torch.cuda.synchronize()
-                g_tok, g_len, g_ent = run_k_pointers(st, hd)
-                assert np.array_equal(g_tok, base[0]), (path, split, rep)
+            # every loop form; graph replays with eager work and syncs in between
+            for mode in (tms.LOOP_RESIDENT, tms.LOOP_GRAPH, tms.LOOP_STREAM):
+                tms.state_set_loop(st.h, mode)
+                for rep in range(3 if mode == tms.LOOP_GRAPH else 1):
+                    st.reset()
+                    torch.cuda.synchronize()
+                    g_tok, g_len, g_ent = run_k_pointers(st, hd)
+                    assert np.array_equal(g_tok, base[0]), (path, split, mode, rep)
+                    ex = st.export(live=True)
+                    if mode == tms.LOOP_RESIDENT:
+                        ref_state = ex
+                    else:
+                        for key in ("node", "depth", "done", "status", "finished", "n_emitted", "entries", "live"):
+                            assert np.array_equal(ex[key], ref_state[key]), (key, mode)
         st.close()
         trie.close()
     # batch shuffle: permuting the sequences permutes the outputs, nothing else
@@ -433,3 +441,51 @@ def test_gather_gemv_stress_shape_sampled():
             b, j = int(rng.integers(0, 64)), int(rng.integers(0, 256))
             want, sa = oracle.logit(emb_np, int(sets[si, b, j]), hid[b])
             assert abs(float(o[b, j]) - want) <= 2e-3 * abs(want) + gamma(H + 1) * sa
+
+
+# ---------------------------------------------------------------------------
+# Resident-loop variants: register-held path/entry lists and their memory
+# fallbacks, live counts in LDS or in device memory
+# ---------------------------------------------------------------------------
+
+def _loop_forms_agree(cat, V, k, B, H, path, seed, where):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    otr = oracle.Trie(cat, V, V - 2, V - 1)
+    T = k * (otr.max_depth + 1)
+    emb = _rand_table(rng, V, H, "bf16")
+    hid = _rand_hidden(rng, T, B, H, "bf16")
+    trie = tms.Trie(cat, V, V - 2, V - 1, path=path)
+    st = tms.State(trie, B, k, to_dev(emb))
+    hd = to_dev(hid)
+    tok_r, len_r, ent_r = run_k_pointers(st, hd)
+    ex_r = st.export(live=True)
+    compare(tok_r, oracle.decode(otr, k, emb, hid), H, None, len_r, ent_r, where=where)
+    tms.state_set_loop(st.h, tms.LOOP_GRAPH)
+    st.reset()
+    tok_g, len_g, ent_g = run_k_pointers(st, hd)
+    ex_g = st.export(live=True)
+    assert np.array_equal(tok_r, tok_g) and np.array_equal(len_r, len_g) and np.array_equal(ent_r, ent_g)
+    for key in ("node", "depth", "done", "status", "finished", "n_emitted", "entries", "live"):
+        assert np.array_equal(ex_r[key], ex_g[key]), (where, key)
+    return trie.info
+
+
+def test_loop_deep_entries():
+    """Entries longer than a wavefront (path kept in device memory)."""
+    rng = np.random.Generator(np.random.PCG64(40))
+    cat = [[int(x) for x in rng.integers(0, 100, size=int(rng.integers(60, 81)))] for _ in range(20)]
+    info = _loop_forms_agree(cat, 600, 3, 3, 256, tms.PATH_AUTO, 1, "deep")
+    assert info["max_depth"] > 64
+
+
+def test_loop_many_pointers():
+    """k above a wavefront (completed entries kept in device memory)."""
+    cat = random_catalog(41, 100, 3, 300)
+    _loop_forms_agree(cat, 600, 70, 3, 256, tms.PATH_AUTO, 2, "many_k")
+
+
+def test_loop_fast_store_live_in_memory():
+    """A fast-path trie whose live counts do not fit LDS."""
+    cat = random_catalog(42, 3000, 6, 200, min_len=3)
+    info = _loop_forms_agree(cat, 1024, 4, 5, 512, tms.PATH_FAST, 3, "fast_global_live")
+    assert info["path"] == tms.PATH_FAST and info["n_edges"] * 4 > 65536

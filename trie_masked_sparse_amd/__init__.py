@@ -24,6 +24,7 @@ OK, ERR_INVALID_ARG, ERR_CATALOG, ERR_FANOUT, ERR_K, ERR_EMPTY_MASK, ERR_NOT_WAL
     ERR_BUSY, ERR_OOM, ERR_HIP = range(11)
 F32, BF16 = 0, 1
 PATH_AUTO, PATH_FAST, PATH_GLOBAL = 0, 1, 2
+LOOP_RESIDENT, LOOP_GRAPH, LOOP_STREAM = 0, 1, 2
 
 # every symbol declared in include/tms.h
 EXPORTS = (
@@ -31,7 +32,7 @@ EXPORTS = (
     "tms_state_create", "tms_state_reset", "tms_state_sync_status", "tms_state_export", "tms_state_free",
     "tms_decode_step_sparse", "tms_decode_step_dense_masked", "tms_decode_k_pointers",
     "tms_advance_forced", "tms_legal_set", "tms_gather_gemv", "tms_debug_set_live",
-    "tms_state_set_split", "tms_state_get_launch", "tms_status_str", "tms_last_error",
+    "tms_state_set_split", "tms_state_set_loop", "tms_state_get_launch", "tms_status_str", "tms_last_error",
 )
 
 
@@ -77,6 +78,7 @@ def lib():
             "tms_gather_gemv": [P, C.c_int, i32, i32, P, P, P, i32, i32, P, P],
             "tms_debug_set_live": [P, i32, i32, i32, P],
             "tms_state_set_split": [P, i32],
+            "tms_state_set_loop": [P, i32],
             "tms_state_get_launch": [P, P, P],
         }
         for name, args in sig.items():
@@ -222,6 +224,10 @@ def state_free(st):
 
 def state_set_split(st, split: int):
     _check(lib().tms_state_set_split(st, split), "state_set_split")
+
+
+def state_set_loop(st, mode: int):
+    _check(lib().tms_state_set_loop(st, mode), "state_set_loop")
 
 
 def state_get_launch(st):

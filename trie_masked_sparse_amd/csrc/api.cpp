@@ -10,7 +10,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/tms.h"
+#include "tms.h"
 #include "kernels.h"
 #include "trie_build.h"
 
@@ -33,7 +33,7 @@ struct tms_state {
   tms::DevState dev{};
   int split = 1, split_default = 1;
   bool fast = false;
-  bool use_graph = true;
+  int loop_mode = TMS_LOOP_RESIDENT;
   hipStream_t capture = nullptr;
   hipGraph_t graph = nullptr;
   hipGraphExec_t gexec = nullptr;
@@ -169,6 +169,7 @@ tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_
   const size_t o_tok = c.take<int32_t>(h.n_edges);
   const size_t o_child = c.take<int32_t>(h.n_edges);
   const size_t o_live0 = c.take<int32_t>(live_stride);
+  const size_t o_rec = c.take<int32_t>(size_t(h.n_nodes) * 4);
   hipError_t e = hipGetDevice(&t->device);
   if (e == hipSuccess) e = hipMalloc(&t->dmem, c.off);
   if (e != hipSuccess) {
@@ -180,11 +181,18 @@ tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_
   hipStream_t s = static_cast<hipStream_t>(stream);
   std::vector<int32_t> live0(live_stride, 0);
   std::copy(h.live0.begin(), h.live0.end(), live0.begin());
+  std::vector<int32_t> rec(size_t(h.n_nodes) * 4, 0);
+  for (int32_t n = 0; n < h.n_nodes; ++n) {
+    rec[4 * size_t(n)] = h.begin[n];
+    rec[4 * size_t(n) + 1] = h.begin[n + 1];
+    rec[4 * size_t(n) + 2] = h.entry[n];
+  }
   e = hipMemcpyAsync(base + o_begin, h.begin.data(), 4 * h.begin.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipMemcpyAsync(base + o_entry, h.entry.data(), 4 * h.entry.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipMemcpyAsync(base + o_tok, h.tok.data(), 4 * h.tok.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipMemcpyAsync(base + o_child, h.child.data(), 4 * h.child.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipMemcpyAsync(base + o_live0, live0.data(), 4 * live0.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(base + o_rec, rec.data(), 4 * rec.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     (void)hipFree(t->dmem);
@@ -197,6 +205,7 @@ tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_
   d.tok = reinterpret_cast<const int32_t*>(base + o_tok);
   d.child = reinterpret_cast<const int32_t*>(base + o_child);
   d.live0 = reinterpret_cast<const int32_t*>(base + o_live0);
+  d.node_rec = reinterpret_cast<const tms::NodeRec*>(base + o_rec);
   d.n_nodes = h.n_nodes;
   d.n_edges = h.n_edges;
   d.n_entries = h.n_entries;
@@ -319,7 +328,10 @@ tms_status tms_state_create(tms_trie* trie, int32_t B, int32_t k, const void* em
     const int v = std::atoi(env);
     if (v > 0) st->split = v;
   }
-  if (const char* env = std::getenv("TMS_GRAPH")) st->use_graph = std::atoi(env) != 0;
+  if (const char* env = std::getenv("TMS_LOOP")) {
+    const int v = std::atoi(env);
+    if (v >= TMS_LOOP_RESIDENT && v <= TMS_LOOP_STREAM) st->loop_mode = v;
+  }
   st->host_status.assign(B, 0);
   e = hipStreamCreateWithFlags(&st->capture, hipStreamNonBlocking);
   if (e != hipSuccess) {
@@ -425,6 +437,20 @@ tms_status tms_decode_k_pointers(tms_state* st, const void* hidden_seq, int32_t 
   if (T < need)
     return fail(TMS_ERR_INVALID_ARG, "T = " + std::to_string(T) + " < k*(max_depth+1) = " + std::to_string(need));
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (st->loop_mode == TMS_LOOP_RESIDENT) {
+    tms::LoopIO io{};
+    io.emb = st->emb;
+    io.hidden_seq = hidden_seq;
+    io.H = st->H;
+    io.V = st->trie->host.vocab;
+    io.T = T;
+    io.tokens_bt = tokens;
+    io.len = len;
+    io.entries = entries;
+    const bool lds_live = tms::loop_lds_bytes(st->trie->dev, st->dev) <= 65536;
+    TMS_HIP(tms::launch_loop(st->trie->dev, st->dev, io, st->dtype, st->fast, lds_live, s), "loop launch");
+    return TMS_OK;
+  }
   const size_t step_bytes = size_t(st->B) * st->H * elem_size(st->dtype);
   auto enqueue = [&](hipStream_t q) -> hipError_t {
     for (int32_t t = 0; t < T; ++t) {
@@ -437,7 +463,7 @@ tms_status tms_decode_k_pointers(tms_state* st, const void* hidden_seq, int32_t 
     }
     return tms::launch_finalize(st->dev, len, entries, q);
   };
-  if (!st->use_graph) {
+  if (st->loop_mode == TMS_LOOP_STREAM) {
     TMS_HIP(enqueue(s), "step loop launch");
     return TMS_OK;
   }
@@ -507,6 +533,13 @@ tms_status tms_debug_set_live(tms_state* st, int32_t s, int32_t edge, int32_t va
 tms_status tms_state_set_split(tms_state* st, int32_t split) {
   if (!st || split < 0 || split > 4096) return fail(TMS_ERR_INVALID_ARG, "split must be in [0, 4096]");
   st->split = split == 0 ? st->split_default : split;
+  destroy_graph(st);
+  return TMS_OK;
+}
+
+tms_status tms_state_set_loop(tms_state* st, int32_t mode) {
+  if (!st || mode < TMS_LOOP_RESIDENT || mode > TMS_LOOP_STREAM) return fail(TMS_ERR_INVALID_ARG, "unknown loop mode");
+  st->loop_mode = mode;
   destroy_graph(st);
   return TMS_OK;
 }

@@ -9,12 +9,19 @@ namespace tms {
 enum : int32_t { kSeqOk = 0, kSeqEmptyMask = 5, kSeqNotWalkable = 6, kSeqNotDone = 7 };
 enum : int32_t { kChildSep = -1, kChildStop = -2 };
 
+// One 16-byte record per node: its edge range [b0, b1) and the catalog entry
+// ending there (-1 if none).
+struct alignas(16) NodeRec {
+  int32_t b0, b1, ent, pad;
+};
+
 struct DevTrie {
   const int32_t* begin;  // [n_nodes+1]
   const int32_t* entry;  // [n_nodes]
   const int32_t* tok;    // [n_edges]
   const int32_t* child;  // [n_edges]
   const int32_t* live0;  // [live_stride], zero padded past n_edges
+  const NodeRec* node_rec;  // [n_nodes]
   int32_t n_nodes, n_edges, n_entries, cap, max_depth, sep, stop, vocab;
   int32_t live_stride;   // n_edges rounded up to a multiple of 4
 };
@@ -51,10 +58,24 @@ struct StepIO {
   int32_t T, t;
 };
 
+// Inputs and outputs of the resident device loop.
+struct LoopIO {
+  const void* emb;         // [V][H]
+  const void* hidden_seq;  // [T][B][H]
+  int32_t H, V, T;
+  int32_t* tokens_bt;      // [B][T]
+  int32_t* len;            // [B] or null
+  int32_t* entries;        // [B][k] or null
+};
+
 // dtype: 0 fp32, 1 bf16.  Every launcher returns hipGetLastError().
 hipError_t launch_reset(const DevTrie& tr, const DevState& st, hipStream_t s);
 hipError_t launch_step_sparse(const DevTrie& tr, const DevState& st, const StepIO& io, int dtype,
                               bool fast, int split, hipStream_t s);
+hipError_t launch_loop(const DevTrie& tr, const DevState& st, const LoopIO& io, int dtype, bool fast,
+                       bool lds_live, hipStream_t s);
+// LDS bytes the fast-path loop kernel keeps per sequence (live counts + spent flags).
+size_t loop_lds_bytes(const DevTrie& tr, const DevState& st);
 hipError_t launch_dense_step(const DevTrie& tr, const DevState& st, const StepIO& io, int dtype,
                              float* full_logits, int grid, hipStream_t s);
 hipError_t launch_forced(const DevTrie& tr, const DevState& st, const int32_t* forced, hipStream_t s);

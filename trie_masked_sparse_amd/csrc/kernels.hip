@@ -20,8 +20,8 @@
 //   lane l of a wavefront owns 16-byte chunks c = 0,1,.. of a row, i.e. the
 //   elements [c*CH + l*EL, c*CH + l*EL + EL) with EL = 4 (fp32) or 8 (bf16) and
 //   CH = 64*EL; it accumulates h[i]*E[v][i] in fp32 with fused multiply-adds in
-//   ascending element order; the 64 partial sums are then combined by an
-//   xor butterfly (lane distance 32, 16, 8, 4, 2, 1).  The order depends only on
+//   ascending element order; the 64 partial sums are then combined by a fixed
+//   6-level tree (see wave_sum).  The order depends only on
 //   H, never on the workgroup, slot, batch size or path, so equal rows give
 //   equal logits and every path gives bit-identical logits.
 //
@@ -45,6 +45,12 @@ constexpr int kWavesPerBlock = kBlock / kWave;
 // scalar-load views: wave-uniform addresses read through the scalar cache
 typedef const __attribute__((address_space(4))) int32_t* cint_p;
 typedef const __attribute__((address_space(4))) uint32_t* cuint_p;
+
+// node record through the scalar cache (three adjacent dwords of a 16-byte record)
+__device__ __forceinline__ NodeRec rec_scalar(const NodeRec* recs, int n) {
+  const cint_p p = (cint_p)(recs + n);
+  return NodeRec{p[0], p[1], p[2], 0};
+}
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
 
@@ -74,42 +80,87 @@ __device__ __forceinline__ float fma_chunk(const uint4& h, const uint4& e, float
   return acc;
 }
 
+// Sum over the 64 lanes in a fixed tree of depth 6: four in-row DPP levels
+// (partner lane i^1, i^2, then the mirror lane within 8 and within 16, so
+// each level adds two equal-size partial sums and every lane of a 16-lane row
+// ends with the same row sum), then (row0 + row1) + (row2 + row3).  The result
+// is wave-uniform.
+#define TMS_DPP(v, ctrl) __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), (ctrl), 0xF, 0xF, false))
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  v += TMS_DPP(v, 0xB1);   // quad_perm [1,0,3,2]
+  v += TMS_DPP(v, 0x4E);   // quad_perm [2,3,0,1]
+  v += TMS_DPP(v, 0x141);  // row_half_mirror
+  v += TMS_DPP(v, 0x140);  // row_mirror
+  const int b = __float_as_int(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(b, 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(b, 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(b, 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(b, 48));
+  return (r0 + r1) + (r2 + r3);
+}
+#undef TMS_DPP
+
+// Workgroup barrier that orders LDS only: outstanding global loads and stores
+// stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Dot products of up to U rows with the hidden chunks hq held by this lane.
-// rows[u] < 0 skips row u.  All loads are issued before any arithmetic.
-template <int DT, int NC, int U>
-__device__ __forceinline__ void dot_rows(const uint4* __restrict__ emb, int nq, const int (&rows)[U],
-                                         const uint4 (&hq)[NC], float (&out)[U], int lane) {
-  uint4 raw[U][NC];
+// Row loads of up to U rows (rows[u] < 0 skips row u).  Lanes past the end of
+// a partial chunk re-read the row's first chunk and are zeroed afterwards, so
+// the loads need no per-lane branches; chunks past the row end are skipped.
+template <int NC, int U>
+__device__ __forceinline__ void issue_rows(const uint4* __restrict__ emb, int nq, const int (&rows)[U],
+                                           uint4 (&raw)[U][NC], int lane) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    if (rows[u] >= 0) {
-      const uint4* p = emb + (int64_t)rows[u] * nq + lane;
+    if (rows[u] < 0) continue;
+    const uint4* p = emb + (int64_t)rows[u] * nq;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) raw[u][c] = (c * kWave + lane < nq) ? p[c * kWave] : make_uint4(0, 0, 0, 0);
+    for (int c = 0; c < NC; ++c) {
+      if (c * kWave >= nq) break;
+      const int i = c * kWave + lane;
+      raw[u][c] = p[i < nq ? i : 0];
     }
   }
+}
+
+// Finish the dot products started by issue_rows (fixed order, see above).
+template <int DT, int NC, int U>
+__device__ __forceinline__ void finish_rows(int nq, const int (&rows)[U], const uint4 (&raw)[U][NC],
+                                            const uint4 (&hq)[NC], float (&out)[U], int lane) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     float acc = 0.0f;
     if (rows[u] >= 0) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        if (c * kWave + lane < nq) acc = fma_chunk<DT>(hq[c], raw[u][c], acc);
+      for (int c = 0; c < NC; ++c) {
+        if (c * kWave >= nq) break;
+        const float a = fma_chunk<DT>(hq[c], raw[u][c], acc);
+        acc = (c * kWave + lane < nq) ? a : acc;
+      }
     }
     out[u] = wave_sum(acc);
   }
 }
 
+template <int DT, int NC, int U>
+__device__ __forceinline__ void dot_rows(const uint4* __restrict__ emb, int nq, const int (&rows)[U],
+                                         const uint4 (&hq)[NC], float (&out)[U], int lane) {
+  uint4 raw[U][NC];
+  issue_rows<NC, U>(emb, nq, rows, raw, lane);
+  finish_rows<DT, NC, U>(nq, rows, raw, hq, out, lane);
+}
+
 template <int NC>
 __device__ __forceinline__ void load_hidden(const uint4* __restrict__ h, int nq, uint4 (&hq)[NC], int lane) {
 #pragma unroll
-  for (int c = 0; c < NC; ++c) hq[c] = (c * kWave + lane < nq) ? h[c * kWave + lane] : make_uint4(0, 0, 0, 0);
+  for (int c = 0; c < NC; ++c) {
+    const int i = c * kWave + lane;
+    hq[c] = c * kWave < nq ? h[i < nq ? i : 0] : make_uint4(0, 0, 0, 0);
+  }
 }
 
 __device__ __forceinline__ unsigned long long pack_key(float x, uint32_t id) {
@@ -138,9 +189,10 @@ __device__ __forceinline__ bool load_seq(const DevTrie& tr, const DevState& st, 
   q.node = ((cint_p)st.node)[s];
   q.depth = ((cint_p)st.depth)[s];
   q.done = ((cint_p)st.done)[s];
-  q.b0 = ((cint_p)tr.begin)[q.node];
-  q.b1 = ((cint_p)tr.begin)[q.node + 1];
-  const int ent = ((cint_p)tr.entry)[q.node];
+  const NodeRec rec = rec_scalar(tr.node_rec, q.node);
+  q.b0 = rec.b0;
+  q.b1 = rec.b1;
+  const int ent = rec.ent;
   bool ctl = false;
   if (ent >= 0) {
     const uint32_t w = ((cuint_p)st.spent)[(int64_t)s * st.spent_words + (ent >> 5)];
@@ -154,6 +206,11 @@ __device__ __forceinline__ bool load_seq(const DevTrie& tr, const DevState& st, 
 
 __device__ __forceinline__ bool edge_ok(int child, int live, const Seq& q) {
   return child >= 0 ? live > 0 : (child == kChildSep ? q.sep_ok : q.stop_ok);
+}
+
+// edge_ok without short-circuit evaluation
+__device__ __forceinline__ bool edge_ok_bits(int child, int live, const Seq& q) {
+  return ((child >= 0) & (live > 0)) | ((child == kChildSep) & q.sep_ok) | ((child == kChildStop) & q.stop_ok);
 }
 
 __device__ __forceinline__ void write_step_out(const StepIO& io, int s, int tok, float logit) {
@@ -222,19 +279,153 @@ __device__ __forceinline__ int find_edge(const DevTrie& tr, const Seq& q, int to
   return -1;
 }
 
-// ---------------------------------------------------------------------------
-// Fused sparse step: materialise the legal set, gather-GEMV, argmax, advance.
-// Grid: B * split workgroups of 256 threads; workgroup g serves sequence
-// g / split.  Wavefront wv of the sequence's W = 4*split wavefronts takes the
-// edges b0+wv, b0+wv+W, ... of the current node.  The last workgroup of a
-// sequence to finish (arrival counter) reads the combined key and advances.
+// How a scan reads live counts: through the scalar cache (state not written
+// earlier in the same kernel), from LDS, or with ordinary vector loads.
+enum { kLiveScalar = 0, kLiveLds = 1, kLiveVector = 2 };
+
+template <int LIVE>
+__device__ __forceinline__ int read_live_uniform(const int32_t* live, int e) {
+  if constexpr (LIVE == kLiveScalar) return ((cint_p)live)[e];
+  else return __builtin_amdgcn_readfirstlane(live[e]);
+}
+
+// A wavefront's best candidate, carried to the advance so that it needs no
+// further trie reads: the edge's child, its token and the child's record.
+struct Cand {
+  int child, tok, b0, b1, ent;
+};
+
+// Scan the current node's edge range for this wavefront's share of the
+// edges (b0+wv, b0+wv+W, ...), compute a logit for every legal edge and
+// return the wavefront's best packed key (0 if it had no legal edge).
 // FAST: edge records through wave-uniform scalar loads, U edges per pass.
-// GLOBAL: 64 edges per pass through per-lane vector loads, legal ones
-// compacted with a ballot, U rows in flight.
+// GLOBAL: 64 edges per pass through per-lane vector loads, the legal ones
+// compacted with a ballot, U rows in flight.  With CAND the child's node
+// record is fetched alongside the row gathers and returned in cand.
+template <int DT, int NC, bool FAST, int LIVE, bool CAND>
+__device__ __forceinline__ unsigned long long scan_node(const DevTrie& tr, const Seq& q, const int32_t* live,
+                                                        const uint4* __restrict__ emb, int nq,
+                                                        const uint4 (&hq)[NC], int wv, int W, int lane,
+                                                        Cand& cand) {
+  constexpr int U = rows_per_pass(NC);
+  unsigned long long best = 0;
+  if constexpr (FAST) {
+    const cint_p ctok = (cint_p)tr.tok;
+    const cint_p cchild = (cint_p)tr.child;
+    auto pass = [&](int e0) {
+      int rows[U], edges[U], chs[U];
+      // edge records for all U slots first (indices clamped into the range,
+      // out-of-range slots masked afterwards), then one wait
+      int cs[U], ts[U], lvs[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + u * W;
+        const int ee = e < q.b1 ? e : q.b1 - 1;  // every node has at least one edge
+        cs[u] = cchild[ee];
+        ts[u] = ctok[ee];
+        lvs[u] = read_live_uniform<LIVE>(live, ee);  // control edges hold 0
+      }
+      // consume every record here so that all of them are requested together,
+      // before the first row gather (the compiler would otherwise sink them)
+#pragma unroll
+      for (int u = 0; u < U; ++u) asm volatile("" ::"s"(cs[u]), "s"(ts[u]), "s"(lvs[u]));
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + u * W;
+        // bitwise, so that every record load above is used unconditionally
+        const bool ok = (e < q.b1) & edge_ok_bits(cs[u], lvs[u], q);
+        edges[u] = e;
+        rows[u] = ts[u] | -(int)!ok;
+        chs[u] = ok ? cs[u] : -3;
+      }
+      uint4 raw[U][NC];
+      issue_rows<NC, U>(emb, nq, rows, raw, lane);
+      NodeRec recs[U];
+      if constexpr (CAND) {
+        // the children's records travel with the row gathers
+#pragma unroll
+        for (int u = 0; u < U; ++u) recs[u] = chs[u] >= 0 ? tr.node_rec[chs[u]] : NodeRec{0, 0, -1, 0};
+      }
+      float l[U];
+      finish_rows<DT, NC, U>(nq, rows, raw, hq, l, lane);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (rows[u] < 0) continue;
+        const unsigned long long k = pack_key(l[u], (uint32_t)edges[u]);
+        if (k > best) {
+          best = k;
+          if constexpr (CAND) cand = Cand{chs[u], rows[u], recs[u].b0, recs[u].b1, recs[u].ent};
+        }
+      }
+    };
+    pass(q.b0 + wv);
+    for (int e0 = q.b0 + wv + U * W; e0 < q.b1; e0 += U * W) pass(e0);
+  } else {
+    for (int base = q.b0 + wv; base < q.b1; base += kWave * W) {
+      const int e = base + lane * W;
+      int tk = -1, ch = -3;
+      NodeRec rec{0, 0, -1, 0};
+      {
+        const int ee = e < q.b1 ? e : q.b1 - 1;
+        const int c = tr.child[ee];
+        const int t = tr.tok[ee];
+        const int lv = live[ee];  // control edges hold 0
+        const bool ok = (e < q.b1) & edge_ok_bits(c, lv, q);
+        tk = t | -(int)!ok;
+        ch = ok ? c : -3;
+      }
+      if constexpr (CAND) {
+        if (ch >= 0) rec = tr.node_rec[ch];
+      }
+      unsigned long long m = __ballot(tk >= 0);
+      while (m) {
+        int rows[U], edges[U], chs[U], r0[U], r1[U], r2[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (m) {
+            const int j = (int)__builtin_ctzll(m);
+            m &= m - 1;
+            rows[u] = __builtin_amdgcn_readlane(tk, j);
+            edges[u] = base + j * W;
+            if constexpr (CAND) {
+              chs[u] = __builtin_amdgcn_readlane(ch, j);
+              r0[u] = __builtin_amdgcn_readlane(rec.b0, j);
+              r1[u] = __builtin_amdgcn_readlane(rec.b1, j);
+              r2[u] = __builtin_amdgcn_readlane(rec.ent, j);
+            }
+          } else {
+            rows[u] = -1;
+            edges[u] = 0;
+            chs[u] = r0[u] = r1[u] = r2[u] = 0;
+          }
+        }
+        float l[U];
+        dot_rows<DT, NC, U>(emb, nq, rows, hq, l, lane);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (rows[u] < 0) continue;
+          const unsigned long long k = pack_key(l[u], (uint32_t)edges[u]);
+          if (k > best) {
+            best = k;
+            if constexpr (CAND) cand = Cand{chs[u], rows[u], r0[u], r1[u], r2[u]};
+          }
+        }
+      }
+    }
+  }
+  return best;
+}
+
+// ---------------------------------------------------------------------------
+// Fused sparse step (the host-argument form): materialise the legal set,
+// gather-GEMV, argmax, advance, in one launch.
+// Grid: B * split workgroups of 256 threads; workgroup g serves sequence
+// g / split and its wavefronts take a strided share of the node's edges.  The
+// last workgroup of a sequence to finish (arrival counter) reads the combined
+// key and advances; with split == 1 no cross-workgroup traffic is needed.
 // ---------------------------------------------------------------------------
 template <int DT, int NC, bool FAST>
 __global__ __launch_bounds__(kBlock) void step_sparse_kernel(DevTrie tr, DevState st, StepIO io, int split) {
-  constexpr int U = rows_per_pass(NC);
   constexpr int EL = DT == 0 ? 4 : 8;
   const int g = blockIdx.x;
   const int s = g / split;
@@ -250,63 +441,10 @@ __global__ __launch_bounds__(kBlock) void step_sparse_kernel(DevTrie tr, DevStat
   const int nq = io.H / EL;
   uint4 hq[NC];
   load_hidden<NC>((const uint4*)io.hidden + (int64_t)s * nq, nq, hq, lane);
-  const uint4* emb = (const uint4*)io.emb;
   const int32_t* live = st.live + (int64_t)s * tr.live_stride;
-  unsigned long long best = 0;
-
-  if constexpr (FAST) {
-    const cint_p ctok = (cint_p)tr.tok;
-    const cint_p cchild = (cint_p)tr.child;
-    const cint_p clive = (cint_p)live;
-    for (int e0 = q.b0 + wv; e0 < q.b1; e0 += U * W) {
-      int rows[U], edges[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int e = e0 + u * W;
-        edges[u] = e;
-        rows[u] = -1;
-        if (e < q.b1) {
-          const int c = cchild[e];
-          if (edge_ok(c, c >= 0 ? clive[e] : 0, q)) rows[u] = ctok[e];
-        }
-      }
-      float l[U];
-      dot_rows<DT, NC, U>(emb, nq, rows, hq, l, lane);
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (rows[u] >= 0) best = max(best, pack_key(l[u], (uint32_t)edges[u]));
-    }
-  } else {
-    for (int base = q.b0 + wv; base < q.b1; base += kWave * W) {
-      const int e = base + lane * W;
-      int tk = -1;
-      if (e < q.b1) {
-        const int c = tr.child[e];
-        if (edge_ok(c, c >= 0 ? live[e] : 0, q)) tk = tr.tok[e];
-      }
-      unsigned long long m = __ballot(tk >= 0);
-      while (m) {
-        int rows[U], edges[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          if (m) {
-            const int j = (int)__builtin_ctzll(m);
-            m &= m - 1;
-            rows[u] = __builtin_amdgcn_readlane(tk, j);
-            edges[u] = base + j * W;
-          } else {
-            rows[u] = -1;
-            edges[u] = 0;
-          }
-        }
-        float l[U];
-        dot_rows<DT, NC, U>(emb, nq, rows, hq, l, lane);
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          if (rows[u] >= 0) best = max(best, pack_key(l[u], (uint32_t)edges[u]));
-      }
-    }
-  }
+  Cand unused;
+  const unsigned long long best = scan_node<DT, NC, FAST, kLiveScalar, false>(tr, q, live, (const uint4*)io.emb,
+                                                                              nq, hq, wv, W, lane, unused);
 
   __shared__ unsigned long long s_best[kWavesPerBlock];
   __shared__ unsigned long long s_key;
@@ -335,6 +473,213 @@ __global__ __launch_bounds__(kBlock) void step_sparse_kernel(DevTrie tr, DevStat
   if (lane == 0 && split > 1) {
     __hip_atomic_store(&st.key[s], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&st.arrive[s], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Resident device loop (section "The whole loop on the device"): one
+// workgroup per sequence runs every step of the answer without returning to
+// the host or launching again; token, node, path and no-repeat state stay on
+// the device.  Each step is the same scan, arithmetic and tie rule as the
+// step kernel, so the two forms give bit-identical results.  Only this
+// workgroup touches its sequence's state, so steps need no cross-workgroup
+// synchronisation, only workgroup barriers.  FAST: the sequence's live counts
+// and spent flags are copied into LDS for the duration of the loop; GLOBAL:
+// they stay in device memory.
+// ---------------------------------------------------------------------------
+constexpr int kLoopBlock = 512;
+constexpr int kLoopWaves = kLoopBlock / kWave;
+
+template <int DT, int NC, bool FAST, bool LDS_LIVE>
+__global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState st, LoopIO io) {
+  constexpr int EL = DT == 0 ? 4 : 8;
+  extern __shared__ int32_t lds[];
+  __shared__ unsigned long long s_best[kLoopWaves];
+  __shared__ Cand s_cand[kLoopWaves];
+  __shared__ int s_next[8];
+  const int s = blockIdx.x;
+  const int lane = __lane_id();
+  const int wv = wave_id();
+  const int W = kLoopWaves;
+  const int nq = io.H / EL;
+  const int64_t ls = tr.live_stride;
+  int32_t* g_live = st.live + (int64_t)s * ls;
+  uint32_t* g_spent = st.spent + (int64_t)s * st.spent_words;
+  int32_t* live = LDS_LIVE ? lds : g_live;
+  uint32_t* spent = LDS_LIVE ? reinterpret_cast<uint32_t*>(lds + ls) : g_spent;
+  if constexpr (LDS_LIVE) {
+    const int4* src = reinterpret_cast<const int4*>(g_live);
+    int4* dst = reinterpret_cast<int4*>(lds);
+    for (int i = threadIdx.x; i < (int)(ls / 4); i += kLoopBlock) dst[i] = src[i];
+    for (int i = threadIdx.x; i < st.spent_words; i += kLoopBlock) spent[i] = g_spent[i];
+  }
+  int node = st.node[s], depth = st.depth[s], done = st.done[s];
+  int status = st.status[s], fin = st.finished[s], nemit = st.nemit[s];
+  int32_t* path = st.path + (int64_t)s * st.path_stride;
+  int32_t* entries = st.entries + (int64_t)s * st.k;
+  int32_t* tokens = io.tokens_bt + (int64_t)s * io.T;
+  // Wavefront 0 keeps the current path (lane d: edge at depth d), the
+  // completed entries (lane j: entry j) and the tokens of the last 64 steps
+  // (lane t % 64) in registers; they reach device memory only at the end (or
+  // every 64 steps for tokens), so the step barriers need not wait for stores.
+  const bool reg_lists = st.path_stride <= kWave && st.k <= kWave;
+  int my_path = -1, my_ent = -1, my_tok = -1;
+  if (wv == 0 && reg_lists) {
+    if (lane < depth) my_path = path[lane];
+    if (lane < done) my_ent = entries[lane];
+  }
+  const NodeRec root = rec_scalar(tr.node_rec, 0);
+  NodeRec rec = rec_scalar(tr.node_rec, node);
+  __syncthreads();
+  bool ctl0 = false;
+  if (rec.ent >= 0) ctl0 = ((__builtin_amdgcn_readfirstlane(spent[rec.ent >> 5]) >> (rec.ent & 31)) & 1) == 0;
+  bool sep_ok = ctl0 && done + 1 < st.k, stop_ok = ctl0 && done + 1 >= st.k;
+  const uint4* hid = (const uint4*)io.hidden_seq;
+  const uint4* emb = (const uint4*)io.emb;
+  uint4 hq[NC];
+  if (io.T > 0) load_hidden<NC>(hid + (int64_t)s * nq, nq, hq, lane);
+  int t = 0;
+  int t_flushed = 0;  // tokens [0, t_flushed) are in device memory
+  for (; t < io.T && status == kSeqOk && !fin; ++t) {
+    Seq q;
+    q.node = node;
+    q.depth = depth;
+    q.done = done;
+    q.b0 = rec.b0;
+    q.b1 = rec.b1;
+    q.sep_ok = sep_ok;
+    q.stop_ok = stop_ok;
+    Cand cand{0, 0, 0, 0, 0};
+    const unsigned long long best = scan_node<DT, NC, FAST, LDS_LIVE ? kLiveLds : kLiveVector, true>(
+        tr, q, live, emb, nq, hq, wv, W, lane, cand);
+    // the next step's hidden vector does not depend on this step: fetch it now
+    if (t + 1 < io.T) load_hidden<NC>(hid + ((int64_t)(t + 1) * st.B + s) * nq, nq, hq, lane);
+    if (lane == 0) {
+      s_best[wv] = best;
+      s_cand[wv] = cand;
+    }
+    lds_barrier();
+    if (wv == 0) {
+      int wi = 0;
+      unsigned long long key = s_best[0];
+#pragma unroll
+      for (int i = 1; i < kLoopWaves; ++i) {
+        const unsigned long long k = s_best[i];
+        if (k > key) {
+          key = k;
+          wi = i;
+        }
+      }
+      int tok = -1;
+      if (!key) {
+        status = kSeqEmptyMask;
+      } else {
+        const int e = (int)key_id(key);
+        const Cand c = s_cand[wi];
+        tok = c.tok;
+        if (c.child >= 0) {
+          if (reg_lists) {
+            if (lane == depth) my_path = e;
+          } else {
+            if (lane == 0) path[depth] = e;
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // read back by this wavefront
+          }
+          depth += 1;
+          node = c.child;
+          rec = NodeRec{c.b0, c.b1, c.ent, 0};
+        } else {
+          // a pointer completes: release its path, spend its terminal
+          const int ent = rec.ent;
+          if (reg_lists) {
+            if (lane < depth) live[my_path] -= 1;  // distinct edges
+            if (lane == done) my_ent = ent;
+          } else {
+            for (int i = lane; i < depth; i += kWave) live[path[i]] -= 1;
+            if (lane == 0) entries[done] = ent;
+          }
+          if (lane == 0) spent[ent >> 5] |= 1u << (ent & 31);
+          if (!LDS_LIVE || !reg_lists) {
+            // live counts, spent flags or entries in device memory are read
+            // again in later steps
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          }
+          done += 1;
+          depth = 0;
+          if (c.child == kChildStop) {
+            fin = 1;
+          } else {
+            node = 0;
+            rec = root;
+          }
+        }
+        nemit += 1;
+      }
+      // control edges of the node reached: terminal, not yet spent, exactly-k rule
+      bool ctl = false;
+      if (rec.ent >= 0 && !fin && status == kSeqOk) {
+        bool sp;
+        if (reg_lists) sp = __ballot(lane < done && my_ent == rec.ent) != 0ull;
+        else sp = ((__builtin_amdgcn_readfirstlane(spent[rec.ent >> 5]) >> (rec.ent & 31)) & 1) != 0;
+        ctl = !sp;
+      }
+      const bool more = done + 1 < st.k;
+      if (lane == (t & (kWave - 1))) my_tok = tok;
+      if ((t & (kWave - 1)) == kWave - 1) {
+        tokens[t_flushed + lane] = my_tok;
+        t_flushed += kWave;
+      }
+      if (lane == 0) {
+        s_next[0] = node;
+        s_next[1] = depth;
+        s_next[2] = done;
+        s_next[3] = fin | (status << 1);
+        s_next[4] = rec.b0;
+        s_next[5] = rec.b1;
+        s_next[6] = rec.ent;
+        s_next[7] = (ctl && more ? 1 : 0) | (ctl && !more ? 2 : 0);
+      }
+    }
+    if constexpr (LDS_LIVE) lds_barrier();
+    else __syncthreads();  // live counts in device memory: order them too
+    node = s_next[0];
+    depth = s_next[1];
+    done = s_next[2];
+    fin = s_next[3] & 1;
+    status = s_next[3] >> 1;
+    rec = NodeRec{s_next[4], s_next[5], s_next[6], 0};
+    sep_ok = (s_next[7] & 1) != 0;
+    stop_ok = (s_next[7] & 2) != 0;
+  }
+  if (wv == 0) {
+    // tokens of the steps since the last flush, then -1 for the steps not run
+    const int tf = __builtin_amdgcn_readfirstlane(t_flushed);
+    if (tf + lane < t) tokens[tf + lane] = my_tok;
+    if (reg_lists) {
+      if (lane < depth) path[lane] = my_path;
+      if (lane < done) entries[lane] = my_ent;
+    }
+  }
+  for (int i = t + threadIdx.x; i < io.T; i += kLoopBlock) tokens[i] = -1;
+  if (status == kSeqOk && !fin) status = kSeqNotDone;
+  if (threadIdx.x == 0) {
+    st.node[s] = node;
+    st.depth[s] = depth;
+    st.done[s] = done;
+    st.status[s] = status;
+    st.finished[s] = fin;
+    st.nemit[s] = nemit;
+    if (io.len) io.len[s] = nemit;
+  }
+  if (wv == 0 && io.entries) {
+    for (int j = lane; j < st.k; j += kWave)
+      io.entries[(int64_t)s * st.k + j] = (reg_lists && j < kWave) ? (j < done ? my_ent : entries[j]) : entries[j];
+  }
+  if constexpr (LDS_LIVE) {
+    __syncthreads();
+    const int4* src = reinterpret_cast<const int4*>(lds);
+    int4* dst = reinterpret_cast<int4*>(g_live);
+    for (int i = threadIdx.x; i < (int)(ls / 4); i += kLoopBlock) dst[i] = src[i];
+    for (int i = threadIdx.x; i < st.spent_words; i += kLoopBlock) g_spent[i] = spent[i];
   }
 }
 
@@ -568,6 +913,20 @@ struct StepLaunch {
 };
 
 template <int DT, int NC>
+struct LoopLaunch {
+  static hipError_t run(const DevTrie& tr, const DevState& st, const LoopIO& io, bool fast, bool lds_live,
+                        hipStream_t s) {
+    const dim3 grid((unsigned)st.B), block(kLoopBlock);
+    const size_t lds = lds_live ? sizeof(int32_t) * ((size_t)tr.live_stride + (size_t)st.spent_words) : 0;
+    if (fast && lds_live) hipLaunchKernelGGL((loop_kernel<DT, NC, true, true>), grid, block, lds, s, tr, st, io);
+    else if (fast) hipLaunchKernelGGL((loop_kernel<DT, NC, true, false>), grid, block, 0, s, tr, st, io);
+    else if (lds_live) hipLaunchKernelGGL((loop_kernel<DT, NC, false, true>), grid, block, lds, s, tr, st, io);
+    else hipLaunchKernelGGL((loop_kernel<DT, NC, false, false>), grid, block, 0, s, tr, st, io);
+    return hipGetLastError();
+  }
+};
+
+template <int DT, int NC>
 struct DenseLaunch {
   static hipError_t run(const DevState& st, const StepIO& io, float* full, int grid, hipStream_t s) {
     hipLaunchKernelGGL((dense_head_kernel<DT, NC>), dim3(grid), dim3(kBlock), 0, s, st, io, full);
@@ -607,6 +966,15 @@ hipError_t launch_reset(const DevTrie& tr, const DevState& st, hipStream_t s) {
 hipError_t launch_step_sparse(const DevTrie& tr, const DevState& st, const StepIO& io, int dtype, bool fast,
                               int split, hipStream_t s) {
   return dispatch<StepLaunch>(dtype, chunks_for(dtype, io.H), tr, st, io, fast, split, s);
+}
+
+hipError_t launch_loop(const DevTrie& tr, const DevState& st, const LoopIO& io, int dtype, bool fast,
+                       bool lds_live, hipStream_t s) {
+  return dispatch<LoopLaunch>(dtype, chunks_for(dtype, io.H), tr, st, io, fast, lds_live, s);
+}
+
+size_t loop_lds_bytes(const DevTrie& tr, const DevState& st) {
+  return sizeof(int32_t) * ((size_t)tr.live_stride + (size_t)st.spent_words);
 }
 
 hipError_t launch_dense_step(const DevTrie& tr, const DevState& st, const StepIO& io, int dtype, float* full,
