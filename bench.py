@@ -10,10 +10,11 @@ after W warmup steps, bracketed by device synchronisations.
 Also reported on the same line: the loop kernel's roofline (algorithmic bytes
 of one answer / that launch's duration, timed with HIP events on the launch
 stream), the same answers through the hipGraph of per-step kernels, the
-batch-64 workloads, the gather-GEMV bandwidth stress shape
-(64 x 256 distinct rows per launch cycling through 9 disjoint row sets, 604 MB
-of the 622 MB table), the dense+mask step, and the CPU oracle timed on this
-host (cpu_baseline leg, the only place the oracle is used here).
+batch-64 workloads, the gather-GEMV bandwidth stress shapes (64 sequences x
+256 or x 887 distinct rows per launch, cycling through disjoint row sets of
+the 622 MB table), the dense+mask step, and the CPU oracle timed on this host
+(cpu_baseline leg, the only place the oracle is used here).  --only copyref
+runs a 256 MiB device copy that calibrates the HBM byte counters.
 """
 from __future__ import annotations
 
@@ -70,10 +71,16 @@ class Workload:
         self.esz = 2 if c.dtype == "bf16" else 4
         self.np = np
 
-    def decode(self):
+    def decode(self, ev=None):
+        """One bench step: reset, then the whole answer.  ev: optional pair of
+        events recorded around the decode launch (after the reset)."""
         import trie_masked_sparse_amd as tms
         self.state.reset()
+        if ev:
+            ev[0].record()
         tms.decode_k_pointers(self.state.h, self.hid, self.tokens, self.len, self.entries)
+        if ev:
+            ev[1].record()
 
     def legal_profile(self):
         """Per step: legal-set sizes and unique rows, from the library's own
@@ -121,49 +128,38 @@ def time_decode(w: Workload, steps: int, warmup: int):
         w.decode()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
     e0.record()
-    for _ in range(steps):
-        w.decode()
+    for i in range(steps):
+        w.decode(evs[i])
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = e0.elapsed_time(e1)
+    decode_us = sum(a.elapsed_time(b) for a, b in evs) * 1e3 / steps  # the decode launch alone
     ln = w.len.cpu().numpy()
     assert (w.state.status() == 0).all(), "decode reported a device error"
     steps_per_call = int(ln.max())  # lockstep steps that emitted a token
     tokens_per_call = int(ln.sum())
     return {
-        "wall_s": wall, "gpu_ms": gpu_ms, "ms_per_call": wall * 1e3 / steps,
+        "wall_s": wall, "gpu_ms": gpu_ms, "ms_per_call": wall * 1e3 / steps, "decode_launch_us": decode_us,
         "steps_per_s": steps_per_call * steps / wall, "tokens_per_s": tokens_per_call * steps / wall,
         "steps_per_call": steps_per_call, "tokens_per_call": tokens_per_call, "launches_per_call": w.T,
     }
 
 
-def reset_us(w: Workload, n: int = 50):
-    import torch
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(n):
-        w.state.reset()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / n
-
-
 def loop_roofline(w: Workload, timed: dict, steps: int):
     """Algorithmic bytes of one whole answer (the resident loop kernel's launch)
-    over that launch's duration: the event-timed region divided by the number
-    of answers, minus the separately timed state reset."""
+    over that launch's average duration, from the event pairs recorded around
+    each decode launch inside the timed region."""
     n_rows, n_act, n_uni = w.legal_profile()
     H, esz = w.c.hidden, w.esz
     gathered = float(((n_rows + n_act) * H * esz).sum())   # legal rows + hidden vectors
     unique = float(((n_uni + n_act) * H * esz).sum())
-    r_us = reset_us(w)
-    launch_us = timed["gpu_ms"] * 1e3 / steps - r_us
+    launch_us = timed["decode_launch_us"]
     return {
-        "kernel": "loop_kernel", "avg_launch_us": launch_us, "reset_us": r_us,
+        "kernel": "loop_kernel", "avg_launch_us": launch_us,
         "alg_bytes_per_launch": gathered, "unique_bytes_per_launch": unique,
         "achieved_GBps": gathered / (launch_us * 1e-6) / 1e9, "unique_GBps": unique / (launch_us * 1e-6) / 1e9,
         "rows_per_step": [int(x) for x in n_rows],
@@ -180,15 +176,17 @@ def graph_mode(w: Workload, steps: int, warmup: int):
             "step_kernel_launches_per_call": w.T}
 
 
-def stress_gemv(steps: int, warmup: int, emb, emb_np):
-    """64 sequences x 256 distinct rows per launch, 9 disjoint row sets."""
+def stress_gemv(steps: int, warmup: int, emb, emb_np, rows_per_seq: int):
+    """64 sequences x rows_per_seq distinct rows per launch, cycling through
+    disjoint row sets so that no launch re-reads a row of the previous one."""
     import numpy as np
     import torch
 
     import trie_masked_sparse_amd as tms
     from synth import bf16_bits_from_f32, stress_rows
     V, H = emb_np.shape
-    B, R, S = 64, 256, 9
+    B, R = 64, rows_per_seq
+    S = V // (B * R)
     sets = [_to_dev(np.ascontiguousarray(s)) for s in stress_rows(V, B, R, S)]
     rng = np.random.Generator(np.random.PCG64(5))
     hid = _to_dev(bf16_bits_from_f32(rng.standard_normal((B, H), dtype=np.float32)))
@@ -204,30 +202,26 @@ def stress_gemv(steps: int, warmup: int, emb, emb_np):
         tms.gather_gemv(emb, hid, sets[i % S], n, out)
     e1.record()
     torch.cuda.synchronize()
-    durs = np.array([e0.elapsed_time(e1) * 1e3 / iters])  # back-to-back launches, us each
+    us = e0.elapsed_time(e1) * 1e3 / iters  # back-to-back launches on the launch stream
     nbytes = B * R * H * 2 + B * H * 2
-    return {"shape": "64 seq x 256 distinct rows, H=2048 bf16, 9 disjoint sets (604 MB)",
-            "avg_launch_us": float(durs.mean()), "alg_bytes_per_launch": nbytes,
-            "achieved_GBps": nbytes / (durs.mean() * 1e-6) / 1e9,
-            "frac_of_8TBps": nbytes / (durs.mean() * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {"shape": f"64 seq x {R} distinct rows, H={H} bf16, {S} disjoint sets ({S * B * R * H * 2 >> 20} MiB)",
+            "kernel": "gather_gemv_kernel", "avg_launch_us": us, "alg_bytes_per_launch": nbytes,
+            "achieved_GBps": gbps, "frac_of_8TBps": gbps / HBM_PEAK_GBPS,
+            "traffic": _pmc_traffic("gather_gemv", f"stress64x{R}")}
 
 
-def stream_read_GBps():
-    """Reference: torch's sum over 2 GiB of bf16 (a plain streaming read)."""
+def copy_reference(reps: int = 5):
+    """A plain device-to-device copy of 256 MiB (torch's copy kernel): the known
+    byte count that calibrates the HBM counters FETCH_SIZE and WRITE_SIZE."""
     import torch
-    x = torch.ones(1 << 30, dtype=torch.bfloat16, device="cuda")
-    for _ in range(3):
-        x.sum()
+    src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(10):
-        x.sum()
-    e1.record()
+    for _ in range(reps):
+        dst.copy_(src)
     torch.cuda.synchronize()
-    gbps = 10 * x.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del x
-    return gbps
+    return {"bytes_read": src.numel(), "bytes_written": dst.numel(), "reps": reps}
 
 
 def dense_step_us(w: Workload, reps=5):
@@ -288,7 +282,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--only", default="", help="comma list: headline,b64,stress,dense,cpu (default all)")
+    ap.add_argument("--only", default="",
+                    help="comma list of headline,b64,stress,dense,cpu,copyref (default: all but copyref)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
@@ -297,7 +292,7 @@ def main():
     only = set(filter(None, args.only.split(",")))
 
     def want(x):
-        return not only or x in only
+        return (not only and x != "copyref") or x in only
 
     import torch
 
@@ -336,9 +331,11 @@ def main():
         also["dense_masked_product_B1"] = dense_step_us(w)
         _log(f"dense {also['dense_masked_product_B1']}")
     if want("stress"):
-        also["gather_gemv_stress"] = stress_gemv(max(3, args.steps // 5), 2, w.emb, w.emb_np)
-        _log(f"stress {also['gather_gemv_stress']}")
-        also["stream_read_GBps"] = stream_read_GBps()
+        for rows in (256, 887):
+            also[f"gather_gemv_stress_64x{rows}"] = stress_gemv(max(3, args.steps // 5), 2, w.emb, w.emb_np, rows)
+            _log(f"stress {also[f'gather_gemv_stress_64x{rows}']}")
+    if want("copyref"):
+        also["copy_reference"] = copy_reference()
     if want("b64"):
         for cid in ("structured", "unstructured"):
             _log(f"{cid} workload")

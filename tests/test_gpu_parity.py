@@ -489,3 +489,24 @@ def test_loop_fast_store_live_in_memory():
     cat = random_catalog(42, 3000, 6, 200, min_len=3)
     info = _loop_forms_agree(cat, 1024, 4, 5, 512, tms.PATH_FAST, 3, "fast_global_live")
     assert info["path"] == tms.PATH_FAST and info["n_edges"] * 4 > 65536
+
+
+def test_bf16_pair_product_rounding():
+    """How one v_dot2_f32_bf16 rounds (an in-bounds check through the sparse
+    head with H = 8, where lane 0 holds the whole row): 1.0 from the first
+    pair, then products 2^-24 and 2^-25 from the second pair.  A single
+    rounding of the pair sum (or of the exact three-term sum) gives 1 + 2^-23;
+    adding the products to the running sum one at a time gives 1.0.  Either way
+    a pair costs at most two roundings, the assumption behind the tie bound."""
+    from synth import bf16_bits_from_f32
+    h = np.zeros((1, 8), np.float32)
+    e = np.zeros((2, 8), np.float32)
+    h[0, :4] = [1.0, 0.0, 2.0 ** -12, 2.0 ** -13]
+    e[0, :4] = [1.0, 0.0, 2.0 ** -12, 2.0 ** -12]
+    hb, eb = bf16_bits_from_f32(h), bf16_bits_from_f32(e)
+    out = torch.zeros((1, 2), dtype=torch.float32, device="cuda")
+    tms.gather_gemv(to_dev(eb), to_dev(hb), torch.tensor([[0, 1]], dtype=torch.int32, device="cuda"),
+                    torch.tensor([1], dtype=torch.int32, device="cuda"), out)
+    got = float(out[0, 0])
+    assert got in (1.0 + 2.0 ** -23, 1.0), got
+    print("v_dot2_f32_bf16 pair:", "single rounding" if got != 1.0 else "sequential")

@@ -88,6 +88,16 @@ int default_split(int B, int cap) {
   return std::max(1, s);
 }
 
+// Gather-GEMV workgroups per sequence: 4096 wavefronts for short lists (one
+// pass of rows each), 2048 for long ones (several double-buffered passes),
+// the faster choice in measurements at 64 x 256 and 64 x 887 rows.
+int gemv_split(int B, int cap) {
+  const int target_waves = int64_t(B) * cap <= 32768 ? 4096 : 2048;
+  int s = (target_waves + 4 * B - 1) / (4 * B);
+  s = std::min(s, std::max(1, (cap + 3) / 4));
+  return std::max(1, s);
+}
+
 void destroy_graph(tms_state* st) {
   if (st->gexec) (void)hipGraphExecDestroy(st->gexec);
   if (st->graph) (void)hipGraphDestroy(st->graph);
@@ -513,7 +523,13 @@ tms_status tms_gather_gemv(const void* emb, tms_dtype dtype, int32_t V, int32_t 
   if (dtype != TMS_F32 && dtype != TMS_BF16) return fail(TMS_ERR_INVALID_ARG, "dtype must be fp32 or bf16");
   if (V < 1 || B < 1 || cap < 1 || B > (1 << 24)) return fail(TMS_ERR_INVALID_ARG, "bad sizes");
   if (tms::chunks_for(dtype, H) == 0) return fail(TMS_ERR_INVALID_ARG, "unsupported H");
-  const int split = default_split(B, cap);
+  // workgroups per sequence: each wavefront owns at most 64 consecutive slots
+  static const int env_split = [] {
+    const char* e = std::getenv("TMS_GEMV_SPLIT");
+    return e ? std::atoi(e) : 0;
+  }();
+  int split = env_split > 0 ? env_split : gemv_split(B, cap);
+  split = std::max(split, (cap + 255) / 256);
   if (int64_t(B) * split > (int64_t(1) << 31) - 1) return fail(TMS_ERR_INVALID_ARG, "grid too large");
   TMS_HIP(tms::launch_gather_gemv(emb, dtype, V, H, hidden, rows, n_rows, B, cap, out, split,
                                   static_cast<hipStream_t>(stream)),

@@ -19,8 +19,9 @@
 // Arithmetic contract (identical in every kernel that produces a logit):
 //   lane l of a wavefront owns 16-byte chunks c = 0,1,.. of a row, i.e. the
 //   elements [c*CH + l*EL, c*CH + l*EL + EL) with EL = 4 (fp32) or 8 (bf16) and
-//   CH = 64*EL; it accumulates h[i]*E[v][i] in fp32 with fused multiply-adds in
-//   ascending element order; the 64 partial sums are then combined by a fixed
+//   CH = 64*EL; it accumulates h[i]*E[v][i] in fp32 in ascending element order
+//   (fp32: one fused multiply-add per element; bf16: one v_dot2_f32_bf16 per
+//   pair of adjacent elements); the 64 partial sums are then combined by a fixed
 //   6-level tree (see wave_sum).  The order depends only on
 //   H, never on the workgroup, slot, batch size or path, so equal rows give
 //   equal logits and every path gives bit-identical logits.
@@ -56,10 +57,17 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 
 __host__ __device__ constexpr int rows_per_pass(int nc) { return nc <= 4 ? 4 : (nc == 8 ? 2 : 1); }
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// acc += h . e over one 16-byte chunk, ascending element order
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t h, uint32_t e, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, h), __builtin_bit_cast(bf16x2_t, e), acc,
+                                         false);
+}
+
+// acc += h . e over one 16-byte chunk in ascending element order: fp32 rows
+// one fused multiply-add per element; bf16 rows one v_dot2_f32_bf16 per pair
+// of adjacent elements (both products added to the fp32 running sum).
 template <int DT>
 __device__ __forceinline__ float fma_chunk(const uint4& h, const uint4& e, float acc) {
   if constexpr (DT == 0) {
@@ -68,14 +76,10 @@ __device__ __forceinline__ float fma_chunk(const uint4& h, const uint4& e, float
     acc = fmaf(__uint_as_float(h.z), __uint_as_float(e.z), acc);
     acc = fmaf(__uint_as_float(h.w), __uint_as_float(e.w), acc);
   } else {
-    acc = fmaf(bf16_lo(h.x), bf16_lo(e.x), acc);
-    acc = fmaf(bf16_hi(h.x), bf16_hi(e.x), acc);
-    acc = fmaf(bf16_lo(h.y), bf16_lo(e.y), acc);
-    acc = fmaf(bf16_hi(h.y), bf16_hi(e.y), acc);
-    acc = fmaf(bf16_lo(h.z), bf16_lo(e.z), acc);
-    acc = fmaf(bf16_hi(h.z), bf16_hi(e.z), acc);
-    acc = fmaf(bf16_lo(h.w), bf16_lo(e.w), acc);
-    acc = fmaf(bf16_hi(h.w), bf16_hi(e.w), acc);
+    acc = dot2_bf16(h.x, e.x, acc);
+    acc = dot2_bf16(h.y, e.y, acc);
+    acc = dot2_bf16(h.z, e.z, acc);
+    acc = dot2_bf16(h.w, e.w, acc);
   }
   return acc;
 }
@@ -111,7 +115,12 @@ __device__ __forceinline__ void lds_barrier() {
 // Row loads of up to U rows (rows[u] < 0 skips row u).  Lanes past the end of
 // a partial chunk re-read the row's first chunk and are zeroed afterwards, so
 // the loads need no per-lane branches; chunks past the row end are skipped.
-template <int NC, int U>
+// NT marks the loads non-temporal (rows read once per launch: the explicit
+// row-list head and the dense head); the decode step keeps rows cacheable
+// because sequences at the same node share them.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+template <int NC, int U, bool NT = false>
 __device__ __forceinline__ void issue_rows(const uint4* __restrict__ emb, int nq, const int (&rows)[U],
                                            uint4 (&raw)[U][NC], int lane) {
 #pragma unroll
@@ -122,7 +131,13 @@ __device__ __forceinline__ void issue_rows(const uint4* __restrict__ emb, int nq
     for (int c = 0; c < NC; ++c) {
       if (c * kWave >= nq) break;
       const int i = c * kWave + lane;
-      raw[u][c] = p[i < nq ? i : 0];
+      const uint4* a = p + (i < nq ? i : 0);
+      if constexpr (NT) {
+        const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(a));
+        raw[u][c] = make_uint4(v.x, v.y, v.z, v.w);
+      } else {
+        raw[u][c] = *a;
+      }
     }
   }
 }
@@ -133,11 +148,15 @@ __device__ __forceinline__ void finish_rows(int nq, const int (&rows)[U], const 
                                             const uint4 (&hq)[NC], float (&out)[U], int lane) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
+    out[u] = 0.0f;
+    if (rows[u] < 0) continue;
     float acc = 0.0f;
-    if (rows[u] >= 0) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        if (c * kWave >= nq) break;
+    for (int c = 0; c < NC; ++c) {
+      if (c * kWave >= nq) break;
+      if ((c + 1) * kWave <= nq) {
+        acc = fma_chunk<DT>(hq[c], raw[u][c], acc);  // full chunk
+      } else {
         const float a = fma_chunk<DT>(hq[c], raw[u][c], acc);
         acc = (c * kWave + lane < nq) ? a : acc;
       }
@@ -146,11 +165,11 @@ __device__ __forceinline__ void finish_rows(int nq, const int (&rows)[U], const 
   }
 }
 
-template <int DT, int NC, int U>
+template <int DT, int NC, int U, bool NT = false>
 __device__ __forceinline__ void dot_rows(const uint4* __restrict__ emb, int nq, const int (&rows)[U],
                                          const uint4 (&hq)[NC], float (&out)[U], int lane) {
   uint4 raw[U][NC];
-  issue_rows<NC, U>(emb, nq, rows, raw, lane);
+  issue_rows<NC, U, NT>(emb, nq, rows, raw, lane);
   finish_rows<DT, NC, U>(nq, rows, raw, hq, out, lane);
 }
 
@@ -732,7 +751,7 @@ __global__ __launch_bounds__(kBlock) void dense_head_kernel(DevState st, StepIO 
     for (int b = 0; b < st.B; ++b) {
       if (st.B > 1) load_hidden<NC>((const uint4*)io.hidden + (int64_t)b * nq, nq, hq, lane);
       float l[U];
-      dot_rows<DT, NC, U>(emb, nq, rows, hq, l, lane);
+      dot_rows<DT, NC, U, true>(emb, nq, rows, hq, l, lane);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (rows[u] < 0) continue;
@@ -806,11 +825,31 @@ __global__ __launch_bounds__(kWave) void legal_set_kernel(DevTrie tr, DevState s
 }
 
 // The sparse head alone over explicit row lists (same arithmetic as the step).
+// Wavefront wv of a sequence's W = 4*split wavefronts owns the R consecutive
+// list slots [wv*R, wv*R + R) (R <= 64): one coalesced load brings all its
+// row ids, the count is read alongside, and the rows go through passes of U
+// with the next pass's gathers in flight while the current pass is reduced.
+template <int U>
+__device__ __forceinline__ void pop_rows(unsigned long long& m, int id, int (&rows)[U], int (&slots)[U]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (m) {
+      const int j = (int)__builtin_ctzll(m);
+      m &= m - 1;
+      rows[u] = __builtin_amdgcn_readlane(id, j);
+      slots[u] = j;
+    } else {
+      rows[u] = -1;
+      slots[u] = 0;
+    }
+  }
+}
+
 template <int DT, int NC>
 __global__ __launch_bounds__(kBlock) void gather_gemv_kernel(const uint4* __restrict__ emb, int V, int H,
                                                              const uint4* __restrict__ hidden,
                                                              const int32_t* rows_in, const int32_t* n_rows,
-                                                             int cap, float* out, int split) {
+                                                             int cap, float* out, int split, int R) {
   constexpr int U = rows_per_pass(NC);
   constexpr int EL = DT == 0 ? 4 : 8;
   const int g = blockIdx.x;
@@ -818,32 +857,39 @@ __global__ __launch_bounds__(kBlock) void gather_gemv_kernel(const uint4* __rest
   const int w = g - s * split;
   const int lane = __lane_id();
   const int wv = w * kWavesPerBlock + wave_id();
-  const int W = split * kWavesPerBlock;
+  const int j0 = wv * R;
+  if (j0 >= cap) return;
+  const int jl = j0 + lane;
+  const bool in_cap = lane < R && jl < cap;
+  const int id = in_cap ? rows_in[(int64_t)s * cap + jl] : -1;  // slots inside [B][cap]
   const int n = min(((cint_p)n_rows)[s], cap);
-  if (n <= 0) return;
   const int nq = H / EL;
   uint4 hq[NC];
   load_hidden<NC>(hidden + (int64_t)s * nq, nq, hq, lane);
-  const cint_p crow = (cint_p)(rows_in + (int64_t)s * cap);
-  float* o = out + (int64_t)s * cap;
-  for (int j0 = wv; j0 < n; j0 += U * W) {
-    int rows[U];
-    bool bad[U];
+  float* o = out + (int64_t)s * cap + j0;
+  const bool listed = in_cap && jl < n;
+  const bool valid = listed && id >= 0 && id < V;
+  if (listed && !valid) o[lane] = NAN;
+  unsigned long long m = __ballot(valid);
+  int rows_a[U], slots_a[U], rows_b[U], slots_b[U];
+  uint4 raw_a[U][NC], raw_b[U][NC];
+  float l[U];
+  pop_rows<U>(m, id, rows_a, slots_a);
+  issue_rows<NC, U, true>(emb, nq, rows_a, raw_a, lane);
+  while (rows_a[0] >= 0) {
+    pop_rows<U>(m, id, rows_b, slots_b);
+    issue_rows<NC, U, true>(emb, nq, rows_b, raw_b, lane);
+    finish_rows<DT, NC, U>(nq, rows_a, raw_a, hq, l, lane);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = j0 + u * W;
-      const int r = j < n ? crow[j] : -1;
-      const bool valid = r >= 0 && r < V;
-      bad[u] = j < n && !valid;
-      rows[u] = valid ? r : -1;
-    }
-    float l[U];
-    dot_rows<DT, NC, U>(emb, nq, rows, hq, l, lane);
+    for (int u = 0; u < U; ++u)
+      if (rows_a[u] >= 0 && lane == u) o[slots_a[u]] = l[u];
+    if (rows_b[0] < 0) break;
+    pop_rows<U>(m, id, rows_a, slots_a);
+    issue_rows<NC, U, true>(emb, nq, rows_a, raw_a, lane);
+    finish_rows<DT, NC, U>(nq, rows_b, raw_b, hq, l, lane);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = j0 + u * W;
-      if (lane == u && j < n) o[j] = bad[u] ? NAN : l[u];
-    }
+    for (int u = 0; u < U; ++u)
+      if (rows_b[u] >= 0 && lane == u) o[slots_b[u]] = l[u];
   }
 }
 
@@ -938,8 +984,10 @@ template <int DT, int NC>
 struct GemvLaunch {
   static hipError_t run(const void* emb, int V, int H, const void* hidden, const int32_t* rows,
                         const int32_t* n_rows, int B, int cap, float* out, int split, hipStream_t s) {
+    const int W = split * kWavesPerBlock;
+    const int R = (cap + W - 1) / W;
     hipLaunchKernelGGL((gather_gemv_kernel<DT, NC>), dim3((unsigned)(B * split)), dim3(kBlock), 0, s,
-                       (const uint4*)emb, V, H, (const uint4*)hidden, rows, n_rows, cap, out, split);
+                       (const uint4*)emb, V, H, (const uint4*)hidden, rows, n_rows, cap, out, split, R);
     return hipGetLastError();
   }
 };
