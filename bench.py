@@ -128,16 +128,22 @@ def time_decode(w: Workload, steps: int, warmup: int):
         w.decode()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
     e0.record()
     for i in range(steps):
-        w.decode(evs[i])
+        w.decode()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = e0.elapsed_time(e1)
-    decode_us = sum(a.elapsed_time(b) for a, b in evs) * 1e3 / steps  # the decode launch alone
+    # a second pass of the same bench steps with an event pair around each
+    # decode launch: the loop kernel's own duration, for the roofline (kept out
+    # of the region above, where the extra markers would lengthen the timeline)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        w.decode(evs[i])
+    torch.cuda.synchronize()
+    decode_us = sum(a.elapsed_time(b) for a, b in evs) * 1e3 / steps
     ln = w.len.cpu().numpy()
     assert (w.state.status() == 0).all(), "decode reported a device error"
     steps_per_call = int(ln.max())  # lockstep steps that emitted a token
@@ -242,7 +248,10 @@ def dense_step_us(w: Workload, reps=5):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / n
     table = w.c.vocab * w.c.hidden * w.esz
-    return {"B": w.B, "us_per_step": us, "table_GBps": table / (us * 1e-6) / 1e9}
+    flops = 2.0 * w.B * w.c.vocab * w.c.hidden
+    return {"B": w.B, "us_per_step": us, "table_GBps": table / (us * 1e-6) / 1e9,
+            "head": "matrix cores (v_mfma_f32_16x16x32_bf16)" if w.B > 1 and w.c.dtype == "bf16" else "vector units",
+            "TFLOPs": flops / (us * 1e-6) / 1e12}
 
 
 def cpu_baseline(w: Workload, min_seconds: float):
@@ -330,6 +339,10 @@ def main():
     if want("dense"):
         also["dense_masked_product_B1"] = dense_step_us(w)
         _log(f"dense {also['dense_masked_product_B1']}")
+        wd = Workload("structured")
+        also["dense_masked_structured_B64"] = dense_step_us(wd)
+        _log(f"dense B=64 {also['dense_masked_structured_B64']}")
+        wd.close()
     if want("stress"):
         for rows in (256, 887):
             also[f"gather_gemv_stress_64x{rows}"] = stress_gemv(max(3, args.steps // 5), 2, w.emb, w.emb_np, rows)

@@ -77,10 +77,13 @@ def run_step_loop(state: tms.State, hid_dev: torch.Tensor, dense: bool = False, 
     return toks.cpu().numpy().T.copy(), lg.cpu().numpy().T.copy()
 
 
-def compare(gpu_tokens, ref, H, gpu_logits=None, gpu_len=None, gpu_entries=None, where=""):
-    """Apply the comparison rules; returns the list of tie-explained flips."""
+def compare(gpu_tokens, ref, H, gpu_logits=None, gpu_len=None, gpu_entries=None, where="", depth=None):
+    """Apply the comparison rules; returns the list of tie-explained flips.
+    depth: summation depth behind the tie bound (default: the vector kernels'
+    declared tree; H + 1 for the matrix-core head, whose order is the
+    hardware's)."""
     B, T = ref["tokens"].shape
-    d = tree_depth(H)
+    d = tree_depth(H) if depth is None else depth
     flips = []
     for b in range(B):
         flipped = False

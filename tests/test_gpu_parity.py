@@ -246,31 +246,53 @@ def test_two_tries_no_contamination():
 # Dense + mask cross-check
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("cid,B", [("tiny", 1), ("product", 1), ("structured", 8), ("unstructured", 4)])
-def test_dense_masked_matches_sparse(cid, B):
+@pytest.mark.parametrize("cid,B", [("tiny", 1), ("product", 1), ("structured", 8), ("unstructured", 4),
+                                   ("structured", 64), ("large", 24)])
+def test_dense_masked_matches_sparse(cid, B, monkeypatch):
+    """Dense head + mask against the sparse step and the oracle.  B = 1 (and the
+    vector head at any B) uses the sparse head's per-row arithmetic, so logits
+    and tokens are bit-identical; the matrix-core head at B > 1 sums in its own
+    order, so it is held to the oracle with the any-order tolerance and tie
+    rule."""
     c, otr, T, hid = config_case(cid, B=B)
+    if cid == "large":
+        T = 12  # the first answers' steps; the oracle below decodes the same prefix
+        hid = hid[:T]
     trie = tms.Trie(catalog(cid), c.vocab, c.sep, c.stop)
-    st = tms.State(trie, B, c.k, dev_embedding(cid))
     hd = to_dev(hid)
+    st = tms.State(trie, B, c.k, dev_embedding(cid))
     s_tok, s_lg = run_step_loop(st, hd)
     st.reset()
-    full = torch.zeros((T, B, c.vocab), dtype=torch.float32, device="cuda") if B == 1 else None
+    nfull = min(T, 3)
+    full = torch.zeros((T, B, c.vocab), dtype=torch.float32, device="cuda") if B * c.vocab * T <= 60_000_000 else None
     d_tok, d_lg = run_step_loop(st, hd, dense=True, full=full)
-    # same per-row arithmetic: identical tokens and identical logits
-    assert np.array_equal(d_tok, s_tok)
-    assert np.array_equal(d_lg, s_lg, equal_nan=True)
     ref = oracle.decode(otr, c.k, embedding(cid), hid)
-    compare(d_tok, ref, c.hidden, d_lg, where=cid + "/dense")
+    mfma = B > 1 and c.dtype == "bf16"
+    if not mfma:
+        assert np.array_equal(d_tok, s_tok)
+        assert np.array_equal(d_lg, s_lg, equal_nan=True)
+    compare(d_tok, ref, c.hidden, d_lg, where=cid + "/dense", depth=c.hidden + 1 if mfma else None)
+    if mfma:
+        # the vector head at the same B: bit-identical to the sparse step
+        monkeypatch.setenv("TMS_DENSE_VECTOR", "1")
+        st2 = tms.State(trie, B, c.k, dev_embedding(cid))
+        v_tok, v_lg = run_step_loop(st2, hd, dense=True)
+        assert np.array_equal(v_tok, s_tok)
+        assert np.array_equal(v_lg, s_lg, equal_nan=True)
+        st2.close()
     if full is not None:
         fl = full.cpu().numpy()
         emb_np = embedding(cid)
         rng = np.random.Generator(np.random.PCG64(9))
-        for t in (0, 1, T // 2):
-            rows = np.arange(c.vocab) if c.vocab <= 8192 else rng.choice(c.vocab, 2048, replace=False)
-            for v in rows:
-                want, sa = oracle.logit(emb_np, int(v), hid[t, 0])
-                tol = 2e-3 * abs(want) + gamma(c.hidden + 1) * sa
-                assert abs(float(fl[t, 0, v]) - want) <= tol, (cid, t, v)
+        for t in range(nfull):
+            for b in sorted(set([0, B - 1])):
+                rows = np.arange(c.vocab) if c.vocab <= 8192 else rng.choice(c.vocab, 512, replace=False)
+                for v in rows:
+                    want, sa = oracle.logit(emb_np, int(v), hid[t, b])
+                    tol = 2e-3 * abs(want) + gamma(c.hidden + 1) * sa
+                    assert abs(float(fl[t, b, v]) - want) <= tol, (cid, t, b, v)
+    st.close()
+    trie.close()
 
 
 # ---------------------------------------------------------------------------

@@ -34,6 +34,7 @@ struct tms_state {
   int split = 1, split_default = 1;
   bool fast = false;
   int loop_mode = TMS_LOOP_RESIDENT;
+  bool dense_mfma = true;  // matrix-core dense head where it applies
   hipStream_t capture = nullptr;
   hipGraph_t graph = nullptr;
   hipGraphExec_t gexec = nullptr;
@@ -164,6 +165,10 @@ tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_
   // hot CSR bytes read by the step: begin, tok, child
   const int64_t hot = 4ll * (h.n_nodes + 1) + 8ll * h.n_edges;
   const bool fast_ok = h.cap <= 256 && hot <= 65536;
+  if (h.n_edges >= (1 << 29)) {
+    delete t;
+    return fail(TMS_ERR_CATALOG, "trie has 2^29 or more edges");
+  }
   if (path == TMS_PATH_FAST && h.cap > 256) {
     delete t;
     return fail(TMS_ERR_FANOUT, "fast path needs every node to have at most 256 edges; widest has " +
@@ -338,6 +343,7 @@ tms_status tms_state_create(tms_trie* trie, int32_t B, int32_t k, const void* em
     const int v = std::atoi(env);
     if (v > 0) st->split = v;
   }
+  if (const char* env = std::getenv("TMS_DENSE_VECTOR")) st->dense_mfma = std::atoi(env) == 0;
   if (const char* env = std::getenv("TMS_LOOP")) {
     const int v = std::atoi(env);
     if (v >= TMS_LOOP_RESIDENT && v <= TMS_LOOP_STREAM) st->loop_mode = v;
@@ -432,7 +438,7 @@ tms_status tms_decode_step_dense_masked(tms_state* st, const void* hidden, int32
   tms::StepIO io = make_io(st, hidden);
   io.out_tok = tok;
   io.out_logit = logit;
-  TMS_HIP(tms::launch_dense_step(st->trie->dev, st->dev, io, st->dtype, full_logits, 1024,
+  TMS_HIP(tms::launch_dense_step(st->trie->dev, st->dev, io, st->dtype, full_logits, 1024, st->dense_mfma,
                                  static_cast<hipStream_t>(stream)),
           "dense step launch");
   return TMS_OK;
@@ -457,8 +463,17 @@ tms_status tms_decode_k_pointers(tms_state* st, const void* hidden_seq, int32_t 
     io.tokens_bt = tokens;
     io.len = len;
     io.entries = entries;
-    const bool lds_live = tms::loop_lds_bytes(st->trie->dev, st->dev) <= 65536;
-    TMS_HIP(tms::launch_loop(st->trie->dev, st->dev, io, st->dtype, st->fast, lds_live, s), "loop launch");
+    // LDS budget per workgroup for the loop's on-chip copy (the part offers
+    // 160 KiB; a little is left for the kernel's own shared variables)
+    const size_t budget = 160 * 1024 - 2048;
+    int mode;
+    if (st->fast) {
+      mode = tms::loop_lds_bytes(st->trie->dev, st->dev, true) <= budget ? tms::kLoopTrieLds : tms::kLoopFastGlobal;
+    } else {
+      mode = tms::loop_lds_bytes(st->trie->dev, st->dev, false) <= budget ? tms::kLoopVectorLds
+                                                                           : tms::kLoopVectorGlobal;
+    }
+    TMS_HIP(tms::launch_loop(st->trie->dev, st->dev, io, st->dtype, mode, s), "loop launch");
     return TMS_OK;
   }
   const size_t step_bytes = size_t(st->B) * st->H * elem_size(st->dtype);

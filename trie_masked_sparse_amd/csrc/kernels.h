@@ -72,12 +72,22 @@ struct LoopIO {
 hipError_t launch_reset(const DevTrie& tr, const DevState& st, hipStream_t s);
 hipError_t launch_step_sparse(const DevTrie& tr, const DevState& st, const StepIO& io, int dtype,
                               bool fast, int split, hipStream_t s);
-hipError_t launch_loop(const DevTrie& tr, const DevState& st, const LoopIO& io, int dtype, bool fast,
-                       bool lds_live, hipStream_t s);
-// LDS bytes the fast-path loop kernel keeps per sequence (live counts + spent flags).
-size_t loop_lds_bytes(const DevTrie& tr, const DevState& st);
+// Variants of the resident loop: trie, live counts and spent bits in LDS
+// (fast path); trie through the scalar cache with live counts in device
+// memory (fast path, too big for LDS); vector edge reads with live counts in
+// LDS, or in device memory (global path).
+enum { kLoopTrieLds = 0, kLoopFastGlobal = 1, kLoopVectorLds = 2, kLoopVectorGlobal = 3 };
+hipError_t launch_loop(const DevTrie& tr, const DevState& st, const LoopIO& io, int dtype, int mode,
+                       hipStream_t s);
+// LDS bytes of the resident loop's per-sequence copy (live counts, spent bits,
+// and the trie arrays when trie = true).
+size_t loop_lds_bytes(const DevTrie& tr, const DevState& st, bool trie);
+// Dense step: bitmask, all-V head, masked argmax, advance.  With mfma and a
+// bf16 table, 2 <= B <= 256 and H % 32 == 0 the head runs on the matrix cores;
+// otherwise on the vector units with the sparse head's per-row arithmetic.
 hipError_t launch_dense_step(const DevTrie& tr, const DevState& st, const StepIO& io, int dtype,
-                             float* full_logits, int grid, hipStream_t s);
+                             float* full_logits, int grid, bool mfma, hipStream_t s);
+bool dense_uses_mfma(int dtype, int B, int H);
 hipError_t launch_forced(const DevTrie& tr, const DevState& st, const int32_t* forced, hipStream_t s);
 hipError_t launch_legal_set(const DevTrie& tr, const DevState& st, int32_t* legal_tok,
                             int32_t* n_legal, hipStream_t s);

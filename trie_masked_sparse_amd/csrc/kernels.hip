@@ -314,23 +314,56 @@ struct Cand {
   int child, tok, b0, b1, ent;
 };
 
+// Where a scan reads edge records: through the scalar cache from device
+// memory (FAST), from a copy of the trie in LDS (FAST inside the resident
+// loop), or with per-lane vector loads (GLOBAL).
+enum { kMetaScalar = 0, kMetaLds = 1, kMetaVector = 2 };
+
+// The trie arrays a scan reads (device memory, or their LDS copies).
+struct TrieView {
+  const int32_t* begin;
+  const int32_t* entry;
+  const int32_t* tok;
+  const int32_t* child;
+};
+
+// Resident-loop keys carry the wavefront index in their three low bits (below
+// the edge order, so the tie rule is unchanged: edges are distinct): one LDS
+// max then names both the winner and the wavefront holding its payload.
+__device__ __forceinline__ unsigned long long pack_key_wave(float x, uint32_t edge, int wv) {
+  const unsigned long long k = pack_key(x, 0u);
+  return (k & 0xFFFFFFFF00000000ull) | (unsigned long long)(((0x1FFFFFFFu - edge) << 3) | (uint32_t)wv);
+}
+__device__ __forceinline__ uint32_t key_wave_edge(unsigned long long k) {
+  return 0x1FFFFFFFu - ((uint32_t)k >> 3);
+}
+
+template <int META>
+__device__ __forceinline__ int meta_uniform(const int32_t* p, int i) {
+  if constexpr (META == kMetaScalar) return ((cint_p)p)[i];
+  else return __builtin_amdgcn_readfirstlane(p[i]);
+}
+
 // Scan the current node's edge range for this wavefront's share of the
 // edges (b0+wv, b0+wv+W, ...), compute a logit for every legal edge and
 // return the wavefront's best packed key (0 if it had no legal edge).
-// FAST: edge records through wave-uniform scalar loads, U edges per pass.
-// GLOBAL: 64 edges per pass through per-lane vector loads, the legal ones
-// compacted with a ballot, U rows in flight.  With CAND the child's node
-// record is fetched alongside the row gathers and returned in cand.
-template <int DT, int NC, bool FAST, int LIVE, bool CAND>
-__device__ __forceinline__ unsigned long long scan_node(const DevTrie& tr, const Seq& q, const int32_t* live,
-                                                        const uint4* __restrict__ emb, int nq,
-                                                        const uint4 (&hq)[NC], int wv, int W, int lane,
+// kMetaScalar/kMetaLds: wave-uniform edge records, U edges per pass, all
+// requested before one wait.  kMetaVector: 64 edges per pass through per-lane
+// vector loads, the legal ones compacted with a ballot, U rows in flight.
+// With CAND the child's node record is fetched alongside the row gathers and
+// returned in cand, and keys carry the wavefront index (pack_key_wave).
+template <int DT, int NC, int META, int LIVE, bool CAND>
+__device__ __forceinline__ unsigned long long scan_node(const DevTrie& tr, const TrieView& tv, const Seq& q,
+                                                        const int32_t* live, const uint4* __restrict__ emb,
+                                                        int nq, const uint4 (&hq)[NC], int wv, int W, int lane,
                                                         Cand& cand) {
   constexpr int U = rows_per_pass(NC);
   unsigned long long best = 0;
-  if constexpr (FAST) {
-    const cint_p ctok = (cint_p)tr.tok;
-    const cint_p cchild = (cint_p)tr.child;
+  auto key_of = [&](float l, int e) -> unsigned long long {
+    if constexpr (CAND) return pack_key_wave(l, (uint32_t)e, wv);
+    else return pack_key(l, (uint32_t)e);
+  };
+  if constexpr (META != kMetaVector) {
     auto pass = [&](int e0) {
       int rows[U], edges[U], chs[U];
       // edge records for all U slots first (indices clamped into the range,
@@ -340,8 +373,8 @@ __device__ __forceinline__ unsigned long long scan_node(const DevTrie& tr, const
       for (int u = 0; u < U; ++u) {
         const int e = e0 + u * W;
         const int ee = e < q.b1 ? e : q.b1 - 1;  // every node has at least one edge
-        cs[u] = cchild[ee];
-        ts[u] = ctok[ee];
+        cs[u] = meta_uniform<META>(tv.child, ee);
+        ts[u] = meta_uniform<META>(tv.tok, ee);
         lvs[u] = read_live_uniform<LIVE>(live, ee);  // control edges hold 0
       }
       // consume every record here so that all of them are requested together,
@@ -363,14 +396,23 @@ __device__ __forceinline__ unsigned long long scan_node(const DevTrie& tr, const
       if constexpr (CAND) {
         // the children's records travel with the row gathers
 #pragma unroll
-        for (int u = 0; u < U; ++u) recs[u] = chs[u] >= 0 ? tr.node_rec[chs[u]] : NodeRec{0, 0, -1, 0};
+        for (int u = 0; u < U; ++u) {
+          if (chs[u] < 0) {
+            recs[u] = NodeRec{0, 0, -1, 0};
+          } else if constexpr (META == kMetaLds) {
+            recs[u] = NodeRec{meta_uniform<META>(tv.begin, chs[u]), meta_uniform<META>(tv.begin, chs[u] + 1),
+                              meta_uniform<META>(tv.entry, chs[u]), 0};
+          } else {
+            recs[u] = tr.node_rec[chs[u]];
+          }
+        }
       }
       float l[U];
       finish_rows<DT, NC, U>(nq, rows, raw, hq, l, lane);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (rows[u] < 0) continue;
-        const unsigned long long k = pack_key(l[u], (uint32_t)edges[u]);
+        const unsigned long long k = key_of(l[u], edges[u]);
         if (k > best) {
           best = k;
           if constexpr (CAND) cand = Cand{chs[u], rows[u], recs[u].b0, recs[u].b1, recs[u].ent};
@@ -423,7 +465,7 @@ __device__ __forceinline__ unsigned long long scan_node(const DevTrie& tr, const
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           if (rows[u] < 0) continue;
-          const unsigned long long k = pack_key(l[u], (uint32_t)edges[u]);
+          const unsigned long long k = key_of(l[u], edges[u]);
           if (k > best) {
             best = k;
             if constexpr (CAND) cand = Cand{chs[u], rows[u], r0[u], r1[u], r2[u]};
@@ -462,8 +504,9 @@ __global__ __launch_bounds__(kBlock) void step_sparse_kernel(DevTrie tr, DevStat
   load_hidden<NC>((const uint4*)io.hidden + (int64_t)s * nq, nq, hq, lane);
   const int32_t* live = st.live + (int64_t)s * tr.live_stride;
   Cand unused;
-  const unsigned long long best = scan_node<DT, NC, FAST, kLiveScalar, false>(tr, q, live, (const uint4*)io.emb,
-                                                                              nq, hq, wv, W, lane, unused);
+  const TrieView tv{tr.begin, tr.entry, tr.tok, tr.child};
+  const unsigned long long best = scan_node<DT, NC, FAST ? kMetaScalar : kMetaVector, kLiveScalar, false>(
+      tr, tv, q, live, (const uint4*)io.emb, nq, hq, wv, W, lane, unused);
 
   __shared__ unsigned long long s_best[kWavesPerBlock];
   __shared__ unsigned long long s_key;
@@ -509,28 +552,64 @@ __global__ __launch_bounds__(kBlock) void step_sparse_kernel(DevTrie tr, DevStat
 constexpr int kLoopBlock = 512;
 constexpr int kLoopWaves = kLoopBlock / kWave;
 
-template <int DT, int NC, bool FAST, bool LDS_LIVE>
+// LDS layout of the resident loop (in int32 words, each part a multiple of 4):
+// live counts, spent bits and, with the trie in LDS, begin/entry/tok/child.
+struct LoopLds {
+  int live, spent, begin, entry, tok, child, total;
+};
+__host__ __device__ inline int round4(int n) { return (n + 3) & ~3; }
+__host__ __device__ inline LoopLds loop_lds_layout(const DevTrie& tr, const DevState& st, bool trie) {
+  LoopLds o;
+  o.live = 0;
+  o.spent = o.live + tr.live_stride;
+  o.begin = o.spent + round4(st.spent_words);
+  o.entry = o.begin + (trie ? round4(tr.n_nodes + 1) : 0);
+  o.tok = o.entry + (trie ? round4(tr.n_nodes) : 0);
+  o.child = o.tok + (trie ? round4(tr.n_edges) : 0);
+  o.total = o.child + (trie ? round4(tr.n_edges) : 0);
+  return o;
+}
+
+// n int32 words from device memory into LDS as 16-byte moves; the device
+// buffers are padded to 256 bytes and the LDS parts to 4 words.
+__device__ __forceinline__ void copy_to_lds(int32_t* dst, const int32_t* src, int n) {
+  const int n4 = (n + 3) >> 2;
+  for (int i = threadIdx.x; i < n4; i += kLoopBlock)
+    reinterpret_cast<int4*>(dst)[i] = reinterpret_cast<const int4*>(src)[i];
+}
+
+template <int DT, int NC, int META, bool LDS_LIVE>
 __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState st, LoopIO io) {
   constexpr int EL = DT == 0 ? 4 : 8;
+  constexpr bool TRIE_LDS = META == kMetaLds;
+  static_assert(!TRIE_LDS || LDS_LIVE, "the LDS trie comes with LDS live counts");
   extern __shared__ int32_t lds[];
-  __shared__ unsigned long long s_best[kLoopWaves];
+  __shared__ unsigned long long s_key;
   __shared__ Cand s_cand[kLoopWaves];
   __shared__ int s_next[8];
+  __shared__ NodeRec s_root;
   const int s = blockIdx.x;
   const int lane = __lane_id();
   const int wv = wave_id();
   const int W = kLoopWaves;
   const int nq = io.H / EL;
   const int64_t ls = tr.live_stride;
+  const LoopLds lay = loop_lds_layout(tr, st, TRIE_LDS);
   int32_t* g_live = st.live + (int64_t)s * ls;
   uint32_t* g_spent = st.spent + (int64_t)s * st.spent_words;
-  int32_t* live = LDS_LIVE ? lds : g_live;
-  uint32_t* spent = LDS_LIVE ? reinterpret_cast<uint32_t*>(lds + ls) : g_spent;
+  int32_t* live = LDS_LIVE ? lds + lay.live : g_live;
+  uint32_t* spent = LDS_LIVE ? reinterpret_cast<uint32_t*>(lds + lay.spent) : g_spent;
+  TrieView tv{tr.begin, tr.entry, tr.tok, tr.child};
   if constexpr (LDS_LIVE) {
-    const int4* src = reinterpret_cast<const int4*>(g_live);
-    int4* dst = reinterpret_cast<int4*>(lds);
-    for (int i = threadIdx.x; i < (int)(ls / 4); i += kLoopBlock) dst[i] = src[i];
+    copy_to_lds(lds + lay.live, g_live, (int)ls);
     for (int i = threadIdx.x; i < st.spent_words; i += kLoopBlock) spent[i] = g_spent[i];
+  }
+  if constexpr (TRIE_LDS) {
+    copy_to_lds(lds + lay.begin, tr.begin, tr.n_nodes + 1);
+    copy_to_lds(lds + lay.entry, tr.entry, tr.n_nodes);
+    copy_to_lds(lds + lay.tok, tr.tok, tr.n_edges);
+    copy_to_lds(lds + lay.child, tr.child, tr.n_edges);
+    tv = TrieView{lds + lay.begin, lds + lay.entry, lds + lay.tok, lds + lay.child};
   }
   int node = st.node[s], depth = st.depth[s], done = st.done[s];
   int status = st.status[s], fin = st.finished[s], nemit = st.nemit[s];
@@ -547,8 +626,11 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
     if (lane < depth) my_path = path[lane];
     if (lane < done) my_ent = entries[lane];
   }
-  const NodeRec root = rec_scalar(tr.node_rec, 0);
   NodeRec rec = rec_scalar(tr.node_rec, node);
+  if (threadIdx.x == 0) {
+    s_root = rec_scalar(tr.node_rec, 0);
+    s_key = 0ull;
+  }
   __syncthreads();
   bool ctl0 = false;
   if (rec.ent >= 0) ctl0 = ((__builtin_amdgcn_readfirstlane(spent[rec.ent >> 5]) >> (rec.ent & 31)) & 1) == 0;
@@ -569,32 +651,23 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
     q.sep_ok = sep_ok;
     q.stop_ok = stop_ok;
     Cand cand{0, 0, 0, 0, 0};
-    const unsigned long long best = scan_node<DT, NC, FAST, LDS_LIVE ? kLiveLds : kLiveVector, true>(
-        tr, q, live, emb, nq, hq, wv, W, lane, cand);
+    const unsigned long long best = scan_node<DT, NC, META, LDS_LIVE ? kLiveLds : kLiveVector, true>(
+        tr, tv, q, live, emb, nq, hq, wv, W, lane, cand);
     // the next step's hidden vector does not depend on this step: fetch it now
     if (t + 1 < io.T) load_hidden<NC>(hid + ((int64_t)(t + 1) * st.B + s) * nq, nq, hq, lane);
     if (lane == 0) {
-      s_best[wv] = best;
+      if (best) __hip_atomic_fetch_max(&s_key, best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       s_cand[wv] = cand;
     }
     lds_barrier();
     if (wv == 0) {
-      int wi = 0;
-      unsigned long long key = s_best[0];
-#pragma unroll
-      for (int i = 1; i < kLoopWaves; ++i) {
-        const unsigned long long k = s_best[i];
-        if (k > key) {
-          key = k;
-          wi = i;
-        }
-      }
+      const unsigned long long key = s_key;
       int tok = -1;
       if (!key) {
         status = kSeqEmptyMask;
       } else {
-        const int e = (int)key_id(key);
-        const Cand c = s_cand[wi];
+        const int e = (int)key_wave_edge(key);
+        const Cand c = s_cand[key & 7];
         tok = c.tok;
         if (c.child >= 0) {
           if (reg_lists) {
@@ -628,7 +701,7 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
             fin = 1;
           } else {
             node = 0;
-            rec = root;
+            rec = s_root;
           }
         }
         nemit += 1;
@@ -648,6 +721,7 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
         t_flushed += kWave;
       }
       if (lane == 0) {
+        s_key = 0ull;
         s_next[0] = node;
         s_next[1] = depth;
         s_next[2] = done;
@@ -695,9 +769,8 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
   }
   if constexpr (LDS_LIVE) {
     __syncthreads();
-    const int4* src = reinterpret_cast<const int4*>(lds);
     int4* dst = reinterpret_cast<int4*>(g_live);
-    for (int i = threadIdx.x; i < (int)(ls / 4); i += kLoopBlock) dst[i] = src[i];
+    for (int i = threadIdx.x; i < (int)(ls / 4); i += kLoopBlock) dst[i] = reinterpret_cast<const int4*>(live)[i];
     for (int i = threadIdx.x; i < st.spent_words; i += kLoopBlock) g_spent[i] = spent[i];
   }
 }
@@ -761,6 +834,109 @@ __global__ __launch_bounds__(kBlock) void dense_head_kernel(DevState st, StepIO 
         if (((word >> (v & 31)) & 1u) && lane == 0)
           __hip_atomic_fetch_max(&st.key[b], pack_key(l[u], (uint32_t)v), __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+}
+
+// Dense head for B > 1 on the matrix cores (the one dense contraction of the
+// path: [B x H] . [H x V]).  logits = h . E^T through v_mfma_f32_16x16x32_bf16
+// (fp32 accumulation in the matrix core's own order).  A workgroup of four
+// wavefronts takes 64*MT vocabulary rows, MT tiles of 16 per wavefront
+// (operand A: lane l holds row l%16, elements 8*(l/16)..+8 of the current
+// 32-wide K step); all B sequences go in tiles of 16 (operand B from LDS,
+// where the hidden vectors of each 128-wide K block are staged with padded
+// rows, 17 KB at B = 64 so that eight workgroups fit a compute unit); the
+// table operand is loaded one K step ahead; the result tile has
+// lane l holding sequence l%16, rows 4*(l/16)+i.  Masked-in logits go to
+// the per-sequence key with an atomic max; full logits are written if asked.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kDenseKB = 128;                   // K block staged in LDS
+constexpr int kDenseStride = kDenseKB / 8 + 1;  // uint4 per staged row (+1 against bank conflicts)
+
+// Stage the hidden vectors' K block [kb, kb + kDenseKB) into an LDS buffer.
+__device__ __forceinline__ void stage_hidden(uint4* buf, const uint4* hid, int B, int nseq, int nq, int kb) {
+  const int qb = kb / 8;
+  for (int idx = threadIdx.x; idx < nseq * (kDenseKB / 8); idx += kBlock) {
+    const int sq = idx / (kDenseKB / 8), qq = idx % (kDenseKB / 8);
+    buf[sq * kDenseStride + qq] = (sq < B && qb + qq < nq) ? hid[(int64_t)sq * nq + qb + qq] : make_uint4(0, 0, 0, 0);
+  }
+}
+
+template <int MAXT, int MT>
+__global__ __launch_bounds__(kBlock) void dense_mfma_kernel(DevState st, StepIO io, float* full_logits, int ntiles) {
+  extern __shared__ uint4 sh[];  // [ntiles*16][kDenseStride]
+  const int lane = __lane_id();
+  const int wv = wave_id();
+  const int V = io.V, H = io.H, B = st.B;
+  const int nq = H / 8;
+  const uint4* emb = (const uint4*)io.emb;
+  const uint4* hid = (const uint4*)io.hidden;
+  const int nseq = ntiles * 16;
+  constexpr int kRows = 4 * MT * 16;  // rows per workgroup
+  const int nblk = (V + kRows - 1) / kRows;
+  for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    const int m0 = blk * kRows + wv * (MT * 16);
+    const uint4* arow_p[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) arow_p[m] = emb + (int64_t)min(m0 + m * 16 + (lane & 15), V - 1) * nq;
+    f32x4_t acc[MT][MAXT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int t = 0; t < MAXT; ++t) acc[m][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // Operand A one K step ahead.  One load covers 64 bytes of each of 16
+    // rows, half a 128-byte line: the next K step reads the other half, so
+    // these are ordinary (cached) loads; a non-temporal hint costs ~18% here.
+    u32x4_t an[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      an[m] = *reinterpret_cast<const u32x4_t*>(arow_p[m] + (lane >> 4));
+    for (int kb = 0; kb < H; kb += kDenseKB) {
+      __syncthreads();  // the previous block is consumed
+      stage_hidden(sh, hid, B, nseq, nq, kb);
+      __syncthreads();
+      const int kend = min(kDenseKB, H - kb);
+      for (int ks = 0; ks < kend; ks += 32) {
+        bf16x8_t a[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) a[m] = __builtin_bit_cast(bf16x8_t, an[m]);
+        const int kn = kb + ks + 32;  // next K step
+        if (kn < H) {
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+            an[m] = *reinterpret_cast<const u32x4_t*>(arow_p[m] + kn / 8 + (lane >> 4));
+        }
+#pragma unroll
+        for (int t = 0; t < MAXT; ++t) {
+          if (t < ntiles) {
+            const bf16x8_t b = __builtin_bit_cast(bf16x8_t, sh[(t * 16 + (lane & 15)) * kDenseStride + ks / 8 + (lane >> 4)]);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], b, acc[m][t], 0, 0, 0);
+          }
+        }
+      }
+    }
+    // epilogue: tile m, sequence t*16 + lane%16, rows m0 + m*16 + 4*(lane/16) + i
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int r0 = m0 + m * 16 + 4 * (lane >> 4);
+#pragma unroll
+      for (int t = 0; t < MAXT; ++t) {
+        if (t >= ntiles) continue;
+        const int sq = t * 16 + (lane & 15);
+        if (sq >= B) continue;
+        const uint32_t word = r0 < V ? st.mask[(int64_t)sq * st.mask_words + (r0 >> 5)] : 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = r0 + i;
+          if (r >= V) continue;
+          const float l = acc[m][t][i];
+          if (full_logits) full_logits[(int64_t)sq * V + r] = l;
+          if ((word >> ((r0 & 31) + i)) & 1u)
+            __hip_atomic_fetch_max(&st.key[sq], pack_key(l, (uint32_t)r), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
     }
   }
@@ -960,15 +1136,27 @@ struct StepLaunch {
 
 template <int DT, int NC>
 struct LoopLaunch {
-  static hipError_t run(const DevTrie& tr, const DevState& st, const LoopIO& io, bool fast, bool lds_live,
-                        hipStream_t s) {
-    const dim3 grid((unsigned)st.B), block(kLoopBlock);
-    const size_t lds = lds_live ? sizeof(int32_t) * ((size_t)tr.live_stride + (size_t)st.spent_words) : 0;
-    if (fast && lds_live) hipLaunchKernelGGL((loop_kernel<DT, NC, true, true>), grid, block, lds, s, tr, st, io);
-    else if (fast) hipLaunchKernelGGL((loop_kernel<DT, NC, true, false>), grid, block, 0, s, tr, st, io);
-    else if (lds_live) hipLaunchKernelGGL((loop_kernel<DT, NC, false, true>), grid, block, lds, s, tr, st, io);
-    else hipLaunchKernelGGL((loop_kernel<DT, NC, false, false>), grid, block, 0, s, tr, st, io);
+  template <int META, bool LIVE>
+  static hipError_t go(const DevTrie& tr, const DevState& st, const LoopIO& io, hipStream_t s) {
+    const size_t lds = LIVE ? sizeof(int32_t) * (size_t)loop_lds_layout(tr, st, META == kMetaLds).total : 0;
+    auto* k = &loop_kernel<DT, NC, META, LIVE>;
+    static size_t allowed = 65536;  // per instantiation; raised once as needed
+    if (lds > allowed) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      allowed = lds;
+    }
+    hipLaunchKernelGGL(k, dim3((unsigned)st.B), dim3(kLoopBlock), lds, s, tr, st, io);
     return hipGetLastError();
+  }
+  static hipError_t run(const DevTrie& tr, const DevState& st, const LoopIO& io, int mode, hipStream_t s) {
+    switch (mode) {
+      case kLoopTrieLds: return go<kMetaLds, true>(tr, st, io, s);
+      case kLoopFastGlobal: return go<kMetaScalar, false>(tr, st, io, s);
+      case kLoopVectorLds: return go<kMetaVector, true>(tr, st, io, s);
+      default: return go<kMetaVector, false>(tr, st, io, s);
+    }
   }
 };
 
@@ -1016,21 +1204,48 @@ hipError_t launch_step_sparse(const DevTrie& tr, const DevState& st, const StepI
   return dispatch<StepLaunch>(dtype, chunks_for(dtype, io.H), tr, st, io, fast, split, s);
 }
 
-hipError_t launch_loop(const DevTrie& tr, const DevState& st, const LoopIO& io, int dtype, bool fast,
-                       bool lds_live, hipStream_t s) {
-  return dispatch<LoopLaunch>(dtype, chunks_for(dtype, io.H), tr, st, io, fast, lds_live, s);
+hipError_t launch_loop(const DevTrie& tr, const DevState& st, const LoopIO& io, int dtype, int mode,
+                       hipStream_t s) {
+  return dispatch<LoopLaunch>(dtype, chunks_for(dtype, io.H), tr, st, io, mode, s);
 }
 
-size_t loop_lds_bytes(const DevTrie& tr, const DevState& st) {
-  return sizeof(int32_t) * ((size_t)tr.live_stride + (size_t)st.spent_words);
+size_t loop_lds_bytes(const DevTrie& tr, const DevState& st, bool trie) {
+  return sizeof(int32_t) * (size_t)loop_lds_layout(tr, st, trie).total;
 }
+
+template <int MAXT, int MT>
+hipError_t launch_dense_mfma(const DevState& st, const StepIO& io, float* full, hipStream_t s) {
+  const int ntiles = (st.B + 15) / 16;
+  const size_t lds = sizeof(uint4) * (size_t)ntiles * 16 * kDenseStride;
+  auto* k = &dense_mfma_kernel<MAXT, MT>;
+  static size_t allowed = 65536;
+  if (lds > allowed) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+    allowed = lds;
+  }
+  const int nblk = (io.V + 64 * MT - 1) / (64 * MT);
+  hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(kBlock), lds, s, st, io, full, ntiles);
+  return hipGetLastError();
+}
+
+bool dense_uses_mfma(int dtype, int B, int H) { return dtype == 1 && B >= 2 && B <= 256 && H % 32 == 0; }
 
 hipError_t launch_dense_step(const DevTrie& tr, const DevState& st, const StepIO& io, int dtype, float* full,
-                             int grid, hipStream_t s) {
+                             int grid, bool mfma, hipStream_t s) {
   hipLaunchKernelGGL(dense_mask_kernel, dim3(st.B), dim3(kBlock), st.mask_words * sizeof(uint32_t), s, tr, st);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  err = dispatch<DenseLaunch>(dtype, chunks_for(dtype, io.H), st, io, full, grid, s);
+  if (mfma && dense_uses_mfma(dtype, st.B, io.H)) {
+    // one 16-row tile per wavefront keeps many workgroups (2374 at V = 151936)
+    // for balance and latency hiding
+    err = st.B <= 64 ? launch_dense_mfma<4, 1>(st, io, full, s)
+        : st.B <= 128 ? launch_dense_mfma<8, 1>(st, io, full, s)
+                      : launch_dense_mfma<16, 1>(st, io, full, s);
+  } else {
+    err = dispatch<DenseLaunch>(dtype, chunks_for(dtype, io.H), st, io, full, grid, s);
+  }
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dense_advance_kernel, dim3(st.B), dim3(kWave), 0, s, tr, st, io);
   return hipGetLastError();
