@@ -532,3 +532,64 @@ def test_bf16_pair_product_rounding():
     got = float(out[0, 0])
     assert got in (1.0 + 2.0 ** -23, 1.0), got
     print("v_dot2_f32_bf16 pair:", "single rounding" if got != 1.0 else "sequential")
+
+
+def _chain_catalog(seed, n, V):
+    """Entries with long single-child runs and a few branch points: most steps
+    have one legal token, so the resident loop's forced steps dominate."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    stems = [[int(x) for x in rng.integers(0, V - 2, size=int(rng.integers(20, 70)))] for _ in range(4)]
+    cat = []
+    while len(cat) < n:
+        st = stems[int(rng.integers(0, len(stems)))]
+        cut = int(rng.integers(1, len(st)))
+        tail = [int(x) for x in rng.integers(0, V - 2, size=int(rng.integers(1, 30)))]
+        e = st[:cut] + tail
+        if e not in cat:
+            cat.append(e)
+    return cat
+
+
+@pytest.mark.parametrize("path", [tms.PATH_FAST, tms.PATH_GLOBAL])
+def test_loop_forced_spans_from_mid_answer(path):
+    """The resident loop skips the head on steps with one legal token.  Start
+    it from states left by `cut` host-driven steps (inside a forced run, at a
+    branch, after a completion, past the 64-token flush boundary): tokens and
+    final state must match a whole-answer loop, the per-step loop form (which
+    always runs the head) and the oracle."""
+    V, H, k, B = 700, 256, 3, 4
+    cat = _chain_catalog(50 + path, 40, V)
+    otr = oracle.Trie(cat, V, V - 2, V - 1)
+    rng = np.random.Generator(np.random.PCG64(60 + path))
+    T = k * (otr.max_depth + 1)
+    emb = _rand_table(rng, V, H, "bf16")
+    hid = _rand_hidden(rng, T, B, H, "bf16")
+    ref = oracle.decode(otr, k, emb, hid)
+    trie = tms.Trie(cat, V, V - 2, V - 1, path=path)
+    st = tms.State(trie, B, k, to_dev(emb))
+    hd = to_dev(hid)
+    tok_full, len_full, ent_full = run_k_pointers(st, hd)
+    ex_full = st.export(live=True)
+    compare(tok_full, ref, H, None, len_full, ent_full, where="forced full")
+    n_forced = int((ref["nlegal"] == 1).sum())
+    assert n_forced >= 0.6 * int(ref["len"].sum())  # most steps are forced here
+    for cut in (1, 5, 37, 63, 64, 65, 100, T - 1):
+        if cut >= T:
+            continue
+        # hidden vectors of the remaining steps, padded to the loop's minimum T
+        rest = torch.zeros_like(hd)
+        rest[: T - cut] = hd[cut:]
+        for mode in (tms.LOOP_RESIDENT, tms.LOOP_STREAM):
+            tms.state_set_loop(st.h, mode)
+            st.reset()
+            a, _ = run_step_loop(st, hd[:cut])
+            b_, ln, en = run_k_pointers(st, rest)
+            whole = np.concatenate([a, b_[:, : T - cut]], axis=1)
+            assert np.array_equal(whole, tok_full), (cut, mode)
+            assert (b_[:, T - cut:] == -1).all(), (cut, mode)
+            assert np.array_equal(ln, len_full) and np.array_equal(en, ent_full), (cut, mode)
+            ex = st.export(live=True)
+            for key in ("node", "depth", "done", "status", "finished", "n_emitted", "entries", "live"):
+                assert np.array_equal(ex[key], ex_full[key]), (cut, mode, key)
+    st.close()
+    trie.close()

@@ -538,6 +538,28 @@ __global__ __launch_bounds__(kBlock) void step_sparse_kernel(DevTrie tr, DevStat
   }
 }
 
+// A forced step (sections "Masked sampling inside the sampler" and "The
+// sparse output layer": with a single legal token the argmax over the legal
+// set is that token whatever the logits).  Returns the node's one legal edge
+// when the node has at most 64 edges and exactly one of them is legal, else
+// -1 (more than one, none, or a node too wide to check in one pass: the full
+// step handles those, including the empty-mask error).  Every wavefront of
+// the resident loop evaluates it from the same state, so all of them take the
+// same branch without a barrier.
+__device__ __forceinline__ int forced_edge(const TrieView& tv, const int32_t* live, const Seq& q, int lane) {
+  const int f = q.b1 - q.b0;
+  if (f > kWave) return -1;
+  const int e = q.b0 + lane;
+  int c = kChildSep - 8, lv = 0;  // lanes past the range: matches no edge kind
+  if (lane < f) {
+    c = tv.child[e];
+    lv = live[e];  // read for every edge (in range of the live array), used for content edges
+  }
+  const unsigned long long m = __ballot(edge_ok_bits(c, lv, q));
+  if (__popcll(m) != 1) return -1;
+  return q.b0 + (int)__builtin_ctzll(m);
+}
+
 // ---------------------------------------------------------------------------
 // Resident device loop (section "The whole loop on the device"): one
 // workgroup per sequence runs every step of the answer without returning to
@@ -641,6 +663,31 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
   if (io.T > 0) load_hidden<NC>(hid + (int64_t)s * nq, nq, hq, lane);
   int t = 0;
   int t_flushed = 0;  // tokens [0, t_flushed) are in device memory
+  int hq_t = 0;          // step whose hidden vector is in (or on its way to) hq
+  // Wavefront 0: the token of step t goes to lane t % 64; every 64 steps the
+  // lanes are written out.
+  auto record = [&](int tok) {
+    if (lane == (t & (kWave - 1))) my_tok = tok;
+    if ((t & (kWave - 1)) == kWave - 1) {
+      tokens[t_flushed + lane] = my_tok;
+      t_flushed += kWave;
+    }
+  };
+  // Wavefront 0: a pointer completes; release its path, spend its terminal.
+  auto release = [&](int ent) {
+    if (reg_lists) {
+      if (lane < depth) live[my_path] -= 1;  // distinct edges
+      if (lane == done) my_ent = ent;
+    } else {
+      for (int i = lane; i < depth; i += kWave) live[path[i]] -= 1;
+      if (lane == 0) entries[done] = ent;
+    }
+    if (lane == 0) spent[ent >> 5] |= 1u << (ent & 31);
+    if (!LDS_LIVE || !reg_lists) {
+      // live counts, spent flags or entries in device memory are read again
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+  };
   for (; t < io.T && status == kSeqOk && !fin; ++t) {
     Seq q;
     q.node = node;
@@ -650,11 +697,66 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
     q.b1 = rec.b1;
     q.sep_ok = sep_ok;
     q.stop_ok = stop_ok;
+    const int fe = forced_edge(tv, live, q, lane);
+    if (fe >= 0) {
+      // forced: no rows, no reduction; a content edge needs no barrier
+      const int c = __builtin_amdgcn_readfirstlane(tv.child[fe]);
+      const int tok = __builtin_amdgcn_readfirstlane(tv.tok[fe]);
+      if (c >= 0) {
+        if (wv == 0) {
+          if (reg_lists) {
+            if (lane == depth) my_path = fe;
+          } else {
+            if (lane == 0) path[depth] = fe;
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          }
+        }
+        depth += 1;
+        node = c;
+        if constexpr (TRIE_LDS)
+          rec = NodeRec{__builtin_amdgcn_readfirstlane(tv.begin[c]), __builtin_amdgcn_readfirstlane(tv.begin[c + 1]),
+                        __builtin_amdgcn_readfirstlane(tv.entry[c]), 0};
+        else
+          rec = rec_scalar(tr.node_rec, c);
+      } else {
+        // every wavefront has finished reading live counts of this answer's
+        // path before wavefront 0 releases it, and sees the result after
+        if constexpr (LDS_LIVE) lds_barrier();
+        else __syncthreads();
+        if (wv == 0) release(rec.ent);
+        if constexpr (LDS_LIVE) lds_barrier();
+        else __syncthreads();
+        done += 1;
+        depth = 0;
+        if (c == kChildStop) {
+          fin = 1;
+        } else {
+          node = 0;
+          rec = s_root;
+        }
+      }
+      if (wv == 0) {
+        nemit += 1;
+        record(tok);
+      }
+      const bool ctl = rec.ent >= 0 && !fin &&
+                       ((__builtin_amdgcn_readfirstlane(spent[rec.ent >> 5]) >> (rec.ent & 31)) & 1) == 0;
+      sep_ok = ctl && done + 1 < st.k;
+      stop_ok = ctl && done + 1 >= st.k;
+      continue;
+    }
+    if (hq_t != t) {
+      load_hidden<NC>(hid + ((int64_t)t * st.B + s) * nq, nq, hq, lane);
+      hq_t = t;
+    }
     Cand cand{0, 0, 0, 0, 0};
     const unsigned long long best = scan_node<DT, NC, META, LDS_LIVE ? kLiveLds : kLiveVector, true>(
         tr, tv, q, live, emb, nq, hq, wv, W, lane, cand);
     // the next step's hidden vector does not depend on this step: fetch it now
-    if (t + 1 < io.T) load_hidden<NC>(hid + ((int64_t)(t + 1) * st.B + s) * nq, nq, hq, lane);
+    if (t + 1 < io.T) {
+      load_hidden<NC>(hid + ((int64_t)(t + 1) * st.B + s) * nq, nq, hq, lane);
+      hq_t = t + 1;
+    }
     if (lane == 0) {
       if (best) __hip_atomic_fetch_max(&s_key, best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       s_cand[wv] = cand;
@@ -680,21 +782,7 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
           node = c.child;
           rec = NodeRec{c.b0, c.b1, c.ent, 0};
         } else {
-          // a pointer completes: release its path, spend its terminal
-          const int ent = rec.ent;
-          if (reg_lists) {
-            if (lane < depth) live[my_path] -= 1;  // distinct edges
-            if (lane == done) my_ent = ent;
-          } else {
-            for (int i = lane; i < depth; i += kWave) live[path[i]] -= 1;
-            if (lane == 0) entries[done] = ent;
-          }
-          if (lane == 0) spent[ent >> 5] |= 1u << (ent & 31);
-          if (!LDS_LIVE || !reg_lists) {
-            // live counts, spent flags or entries in device memory are read
-            // again in later steps
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-          }
+          release(rec.ent);
           done += 1;
           depth = 0;
           if (c.child == kChildStop) {
@@ -715,11 +803,7 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
         ctl = !sp;
       }
       const bool more = done + 1 < st.k;
-      if (lane == (t & (kWave - 1))) my_tok = tok;
-      if ((t & (kWave - 1)) == kWave - 1) {
-        tokens[t_flushed + lane] = my_tok;
-        t_flushed += kWave;
-      }
+      record(tok);
       if (lane == 0) {
         s_key = 0ull;
         s_next[0] = node;
