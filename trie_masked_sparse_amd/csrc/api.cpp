@@ -185,6 +185,8 @@ tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_
   const size_t o_child = c.take<int32_t>(h.n_edges);
   const size_t o_live0 = c.take<int32_t>(live_stride);
   const size_t o_rec = c.take<int32_t>(size_t(h.n_nodes) * 4);
+  const size_t o_erec = c.take<int32_t>(size_t(h.n_edges) * 4);
+  const size_t o_cent = c.take<int32_t>(live_stride);
   hipError_t e = hipGetDevice(&t->device);
   if (e == hipSuccess) e = hipMalloc(&t->dmem, c.off);
   if (e != hipSuccess) {
@@ -202,12 +204,26 @@ tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_
     rec[4 * size_t(n) + 1] = h.begin[n + 1];
     rec[4 * size_t(n) + 2] = h.entry[n];
   }
+  std::vector<int32_t> erec(size_t(h.n_edges) * 4, 0);
+  std::vector<int32_t> cent(live_stride, -1);
+  for (int32_t x = 0; x < h.n_edges; ++x) {
+    const int32_t ch = h.child[x];
+    erec[4 * size_t(x)] = ch;
+    erec[4 * size_t(x) + 1] = h.tok[x];
+    if (ch >= 0) {
+      erec[4 * size_t(x) + 2] = h.begin[ch];
+      erec[4 * size_t(x) + 3] = h.begin[ch + 1];
+      cent[x] = h.entry[ch];
+    }
+  }
   e = hipMemcpyAsync(base + o_begin, h.begin.data(), 4 * h.begin.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipMemcpyAsync(base + o_entry, h.entry.data(), 4 * h.entry.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipMemcpyAsync(base + o_tok, h.tok.data(), 4 * h.tok.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipMemcpyAsync(base + o_child, h.child.data(), 4 * h.child.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipMemcpyAsync(base + o_live0, live0.data(), 4 * live0.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipMemcpyAsync(base + o_rec, rec.data(), 4 * rec.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(base + o_erec, erec.data(), 4 * erec.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(base + o_cent, cent.data(), 4 * cent.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     (void)hipFree(t->dmem);
@@ -221,6 +237,8 @@ tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_
   d.child = reinterpret_cast<const int32_t*>(base + o_child);
   d.live0 = reinterpret_cast<const int32_t*>(base + o_live0);
   d.node_rec = reinterpret_cast<const tms::NodeRec*>(base + o_rec);
+  d.erec = reinterpret_cast<const tms::EdgeRec*>(base + o_erec);
+  d.cent = reinterpret_cast<const int32_t*>(base + o_cent);
   d.n_nodes = h.n_nodes;
   d.n_edges = h.n_edges;
   d.n_entries = h.n_entries;

@@ -15,6 +15,14 @@ struct alignas(16) NodeRec {
   int32_t b0, b1, ent, pad;
 };
 
+// One 16-byte record per edge: the child node (kChildSep/kChildStop for
+// control edges), the token, and the child's edge range [b0, b1) (0, 0 for
+// control edges).  With the child's entry (a separate array) one read of an
+// edge gives everything a step needs to move along it.
+struct alignas(16) EdgeRec {
+  int32_t child, tok, b0, b1;
+};
+
 struct DevTrie {
   const int32_t* begin;  // [n_nodes+1]
   const int32_t* entry;  // [n_nodes]
@@ -22,6 +30,8 @@ struct DevTrie {
   const int32_t* child;  // [n_edges]
   const int32_t* live0;  // [live_stride], zero padded past n_edges
   const NodeRec* node_rec;  // [n_nodes]
+  const EdgeRec* erec;      // [n_edges]
+  const int32_t* cent;      // [live_stride] entry of the edge's child (-1: none or control edge), -1 padded
   int32_t n_nodes, n_edges, n_entries, cap, max_depth, sep, stop, vocab;
   int32_t live_stride;   // n_edges rounded up to a multiple of 4
 };

@@ -319,13 +319,26 @@ struct Cand {
 // loop), or with per-lane vector loads (GLOBAL).
 enum { kMetaScalar = 0, kMetaLds = 1, kMetaVector = 2 };
 
-// The trie arrays a scan reads (device memory, or their LDS copies).
+// The trie arrays a scan reads (device memory, or their LDS copies): edge
+// records and the entries of the edges' children.
 struct TrieView {
-  const int32_t* begin;
-  const int32_t* entry;
-  const int32_t* tok;
-  const int32_t* child;
+  const EdgeRec* erec;
+  const int32_t* cent;
 };
+
+// A wave-uniform edge record: scalar loads (kMetaScalar) or one 16-byte read
+// whose fields are moved to scalar registers.
+template <int META>
+__device__ __forceinline__ EdgeRec erec_uniform(const EdgeRec* p, int i) {
+  if constexpr (META == kMetaScalar) {
+    const cint_p q = (cint_p)(p + i);
+    return EdgeRec{q[0], q[1], q[2], q[3]};
+  } else {
+    const EdgeRec r = p[i];
+    return EdgeRec{__builtin_amdgcn_readfirstlane(r.child), __builtin_amdgcn_readfirstlane(r.tok),
+                   __builtin_amdgcn_readfirstlane(r.b0), __builtin_amdgcn_readfirstlane(r.b1)};
+  }
+}
 
 // Resident-loop keys carry the wavefront index in their three low bits (below
 // the edge order, so the tie rule is unchanged: edges are distinct): one LDS
@@ -368,45 +381,34 @@ __device__ __forceinline__ unsigned long long scan_node(const DevTrie& tr, const
       int rows[U], edges[U], chs[U];
       // edge records for all U slots first (indices clamped into the range,
       // out-of-range slots masked afterwards), then one wait
-      int cs[U], ts[U], lvs[U];
+      EdgeRec rs[U];
+      int lvs[U], ces[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int e = e0 + u * W;
         const int ee = e < q.b1 ? e : q.b1 - 1;  // every node has at least one edge
-        cs[u] = meta_uniform<META>(tv.child, ee);
-        ts[u] = meta_uniform<META>(tv.tok, ee);
+        rs[u] = erec_uniform<META>(tv.erec, ee);
         lvs[u] = read_live_uniform<LIVE>(live, ee);  // control edges hold 0
+        ces[u] = CAND ? meta_uniform<META>(tv.cent, ee) : -1;
       }
       // consume every record here so that all of them are requested together,
       // before the first row gather (the compiler would otherwise sink them)
 #pragma unroll
-      for (int u = 0; u < U; ++u) asm volatile("" ::"s"(cs[u]), "s"(ts[u]), "s"(lvs[u]));
+      for (int u = 0; u < U; ++u) {
+        asm volatile("" ::"s"(rs[u].child), "s"(rs[u].tok), "s"(lvs[u]));
+        if constexpr (CAND) asm volatile("" ::"s"(rs[u].b0), "s"(rs[u].b1), "s"(ces[u]));
+      }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int e = e0 + u * W;
         // bitwise, so that every record load above is used unconditionally
-        const bool ok = (e < q.b1) & edge_ok_bits(cs[u], lvs[u], q);
+        const bool ok = (e < q.b1) & edge_ok_bits(rs[u].child, lvs[u], q);
         edges[u] = e;
-        rows[u] = ts[u] | -(int)!ok;
-        chs[u] = ok ? cs[u] : -3;
+        rows[u] = rs[u].tok | -(int)!ok;
+        chs[u] = ok ? rs[u].child : -3;
       }
       uint4 raw[U][NC];
       issue_rows<NC, U>(emb, nq, rows, raw, lane);
-      NodeRec recs[U];
-      if constexpr (CAND) {
-        // the children's records travel with the row gathers
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          if (chs[u] < 0) {
-            recs[u] = NodeRec{0, 0, -1, 0};
-          } else if constexpr (META == kMetaLds) {
-            recs[u] = NodeRec{meta_uniform<META>(tv.begin, chs[u]), meta_uniform<META>(tv.begin, chs[u] + 1),
-                              meta_uniform<META>(tv.entry, chs[u]), 0};
-          } else {
-            recs[u] = tr.node_rec[chs[u]];
-          }
-        }
-      }
       float l[U];
       finish_rows<DT, NC, U>(nq, rows, raw, hq, l, lane);
 #pragma unroll
@@ -415,7 +417,7 @@ __device__ __forceinline__ unsigned long long scan_node(const DevTrie& tr, const
         const unsigned long long k = key_of(l[u], edges[u]);
         if (k > best) {
           best = k;
-          if constexpr (CAND) cand = Cand{chs[u], rows[u], recs[u].b0, recs[u].b1, recs[u].ent};
+          if constexpr (CAND) cand = Cand{chs[u], rows[u], rs[u].b0, rs[u].b1, ces[u]};
         }
       }
     };
@@ -428,15 +430,12 @@ __device__ __forceinline__ unsigned long long scan_node(const DevTrie& tr, const
       NodeRec rec{0, 0, -1, 0};
       {
         const int ee = e < q.b1 ? e : q.b1 - 1;
-        const int c = tr.child[ee];
-        const int t = tr.tok[ee];
+        const EdgeRec r = tr.erec[ee];
         const int lv = live[ee];  // control edges hold 0
-        const bool ok = (e < q.b1) & edge_ok_bits(c, lv, q);
-        tk = t | -(int)!ok;
-        ch = ok ? c : -3;
-      }
-      if constexpr (CAND) {
-        if (ch >= 0) rec = tr.node_rec[ch];
+        const bool ok = (e < q.b1) & edge_ok_bits(r.child, lv, q);
+        tk = r.tok | -(int)!ok;
+        ch = ok ? r.child : -3;
+        if constexpr (CAND) rec = NodeRec{r.b0, r.b1, tr.cent[ee], 0};
       }
       unsigned long long m = __ballot(tk >= 0);
       while (m) {
@@ -504,7 +503,7 @@ __global__ __launch_bounds__(kBlock) void step_sparse_kernel(DevTrie tr, DevStat
   load_hidden<NC>((const uint4*)io.hidden + (int64_t)s * nq, nq, hq, lane);
   const int32_t* live = st.live + (int64_t)s * tr.live_stride;
   Cand unused;
-  const TrieView tv{tr.begin, tr.entry, tr.tok, tr.child};
+  const TrieView tv{tr.erec, tr.cent};
   const unsigned long long best = scan_node<DT, NC, FAST ? kMetaScalar : kMetaVector, kLiveScalar, false>(
       tr, tv, q, live, (const uint4*)io.emb, nq, hq, wv, W, lane, unused);
 
@@ -546,18 +545,24 @@ __global__ __launch_bounds__(kBlock) void step_sparse_kernel(DevTrie tr, DevStat
 // step handles those, including the empty-mask error).  Every wavefront of
 // the resident loop evaluates it from the same state, so all of them take the
 // same branch without a barrier.
-__device__ __forceinline__ int forced_edge(const TrieView& tv, const int32_t* live, const Seq& q, int lane) {
+__device__ __forceinline__ int forced_edge(const TrieView& tv, const int32_t* live, const Seq& q, int lane,
+                                           Cand& c) {
   const int f = q.b1 - q.b0;
   if (f > kWave) return -1;
   const int e = q.b0 + lane;
-  int c = kChildSep - 8, lv = 0;  // lanes past the range: matches no edge kind
+  EdgeRec r{kChildSep - 8, 0, 0, 0};  // lanes past the range: matches no edge kind
+  int lv = 0, ce = -1;
   if (lane < f) {
-    c = tv.child[e];
+    r = tv.erec[e];
     lv = live[e];  // read for every edge (in range of the live array), used for content edges
+    ce = tv.cent[e];
   }
-  const unsigned long long m = __ballot(edge_ok_bits(c, lv, q));
+  const unsigned long long m = __ballot(edge_ok_bits(r.child, lv, q));
   if (__popcll(m) != 1) return -1;
-  return q.b0 + (int)__builtin_ctzll(m);
+  const int w = (int)__builtin_ctzll(m);
+  c = Cand{__builtin_amdgcn_readlane(r.child, w), __builtin_amdgcn_readlane(r.tok, w),
+           __builtin_amdgcn_readlane(r.b0, w), __builtin_amdgcn_readlane(r.b1, w), __builtin_amdgcn_readlane(ce, w)};
+  return q.b0 + w;
 }
 
 // ---------------------------------------------------------------------------
@@ -575,20 +580,19 @@ constexpr int kLoopBlock = 512;
 constexpr int kLoopWaves = kLoopBlock / kWave;
 
 // LDS layout of the resident loop (in int32 words, each part a multiple of 4):
-// live counts, spent bits and, with the trie in LDS, begin/entry/tok/child.
+// live counts, spent bits and, with the trie in LDS, edge records and the
+// entries of the edges' children.
 struct LoopLds {
-  int live, spent, begin, entry, tok, child, total;
+  int live, spent, erec, cent, total;
 };
 __host__ __device__ inline int round4(int n) { return (n + 3) & ~3; }
 __host__ __device__ inline LoopLds loop_lds_layout(const DevTrie& tr, const DevState& st, bool trie) {
   LoopLds o;
   o.live = 0;
   o.spent = o.live + tr.live_stride;
-  o.begin = o.spent + round4(st.spent_words);
-  o.entry = o.begin + (trie ? round4(tr.n_nodes + 1) : 0);
-  o.tok = o.entry + (trie ? round4(tr.n_nodes) : 0);
-  o.child = o.tok + (trie ? round4(tr.n_edges) : 0);
-  o.total = o.child + (trie ? round4(tr.n_edges) : 0);
+  o.erec = o.spent + round4(st.spent_words);
+  o.cent = o.erec + (trie ? 4 * tr.n_edges : 0);
+  o.total = o.cent + (trie ? tr.live_stride : 0);
   return o;
 }
 
@@ -600,15 +604,31 @@ __device__ __forceinline__ void copy_to_lds(int32_t* dst, const int32_t* src, in
     reinterpret_cast<int4*>(dst)[i] = reinterpret_cast<const int4*>(src)[i];
 }
 
-template <int DT, int NC, int META, bool LDS_LIVE>
+// Every wavefront of the loop holds the same copy of the sequence's state
+// (node, depth, pointers done, the node's record and control-edge flags) and
+// takes every decision itself from the same inputs, so the steps need
+// barriers only where LDS is written: once per step that reads the head
+// (winning keys and payloads go through LDS) and around the release of a
+// completed pointer's live counts.  Wavefront 0 alone keeps the path, the
+// completed entries and the emitted tokens.
+//   Keys rotate over three LDS slots and payloads over two, indexed by the
+// number of head steps so far: the slot a step fills was last read two head
+// steps earlier, before the barrier of the previous head step, and is cleared
+// by wavefront 0 before that of the current one.
+// SMALL: path, completed entries and spent flags are known to fit the
+// register-held lists (depth, k and spent words at most 64); the general
+// instantiations decide at run time.
+template <int DT, int NC, int META, bool LDS_LIVE, bool SMALL>
 __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState st, LoopIO io) {
   constexpr int EL = DT == 0 ? 4 : 8;
   constexpr bool TRIE_LDS = META == kMetaLds;
+  // With the trie in LDS the winner's record is read again from LDS after the
+  // barrier; otherwise each wavefront's best candidate carries it (PAYLOAD).
+  constexpr bool PAYLOAD = !TRIE_LDS;
   static_assert(!TRIE_LDS || LDS_LIVE, "the LDS trie comes with LDS live counts");
-  extern __shared__ int32_t lds[];
-  __shared__ unsigned long long s_key;
-  __shared__ Cand s_cand[kLoopWaves];
-  __shared__ int s_next[8];
+  extern __shared__ __attribute__((aligned(16))) int32_t lds[];
+  __shared__ unsigned long long s_key[3];
+  __shared__ Cand s_cand[2][kLoopWaves];
   __shared__ NodeRec s_root;
   const int s = blockIdx.x;
   const int lane = __lane_id();
@@ -621,17 +641,21 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
   uint32_t* g_spent = st.spent + (int64_t)s * st.spent_words;
   int32_t* live = LDS_LIVE ? lds + lay.live : g_live;
   uint32_t* spent = LDS_LIVE ? reinterpret_cast<uint32_t*>(lds + lay.spent) : g_spent;
-  TrieView tv{tr.begin, tr.entry, tr.tok, tr.child};
+  // spent flags of up to 2048 entries live in a register of every wavefront
+  // (lane l: word l); beyond that in LDS or device memory
+  const bool sreg_ok = SMALL || st.spent_words <= kWave;
+  uint32_t sreg = 0u;
+  if (sreg_ok && lane < st.spent_words) sreg = g_spent[lane];
+  TrieView tv{tr.erec, tr.cent};
   if constexpr (LDS_LIVE) {
     copy_to_lds(lds + lay.live, g_live, (int)ls);
-    for (int i = threadIdx.x; i < st.spent_words; i += kLoopBlock) spent[i] = g_spent[i];
+    if (!sreg_ok)
+      for (int i = threadIdx.x; i < st.spent_words; i += kLoopBlock) spent[i] = g_spent[i];
   }
   if constexpr (TRIE_LDS) {
-    copy_to_lds(lds + lay.begin, tr.begin, tr.n_nodes + 1);
-    copy_to_lds(lds + lay.entry, tr.entry, tr.n_nodes);
-    copy_to_lds(lds + lay.tok, tr.tok, tr.n_edges);
-    copy_to_lds(lds + lay.child, tr.child, tr.n_edges);
-    tv = TrieView{lds + lay.begin, lds + lay.entry, lds + lay.tok, lds + lay.child};
+    copy_to_lds(lds + lay.erec, reinterpret_cast<const int32_t*>(tr.erec), 4 * tr.n_edges);
+    copy_to_lds(lds + lay.cent, tr.cent, (int)ls);
+    tv = TrieView{reinterpret_cast<const EdgeRec*>(lds + lay.erec), lds + lay.cent};
   }
   int node = st.node[s], depth = st.depth[s], done = st.done[s];
   int status = st.status[s], fin = st.finished[s], nemit = st.nemit[s];
@@ -642,7 +666,7 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
   // completed entries (lane j: entry j) and the tokens of the last 64 steps
   // (lane t % 64) in registers; they reach device memory only at the end (or
   // every 64 steps for tokens), so the step barriers need not wait for stores.
-  const bool reg_lists = st.path_stride <= kWave && st.k <= kWave;
+  const bool reg_lists = SMALL || (st.path_stride <= kWave && st.k <= kWave);
   int my_path = -1, my_ent = -1, my_tok = -1;
   if (wv == 0 && reg_lists) {
     if (lane < depth) my_path = path[lane];
@@ -651,11 +675,15 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
   NodeRec rec = rec_scalar(tr.node_rec, node);
   if (threadIdx.x == 0) {
     s_root = rec_scalar(tr.node_rec, 0);
-    s_key = 0ull;
+    s_key[0] = s_key[1] = s_key[2] = 0ull;
   }
   __syncthreads();
-  bool ctl0 = false;
-  if (rec.ent >= 0) ctl0 = ((__builtin_amdgcn_readfirstlane(spent[rec.ent >> 5]) >> (rec.ent & 31)) & 1) == 0;
+  auto is_spent = [&](int ent) -> bool {
+    const uint32_t w = sreg_ok ? (uint32_t)__builtin_amdgcn_readlane((int)sreg, ent >> 5)
+                               : (uint32_t)__builtin_amdgcn_readfirstlane(spent[ent >> 5]);
+    return ((w >> (ent & 31)) & 1u) != 0u;
+  };
+  bool ctl0 = rec.ent >= 0 && !is_spent(rec.ent);
   bool sep_ok = ctl0 && done + 1 < st.k, stop_ok = ctl0 && done + 1 >= st.k;
   const uint4* hid = (const uint4*)io.hidden_seq;
   const uint4* emb = (const uint4*)io.emb;
@@ -663,7 +691,8 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
   if (io.T > 0) load_hidden<NC>(hid + (int64_t)s * nq, nq, hq, lane);
   int t = 0;
   int t_flushed = 0;  // tokens [0, t_flushed) are in device memory
-  int hq_t = 0;          // step whose hidden vector is in (or on its way to) hq
+  int hq_t = 0;       // step whose hidden vector is in (or on its way to) hq
+  int nhead = 0;      // steps so far that read the head
   // Wavefront 0: the token of step t goes to lane t % 64; every 64 steps the
   // lanes are written out.
   auto record = [&](int tok) {
@@ -673,20 +702,57 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
       t_flushed += kWave;
     }
   };
-  // Wavefront 0: a pointer completes; release its path, spend its terminal.
-  auto release = [&](int ent) {
-    if (reg_lists) {
-      if (lane < depth) live[my_path] -= 1;  // distinct edges
-      if (lane == done) my_ent = ent;
+  // Move along edge e with payload c (every wavefront).  Completing a pointer:
+  // wavefront 0 releases its path's live counts, records the entry and spends
+  // the terminal; the barrier after it publishes the new counts.  The caller
+  // guarantees that no wavefront still reads this answer's live counts.
+  auto take = [&](int e, const Cand& c) {
+    if (c.child >= 0) {
+      if (wv == 0) {
+        if (reg_lists) {
+          if (lane == depth) my_path = e;
+        } else {
+          if (lane == 0) path[depth] = e;
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // read back by this wavefront
+        }
+      }
+      depth += 1;
+      node = c.child;
+      rec = NodeRec{c.b0, c.b1, c.ent, 0};
     } else {
-      for (int i = lane; i < depth; i += kWave) live[path[i]] -= 1;
-      if (lane == 0) entries[done] = ent;
+      const int ent = rec.ent;
+      if (wv == 0) {
+        if (reg_lists) {
+          if (lane < depth) live[my_path] -= 1;  // distinct edges
+          if (lane == done) my_ent = ent;
+        } else {
+          for (int i = lane; i < depth; i += kWave) live[path[i]] -= 1;
+          if (lane == 0) entries[done] = ent;
+        }
+        if (!sreg_ok && lane == 0) spent[ent >> 5] |= 1u << (ent & 31);
+        if (!LDS_LIVE || !reg_lists || !sreg_ok) {
+          // live counts, spent flags or entries in device memory are read again
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+      }
+      if (sreg_ok && lane == (ent >> 5)) sreg |= 1u << (ent & 31);
+      if constexpr (LDS_LIVE) lds_barrier();
+      else __syncthreads();
+      done += 1;
+      depth = 0;
+      if (c.child == kChildStop) {
+        fin = 1;
+      } else {
+        node = 0;
+        rec = s_root;
+      }
     }
-    if (lane == 0) spent[ent >> 5] |= 1u << (ent & 31);
-    if (!LDS_LIVE || !reg_lists) {
-      // live counts, spent flags or entries in device memory are read again
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+    nemit += 1;
+    if (wv == 0) record(c.tok);
+    // control edges of the node reached: terminal, not yet spent, exactly-k rule
+    const bool ctl = rec.ent >= 0 && !fin && !is_spent(rec.ent);
+    sep_ok = ctl && done + 1 < st.k;
+    stop_ok = ctl && done + 1 >= st.k;
   };
   for (; t < io.T && status == kSeqOk && !fin; ++t) {
     Seq q;
@@ -697,60 +763,27 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
     q.b1 = rec.b1;
     q.sep_ok = sep_ok;
     q.stop_ok = stop_ok;
-    const int fe = forced_edge(tv, live, q, lane);
+    Cand fc;
+    const int fe = forced_edge(tv, live, q, lane, fc);
     if (fe >= 0) {
-      // forced: no rows, no reduction; a content edge needs no barrier
-      const int c = __builtin_amdgcn_readfirstlane(tv.child[fe]);
-      const int tok = __builtin_amdgcn_readfirstlane(tv.tok[fe]);
-      if (c >= 0) {
-        if (wv == 0) {
-          if (reg_lists) {
-            if (lane == depth) my_path = fe;
-          } else {
-            if (lane == 0) path[depth] = fe;
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-          }
-        }
-        depth += 1;
-        node = c;
-        if constexpr (TRIE_LDS)
-          rec = NodeRec{__builtin_amdgcn_readfirstlane(tv.begin[c]), __builtin_amdgcn_readfirstlane(tv.begin[c + 1]),
-                        __builtin_amdgcn_readfirstlane(tv.entry[c]), 0};
-        else
-          rec = rec_scalar(tr.node_rec, c);
-      } else {
-        // every wavefront has finished reading live counts of this answer's
-        // path before wavefront 0 releases it, and sees the result after
+      // forced: no rows, no reduction.  A completion first waits until every
+      // wavefront has passed its last read of the path's live counts (forced
+      // steps have no barrier of their own).
+      if (fc.child < 0) {
         if constexpr (LDS_LIVE) lds_barrier();
         else __syncthreads();
-        if (wv == 0) release(rec.ent);
-        if constexpr (LDS_LIVE) lds_barrier();
-        else __syncthreads();
-        done += 1;
-        depth = 0;
-        if (c == kChildStop) {
-          fin = 1;
-        } else {
-          node = 0;
-          rec = s_root;
-        }
       }
-      if (wv == 0) {
-        nemit += 1;
-        record(tok);
-      }
-      const bool ctl = rec.ent >= 0 && !fin &&
-                       ((__builtin_amdgcn_readfirstlane(spent[rec.ent >> 5]) >> (rec.ent & 31)) & 1) == 0;
-      sep_ok = ctl && done + 1 < st.k;
-      stop_ok = ctl && done + 1 >= st.k;
+      take(fe, fc);
       continue;
     }
     if (hq_t != t) {
       load_hidden<NC>(hid + ((int64_t)t * st.B + s) * nq, nq, hq, lane);
       hq_t = t;
     }
+    const int slot = nhead % 3;
+    if (threadIdx.x == 0) s_key[(nhead + 1) % 3] = 0ull;  // the next head step's slot
     Cand cand{0, 0, 0, 0, 0};
-    const unsigned long long best = scan_node<DT, NC, META, LDS_LIVE ? kLiveLds : kLiveVector, true>(
+    const unsigned long long best = scan_node<DT, NC, META, LDS_LIVE ? kLiveLds : kLiveVector, PAYLOAD>(
         tr, tv, q, live, emb, nq, hq, wv, W, lane, cand);
     // the next step's hidden vector does not depend on this step: fetch it now
     if (t + 1 < io.T) {
@@ -758,74 +791,31 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
       hq_t = t + 1;
     }
     if (lane == 0) {
-      if (best) __hip_atomic_fetch_max(&s_key, best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      s_cand[wv] = cand;
+      if (best) __hip_atomic_fetch_max(&s_key[slot], best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if constexpr (PAYLOAD) s_cand[nhead & 1][wv] = cand;
     }
     lds_barrier();
-    if (wv == 0) {
-      const unsigned long long key = s_key;
-      int tok = -1;
-      if (!key) {
-        status = kSeqEmptyMask;
-      } else {
-        const int e = (int)key_wave_edge(key);
-        const Cand c = s_cand[key & 7];
-        tok = c.tok;
-        if (c.child >= 0) {
-          if (reg_lists) {
-            if (lane == depth) my_path = e;
-          } else {
-            if (lane == 0) path[depth] = e;
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // read back by this wavefront
-          }
-          depth += 1;
-          node = c.child;
-          rec = NodeRec{c.b0, c.b1, c.ent, 0};
-        } else {
-          release(rec.ent);
-          done += 1;
-          depth = 0;
-          if (c.child == kChildStop) {
-            fin = 1;
-          } else {
-            node = 0;
-            rec = s_root;
-          }
-        }
-        nemit += 1;
-      }
-      // control edges of the node reached: terminal, not yet spent, exactly-k rule
-      bool ctl = false;
-      if (rec.ent >= 0 && !fin && status == kSeqOk) {
-        bool sp;
-        if (reg_lists) sp = __ballot(lane < done && my_ent == rec.ent) != 0ull;
-        else sp = ((__builtin_amdgcn_readfirstlane(spent[rec.ent >> 5]) >> (rec.ent & 31)) & 1) != 0;
-        ctl = !sp;
-      }
-      const bool more = done + 1 < st.k;
-      record(tok);
-      if (lane == 0) {
-        s_key = 0ull;
-        s_next[0] = node;
-        s_next[1] = depth;
-        s_next[2] = done;
-        s_next[3] = fin | (status << 1);
-        s_next[4] = rec.b0;
-        s_next[5] = rec.b1;
-        s_next[6] = rec.ent;
-        s_next[7] = (ctl && more ? 1 : 0) | (ctl && !more ? 2 : 0);
-      }
+    const unsigned long long key = s_key[slot];
+    const uint32_t klo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)key);
+    const uint32_t khi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(key >> 32));
+    if ((klo | khi) == 0u) {
+      status = kSeqEmptyMask;
+      if (wv == 0) record(-1);
+    } else if constexpr (PAYLOAD) {
+      const Cand w = s_cand[nhead & 1][klo & 7u];
+      const Cand c{__builtin_amdgcn_readfirstlane(w.child), __builtin_amdgcn_readfirstlane(w.tok),
+                   __builtin_amdgcn_readfirstlane(w.b0), __builtin_amdgcn_readfirstlane(w.b1),
+                   __builtin_amdgcn_readfirstlane(w.ent)};
+      take((int)key_wave_edge(((unsigned long long)khi << 32) | klo), c);
+    } else {
+      const int e = (int)key_id(((unsigned long long)khi << 32) | klo);  // plain keys carry the edge
+      const EdgeRec r = tv.erec[e];
+      const Cand c{__builtin_amdgcn_readfirstlane(r.child), __builtin_amdgcn_readfirstlane(r.tok),
+                   __builtin_amdgcn_readfirstlane(r.b0), __builtin_amdgcn_readfirstlane(r.b1),
+                   __builtin_amdgcn_readfirstlane(tv.cent[e])};
+      take(e, c);
     }
-    if constexpr (LDS_LIVE) lds_barrier();
-    else __syncthreads();  // live counts in device memory: order them too
-    node = s_next[0];
-    depth = s_next[1];
-    done = s_next[2];
-    fin = s_next[3] & 1;
-    status = s_next[3] >> 1;
-    rec = NodeRec{s_next[4], s_next[5], s_next[6], 0};
-    sep_ok = (s_next[7] & 1) != 0;
-    stop_ok = (s_next[7] & 2) != 0;
+    nhead += 1;
   }
   if (wv == 0) {
     // tokens of the steps since the last flush, then -1 for the steps not run
@@ -835,6 +825,7 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
       if (lane < depth) path[lane] = my_path;
       if (lane < done) entries[lane] = my_ent;
     }
+    if (sreg_ok && lane < st.spent_words) g_spent[lane] = sreg;
   }
   for (int i = t + threadIdx.x; i < io.T; i += kLoopBlock) tokens[i] = -1;
   if (status == kSeqOk && !fin) status = kSeqNotDone;
@@ -855,7 +846,8 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
     __syncthreads();
     int4* dst = reinterpret_cast<int4*>(g_live);
     for (int i = threadIdx.x; i < (int)(ls / 4); i += kLoopBlock) dst[i] = reinterpret_cast<const int4*>(live)[i];
-    for (int i = threadIdx.x; i < st.spent_words; i += kLoopBlock) g_spent[i] = spent[i];
+    if (!sreg_ok)
+      for (int i = threadIdx.x; i < st.spent_words; i += kLoopBlock) g_spent[i] = spent[i];
   }
 }
 
@@ -1220,10 +1212,10 @@ struct StepLaunch {
 
 template <int DT, int NC>
 struct LoopLaunch {
-  template <int META, bool LIVE>
+  template <int META, bool LIVE, bool SMALL>
   static hipError_t go(const DevTrie& tr, const DevState& st, const LoopIO& io, hipStream_t s) {
     const size_t lds = LIVE ? sizeof(int32_t) * (size_t)loop_lds_layout(tr, st, META == kMetaLds).total : 0;
-    auto* k = &loop_kernel<DT, NC, META, LIVE>;
+    auto* k = &loop_kernel<DT, NC, META, LIVE, SMALL>;
     static size_t allowed = 65536;  // per instantiation; raised once as needed
     if (lds > allowed) {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
@@ -1235,11 +1227,14 @@ struct LoopLaunch {
     return hipGetLastError();
   }
   static hipError_t run(const DevTrie& tr, const DevState& st, const LoopIO& io, int mode, hipStream_t s) {
+    const bool small = st.path_stride <= kWave && st.k <= kWave && st.spent_words <= kWave;
     switch (mode) {
-      case kLoopTrieLds: return go<kMetaLds, true>(tr, st, io, s);
-      case kLoopFastGlobal: return go<kMetaScalar, false>(tr, st, io, s);
-      case kLoopVectorLds: return go<kMetaVector, true>(tr, st, io, s);
-      default: return go<kMetaVector, false>(tr, st, io, s);
+      case kLoopTrieLds:
+        return small ? go<kMetaLds, true, true>(tr, st, io, s) : go<kMetaLds, true, false>(tr, st, io, s);
+      case kLoopFastGlobal: return go<kMetaScalar, false, false>(tr, st, io, s);
+      case kLoopVectorLds:
+        return small ? go<kMetaVector, true, true>(tr, st, io, s) : go<kMetaVector, true, false>(tr, st, io, s);
+      default: return go<kMetaVector, false, false>(tr, st, io, s);
     }
   }
 };
