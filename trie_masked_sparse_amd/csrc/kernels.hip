@@ -687,11 +687,8 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
   bool sep_ok = ctl0 && done + 1 < st.k, stop_ok = ctl0 && done + 1 >= st.k;
   const uint4* hid = (const uint4*)io.hidden_seq;
   const uint4* emb = (const uint4*)io.emb;
-  uint4 hq[NC];
-  if (io.T > 0) load_hidden<NC>(hid + (int64_t)s * nq, nq, hq, lane);
   int t = 0;
   int t_flushed = 0;  // tokens [0, t_flushed) are in device memory
-  int hq_t = 0;       // step whose hidden vector is in (or on its way to) hq
   int nhead = 0;      // steps so far that read the head
   // Wavefront 0: the token of step t goes to lane t % 64; every 64 steps the
   // lanes are written out.
@@ -776,20 +773,16 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
       take(fe, fc);
       continue;
     }
-    if (hq_t != t) {
-      load_hidden<NC>(hid + ((int64_t)t * st.B + s) * nq, nq, hq, lane);
-      hq_t = t;
-    }
+    // this step's hidden vector, requested before the edge records and rows:
+    // it arrives alongside them (a copy carried from earlier steps would have
+    // to be moved and waited for on every forced step)
+    uint4 hq[NC];
+    load_hidden<NC>(hid + ((int64_t)t * st.B + s) * nq, nq, hq, lane);
     const int slot = nhead % 3;
     if (threadIdx.x == 0) s_key[(nhead + 1) % 3] = 0ull;  // the next head step's slot
     Cand cand{0, 0, 0, 0, 0};
     const unsigned long long best = scan_node<DT, NC, META, LDS_LIVE ? kLiveLds : kLiveVector, PAYLOAD>(
         tr, tv, q, live, emb, nq, hq, wv, W, lane, cand);
-    // the next step's hidden vector does not depend on this step: fetch it now
-    if (t + 1 < io.T) {
-      load_hidden<NC>(hid + ((int64_t)(t + 1) * st.B + s) * nq, nq, hq, lane);
-      hq_t = t + 1;
-    }
     if (lane == 0) {
       if (best) __hip_atomic_fetch_max(&s_key[slot], best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       if constexpr (PAYLOAD) s_cand[nhead & 1][wv] = cand;
