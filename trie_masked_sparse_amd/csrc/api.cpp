@@ -187,6 +187,42 @@ tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_
   const size_t o_rec = c.take<int32_t>(size_t(h.n_nodes) * 4);
   const size_t o_erec = c.take<int32_t>(size_t(h.n_edges) * 4);
   const size_t o_cent = c.take<int32_t>(live_stride);
+  // forced runs: chains of nodes with a single edge, each stored once
+  std::vector<int32_t> run(live_stride, 0), run_edge, run_tok;
+  {
+    auto unary = [&](int32_t n) { return h.begin[n + 1] - h.begin[n] == 1; };
+    std::vector<int32_t> chain;
+    for (int32_t n = 0; n < h.n_nodes; ++n) {
+      if (n != 0 && unary(n)) continue;  // edges of single-edge nodes belong to their head's chain
+      for (int32_t x = h.begin[n]; x < h.begin[n + 1]; ++x) {
+        chain.clear();
+        for (int32_t y = x; h.child[y] >= 0 && unary(h.child[y]);) {
+          y = h.begin[h.child[y]];
+          chain.push_back(y);
+        }
+        if (chain.empty()) continue;
+        const int32_t p = static_cast<int32_t>(run_edge.size());
+        for (size_t i = 0; i < chain.size(); ++i) {
+          run_edge.push_back(chain[i]);
+          run_tok.push_back(h.tok[chain[i]]);
+        }
+        // edge x is followed by the whole chain, chain[i] by what follows it
+        const int32_t m = static_cast<int32_t>(chain.size());
+        for (int32_t i = -1; i < m; ++i) {
+          const int32_t edge = i < 0 ? x : chain[i];
+          const int32_t len = std::min(m - 1 - i, 64);
+          run[edge] = len > 0 ? ((p + i + 1) << 7) | len : 0;
+        }
+      }
+    }
+    if (run_edge.size() >= (size_t(1) << 24)) std::fill(run.begin(), run.end(), 0);  // offsets must fit
+  }
+  const int32_t n_run = static_cast<int32_t>(run_edge.size());
+  const size_t o_run = c.take<int32_t>(live_stride);
+  const size_t o_run_edge = c.take<int32_t>((n_run + 3) & ~3);
+  const size_t o_run_tok = c.take<int32_t>((n_run + 3) & ~3);
+  run_edge.resize((n_run + 3) & ~3, 0);
+  run_tok.resize((n_run + 3) & ~3, 0);
   hipError_t e = hipGetDevice(&t->device);
   if (e == hipSuccess) e = hipMalloc(&t->dmem, c.off);
   if (e != hipSuccess) {
@@ -224,6 +260,11 @@ tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_
   if (e == hipSuccess) e = hipMemcpyAsync(base + o_rec, rec.data(), 4 * rec.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipMemcpyAsync(base + o_erec, erec.data(), 4 * erec.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipMemcpyAsync(base + o_cent, cent.data(), 4 * cent.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(base + o_run, run.data(), 4 * run.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && !run_edge.empty())
+    e = hipMemcpyAsync(base + o_run_edge, run_edge.data(), 4 * run_edge.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && !run_tok.empty())
+    e = hipMemcpyAsync(base + o_run_tok, run_tok.data(), 4 * run_tok.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     (void)hipFree(t->dmem);
@@ -239,6 +280,10 @@ tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_
   d.node_rec = reinterpret_cast<const tms::NodeRec*>(base + o_rec);
   d.erec = reinterpret_cast<const tms::EdgeRec*>(base + o_erec);
   d.cent = reinterpret_cast<const int32_t*>(base + o_cent);
+  d.run = reinterpret_cast<const int32_t*>(base + o_run);
+  d.run_edge = reinterpret_cast<const int32_t*>(base + o_run_edge);
+  d.run_tok = reinterpret_cast<const int32_t*>(base + o_run_tok);
+  d.n_run = n_run;
   d.n_nodes = h.n_nodes;
   d.n_edges = h.n_edges;
   d.n_entries = h.n_entries;

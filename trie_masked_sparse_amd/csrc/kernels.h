@@ -32,6 +32,16 @@ struct DevTrie {
   const NodeRec* node_rec;  // [n_nodes]
   const EdgeRec* erec;      // [n_edges]
   const int32_t* cent;      // [live_stride] entry of the edge's child (-1: none or control edge), -1 padded
+  // Forced runs.  A node with a single edge (a content edge: terminals carry
+  // two control edges) leaves one legal token whenever it is reached along a
+  // legal edge, since that edge and the next count the same live pointers.
+  // Each maximal chain of such nodes is stored once, edges and tokens in
+  // order; run[e] = (offset << 7) | length (at most 64) of the part of a chain
+  // that follows edge e, 0 if e's child has more than one edge.
+  const int32_t* run;       // [live_stride]
+  const int32_t* run_edge;  // [n_run]
+  const int32_t* run_tok;   // [n_run]
+  int32_t n_run;            // nodes with a single edge
   int32_t n_nodes, n_edges, n_entries, cap, max_depth, sep, stop, vocab;
   int32_t live_stride;   // n_edges rounded up to a multiple of 4
 };

@@ -311,7 +311,7 @@ __device__ __forceinline__ int read_live_uniform(const int32_t* live, int e) {
 // A wavefront's best candidate, carried to the advance so that it needs no
 // further trie reads: the edge's child, its token and the child's record.
 struct Cand {
-  int child, tok, b0, b1, ent;
+  int child, tok, b0, b1, ent, run;
 };
 
 // Where a scan reads edge records: through the scalar cache from device
@@ -324,6 +324,9 @@ enum { kMetaScalar = 0, kMetaLds = 1, kMetaVector = 2 };
 struct TrieView {
   const EdgeRec* erec;
   const int32_t* cent;
+  const int32_t* run;
+  const int32_t* run_edge;
+  const int32_t* run_tok;
 };
 
 // A wave-uniform edge record: scalar loads (kMetaScalar) or one 16-byte read
@@ -382,7 +385,7 @@ __device__ __forceinline__ unsigned long long scan_node(const DevTrie& tr, const
       // edge records for all U slots first (indices clamped into the range,
       // out-of-range slots masked afterwards), then one wait
       EdgeRec rs[U];
-      int lvs[U], ces[U];
+      int lvs[U], ces[U], rns[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int e = e0 + u * W;
@@ -390,13 +393,14 @@ __device__ __forceinline__ unsigned long long scan_node(const DevTrie& tr, const
         rs[u] = erec_uniform<META>(tv.erec, ee);
         lvs[u] = read_live_uniform<LIVE>(live, ee);  // control edges hold 0
         ces[u] = CAND ? meta_uniform<META>(tv.cent, ee) : -1;
+        rns[u] = CAND ? meta_uniform<META>(tv.run, ee) : 0;
       }
       // consume every record here so that all of them are requested together,
       // before the first row gather (the compiler would otherwise sink them)
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         asm volatile("" ::"s"(rs[u].child), "s"(rs[u].tok), "s"(lvs[u]));
-        if constexpr (CAND) asm volatile("" ::"s"(rs[u].b0), "s"(rs[u].b1), "s"(ces[u]));
+        if constexpr (CAND) asm volatile("" ::"s"(rs[u].b0), "s"(rs[u].b1), "s"(ces[u]), "s"(rns[u]));
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -417,7 +421,7 @@ __device__ __forceinline__ unsigned long long scan_node(const DevTrie& tr, const
         const unsigned long long k = key_of(l[u], edges[u]);
         if (k > best) {
           best = k;
-          if constexpr (CAND) cand = Cand{chs[u], rows[u], rs[u].b0, rs[u].b1, ces[u]};
+          if constexpr (CAND) cand = Cand{chs[u], rows[u], rs[u].b0, rs[u].b1, ces[u], rns[u]};
         }
       }
     };
@@ -426,7 +430,7 @@ __device__ __forceinline__ unsigned long long scan_node(const DevTrie& tr, const
   } else {
     for (int base = q.b0 + wv; base < q.b1; base += kWave * W) {
       const int e = base + lane * W;
-      int tk = -1, ch = -3;
+      int tk = -1, ch = -3, rn = 0;
       NodeRec rec{0, 0, -1, 0};
       {
         const int ee = e < q.b1 ? e : q.b1 - 1;
@@ -435,11 +439,14 @@ __device__ __forceinline__ unsigned long long scan_node(const DevTrie& tr, const
         const bool ok = (e < q.b1) & edge_ok_bits(r.child, lv, q);
         tk = r.tok | -(int)!ok;
         ch = ok ? r.child : -3;
-        if constexpr (CAND) rec = NodeRec{r.b0, r.b1, tr.cent[ee], 0};
+        if constexpr (CAND) {
+          rec = NodeRec{r.b0, r.b1, tr.cent[ee], 0};
+          rn = tr.run[ee];
+        }
       }
       unsigned long long m = __ballot(tk >= 0);
       while (m) {
-        int rows[U], edges[U], chs[U], r0[U], r1[U], r2[U];
+        int rows[U], edges[U], chs[U], r0[U], r1[U], r2[U], r3[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           if (m) {
@@ -452,11 +459,12 @@ __device__ __forceinline__ unsigned long long scan_node(const DevTrie& tr, const
               r0[u] = __builtin_amdgcn_readlane(rec.b0, j);
               r1[u] = __builtin_amdgcn_readlane(rec.b1, j);
               r2[u] = __builtin_amdgcn_readlane(rec.ent, j);
+              r3[u] = __builtin_amdgcn_readlane(rn, j);
             }
           } else {
             rows[u] = -1;
             edges[u] = 0;
-            chs[u] = r0[u] = r1[u] = r2[u] = 0;
+            chs[u] = r0[u] = r1[u] = r2[u] = r3[u] = 0;
           }
         }
         float l[U];
@@ -467,7 +475,7 @@ __device__ __forceinline__ unsigned long long scan_node(const DevTrie& tr, const
           const unsigned long long k = key_of(l[u], edges[u]);
           if (k > best) {
             best = k;
-            if constexpr (CAND) cand = Cand{chs[u], rows[u], r0[u], r1[u], r2[u]};
+            if constexpr (CAND) cand = Cand{chs[u], rows[u], r0[u], r1[u], r2[u], r3[u]};
           }
         }
       }
@@ -503,7 +511,7 @@ __global__ __launch_bounds__(kBlock) void step_sparse_kernel(DevTrie tr, DevStat
   load_hidden<NC>((const uint4*)io.hidden + (int64_t)s * nq, nq, hq, lane);
   const int32_t* live = st.live + (int64_t)s * tr.live_stride;
   Cand unused;
-  const TrieView tv{tr.erec, tr.cent};
+  const TrieView tv{tr.erec, tr.cent, tr.run, tr.run_edge, tr.run_tok};
   const unsigned long long best = scan_node<DT, NC, FAST ? kMetaScalar : kMetaVector, kLiveScalar, false>(
       tr, tv, q, live, (const uint4*)io.emb, nq, hq, wv, W, lane, unused);
 
@@ -551,17 +559,19 @@ __device__ __forceinline__ int forced_edge(const TrieView& tv, const int32_t* li
   if (f > kWave) return -1;
   const int e = q.b0 + lane;
   EdgeRec r{kChildSep - 8, 0, 0, 0};  // lanes past the range: matches no edge kind
-  int lv = 0, ce = -1;
+  int lv = 0, ce = -1, rn = 0;
   if (lane < f) {
     r = tv.erec[e];
     lv = live[e];  // read for every edge (in range of the live array), used for content edges
     ce = tv.cent[e];
+    rn = tv.run[e];
   }
   const unsigned long long m = __ballot(edge_ok_bits(r.child, lv, q));
   if (__popcll(m) != 1) return -1;
   const int w = (int)__builtin_ctzll(m);
   c = Cand{__builtin_amdgcn_readlane(r.child, w), __builtin_amdgcn_readlane(r.tok, w),
-           __builtin_amdgcn_readlane(r.b0, w), __builtin_amdgcn_readlane(r.b1, w), __builtin_amdgcn_readlane(ce, w)};
+           __builtin_amdgcn_readlane(r.b0, w), __builtin_amdgcn_readlane(r.b1, w), __builtin_amdgcn_readlane(ce, w),
+           __builtin_amdgcn_readlane(rn, w)};
   return q.b0 + w;
 }
 
@@ -580,10 +590,10 @@ constexpr int kLoopBlock = 512;
 constexpr int kLoopWaves = kLoopBlock / kWave;
 
 // LDS layout of the resident loop (in int32 words, each part a multiple of 4):
-// live counts, spent bits and, with the trie in LDS, edge records and the
-// entries of the edges' children.
+// live counts, spent bits and, with the trie in LDS, edge records, the
+// entries of the edges' children and the forced-run tables.
 struct LoopLds {
-  int live, spent, erec, cent, total;
+  int live, spent, erec, cent, run, run_edge, run_tok, total;
 };
 __host__ __device__ inline int round4(int n) { return (n + 3) & ~3; }
 __host__ __device__ inline LoopLds loop_lds_layout(const DevTrie& tr, const DevState& st, bool trie) {
@@ -592,7 +602,10 @@ __host__ __device__ inline LoopLds loop_lds_layout(const DevTrie& tr, const DevS
   o.spent = o.live + tr.live_stride;
   o.erec = o.spent + round4(st.spent_words);
   o.cent = o.erec + (trie ? 4 * tr.n_edges : 0);
-  o.total = o.cent + (trie ? tr.live_stride : 0);
+  o.run = o.cent + (trie ? tr.live_stride : 0);
+  o.run_edge = o.run + (trie ? tr.live_stride : 0);
+  o.run_tok = o.run_edge + (trie ? round4(tr.n_run) : 0);
+  o.total = o.run_tok + (trie ? round4(tr.n_run) : 0);
   return o;
 }
 
@@ -609,8 +622,8 @@ __device__ __forceinline__ void copy_to_lds(int32_t* dst, const int32_t* src, in
 // takes every decision itself from the same inputs, so the steps need
 // barriers only where LDS is written: once per step that reads the head
 // (winning keys and payloads go through LDS) and around the release of a
-// completed pointer's live counts.  Wavefront 0 alone keeps the path, the
-// completed entries and the emitted tokens.
+// completed pointer's live counts.  Wavefront 0 alone keeps the path and the
+// completed entries and stores the emitted tokens.
 //   Keys rotate over three LDS slots and payloads over two, indexed by the
 // number of head steps so far: the slot a step fills was last read two head
 // steps earlier, before the barrier of the previous head step, and is cleared
@@ -646,7 +659,7 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
   const bool sreg_ok = SMALL || st.spent_words <= kWave;
   uint32_t sreg = 0u;
   if (sreg_ok && lane < st.spent_words) sreg = g_spent[lane];
-  TrieView tv{tr.erec, tr.cent};
+  TrieView tv{tr.erec, tr.cent, tr.run, tr.run_edge, tr.run_tok};
   if constexpr (LDS_LIVE) {
     copy_to_lds(lds + lay.live, g_live, (int)ls);
     if (!sreg_ok)
@@ -655,19 +668,23 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
   if constexpr (TRIE_LDS) {
     copy_to_lds(lds + lay.erec, reinterpret_cast<const int32_t*>(tr.erec), 4 * tr.n_edges);
     copy_to_lds(lds + lay.cent, tr.cent, (int)ls);
-    tv = TrieView{reinterpret_cast<const EdgeRec*>(lds + lay.erec), lds + lay.cent};
+    copy_to_lds(lds + lay.run, tr.run, (int)ls);
+    copy_to_lds(lds + lay.run_edge, tr.run_edge, tr.n_run);
+    copy_to_lds(lds + lay.run_tok, tr.run_tok, tr.n_run);
+    tv = TrieView{reinterpret_cast<const EdgeRec*>(lds + lay.erec), lds + lay.cent, lds + lay.run,
+                  lds + lay.run_edge, lds + lay.run_tok};
   }
   int node = st.node[s], depth = st.depth[s], done = st.done[s];
   int status = st.status[s], fin = st.finished[s], nemit = st.nemit[s];
   int32_t* path = st.path + (int64_t)s * st.path_stride;
   int32_t* entries = st.entries + (int64_t)s * st.k;
   int32_t* tokens = io.tokens_bt + (int64_t)s * io.T;
-  // Wavefront 0 keeps the current path (lane d: edge at depth d), the
-  // completed entries (lane j: entry j) and the tokens of the last 64 steps
-  // (lane t % 64) in registers; they reach device memory only at the end (or
-  // every 64 steps for tokens), so the step barriers need not wait for stores.
+  // Wavefront 0 keeps the current path (lane d: edge at depth d) and the
+  // completed entries (lane j: entry j) in registers; they reach device
+  // memory at the end.  Tokens are stored as they are emitted (stores are not
+  // waited for by the LDS barriers).
   const bool reg_lists = SMALL || (st.path_stride <= kWave && st.k <= kWave);
-  int my_path = -1, my_ent = -1, my_tok = -1;
+  int my_path = -1, my_ent = -1;
   if (wv == 0 && reg_lists) {
     if (lane < depth) my_path = path[lane];
     if (lane < done) my_ent = entries[lane];
@@ -688,24 +705,57 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
   const uint4* hid = (const uint4*)io.hidden_seq;
   const uint4* emb = (const uint4*)io.emb;
   int t = 0;
-  int t_flushed = 0;  // tokens [0, t_flushed) are in device memory
-  int nhead = 0;      // steps so far that read the head
-  // Wavefront 0: the token of step t goes to lane t % 64; every 64 steps the
-  // lanes are written out.
-  auto record = [&](int tok) {
-    if (lane == (t & (kWave - 1))) my_tok = tok;
-    if ((t & (kWave - 1)) == kWave - 1) {
-      tokens[t_flushed + lane] = my_tok;
-      t_flushed += kWave;
+  int nhead = 0;  // steps so far that read the head
+  // Step t emits control edge `kind` (token tok) at the current terminal:
+  // wavefront 0 releases the path's live counts, records the entry and
+  // spends the terminal; the barrier after it publishes the new counts.
+  // sync_first: some wavefront may still be reading live counts of this
+  // answer (no barrier since its last read), so wait for all of them first.
+  auto complete = [&](int kind, int tok, bool sync_first) {
+    if (sync_first) {
+      if constexpr (LDS_LIVE) lds_barrier();
+      else __syncthreads();
+    }
+    const int ent = rec.ent;
+    if (wv == 0) {
+      if (lane == 0) tokens[t] = tok;
+      if (reg_lists) {
+        if (lane < depth) live[my_path] -= 1;  // distinct edges
+        if (lane == done) my_ent = ent;
+      } else {
+        for (int i = lane; i < depth; i += kWave) live[path[i]] -= 1;
+        if (lane == 0) entries[done] = ent;
+      }
+      if (!sreg_ok && lane == 0) spent[ent >> 5] |= 1u << (ent & 31);
+      if (!LDS_LIVE || !reg_lists || !sreg_ok) {
+        // live counts, spent flags or entries in device memory are read again
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+    }
+    if (sreg_ok && lane == (ent >> 5)) sreg |= 1u << (ent & 31);
+    if constexpr (LDS_LIVE) lds_barrier();
+    else __syncthreads();
+    done += 1;
+    depth = 0;
+    nemit += 1;
+    if (kind == kChildStop) {
+      fin = 1;
+    } else {
+      node = 0;
+      rec = s_root;
     }
   };
-  // Move along edge e with payload c (every wavefront).  Completing a pointer:
-  // wavefront 0 releases its path's live counts, records the entry and spends
-  // the terminal; the barrier after it publishes the new counts.  The caller
-  // guarantees that no wavefront still reads this answer's live counts.
-  auto take = [&](int e, const Cand& c) {
-    if (c.child >= 0) {
+  // Step t takes edge e with payload c (every wavefront).  After a content
+  // edge, the forced run that follows it (single-edge nodes) is emitted at
+  // once, and a leaf terminal reached with its entry unspent completes in
+  // the next step (its only legal edge is sep or stop); each of these counts
+  // as steps and stops at the step budget.
+  auto take = [&](int e, const Cand& c, bool sync_release) {
+    if (c.child < 0) {
+      complete(c.child, c.tok, sync_release);
+    } else {
       if (wv == 0) {
+        if (lane == 0) tokens[t] = c.tok;
         if (reg_lists) {
           if (lane == depth) my_path = e;
         } else {
@@ -716,36 +766,39 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
       depth += 1;
       node = c.child;
       rec = NodeRec{c.b0, c.b1, c.ent, 0};
-    } else {
-      const int ent = rec.ent;
-      if (wv == 0) {
-        if (reg_lists) {
-          if (lane < depth) live[my_path] -= 1;  // distinct edges
-          if (lane == done) my_ent = ent;
-        } else {
-          for (int i = lane; i < depth; i += kWave) live[path[i]] -= 1;
-          if (lane == 0) entries[done] = ent;
+      nemit += 1;
+      int ri = c.run;
+      while ((ri & 127) != 0 && t + 1 < io.T) {
+        const int rl = ri & 127;
+        const int ra = (int)((uint32_t)ri >> 7);
+        const int L = min(rl, io.T - 1 - t);
+        if (wv == 0) {
+          if (lane < L) tokens[t + 1 + lane] = tv.run_tok[ra + lane];
+          if (reg_lists) {
+            const int i = lane - depth;
+            if (i >= 0 && i < L) my_path = tv.run_edge[ra + i];
+          } else {
+            if (lane < L) path[depth + lane] = tv.run_edge[ra + lane];
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // read back by this wavefront
+          }
         }
-        if (!sreg_ok && lane == 0) spent[ent >> 5] |= 1u << (ent & 31);
-        if (!LDS_LIVE || !reg_lists || !sreg_ok) {
-          // live counts, spent flags or entries in device memory are read again
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        }
+        const int el = __builtin_amdgcn_readfirstlane(tv.run_edge[ra + L - 1]);
+        const EdgeRec r = tv.erec[el];
+        const int ce = __builtin_amdgcn_readfirstlane(tv.cent[el]);
+        const int rn = __builtin_amdgcn_readfirstlane(tv.run[el]);
+        node = __builtin_amdgcn_readfirstlane(r.child);
+        rec = NodeRec{__builtin_amdgcn_readfirstlane(r.b0), __builtin_amdgcn_readfirstlane(r.b1), ce, 0};
+        depth += L;
+        t += L;
+        nemit += L;
+        ri = L == rl ? rn : 0;
       }
-      if (sreg_ok && lane == (ent >> 5)) sreg |= 1u << (ent & 31);
-      if constexpr (LDS_LIVE) lds_barrier();
-      else __syncthreads();
-      done += 1;
-      depth = 0;
-      if (c.child == kChildStop) {
-        fin = 1;
-      } else {
-        node = 0;
-        rec = s_root;
+      if (rec.ent >= 0 && rec.b1 - rec.b0 == 2 && t + 1 < io.T && !is_spent(rec.ent)) {
+        t += 1;
+        const bool more = done + 1 < st.k;
+        complete(more ? kChildSep : kChildStop, more ? tr.sep : tr.stop, sync_release);
       }
     }
-    nemit += 1;
-    if (wv == 0) record(c.tok);
     // control edges of the node reached: terminal, not yet spent, exactly-k rule
     const bool ctl = rec.ent >= 0 && !fin && !is_spent(rec.ent);
     sep_ok = ctl && done + 1 < st.k;
@@ -763,14 +816,10 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
     Cand fc;
     const int fe = forced_edge(tv, live, q, lane, fc);
     if (fe >= 0) {
-      // forced: no rows, no reduction.  A completion first waits until every
-      // wavefront has passed its last read of the path's live counts (forced
-      // steps have no barrier of their own).
-      if (fc.child < 0) {
-        if constexpr (LDS_LIVE) lds_barrier();
-        else __syncthreads();
-      }
-      take(fe, fc);
+      // forced: no rows, no reduction and no barrier unless a pointer
+      // completes (forced steps have no barrier of their own, so a release
+      // first waits for every wavefront)
+      take(fe, fc, true);
       continue;
     }
     // this step's hidden vector, requested before the edge records and rows:
@@ -780,7 +829,7 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
     load_hidden<NC>(hid + ((int64_t)t * st.B + s) * nq, nq, hq, lane);
     const int slot = nhead % 3;
     if (threadIdx.x == 0) s_key[(nhead + 1) % 3] = 0ull;  // the next head step's slot
-    Cand cand{0, 0, 0, 0, 0};
+    Cand cand{0, 0, 0, 0, 0, 0};
     const unsigned long long best = scan_node<DT, NC, META, LDS_LIVE ? kLiveLds : kLiveVector, PAYLOAD>(
         tr, tv, q, live, emb, nq, hq, wv, W, lane, cand);
     if (lane == 0) {
@@ -791,29 +840,26 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
     const unsigned long long key = s_key[slot];
     const uint32_t klo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)key);
     const uint32_t khi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(key >> 32));
+    nhead += 1;
     if ((klo | khi) == 0u) {
       status = kSeqEmptyMask;
-      if (wv == 0) record(-1);
+      if (wv == 0 && lane == 0) tokens[t] = -1;
     } else if constexpr (PAYLOAD) {
-      const Cand w = s_cand[nhead & 1][klo & 7u];
+      const Cand w = s_cand[(nhead - 1) & 1][klo & 7u];
       const Cand c{__builtin_amdgcn_readfirstlane(w.child), __builtin_amdgcn_readfirstlane(w.tok),
-                   __builtin_amdgcn_readfirstlane(w.b0), __builtin_amdgcn_readfirstlane(w.b1),
-                   __builtin_amdgcn_readfirstlane(w.ent)};
-      take((int)key_wave_edge(((unsigned long long)khi << 32) | klo), c);
+                   __builtin_amdgcn_readfirstlane(w.b0),    __builtin_amdgcn_readfirstlane(w.b1),
+                   __builtin_amdgcn_readfirstlane(w.ent),   __builtin_amdgcn_readfirstlane(w.run)};
+      take((int)key_wave_edge(((unsigned long long)khi << 32) | klo), c, false);
     } else {
       const int e = (int)key_id(((unsigned long long)khi << 32) | klo);  // plain keys carry the edge
       const EdgeRec r = tv.erec[e];
       const Cand c{__builtin_amdgcn_readfirstlane(r.child), __builtin_amdgcn_readfirstlane(r.tok),
-                   __builtin_amdgcn_readfirstlane(r.b0), __builtin_amdgcn_readfirstlane(r.b1),
-                   __builtin_amdgcn_readfirstlane(tv.cent[e])};
-      take(e, c);
+                   __builtin_amdgcn_readfirstlane(r.b0),    __builtin_amdgcn_readfirstlane(r.b1),
+                   __builtin_amdgcn_readfirstlane(tv.cent[e]), __builtin_amdgcn_readfirstlane(tv.run[e])};
+      take(e, c, false);
     }
-    nhead += 1;
   }
   if (wv == 0) {
-    // tokens of the steps since the last flush, then -1 for the steps not run
-    const int tf = __builtin_amdgcn_readfirstlane(t_flushed);
-    if (tf + lane < t) tokens[tf + lane] = my_tok;
     if (reg_lists) {
       if (lane < depth) path[lane] = my_path;
       if (lane < done) entries[lane] = my_ent;
