@@ -127,7 +127,10 @@ tms_status tms_state_create(tms_trie* trie, int32_t B, int32_t k, const void* em
                             int32_t H, void* stream, tms_state** out);
 
 /* Every sequence back to the root: live = live0, spent cleared, no pointers
- * done, status OK, nothing emitted.  Enqueued on stream (kernels, no memset). */
+ * done, status OK, nothing emitted.  The reset is deferred: the next call on
+ * st carries it out on that call's stream before its own work (the resident
+ * device loop of tms_decode_k_pointers does it inside its kernel; every other
+ * call enqueues a reset kernel first, no memset).  stream is not used. */
 tms_status tms_state_reset(tms_state* st, void* stream);
 
 /* Synchronise stream, copy per-sequence status to host_status [B] (may be

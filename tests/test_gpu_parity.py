@@ -593,3 +593,39 @@ def test_loop_forced_spans_from_mid_answer(path):
                 assert np.array_equal(ex[key], ex_full[key]), (cut, mode, key)
     st.close()
     trie.close()
+
+
+def test_deferred_reset_is_applied_by_every_next_call():
+    """tms_state_reset is carried out by the next call on the state: inside
+    the resident loop, or as a reset kernel before any other call."""
+    c, otr, T, hid = config_case("tiny", B=3)
+    trie = tms.Trie(catalog("tiny"), c.vocab, c.sep, c.stop)
+    st = tms.State(trie, 3, c.k, dev_embedding("tiny"))
+    hd = to_dev(hid)
+    fresh = st.export(live=True)
+    assert (fresh["node"] == 0).all() and (fresh["entries"] == -1).all()
+    tok0, len0, ent0 = run_k_pointers(st, hd)
+    for follow in ("export", "step", "loop", "stream", "legal"):
+        run_k_pointers(st, hd)  # leave a finished state behind
+        st.reset()
+        if follow == "export":
+            ex = st.export(live=True)
+            for key in ("node", "depth", "done", "status", "finished", "n_emitted", "entries", "live"):
+                assert np.array_equal(ex[key], fresh[key]), (follow, key)
+        elif follow == "step":
+            tok, _ = run_step_loop(st, hd)
+            assert np.array_equal(tok, tok0), follow
+        elif follow == "legal":
+            n = torch.zeros(3, dtype=torch.int32, device="cuda")
+            lt = torch.zeros((3, trie.info["cap"]), dtype=torch.int32, device="cuda")
+            tms.legal_set(st.h, lt, n)
+            torch.cuda.synchronize()
+            root = trie.csr()
+            assert (n.cpu().numpy() == root["begin"][1] - root["begin"][0]).all(), follow
+        else:
+            tms.state_set_loop(st.h, tms.LOOP_RESIDENT if follow == "loop" else tms.LOOP_STREAM)
+            tok, ln, ent = run_k_pointers(st, hd)
+            assert np.array_equal(tok, tok0) and np.array_equal(ln, len0) and np.array_equal(ent, ent0), follow
+            tms.state_set_loop(st.h, tms.LOOP_RESIDENT)
+    st.close()
+    trie.close()

@@ -35,6 +35,10 @@ struct tms_state {
   bool fast = false;
   int loop_mode = TMS_LOOP_RESIDENT;
   bool dense_mfma = true;  // matrix-core dense head where it applies
+  // A reset asked for and not yet carried out: the next call on the state
+  // applies it on that call's stream (inside the resident loop's kernel when
+  // that is the next call, otherwise as a reset kernel launched first).
+  bool reset_pending = false;
   hipStream_t capture = nullptr;
   hipGraph_t graph = nullptr;
   hipGraphExec_t gexec = nullptr;
@@ -429,14 +433,30 @@ tms_status tms_state_create(tms_trie* trie, int32_t B, int32_t k, const void* em
   return TMS_OK;
 }
 
-tms_status tms_state_reset(tms_state* st, void* stream) {
-  if (!st) return fail(TMS_ERR_INVALID_ARG, "null state");
+// Carries out a pending reset before another call reads or writes the state.
+static tms_status flush_reset(tms_state* st, void* stream) {
+  if (!st->reset_pending) return TMS_OK;
   TMS_HIP(tms::launch_reset(st->trie->dev, st->dev, static_cast<hipStream_t>(stream)), "reset launch");
+  st->reset_pending = false;
   return TMS_OK;
 }
 
+tms_status tms_state_reset(tms_state* st, void* stream) {
+  if (!st) return fail(TMS_ERR_INVALID_ARG, "null state");
+  (void)stream;
+  st->reset_pending = true;
+  return TMS_OK;
+}
+
+#define TMS_FLUSH_RESET(st, stream)                   \
+  do {                                                \
+    const tms_status frs = flush_reset(st, stream);   \
+    if (frs != TMS_OK) return frs;                    \
+  } while (0)
+
 tms_status tms_state_sync_status(tms_state* st, int32_t* host_status, void* stream) {
   if (!st) return fail(TMS_ERR_INVALID_ARG, "null state");
+  TMS_FLUSH_RESET(st, stream);
   TMS_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "stream synchronize");
   TMS_HIP(hipMemcpy(st->host_status.data(), st->dev.status, 4 * st->B, hipMemcpyDeviceToHost), "status copy");
   if (host_status) std::memcpy(host_status, st->host_status.data(), 4 * st->B);
@@ -452,6 +472,7 @@ tms_status tms_state_sync_status(tms_state* st, int32_t* host_status, void* stre
 tms_status tms_state_export(tms_state* st, int32_t* node, int32_t* depth, int32_t* done, int32_t* status,
                             int32_t* finished, int32_t* n_emitted, int32_t* entries, int32_t* live, void* stream) {
   if (!st) return fail(TMS_ERR_INVALID_ARG, "null state");
+  TMS_FLUSH_RESET(st, stream);
   TMS_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "stream synchronize");
   const size_t b4 = 4 * size_t(st->B);
   const tms::DevState& d = st->dev;
@@ -484,6 +505,7 @@ tms_status tms_state_free(tms_state* st) {
 tms_status tms_decode_step_sparse(tms_state* st, const void* hidden, int32_t* tok, float* logit, void* stream) {
   if (!st) return fail(TMS_ERR_INVALID_ARG, "null state");
   if (!hidden || !aligned16(hidden)) return fail(TMS_ERR_INVALID_ARG, "hidden null or not 16-byte aligned");
+  TMS_FLUSH_RESET(st, stream);
   tms::StepIO io = make_io(st, hidden);
   io.out_tok = tok;
   io.out_logit = logit;
@@ -498,6 +520,7 @@ tms_status tms_decode_step_dense_masked(tms_state* st, const void* hidden, int32
   if (!st) return fail(TMS_ERR_INVALID_ARG, "null state");
   if (!hidden || !aligned16(hidden)) return fail(TMS_ERR_INVALID_ARG, "hidden null or not 16-byte aligned");
   if (size_t(st->dev.mask_words) * 4 > 65536) return fail(TMS_ERR_INVALID_ARG, "vocabulary too large for the dense mask");
+  TMS_FLUSH_RESET(st, stream);
   tms::StepIO io = make_io(st, hidden);
   io.out_tok = tok;
   io.out_logit = logit;
@@ -526,6 +549,7 @@ tms_status tms_decode_k_pointers(tms_state* st, const void* hidden_seq, int32_t 
     io.tokens_bt = tokens;
     io.len = len;
     io.entries = entries;
+    io.reset = st->reset_pending ? 1 : 0;  // the kernel resets its sequence first
     // LDS budget per workgroup for the loop's on-chip copy (the part offers
     // 160 KiB; a little is left for the kernel's own shared variables)
     const size_t budget = 160 * 1024 - 2048;
@@ -537,8 +561,10 @@ tms_status tms_decode_k_pointers(tms_state* st, const void* hidden_seq, int32_t 
                                                                            : tms::kLoopVectorGlobal;
     }
     TMS_HIP(tms::launch_loop(st->trie->dev, st->dev, io, st->dtype, mode, s), "loop launch");
+    st->reset_pending = false;
     return TMS_OK;
   }
+  TMS_FLUSH_RESET(st, stream);
   const size_t step_bytes = size_t(st->B) * st->H * elem_size(st->dtype);
   auto enqueue = [&](hipStream_t q) -> hipError_t {
     for (int32_t t = 0; t < T; ++t) {
@@ -582,12 +608,14 @@ tms_status tms_decode_k_pointers(tms_state* st, const void* hidden_seq, int32_t 
 
 tms_status tms_advance_forced(tms_state* st, const int32_t* tok, void* stream) {
   if (!st || !tok) return fail(TMS_ERR_INVALID_ARG, "null argument");
+  TMS_FLUSH_RESET(st, stream);
   TMS_HIP(tms::launch_forced(st->trie->dev, st->dev, tok, static_cast<hipStream_t>(stream)), "forced launch");
   return TMS_OK;
 }
 
 tms_status tms_legal_set(tms_state* st, int32_t* legal_tok, int32_t* n_legal, void* stream) {
   if (!st || !legal_tok || !n_legal) return fail(TMS_ERR_INVALID_ARG, "null argument");
+  TMS_FLUSH_RESET(st, stream);
   TMS_HIP(tms::launch_legal_set(st->trie->dev, st->dev, legal_tok, n_legal, static_cast<hipStream_t>(stream)),
           "legal set launch");
   return TMS_OK;
@@ -619,6 +647,7 @@ tms_status tms_debug_set_live(tms_state* st, int32_t s, int32_t edge, int32_t va
   if (!st) return fail(TMS_ERR_INVALID_ARG, "null state");
   if (s < 0 || s >= st->B || edge < 0 || edge >= st->trie->host.n_edges)
     return fail(TMS_ERR_INVALID_ARG, "sequence or edge out of range");
+  TMS_FLUSH_RESET(st, stream);
   TMS_HIP(tms::launch_set_live(st->trie->dev, st->dev, s, edge, value, static_cast<hipStream_t>(stream)),
           "set live launch");
   return TMS_OK;

@@ -86,6 +86,7 @@ struct LoopIO {
   int32_t* tokens_bt;      // [B][T]
   int32_t* len;            // [B] or null
   int32_t* entries;        // [B][k] or null
+  int32_t reset;           // 1: reset each sequence's state before the first step
 };
 
 // dtype: 0 fp32, 1 bf16.  Every launcher returns hipGetLastError().

@@ -657,13 +657,21 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
   // spent flags of up to 2048 entries live in a register of every wavefront
   // (lane l: word l); beyond that in LDS or device memory
   const bool sreg_ok = SMALL || st.spent_words <= kWave;
+  // io.reset: start from the reset state (full live counts, nothing spent,
+  // no entries, root) instead of the stored one
+  const bool rst = io.reset != 0;
   uint32_t sreg = 0u;
-  if (sreg_ok && lane < st.spent_words) sreg = g_spent[lane];
+  if (sreg_ok && lane < st.spent_words && !rst) sreg = g_spent[lane];
   TrieView tv{tr.erec, tr.cent, tr.run, tr.run_edge, tr.run_tok};
   if constexpr (LDS_LIVE) {
-    copy_to_lds(lds + lay.live, g_live, (int)ls);
+    copy_to_lds(lds + lay.live, rst ? tr.live0 : g_live, (int)ls);
     if (!sreg_ok)
-      for (int i = threadIdx.x; i < st.spent_words; i += kLoopBlock) spent[i] = g_spent[i];
+      for (int i = threadIdx.x; i < st.spent_words; i += kLoopBlock) spent[i] = rst ? 0u : g_spent[i];
+  } else if (rst) {
+    for (int i = threadIdx.x; i < (int)(ls / 4); i += kLoopBlock)
+      reinterpret_cast<int4*>(g_live)[i] = reinterpret_cast<const int4*>(tr.live0)[i];
+    if (!sreg_ok)
+      for (int i = threadIdx.x; i < st.spent_words; i += kLoopBlock) g_spent[i] = 0u;
   }
   if constexpr (TRIE_LDS) {
     copy_to_lds(lds + lay.erec, reinterpret_cast<const int32_t*>(tr.erec), 4 * tr.n_edges);
@@ -674,10 +682,24 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
     tv = TrieView{reinterpret_cast<const EdgeRec*>(lds + lay.erec), lds + lay.cent, lds + lay.run,
                   lds + lay.run_edge, lds + lay.run_tok};
   }
-  int node = st.node[s], depth = st.depth[s], done = st.done[s];
-  int status = st.status[s], fin = st.finished[s], nemit = st.nemit[s];
+  int node = 0, depth = 0, done = 0, status = kSeqOk, fin = 0, nemit = 0;
+  if (!rst) {
+    node = st.node[s];
+    depth = st.depth[s];
+    done = st.done[s];
+    status = st.status[s];
+    fin = st.finished[s];
+    nemit = st.nemit[s];
+  }
   int32_t* path = st.path + (int64_t)s * st.path_stride;
   int32_t* entries = st.entries + (int64_t)s * st.k;
+  if (rst) {
+    for (int j = threadIdx.x; j < st.k; j += kLoopBlock) entries[j] = -1;
+    if (threadIdx.x == 0) {
+      st.key[s] = 0ull;
+      st.arrive[s] = 0u;
+    }
+  }
   int32_t* tokens = io.tokens_bt + (int64_t)s * io.T;
   // Wavefront 0 keeps the current path (lane d: edge at depth d) and the
   // completed entries (lane j: entry j) in registers; they reach device
@@ -694,7 +716,7 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
     s_root = rec_scalar(tr.node_rec, 0);
     s_key[0] = s_key[1] = s_key[2] = 0ull;
   }
-  __syncthreads();
+  __syncthreads();  // also orders the reset's stores before their first reads
   auto is_spent = [&](int ent) -> bool {
     const uint32_t w = sreg_ok ? (uint32_t)__builtin_amdgcn_readlane((int)sreg, ent >> 5)
                                : (uint32_t)__builtin_amdgcn_readfirstlane(spent[ent >> 5]);
