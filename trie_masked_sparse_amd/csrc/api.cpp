@@ -189,8 +189,6 @@ tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_
   const size_t o_child = c.take<int32_t>(h.n_edges);
   const size_t o_live0 = c.take<int32_t>(live_stride);
   const size_t o_rec = c.take<int32_t>(size_t(h.n_nodes) * 4);
-  const size_t o_erec = c.take<int32_t>(size_t(h.n_edges) * 4);
-  const size_t o_cent = c.take<int32_t>(live_stride);
   // forced runs: chains of nodes with a single edge, each stored once
   std::vector<int32_t> run(live_stride, 0), run_edge, run_tok;
   {
@@ -222,9 +220,15 @@ tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_
     if (run_edge.size() >= (size_t(1) << 24)) std::fill(run.begin(), run.end(), 0);  // offsets must fit
   }
   const int32_t n_run = static_cast<int32_t>(run_edge.size());
-  const size_t o_run = c.take<int32_t>(live_stride);
-  const size_t o_run_edge = c.take<int32_t>((n_run + 3) & ~3);
-  const size_t o_run_tok = c.take<int32_t>((n_run + 3) & ~3);
+  // edge records, children's entries and run tables in one block, in the
+  // order (and word offsets) the resident loop keeps them in LDS, so that
+  // one copy loop brings them on chip
+  const size_t w_erec = 0, w_cent = w_erec + 4 * size_t(h.n_edges), w_run = w_cent + live_stride,
+               w_run_edge = w_run + live_stride, w_run_tok = w_run_edge + ((n_run + 3) & ~3),
+               w_image = w_run_tok + ((n_run + 3) & ~3);
+  const size_t o_image = c.take<int32_t>(w_image);
+  const size_t o_erec = o_image + 4 * w_erec, o_cent = o_image + 4 * w_cent, o_run = o_image + 4 * w_run,
+               o_run_edge = o_image + 4 * w_run_edge, o_run_tok = o_image + 4 * w_run_tok;
   run_edge.resize((n_run + 3) & ~3, 0);
   run_tok.resize((n_run + 3) & ~3, 0);
   hipError_t e = hipGetDevice(&t->device);
@@ -287,6 +291,7 @@ tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_
   d.run = reinterpret_cast<const int32_t*>(base + o_run);
   d.run_edge = reinterpret_cast<const int32_t*>(base + o_run_edge);
   d.run_tok = reinterpret_cast<const int32_t*>(base + o_run_tok);
+  d.image_words = static_cast<int32_t>(w_image);
   d.n_run = n_run;
   d.n_nodes = h.n_nodes;
   d.n_edges = h.n_edges;

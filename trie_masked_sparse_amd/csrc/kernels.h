@@ -42,6 +42,9 @@ struct DevTrie {
   const int32_t* run_edge;  // [n_run]
   const int32_t* run_tok;   // [n_run]
   int32_t n_run;            // nodes with a single edge
+  // erec, cent, run, run_edge and run_tok are laid out back to back from
+  // erec (each part a multiple of 16 bytes): image_words int32 words in all
+  int32_t image_words;
   int32_t n_nodes, n_edges, n_entries, cap, max_depth, sep, stop, vocab;
   int32_t live_stride;   // n_edges rounded up to a multiple of 4
 };

@@ -609,12 +609,28 @@ __host__ __device__ inline LoopLds loop_lds_layout(const DevTrie& tr, const DevS
   return o;
 }
 
-// n int32 words from device memory into LDS as 16-byte moves; the device
-// buffers are padded to 256 bytes and the LDS parts to 4 words.
-__device__ __forceinline__ void copy_to_lds(int32_t* dst, const int32_t* src, int n) {
-  const int n4 = (n + 3) >> 2;
-  for (int i = threadIdx.x; i < n4; i += kLoopBlock)
-    reinterpret_cast<int4*>(dst)[i] = reinterpret_cast<const int4*>(src)[i];
+// Two blocks of n0 and n1 int32 words from device memory into LDS as
+// 16-byte moves, every load of a round issued before its stores (the device
+// buffers are padded to 256 bytes and the LDS parts to 4 words).
+__device__ __forceinline__ void copy2_to_lds(int32_t* d0, const int32_t* s0, int n0, int32_t* d1,
+                                             const int32_t* s1, int n1) {
+  const int a = (n0 + 3) >> 2, b = (n1 + 3) >> 2;
+  const int4* S0 = reinterpret_cast<const int4*>(s0);
+  const int4* S1 = reinterpret_cast<const int4*>(s1);
+  int4* D0 = reinterpret_cast<int4*>(d0);
+  int4* D1 = reinterpret_cast<int4*>(d1);
+  for (int base = 0; base < max(a, b); base += 2 * kLoopBlock) {
+    const int i0 = base + (int)threadIdx.x, i1 = i0 + kLoopBlock;
+    int4 v0, v1, v2, v3;
+    if (i0 < a) v0 = S0[i0];
+    if (i1 < a) v1 = S0[i1];
+    if (i0 < b) v2 = S1[i0];
+    if (i1 < b) v3 = S1[i1];
+    if (i0 < a) D0[i0] = v0;
+    if (i1 < a) D0[i1] = v1;
+    if (i0 < b) D1[i0] = v2;
+    if (i1 < b) D1[i1] = v3;
+  }
 }
 
 // Every wavefront of the loop holds the same copy of the sequence's state
@@ -664,7 +680,9 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
   if (sreg_ok && lane < st.spent_words && !rst) sreg = g_spent[lane];
   TrieView tv{tr.erec, tr.cent, tr.run, tr.run_edge, tr.run_tok};
   if constexpr (LDS_LIVE) {
-    copy_to_lds(lds + lay.live, rst ? tr.live0 : g_live, (int)ls);
+    // live counts, and the trie image when it is kept in LDS
+    copy2_to_lds(lds + lay.live, rst ? tr.live0 : g_live, (int)ls, lds + lay.erec,
+                 reinterpret_cast<const int32_t*>(tr.erec), TRIE_LDS ? tr.image_words : 0);
     if (!sreg_ok)
       for (int i = threadIdx.x; i < st.spent_words; i += kLoopBlock) spent[i] = rst ? 0u : g_spent[i];
   } else if (rst) {
@@ -674,11 +692,6 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
       for (int i = threadIdx.x; i < st.spent_words; i += kLoopBlock) g_spent[i] = 0u;
   }
   if constexpr (TRIE_LDS) {
-    copy_to_lds(lds + lay.erec, reinterpret_cast<const int32_t*>(tr.erec), 4 * tr.n_edges);
-    copy_to_lds(lds + lay.cent, tr.cent, (int)ls);
-    copy_to_lds(lds + lay.run, tr.run, (int)ls);
-    copy_to_lds(lds + lay.run_edge, tr.run_edge, tr.n_run);
-    copy_to_lds(lds + lay.run_tok, tr.run_tok, tr.n_run);
     tv = TrieView{reinterpret_cast<const EdgeRec*>(lds + lay.erec), lds + lay.cent, lds + lay.run,
                   lds + lay.run_edge, lds + lay.run_tok};
   }
@@ -742,10 +755,10 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
     if (wv == 0) {
       if (lane == 0) tokens[t] = tok;
       if (reg_lists) {
-        if (lane < depth) live[my_path] -= 1;  // distinct edges
+        if (lane < depth) atomicSub(&live[my_path], 1);  // distinct edges; no value returned
         if (lane == done) my_ent = ent;
       } else {
-        for (int i = lane; i < depth; i += kWave) live[path[i]] -= 1;
+        for (int i = lane; i < depth; i += kWave) atomicSub(&live[path[i]], 1);
         if (lane == 0) entries[done] = ent;
       }
       if (!sreg_ok && lane == 0) spent[ent >> 5] |= 1u << (ent & 31);
