@@ -207,12 +207,24 @@ tms_status tms_debug_set_live(tms_state* st, int32_t s, int32_t edge, int32_t va
 tms_status tms_state_set_split(tms_state* st, int32_t split);
 
 /* How tms_decode_k_pointers runs its T steps (all bit-identical):
- * RESIDENT: one launch, one workgroup per sequence loops over the steps;
+ * RESIDENT_SOLO: one launch, one workgroup per sequence loops over the steps;
+ * RESIDENT_GROUPED: one phase per pointer; each phase first takes the root
+ *   step of every sequence standing at the root in one grouped launch (each
+ *   root row read once for all of them, "The batched engine"), then runs the
+ *   resident loop until each sequence is back at the root (the last phase
+ *   runs to the end): 2k launches from a reset state, 2(k+1) otherwise;
+ * RESIDENT: GROUPED when B >= 8 and the root has at least 64 edges, else SOLO;
  * GRAPH: a hipGraph of T step kernels (as tms_decode_step_sparse), built on
  *   the first call for a given set of pointers and replayed afterwards;
  * STREAM: the same T step kernels launched directly on the stream.
- * Also read from the TMS_LOOP environment variable (0, 1, 2) at create. */
-typedef enum { TMS_LOOP_RESIDENT = 0, TMS_LOOP_GRAPH = 1, TMS_LOOP_STREAM = 2 } tms_loop_mode;
+ * Also read from the TMS_LOOP environment variable (0..4) at create. */
+typedef enum {
+  TMS_LOOP_RESIDENT = 0,
+  TMS_LOOP_GRAPH = 1,
+  TMS_LOOP_STREAM = 2,
+  TMS_LOOP_RESIDENT_SOLO = 3,
+  TMS_LOOP_RESIDENT_GROUPED = 4
+} tms_loop_mode;
 tms_status tms_state_set_loop(tms_state* st, int32_t mode);
 
 /* Workgroups per sequence used by the fused step, and its grid size. */

@@ -629,3 +629,73 @@ def test_deferred_reset_is_applied_by_every_next_call():
             tms.state_set_loop(st.h, tms.LOOP_RESIDENT)
     st.close()
     trie.close()
+
+
+# ---------------------------------------------------------------------------
+# Root steps grouped across sequences (one phase per pointer)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cid,B", [("tiny", 5), ("structured", 64), ("unstructured", 64)])
+def test_grouped_root_matches_solo_and_oracle(cid, B):
+    """The grouped root head reads each root row once for all sequences at the
+    root; with the same per-row arithmetic the answers and the final state are
+    bit-identical to the one-workgroup-per-sequence loop, from a reset state
+    (k phases) and from mid-answer states (k + 1 phases)."""
+    c, otr, T, hid = config_case(cid, B=B)
+    trie = tms.Trie(catalog(cid), c.vocab, c.sep, c.stop)
+    st = tms.State(trie, B, c.k, dev_embedding(cid))
+    hd = to_dev(hid)
+    keys = ("node", "depth", "done", "status", "finished", "n_emitted", "entries", "live")
+    out = {}
+    for mode in (tms.LOOP_RESIDENT_SOLO, tms.LOOP_RESIDENT_GROUPED, tms.LOOP_RESIDENT_GROUPED):
+        tms.state_set_loop(st.h, mode)
+        st.reset()
+        r = run_k_pointers(st, hd)
+        ex = st.export(live=True)
+        if mode in out:  # a second grouped call: nothing left behind by the first
+            assert all(np.array_equal(a, b) for a, b in zip(r, out[mode][0]))
+        out[mode] = (r, ex)
+    (ts, ls, es), exs = out[tms.LOOP_RESIDENT_SOLO]
+    (tg, lg, eg), exg = out[tms.LOOP_RESIDENT_GROUPED]
+    assert np.array_equal(tg, ts) and np.array_equal(lg, ls) and np.array_equal(eg, es), cid
+    for key in keys:
+        assert np.array_equal(exg[key], exs[key]), (cid, key)
+    ref = oracle.decode(otr, c.k, embedding(cid), hid)
+    compare(tg, ref, c.hidden, None, lg, eg, where=cid + "/grouped")
+    # from states left by host-driven steps: some sequences mid-pointer
+    for cut in (1, 3, T // 2):
+        rest = torch.zeros_like(hd)
+        rest[: T - cut] = hd[cut:]
+        res = {}
+        for mode in (tms.LOOP_RESIDENT_SOLO, tms.LOOP_RESIDENT_GROUPED):
+            tms.state_set_loop(st.h, mode)
+            st.reset()
+            a, _ = run_step_loop(st, hd[:cut])
+            b_, ln, en = run_k_pointers(st, rest)
+            res[mode] = (np.concatenate([a, b_[:, : T - cut]], axis=1), ln, en, st.export(live=True))
+        s_, g_ = res[tms.LOOP_RESIDENT_SOLO], res[tms.LOOP_RESIDENT_GROUPED]
+        assert np.array_equal(g_[0], s_[0]) and np.array_equal(g_[0], ts), (cid, cut)
+        assert np.array_equal(g_[1], s_[1]) and np.array_equal(g_[2], s_[2]), (cid, cut)
+        for key in keys:
+            assert np.array_equal(g_[3][key], s_[3][key]), (cid, cut, key)
+    st.close()
+    trie.close()
+
+
+def test_grouped_root_empty_mask_is_per_sequence():
+    c, otr, T, hid = config_case("tiny", B=3)
+    trie = tms.Trie(catalog("tiny"), c.vocab, c.sep, c.stop)
+    st = tms.State(trie, 3, c.k, dev_embedding("tiny"))
+    tms.state_set_loop(st.h, tms.LOOP_RESIDENT_GROUPED)
+    csr = trie.csr()
+    st.reset()
+    st.export()  # carries out the reset, so the live counts below stick
+    for e in range(csr["begin"][0], csr["begin"][1]):
+        tms.debug_set_live(st.h, 1, e, 0)
+    tok, ln, ent = run_k_pointers(st, to_dev(hid))
+    assert list(st.status()) == [0, tms.ERR_EMPTY_MASK, 0]
+    assert (tok[1] == -1).all()
+    ref = oracle.decode(otr, c.k, embedding("tiny"), hid[:, [0, 2], :])
+    compare(tok[[0, 2]], ref, c.hidden, None, ln[[0, 2]], ent[[0, 2]], where="grouped isolated")
+    st.close()
+    trie.close()

@@ -24,7 +24,7 @@ OK, ERR_INVALID_ARG, ERR_CATALOG, ERR_FANOUT, ERR_K, ERR_EMPTY_MASK, ERR_NOT_WAL
     ERR_BUSY, ERR_OOM, ERR_HIP = range(11)
 F32, BF16 = 0, 1
 PATH_AUTO, PATH_FAST, PATH_GLOBAL = 0, 1, 2
-LOOP_RESIDENT, LOOP_GRAPH, LOOP_STREAM = 0, 1, 2
+LOOP_RESIDENT, LOOP_GRAPH, LOOP_STREAM, LOOP_RESIDENT_SOLO, LOOP_RESIDENT_GROUPED = 0, 1, 2, 3, 4
 
 # every symbol declared in include/tms.h
 EXPORTS = (

@@ -380,6 +380,10 @@ tms_status tms_state_create(tms_trie* trie, int32_t B, int32_t k, const void* em
   const size_t o_entries = c.take<int32_t>(size_t(B) * k);
   const size_t o_key = c.take<unsigned long long>(B);
   const size_t o_arrive = c.take<uint32_t>(B);
+  const size_t o_tstep = c.take<int32_t>(B);
+  // grouped root head: one key per (row tile, sequence); at most one tile per 4 rows
+  const int32_t root_tiles = (trie->host.begin[1] - trie->host.begin[0] + 3) / 4;
+  const size_t o_rkey = c.take<unsigned long long>(size_t(root_tiles) * B);
   const size_t o_live = c.take<int32_t>(size_t(B) * live_stride);
   const size_t o_spent = c.take<uint32_t>(size_t(B) * spent_words);
   const size_t o_mask = c.take<uint32_t>(size_t(B) * mask_words);
@@ -406,6 +410,9 @@ tms_status tms_state_create(tms_trie* trie, int32_t B, int32_t k, const void* em
   d.entries = reinterpret_cast<int32_t*>(base + o_entries);
   d.key = reinterpret_cast<unsigned long long*>(base + o_key);
   d.arrive = reinterpret_cast<uint32_t*>(base + o_arrive);
+  d.tstep = reinterpret_cast<int32_t*>(base + o_tstep);
+  d.rkey = reinterpret_cast<unsigned long long*>(base + o_rkey);
+  d.root_tiles = root_tiles;
   d.live = reinterpret_cast<int32_t*>(base + o_live);
   d.spent = reinterpret_cast<uint32_t*>(base + o_spent);
   d.mask = reinterpret_cast<uint32_t*>(base + o_mask);
@@ -418,7 +425,7 @@ tms_status tms_state_create(tms_trie* trie, int32_t B, int32_t k, const void* em
   if (const char* env = std::getenv("TMS_DENSE_VECTOR")) st->dense_mfma = std::atoi(env) == 0;
   if (const char* env = std::getenv("TMS_LOOP")) {
     const int v = std::atoi(env);
-    if (v >= TMS_LOOP_RESIDENT && v <= TMS_LOOP_STREAM) st->loop_mode = v;
+    if (v >= TMS_LOOP_RESIDENT && v <= TMS_LOOP_RESIDENT_GROUPED) st->loop_mode = v;
   }
   st->host_status.assign(B, 0);
   e = hipStreamCreateWithFlags(&st->capture, hipStreamNonBlocking);
@@ -544,7 +551,9 @@ tms_status tms_decode_k_pointers(tms_state* st, const void* hidden_seq, int32_t 
   if (T < need)
     return fail(TMS_ERR_INVALID_ARG, "T = " + std::to_string(T) + " < k*(max_depth+1) = " + std::to_string(need));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (st->loop_mode == TMS_LOOP_RESIDENT) {
+  const bool resident = st->loop_mode == TMS_LOOP_RESIDENT || st->loop_mode == TMS_LOOP_RESIDENT_SOLO ||
+                        st->loop_mode == TMS_LOOP_RESIDENT_GROUPED;
+  if (resident) {
     tms::LoopIO io{};
     io.emb = st->emb;
     io.hidden_seq = hidden_seq;
@@ -565,7 +574,27 @@ tms_status tms_decode_k_pointers(tms_state* st, const void* hidden_seq, int32_t 
       mode = tms::loop_lds_bytes(st->trie->dev, st->dev, false) <= budget ? tms::kLoopVectorLds
                                                                            : tms::kLoopVectorGlobal;
     }
-    TMS_HIP(tms::launch_loop(st->trie->dev, st->dev, io, st->dtype, mode, s), "loop launch");
+    // Root steps grouped across sequences: one phase per pointer (every
+    // pointer starts at the root), each a grouped root head then the loop up
+    // to the next return to the root; the last phase runs to the end.  Worth
+    // it where the root is wide and shared by many sequences.
+    const tms::HostTrie& h = st->trie->host;
+    const int root_edges = h.begin[1] - h.begin[0];
+    const bool group = st->loop_mode == TMS_LOOP_RESIDENT_GROUPED ||
+                       (st->loop_mode == TMS_LOOP_RESIDENT && st->B >= 8 && root_edges >= 64);
+    if (!group) {
+      TMS_HIP(tms::launch_loop(st->trie->dev, st->dev, io, st->dtype, mode, s), "loop launch");
+    } else {
+      const bool fresh = st->reset_pending;  // every sequence starts at the root
+      const int phases = fresh ? st->k : st->k + 1;
+      for (int p = 0; p < phases; ++p) {
+        io.reset = p == 0 && fresh ? 1 : 0;
+        io.flags = (p > 0 ? tms::kLoopLater : 0) | (p + 1 < phases ? tms::kLoopExitAtRoot : 0) | tms::kLoopRootKey;
+        io.root_tiles = tms::root_head_tiles(st->dtype, st->H, root_edges);
+        TMS_HIP(tms::launch_root_head(st->trie->dev, st->dev, io, st->dtype, root_edges, s), "root head launch");
+        TMS_HIP(tms::launch_loop(st->trie->dev, st->dev, io, st->dtype, mode, s), "loop launch");
+      }
+    }
     st->reset_pending = false;
     return TMS_OK;
   }
@@ -666,7 +695,8 @@ tms_status tms_state_set_split(tms_state* st, int32_t split) {
 }
 
 tms_status tms_state_set_loop(tms_state* st, int32_t mode) {
-  if (!st || mode < TMS_LOOP_RESIDENT || mode > TMS_LOOP_STREAM) return fail(TMS_ERR_INVALID_ARG, "unknown loop mode");
+  if (!st || mode < TMS_LOOP_RESIDENT || mode > TMS_LOOP_RESIDENT_GROUPED)
+    return fail(TMS_ERR_INVALID_ARG, "unknown loop mode");
   st->loop_mode = mode;
   destroy_graph(st);
   return TMS_OK;

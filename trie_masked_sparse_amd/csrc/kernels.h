@@ -65,6 +65,9 @@ struct DevState {
   int32_t* entries;      // [B][k] completed catalog indices, -1 unused
   unsigned long long* key;  // [B] packed (logit, id) argmax slot, 0 = empty
   uint32_t* arrive;      // [B] workgroups of the current step that finished
+  int32_t* tstep;        // [B] steps taken so far in the current phased decode call
+  unsigned long long* rkey;  // [root_tiles][B] best key of each grouped-root row tile per sequence
+  int32_t root_tiles;        // row tiles of the root (4 wavefronts x 1..4 rows each), upper bound
   int32_t* live;         // [B][live_stride]
   uint32_t* spent;       // [B][spent_words] one bit per catalog entry
   uint32_t* mask;        // [B][mask_words] dense-path vocabulary bitmask
@@ -90,7 +93,16 @@ struct LoopIO {
   int32_t* len;            // [B] or null
   int32_t* entries;        // [B][k] or null
   int32_t reset;           // 1: reset each sequence's state before the first step
+  int32_t flags;           // kLoop* bits (phased runs of the resident loop)
+  int32_t root_tiles;      // row tiles written by the last grouped root head (kLoopRootKey)
 };
+
+// Phased resident loop (one phase per pointer, the root steps grouped across
+// sequences by launch_root_head): kLoopLater: not the first phase of the call
+// (step index from DevState::tstep); kLoopExitAtRoot: a sequence that comes
+// back to the root stops there (every phase but the last); kLoopRootKey: the
+// root step of every sequence standing at the root was computed into key[s].
+enum { kLoopLater = 1, kLoopExitAtRoot = 2, kLoopRootKey = 4 };
 
 // dtype: 0 fp32, 1 bf16.  Every launcher returns hipGetLastError().
 hipError_t launch_reset(const DevTrie& tr, const DevState& st, hipStream_t s);
@@ -101,6 +113,13 @@ hipError_t launch_step_sparse(const DevTrie& tr, const DevState& st, const StepI
 // memory (fast path, too big for LDS); vector edge reads with live counts in
 // LDS, or in device memory (global path).
 enum { kLoopTrieLds = 0, kLoopFastGlobal = 1, kLoopVectorLds = 2, kLoopVectorGlobal = 3 };
+// The root step of every sequence at the root (or of all, with io.reset), for
+// the step each is at: per row tile and sequence the best key into st.rkey
+// (root_edges = edges of the root).
+hipError_t launch_root_head(const DevTrie& tr, const DevState& st, const LoopIO& io, int dtype, int root_edges,
+                            hipStream_t s);
+// Row tiles the grouped root head uses for this hidden size (io.root_tiles).
+int root_head_tiles(int dtype, int H, int root_edges);
 hipError_t launch_loop(const DevTrie& tr, const DevState& st, const LoopIO& io, int dtype, int mode,
                        hipStream_t s);
 // LDS bytes of the resident loop's per-sequence copy (live counts, spent bits,

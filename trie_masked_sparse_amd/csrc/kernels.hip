@@ -676,6 +676,10 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
   // io.reset: start from the reset state (full live counts, nothing spent,
   // no entries, root) instead of the stored one
   const bool rst = io.reset != 0;
+  const bool later = (io.flags & kLoopLater) != 0;
+  const bool exit_root = (io.flags & kLoopExitAtRoot) != 0;
+  const bool root_key = (io.flags & kLoopRootKey) != 0;
+  __shared__ unsigned long long s_pre_key;
   uint32_t sreg = 0u;
   if (sreg_ok && lane < st.spent_words && !rst) sreg = g_spent[lane];
   TrieView tv{tr.erec, tr.cent, tr.run, tr.run_edge, tr.run_tok};
@@ -714,6 +718,7 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
     }
   }
   int32_t* tokens = io.tokens_bt + (int64_t)s * io.T;
+  int t = later ? st.tstep[s] : 0;
   // Wavefront 0 keeps the current path (lane d: edge at depth d) and the
   // completed entries (lane j: entry j) in registers; they reach device
   // memory at the end.  Tokens are stored as they are emitted (stores are not
@@ -729,6 +734,18 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
     s_root = rec_scalar(tr.node_rec, 0);
     s_key[0] = s_key[1] = s_key[2] = 0ull;
   }
+  if (root_key && wv == 0) {
+    // this sequence's root step from the grouped head: max over its row tiles
+    unsigned long long m = 0ull;
+    for (int i = lane; i < io.root_tiles; i += kWave) m = max(m, st.rkey[(int64_t)i * st.B + s]);
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)m, d);
+      const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(m >> 32), d);
+      m = max(m, ((unsigned long long)hi << 32) | lo);
+    }
+    if (lane == 0) s_pre_key = m;
+  }
   __syncthreads();  // also orders the reset's stores before their first reads
   auto is_spent = [&](int ent) -> bool {
     const uint32_t w = sreg_ok ? (uint32_t)__builtin_amdgcn_readlane((int)sreg, ent >> 5)
@@ -739,7 +756,7 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
   bool sep_ok = ctl0 && done + 1 < st.k, stop_ok = ctl0 && done + 1 >= st.k;
   const uint4* hid = (const uint4*)io.hidden_seq;
   const uint4* emb = (const uint4*)io.emb;
-  int t = 0;
+  const int t_enter = t;
   int nhead = 0;  // steps so far that read the head
   // Step t emits control edge `kind` (token tok) at the current terminal:
   // wavefront 0 releases the path's live counts, records the entry and
@@ -839,7 +856,30 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
     sep_ok = ctl && done + 1 < st.k;
     stop_ok = ctl && done + 1 >= st.k;
   };
+  if (root_key) {
+    const unsigned long long pre_key = s_pre_key;
+    if (status == kSeqOk && !fin && node == 0 && depth == 0 && t < io.T) {
+      // the root step from the grouped head (same arithmetic and tie rule)
+      const uint32_t klo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)pre_key);
+      const uint32_t khi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(pre_key >> 32));
+      if ((klo | khi) == 0u) {
+        status = kSeqEmptyMask;
+        if (wv == 0 && lane == 0) tokens[t] = -1;
+      } else {
+        const int e = (int)key_id(((unsigned long long)khi << 32) | klo);
+        const EdgeRec r = tv.erec[e];
+        const Cand c{__builtin_amdgcn_readfirstlane(r.child), __builtin_amdgcn_readfirstlane(r.tok),
+                     __builtin_amdgcn_readfirstlane(r.b0),    __builtin_amdgcn_readfirstlane(r.b1),
+                     __builtin_amdgcn_readfirstlane(tv.cent[e]), __builtin_amdgcn_readfirstlane(tv.run[e])};
+        take(e, c, false);
+      }
+      t += 1;
+    }
+  }
   for (; t < io.T && status == kSeqOk && !fin; ++t) {
+    // a phase before the last ends where the sequence is back at the root:
+    // the next phase's grouped head takes that step
+    if (exit_root && node == 0 && depth == 0 && t > t_enter) break;
     Seq q;
     q.node = node;
     q.depth = depth;
@@ -901,9 +941,12 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
     }
     if (sreg_ok && lane < st.spent_words) g_spent[lane] = sreg;
   }
-  for (int i = t + threadIdx.x; i < io.T; i += kLoopBlock) tokens[i] = -1;
-  if (status == kSeqOk && !fin) status = kSeqNotDone;
+  if (!exit_root) {
+    for (int i = t + threadIdx.x; i < io.T; i += kLoopBlock) tokens[i] = -1;
+    if (status == kSeqOk && !fin) status = kSeqNotDone;
+  }
   if (threadIdx.x == 0) {
+    st.tstep[s] = t;
     st.node[s] = node;
     st.depth[s] = depth;
     st.done[s] = done;
@@ -923,6 +966,128 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
     if (!sreg_ok)
       for (int i = threadIdx.x; i < st.spent_words; i += kLoopBlock) g_spent[i] = spent[i];
   }
+}
+
+// ---------------------------------------------------------------------------
+// Node-grouped head at the root (sections "The batched engine" and "The sparse
+// output layer": the rows a batch needs are the union of the legal sets, so a
+// row shared by sequences at the same node is read once for all of them).
+// Every pointer starts at the root, the widest node of a catalog with many
+// first tokens.  Before each pointer phase of the resident loop this kernel
+// takes the root step of every sequence standing there ("members"), each with
+// the hidden vector of its own current step: workgroup (x, y) loads 4*U root
+// rows once and dots them with the vectors of members [y*mt, y*mt+mt) staged in
+// LDS, in the fixed per-row order of the other kernels (bit-identical logits),
+// and each member's legal edges go into key[s] with an atomic max.
+// ---------------------------------------------------------------------------
+template <int DT, int NC>
+__global__ __launch_bounds__(kBlock) void root_head_kernel(DevTrie tr, DevState st, LoopIO io, int mt) {
+  constexpr int EL = DT == 0 ? 4 : 8;
+  constexpr int U = rows_per_pass(NC);
+  constexpr int MPW = 4;  // members staged per wavefront per round
+  // [mt][nq] members' hidden vectors, then int64 hidden offsets[B], int members[B]
+  extern __shared__ uint4 sh[];
+  __shared__ int s_cnt[kWavesPerBlock];
+  __shared__ unsigned long long s_best[16];
+  const int lane = __lane_id();
+  const int wv = wave_id();
+  const int nq = io.H / EL;
+  int64_t* s_off = reinterpret_cast<int64_t*>(sh + (size_t)mt * nq);
+  int* s_mem = reinterpret_cast<int*>(s_off + st.B);
+  const bool rst = io.reset != 0;
+  const bool later = (io.flags & kLoopLater) != 0;
+  if (threadIdx.x < 16) s_best[threadIdx.x] = 0ull;
+  // this wavefront's U root edges (the root is not a terminal: content edges
+  // only); their rows are requested first, so that the member bookkeeping
+  // below overlaps the gathers
+  const int r1 = tr.begin[1];
+  const int e0 = tr.begin[0] + ((int)blockIdx.x * kWavesPerBlock + wv) * U;
+  int rows[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) rows[u] = e0 + u < r1 ? tr.tok[e0 + u] : -1;
+  uint4 raw[U][NC];
+  issue_rows<NC, U>((const uint4*)io.emb, nq, rows, raw, lane);
+  // members in ascending sequence order (every workgroup builds the same list),
+  // with the offset of the hidden vector of each one's current step
+  int n_mem = 0;
+  for (int s0 = 0; s0 < st.B; s0 += kBlock) {
+    const int s = s0 + (int)threadIdx.x;
+    bool ok = false;
+    int t = 0;
+    if (s < st.B) {
+      t = later ? st.tstep[s] : 0;
+      const int stat = st.status[s], fin = st.finished[s], nd = st.node[s], dp = st.depth[s];
+      ok = t < io.T && (rst || (stat == kSeqOk && fin == 0 && nd == 0 && dp == 0));
+    }
+    const unsigned long long m = __ballot(ok);
+    if (lane == 0) s_cnt[wv] = __popcll(m);
+    __syncthreads();
+    int off = n_mem;
+    for (int w = 0; w < wv; ++w) off += s_cnt[w];
+    if (ok) {
+      const int idx = off + __popcll(m & ((1ull << lane) - 1ull));
+      s_mem[idx] = s;
+      s_off[idx] = ((int64_t)t * st.B + s) * nq;
+    }
+    for (int w = 0; w < kWavesPerBlock; ++w) n_mem += s_cnt[w];
+    __syncthreads();
+  }
+  const int m0 = (int)blockIdx.y * mt;
+  const int cnt = min(mt, n_mem - m0);
+  if (cnt <= 0) return;  // the same for the whole workgroup
+  // stage the members' vectors: every load of a round before its stores
+  const uint4* hid = (const uint4*)io.hidden_seq;
+  for (int jb = wv; jb < cnt; jb += kWavesPerBlock * MPW) {
+    uint4 v[MPW][NC];
+#pragma unroll
+    for (int u = 0; u < MPW; ++u) {
+      const int j = jb + u * kWavesPerBlock;
+      if (j < cnt) load_hidden<NC>(hid + s_off[m0 + j], nq, v[u], lane);
+    }
+#pragma unroll
+    for (int u = 0; u < MPW; ++u) {
+      const int j = jb + u * kWavesPerBlock;
+      if (j >= cnt) continue;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        if (c * kWave + lane < nq) sh[j * nq + c * kWave + lane] = v[u][c];
+    }
+  }
+  // lane j checks member j's live counts of the wavefront's edges
+  const int32_t* my_live = nullptr;
+  if (lane < cnt) my_live = rst ? tr.live0 : st.live + (int64_t)s_mem[m0 + lane] * tr.live_stride;
+  unsigned long long legal[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) legal[u] = __ballot(rows[u] >= 0 && lane < cnt && my_live[e0 + u] > 0);
+  __syncthreads();  // staged vectors visible
+  // two members per pass: independent accumulation chains side by side
+  for (int j = 0; j < cnt; j += 2) {
+    const int j1 = min(j + 1, cnt - 1);
+    uint4 hq0[NC], hq1[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int i = c * kWave + lane;
+      const int ii = i < nq ? i : 0;
+      hq0[c] = c * kWave < nq ? sh[j * nq + ii] : make_uint4(0, 0, 0, 0);
+      hq1[c] = c * kWave < nq ? sh[j1 * nq + ii] : make_uint4(0, 0, 0, 0);
+    }
+    float l0[U], l1[U];
+    finish_rows<DT, NC, U>(nq, rows, raw, hq0, l0, lane);
+    finish_rows<DT, NC, U>(nq, rows, raw, hq1, l1, lane);
+    unsigned long long b0 = 0ull, b1 = 0ull;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if ((legal[u] >> j) & 1ull) b0 = max(b0, pack_key(l0[u], (uint32_t)(e0 + u)));
+      if ((legal[u] >> j1) & 1ull) b1 = max(b1, pack_key(l1[u], (uint32_t)(e0 + u)));
+    }
+    if (lane == 0) {
+      if (b0) __hip_atomic_fetch_max(&s_best[j], b0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (b1 && j1 != j) __hip_atomic_fetch_max(&s_best[j1], b1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  }
+  __syncthreads();
+  // this tile's best per member (0: none legal); the loop takes the max over tiles
+  if (threadIdx.x < cnt) st.rkey[(int64_t)blockIdx.x * st.B + s_mem[m0 + threadIdx.x]] = s_best[threadIdx.x];
 }
 
 // ---------------------------------------------------------------------------
@@ -1360,6 +1525,42 @@ hipError_t launch_step_sparse(const DevTrie& tr, const DevState& st, const StepI
 hipError_t launch_loop(const DevTrie& tr, const DevState& st, const LoopIO& io, int dtype, int mode,
                        hipStream_t s) {
   return dispatch<LoopLaunch>(dtype, chunks_for(dtype, io.H), tr, st, io, mode, s);
+}
+
+constexpr int kRootMembers = 4;  // members per workgroup of the grouped root head
+
+int root_head_tiles(int dtype, int H, int root_edges) {
+  const int rows_per_wg = kWavesPerBlock * rows_per_pass(chunks_for(dtype, H));
+  return (root_edges + rows_per_wg - 1) / rows_per_wg;
+}
+
+template <int DT, int NC>
+struct RootLaunch {
+  static hipError_t run(const DevTrie& tr, const DevState& st, const LoopIO& io, int root_edges, hipStream_t s) {
+    constexpr int EL = DT == 0 ? 4 : 8;
+    const int nq = io.H / EL;
+    // members per workgroup: as many hidden vectors as fit 64 KiB of LDS, 1..16
+    const int mt = max(1, min(kRootMembers, 65536 / (nq * 16)));
+    const size_t lds = sizeof(uint4) * (size_t)mt * nq + (sizeof(int64_t) + sizeof(int)) * (size_t)st.B;
+    auto* k = &root_head_kernel<DT, NC>;
+    static size_t allowed = 65536;
+    if (lds > allowed) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      allowed = lds;
+    }
+    const int rows_per_wg = kWavesPerBlock * rows_per_pass(NC);
+    const dim3 grid((unsigned)((root_edges + rows_per_wg - 1) / rows_per_wg), (unsigned)((st.B + mt - 1) / mt));
+    hipLaunchKernelGGL(k, grid, dim3(kBlock), lds, s, tr, st, io, mt);
+    return hipGetLastError();
+  }
+};
+
+hipError_t launch_root_head(const DevTrie& tr, const DevState& st, const LoopIO& io, int dtype, int root_edges,
+                            hipStream_t s) {
+  if (root_edges <= 0) return hipSuccess;
+  return dispatch<RootLaunch>(dtype, chunks_for(dtype, io.H), tr, st, io, root_edges, s);
 }
 
 size_t loop_lds_bytes(const DevTrie& tr, const DevState& st, bool trie) {
