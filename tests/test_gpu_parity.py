@@ -638,14 +638,20 @@ def test_deferred_reset_is_applied_by_every_next_call():
 @pytest.mark.parametrize("cid,B", [("tiny", 5), ("structured", 64), ("unstructured", 64)])
 def test_grouped_root_matches_solo_and_oracle(cid, B):
     """The grouped root head reads each root row once for all sequences at the
-    root; with the same per-row arithmetic the answers and the final state are
-    bit-identical to the one-workgroup-per-sequence loop, from a reset state
-    (k phases) and from mid-answer states (k + 1 phases)."""
+    root.  fp32 tables (vector units, the per-row order of the other kernels)
+    give answers and final states bit-identical to the one-workgroup-per-
+    sequence loop; bf16 tables with H = 2048 go through the matrix cores, so
+    tokens are held to the oracle with the any-order tie bound (depth H + 1)
+    and must equal the solo loop's wherever neither run has a tie-explained
+    flip.  From a reset state (k phases) and from mid-answer states (k + 1)."""
     c, otr, T, hid = config_case(cid, B=B)
+    mfma = c.dtype == "bf16" and c.hidden in (2048, 4096)
+    depth = c.hidden + 1 if mfma else None
     trie = tms.Trie(catalog(cid), c.vocab, c.sep, c.stop)
     st = tms.State(trie, B, c.k, dev_embedding(cid))
     hd = to_dev(hid)
     keys = ("node", "depth", "done", "status", "finished", "n_emitted", "entries", "live")
+    ref = oracle.decode(otr, c.k, embedding(cid), hid)
     out = {}
     for mode in (tms.LOOP_RESIDENT_SOLO, tms.LOOP_RESIDENT_GROUPED, tms.LOOP_RESIDENT_GROUPED):
         tms.state_set_loop(st.h, mode)
@@ -657,11 +663,12 @@ def test_grouped_root_matches_solo_and_oracle(cid, B):
         out[mode] = (r, ex)
     (ts, ls, es), exs = out[tms.LOOP_RESIDENT_SOLO]
     (tg, lg, eg), exg = out[tms.LOOP_RESIDENT_GROUPED]
-    assert np.array_equal(tg, ts) and np.array_equal(lg, ls) and np.array_equal(eg, es), cid
-    for key in keys:
-        assert np.array_equal(exg[key], exs[key]), (cid, key)
-    ref = oracle.decode(otr, c.k, embedding(cid), hid)
-    compare(tg, ref, c.hidden, None, lg, eg, where=cid + "/grouped")
+    fs = compare(ts, ref, c.hidden, None, ls, es, where=cid + "/solo")
+    fg = compare(tg, ref, c.hidden, None, lg, eg, where=cid + "/grouped", depth=depth)
+    if not fs and not fg:
+        assert np.array_equal(tg, ts) and np.array_equal(lg, ls) and np.array_equal(eg, es), cid
+        for key in keys:
+            assert np.array_equal(exg[key], exs[key]), (cid, key)
     # from states left by host-driven steps: some sequences mid-pointer
     for cut in (1, 3, T // 2):
         rest = torch.zeros_like(hd)
@@ -672,12 +679,16 @@ def test_grouped_root_matches_solo_and_oracle(cid, B):
             st.reset()
             a, _ = run_step_loop(st, hd[:cut])
             b_, ln, en = run_k_pointers(st, rest)
-            res[mode] = (np.concatenate([a, b_[:, : T - cut]], axis=1), ln, en, st.export(live=True))
+            whole = np.concatenate([a, b_[:, : T - cut]], axis=1)
+            flips = compare(whole, ref, c.hidden, None, ln, en, where=f"{cid}/cut{cut}/{mode}",
+                            depth=depth if mode == tms.LOOP_RESIDENT_GROUPED else None)
+            res[mode] = (whole, ln, en, st.export(live=True), flips)
         s_, g_ = res[tms.LOOP_RESIDENT_SOLO], res[tms.LOOP_RESIDENT_GROUPED]
-        assert np.array_equal(g_[0], s_[0]) and np.array_equal(g_[0], ts), (cid, cut)
-        assert np.array_equal(g_[1], s_[1]) and np.array_equal(g_[2], s_[2]), (cid, cut)
-        for key in keys:
-            assert np.array_equal(g_[3][key], s_[3][key]), (cid, cut, key)
+        assert (b_[:, T - cut:] == -1).all()
+        if not s_[4] and not g_[4]:
+            assert np.array_equal(g_[0], s_[0]) and np.array_equal(g_[1], s_[1]) and np.array_equal(g_[2], s_[2])
+            for key in keys:
+                assert np.array_equal(g_[3][key], s_[3][key]), (cid, cut, key)
     st.close()
     trie.close()
 

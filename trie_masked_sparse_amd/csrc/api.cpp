@@ -585,6 +585,9 @@ tms_status tms_decode_k_pointers(tms_state* st, const void* hidden_seq, int32_t 
     if (!group) {
       TMS_HIP(tms::launch_loop(st->trie->dev, st->dev, io, st->dtype, mode, s), "loop launch");
     } else {
+      // after a grouped root step a phase reads few live counts: keep them
+      // in device memory rather than copying them through LDS every phase
+      if (mode == tms::kLoopVectorLds) mode = tms::kLoopVectorGlobal;
       const bool fresh = st->reset_pending;  // every sequence starts at the root
       const int phases = fresh ? st->k : st->k + 1;
       for (int p = 0; p < phases; ++p) {

@@ -1021,7 +1021,7 @@ __global__ __launch_bounds__(kBlock) void root_head_kernel(DevTrie tr, DevState 
     }
     const unsigned long long m = __ballot(ok);
     if (lane == 0) s_cnt[wv] = __popcll(m);
-    __syncthreads();
+    lds_barrier();
     int off = n_mem;
     for (int w = 0; w < wv; ++w) off += s_cnt[w];
     if (ok) {
@@ -1030,7 +1030,7 @@ __global__ __launch_bounds__(kBlock) void root_head_kernel(DevTrie tr, DevState 
       s_off[idx] = ((int64_t)t * st.B + s) * nq;
     }
     for (int w = 0; w < kWavesPerBlock; ++w) n_mem += s_cnt[w];
-    __syncthreads();
+    lds_barrier();
   }
   const int m0 = (int)blockIdx.y * mt;
   const int cnt = min(mt, n_mem - m0);
@@ -1059,7 +1059,7 @@ __global__ __launch_bounds__(kBlock) void root_head_kernel(DevTrie tr, DevState 
   unsigned long long legal[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) legal[u] = __ballot(rows[u] >= 0 && lane < cnt && my_live[e0 + u] > 0);
-  __syncthreads();  // staged vectors visible
+  lds_barrier();  // staged vectors visible
   // two members per pass: independent accumulation chains side by side
   for (int j = 0; j < cnt; j += 2) {
     const int j1 = min(j + 1, cnt - 1);
@@ -1085,7 +1085,7 @@ __global__ __launch_bounds__(kBlock) void root_head_kernel(DevTrie tr, DevState 
       if (b1 && j1 != j) __hip_atomic_fetch_max(&s_best[j1], b1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
   }
-  __syncthreads();
+  lds_barrier();
   // this tile's best per member (0: none legal); the loop takes the max over tiles
   if (threadIdx.x < cnt) st.rkey[(int64_t)blockIdx.x * st.B + s_mem[m0 + threadIdx.x]] = s_best[threadIdx.x];
 }
@@ -1255,6 +1255,115 @@ __global__ __launch_bounds__(kBlock) void dense_mfma_kernel(DevState st, StepIO 
       }
     }
   }
+}
+
+// Grouped root head on the matrix cores (bf16, H = 128 * KS): workgroup
+// (x, y) takes root rows [16x, 16x+16) and members [16y, 16y+16).  The four
+// wavefronts split the hidden dimension in quarters; each requests all of its
+// quarter of the 16 rows up front (operand A, KS steps of 32) and reads the
+// members' vectors from LDS (operand B); the four partial 16 x 16 tiles are
+// summed in a fixed order ((w0 + w1) + (w2 + w3)), so results do not depend on
+// scheduling, and each member's best legal edge of the tile goes to rkey.
+template <int KS>
+__global__ __launch_bounds__(kBlock) void root_mfma_kernel(DevTrie tr, DevState st, LoopIO io) {
+  extern __shared__ uint4 sh[];  // [16][nq] members' vectors, then int64 offsets[B], int members[B]
+  __shared__ f32x4_t s_part[3][kWave];
+  __shared__ int s_cnt[kWavesPerBlock];
+  const int lane = __lane_id();
+  const int wv = wave_id();
+  const int nq = io.H / 8;
+  int64_t* s_off = reinterpret_cast<int64_t*>(sh + (size_t)16 * nq);
+  int* s_mem = reinterpret_cast<int*>(s_off + st.B);
+  const bool rst = io.reset != 0;
+  const bool later = (io.flags & kLoopLater) != 0;
+  // operand A first: lane l holds row l % 16, elements 8 (l / 16) .. + 8 of each
+  // 32-wide step of this wavefront's quarter
+  const int r1 = tr.begin[1];
+  const int eb = tr.begin[0] + (int)blockIdx.x * 16;
+  const int my_e = min(eb + (lane & 15), r1 - 1);
+  const uint4* arow = (const uint4*)io.emb + (int64_t)tr.tok[my_e] * nq + wv * (KS * 4) + (lane >> 4);
+  u32x4_t a[KS];
+#pragma unroll
+  for (int j = 0; j < KS; ++j) a[j] = *reinterpret_cast<const u32x4_t*>(arow + j * 4);
+  // members in ascending sequence order (every workgroup builds the same list)
+  int n_mem = 0;
+  for (int s0 = 0; s0 < st.B; s0 += kBlock) {
+    const int s = s0 + (int)threadIdx.x;
+    bool ok = false;
+    int t = 0;
+    if (s < st.B) {
+      t = later ? st.tstep[s] : 0;
+      const int stat = st.status[s], fin = st.finished[s], nd = st.node[s], dp = st.depth[s];
+      ok = t < io.T && (rst || (stat == kSeqOk && fin == 0 && nd == 0 && dp == 0));
+    }
+    const unsigned long long m = __ballot(ok);
+    if (lane == 0) s_cnt[wv] = __popcll(m);
+    lds_barrier();
+    int off = n_mem;
+    for (int w = 0; w < wv; ++w) off += s_cnt[w];
+    if (ok) {
+      const int idx = off + __popcll(m & ((1ull << lane) - 1ull));
+      s_mem[idx] = s;
+      s_off[idx] = ((int64_t)t * st.B + s) * nq;
+    }
+    for (int w = 0; w < kWavesPerBlock; ++w) n_mem += s_cnt[w];
+    lds_barrier();
+  }
+  const int m0 = (int)blockIdx.y * 16;
+  const int cnt = min(16, n_mem - m0);
+  if (cnt <= 0) return;  // the same for the whole workgroup
+  // live counts of this lane's four (row, member) results (wavefront 0 uses them)
+  const int col = lane & 15;
+  int lv[4] = {0, 0, 0, 0};
+  if (wv == 0 && col < cnt) {
+    const int32_t* live = rst ? tr.live0 : st.live + (int64_t)s_mem[m0 + col] * tr.live_stride;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = eb + 4 * (lane >> 4) + i;
+      lv[i] = e < r1 ? live[e] : 0;
+    }
+  }
+  // stage the members' vectors (missing members as zeros): rounds of 16
+  // loads per thread, all issued before their stores
+  constexpr int NQ = KS * 16;  // uint4 per vector (H / 8)
+  constexpr int SL = 16;
+  const uint4* hid = (const uint4*)io.hidden_seq;
+#pragma unroll
+  for (int base = 0; base < 16 * NQ; base += SL * kBlock) {
+    uint4 v[SL];
+#pragma unroll
+    for (int u = 0; u < SL; ++u) {
+      const int i = base + u * kBlock + (int)threadIdx.x;
+      const int j = i / NQ;
+      v[u] = j < cnt ? hid[s_off[m0 + j] + (i - j * NQ)] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < SL; ++u) sh[base + u * kBlock + threadIdx.x] = v[u];
+  }
+  lds_barrier();
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint4* brow = sh + col * nq + wv * (KS * 4) + (lane >> 4);
+#pragma unroll
+  for (int j = 0; j < KS; ++j) {
+    const bf16x8_t b = __builtin_bit_cast(bf16x8_t, brow[j * 4]);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[j]), b, acc, 0, 0, 0);
+  }
+  if (wv > 0) s_part[wv - 1][lane] = acc;
+  lds_barrier();
+  if (wv != 0) return;
+  acc = (acc + s_part[0][lane]) + (s_part[1][lane] + s_part[2][lane]);
+  // lane l: member col, rows 4 (l / 16) + i
+  unsigned long long best = 0ull;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (lv[i] > 0) best = max(best, pack_key(acc[i], (uint32_t)(eb + 4 * (lane >> 4) + i)));
+#pragma unroll
+  for (int d = 16; d < kWave; d <<= 1) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)best, d);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(best >> 32), d);
+    best = max(best, ((unsigned long long)hi << 32) | lo);
+  }
+  if (lane < cnt) st.rkey[(int64_t)blockIdx.x * st.B + s_mem[m0 + lane]] = best;
 }
 
 // One wavefront per sequence: winner token from the key, its edge, advance.
@@ -1529,9 +1638,29 @@ hipError_t launch_loop(const DevTrie& tr, const DevState& st, const LoopIO& io, 
 
 constexpr int kRootMembers = 4;  // members per workgroup of the grouped root head
 
+// The matrix-core root head takes bf16 tables with H = 2048 or 4096.
+bool root_uses_mfma(int dtype, int H) { return dtype == 1 && (H == 2048 || H == 4096); }
+
 int root_head_tiles(int dtype, int H, int root_edges) {
-  const int rows_per_wg = kWavesPerBlock * rows_per_pass(chunks_for(dtype, H));
+  const int rows_per_wg = root_uses_mfma(dtype, H) ? 16 : kWavesPerBlock * rows_per_pass(chunks_for(dtype, H));
   return (root_edges + rows_per_wg - 1) / rows_per_wg;
+}
+
+template <int KS>
+hipError_t launch_root_mfma(const DevTrie& tr, const DevState& st, const LoopIO& io, int root_edges, hipStream_t s) {
+  const int nq = io.H / 8;
+  const size_t lds = sizeof(uint4) * (size_t)16 * nq + (sizeof(int64_t) + sizeof(int)) * (size_t)st.B;
+  auto* k = &root_mfma_kernel<KS>;
+  static size_t allowed = 65536;
+  if (lds > allowed) {
+    hipError_t e =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    allowed = lds;
+  }
+  const dim3 grid((unsigned)((root_edges + 15) / 16), (unsigned)((st.B + 15) / 16));
+  hipLaunchKernelGGL(k, grid, dim3(kBlock), lds, s, tr, st, io);
+  return hipGetLastError();
 }
 
 template <int DT, int NC>
@@ -1560,6 +1689,8 @@ struct RootLaunch {
 hipError_t launch_root_head(const DevTrie& tr, const DevState& st, const LoopIO& io, int dtype, int root_edges,
                             hipStream_t s) {
   if (root_edges <= 0) return hipSuccess;
+  if (root_uses_mfma(dtype, io.H))
+    return io.H == 2048 ? launch_root_mfma<16>(tr, st, io, root_edges, s) : launch_root_mfma<32>(tr, st, io, root_edges, s);
   return dispatch<RootLaunch>(dtype, chunks_for(dtype, io.H), tr, st, io, root_edges, s);
 }
 
