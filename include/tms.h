@@ -217,7 +217,10 @@ tms_status tms_state_set_split(tms_state* st, int32_t split);
  * GRAPH: a hipGraph of T step kernels (as tms_decode_step_sparse), built on
  *   the first call for a given set of pointers and replayed afterwards;
  * STREAM: the same T step kernels launched directly on the stream.
- * Also read from the TMS_LOOP environment variable (0..4) at create. */
+ * Also read from the TMS_LOOP environment variable (0..4) at create.
+ * With TMS_BITMASK=1 in the environment of a call, catalogs of at most 128
+ * entries run the resident loop on the bitmask no-repeat state instead of
+ * live counts (bit-identical results). */
 typedef enum {
   TMS_LOOP_RESIDENT = 0,
   TMS_LOOP_GRAPH = 1,

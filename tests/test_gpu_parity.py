@@ -710,3 +710,42 @@ def test_grouped_root_empty_mask_is_per_sequence():
     compare(tok[[0, 2]], ref, c.hidden, None, ln[[0, 2]], ent[[0, 2]], where="grouped isolated")
     st.close()
     trie.close()
+
+
+@pytest.mark.parametrize("cid", ["tiny", "product", "product_deep"])
+def test_bitmask_state_matches_live_counts(cid, monkeypatch):
+    """Catalogs of at most 128 entries run the resident loop on the bitmask
+    no-repeat state (an edge is live iff one of the entries below it is not
+    spent).  Tokens, lengths, entries and the exported state (live counts
+    rewritten from the masks) are bit-identical to the live-count loop and to
+    the per-step kernel, from a reset state and from mid-answer states."""
+    c, otr, T, hid = config_case(cid, B=4)
+    assert len(catalog(cid)) <= 128
+    trie = tms.Trie(catalog(cid), c.vocab, c.sep, c.stop)
+    st = tms.State(trie, 4, c.k, dev_embedding(cid))
+    hd = to_dev(hid)
+    keys = ("node", "depth", "done", "status", "finished", "n_emitted", "entries", "live")
+    for cut in (0, 1, 4, T // 2):
+        rest = torch.zeros_like(hd)
+        rest[: T - cut] = hd[cut:]
+        res = []
+        for mode, env in ((tms.LOOP_RESIDENT_SOLO, "1"), (tms.LOOP_RESIDENT_SOLO, None), (tms.LOOP_STREAM, None)):
+            if env:
+                monkeypatch.setenv("TMS_BITMASK", env)
+            else:
+                monkeypatch.delenv("TMS_BITMASK", raising=False)
+            tms.state_set_loop(st.h, mode)
+            st.reset()
+            a, _ = run_step_loop(st, hd[:cut]) if cut else (np.zeros((4, 0), np.int32), None)
+            b_, ln, en = run_k_pointers(st, rest)
+            res.append((np.concatenate([a, b_[:, : T - cut]], axis=1), ln, en, st.export(live=True)))
+        for other in res[1:]:
+            assert np.array_equal(res[0][0], other[0]) and np.array_equal(res[0][1], other[1])
+            assert np.array_equal(res[0][2], other[2])
+            for key in keys:
+                assert np.array_equal(res[0][3][key], other[3][key]), (cid, cut, key)
+        if cut == 0:
+            compare(res[0][0], oracle.decode(otr, c.k, embedding(cid), hid), c.hidden, None, res[0][1], res[0][2],
+                    where=cid + "/mask")
+    st.close()
+    trie.close()

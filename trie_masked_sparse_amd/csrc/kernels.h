@@ -42,8 +42,12 @@ struct DevTrie {
   const int32_t* run_edge;  // [n_run]
   const int32_t* run_tok;   // [n_run]
   int32_t n_run;            // nodes with a single edge
-  // erec, cent, run, run_edge and run_tok are laid out back to back from
-  // erec (each part a multiple of 16 bytes): image_words int32 words in all
+  // Bitmask no-repeat state (catalogs of at most 128 entries, else null): for
+  // each edge the set of entries below it, 4 words, bit j = entry j.
+  const uint32_t* emask;    // [n_edges][4]
+  // erec, cent, run, run_edge, run_tok and emask (when present) are laid out
+  // back to back from erec (each part a multiple of 16 bytes): image_words
+  // int32 words in all
   int32_t image_words;
   int32_t n_nodes, n_edges, n_entries, cap, max_depth, sep, stop, vocab;
   int32_t live_stride;   // n_edges rounded up to a multiple of 4
@@ -112,7 +116,8 @@ hipError_t launch_step_sparse(const DevTrie& tr, const DevState& st, const StepI
 // (fast path); trie through the scalar cache with live counts in device
 // memory (fast path, too big for LDS); vector edge reads with live counts in
 // LDS, or in device memory (global path).
-enum { kLoopTrieLds = 0, kLoopFastGlobal = 1, kLoopVectorLds = 2, kLoopVectorGlobal = 3 };
+// kLoopTrieMask: as kLoopTrieLds with the bitmask no-repeat state.
+enum { kLoopTrieLds = 0, kLoopFastGlobal = 1, kLoopVectorLds = 2, kLoopVectorGlobal = 3, kLoopTrieMask = 4 };
 // The root step of every sequence at the root (or of all, with io.reset), for
 // the step each is at: per row tile and sequence the best key into st.rkey
 // (root_edges = edges of the root).

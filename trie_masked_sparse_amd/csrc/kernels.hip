@@ -299,13 +299,33 @@ __device__ __forceinline__ int find_edge(const DevTrie& tr, const Seq& q, int to
 }
 
 // How a scan reads live counts: through the scalar cache (state not written
-// earlier in the same kernel), from LDS, or with ordinary vector loads.
-enum { kLiveScalar = 0, kLiveLds = 1, kLiveVector = 2 };
+// earlier in the same kernel), from LDS, with ordinary vector loads, or as
+// the bitmask no-repeat state (kLiveMask: `live` is the per-edge mask of the
+// entries below each edge, 128 bits, and an edge is live iff one of them is
+// not in the sequence's banned set; section "The batched engine").
+enum { kLiveScalar = 0, kLiveLds = 1, kLiveVector = 2, kLiveMask = 3 };
+
+// The banned set of the bitmask state: spent entries, one bit each (K <= 128).
+struct Ban {
+  uint32_t w0, w1, w2, w3;
+};
+
+__device__ __forceinline__ bool mask_live(const uint4& m, const Ban& b) {
+  return ((m.x & ~b.w0) | (m.y & ~b.w1) | (m.z & ~b.w2) | (m.w & ~b.w3)) != 0u;
+}
 
 template <int LIVE>
-__device__ __forceinline__ int read_live_uniform(const int32_t* live, int e) {
-  if constexpr (LIVE == kLiveScalar) return ((cint_p)live)[e];
-  else return __builtin_amdgcn_readfirstlane(live[e]);
+__device__ __forceinline__ int read_live_uniform(const int32_t* live, int e, const Ban& ban) {
+  if constexpr (LIVE == kLiveScalar) {
+    return ((cint_p)live)[e];
+  } else if constexpr (LIVE == kLiveMask) {
+    const uint4 m = reinterpret_cast<const uint4*>(live)[e];
+    const uint4 u = make_uint4(__builtin_amdgcn_readfirstlane(m.x), __builtin_amdgcn_readfirstlane(m.y),
+                               __builtin_amdgcn_readfirstlane(m.z), __builtin_amdgcn_readfirstlane(m.w));
+    return mask_live(u, ban) ? 1 : 0;
+  } else {
+    return __builtin_amdgcn_readfirstlane(live[e]);
+  }
 }
 
 // A wavefront's best candidate, carried to the advance so that it needs no
@@ -372,7 +392,7 @@ template <int DT, int NC, int META, int LIVE, bool CAND>
 __device__ __forceinline__ unsigned long long scan_node(const DevTrie& tr, const TrieView& tv, const Seq& q,
                                                         const int32_t* live, const uint4* __restrict__ emb,
                                                         int nq, const uint4 (&hq)[NC], int wv, int W, int lane,
-                                                        Cand& cand) {
+                                                        Cand& cand, const Ban& ban = Ban{0u, 0u, 0u, 0u}) {
   constexpr int U = rows_per_pass(NC);
   unsigned long long best = 0;
   auto key_of = [&](float l, int e) -> unsigned long long {
@@ -391,7 +411,7 @@ __device__ __forceinline__ unsigned long long scan_node(const DevTrie& tr, const
         const int e = e0 + u * W;
         const int ee = e < q.b1 ? e : q.b1 - 1;  // every node has at least one edge
         rs[u] = erec_uniform<META>(tv.erec, ee);
-        lvs[u] = read_live_uniform<LIVE>(live, ee);  // control edges hold 0
+        lvs[u] = read_live_uniform<LIVE>(live, ee, ban);  // control edges hold 0
         ces[u] = CAND ? meta_uniform<META>(tv.cent, ee) : -1;
         rns[u] = CAND ? meta_uniform<META>(tv.run, ee) : 0;
       }
@@ -553,8 +573,9 @@ __global__ __launch_bounds__(kBlock) void step_sparse_kernel(DevTrie tr, DevStat
 // step handles those, including the empty-mask error).  Every wavefront of
 // the resident loop evaluates it from the same state, so all of them take the
 // same branch without a barrier.
+template <bool MASK>
 __device__ __forceinline__ int forced_edge(const TrieView& tv, const int32_t* live, const Seq& q, int lane,
-                                           Cand& c) {
+                                           Cand& c, const Ban& ban) {
   const int f = q.b1 - q.b0;
   if (f > kWave) return -1;
   const int e = q.b0 + lane;
@@ -562,7 +583,9 @@ __device__ __forceinline__ int forced_edge(const TrieView& tv, const int32_t* li
   int lv = 0, ce = -1, rn = 0;
   if (lane < f) {
     r = tv.erec[e];
-    lv = live[e];  // read for every edge (in range of the live array), used for content edges
+    // read for every edge (in range of the live array), used for content edges
+    if constexpr (MASK) lv = mask_live(reinterpret_cast<const uint4*>(live)[e], ban) ? 1 : 0;
+    else lv = live[e];
     ce = tv.cent[e];
     rn = tv.run[e];
   }
@@ -593,7 +616,7 @@ constexpr int kLoopWaves = kLoopBlock / kWave;
 // live counts, spent bits and, with the trie in LDS, edge records, the
 // entries of the edges' children and the forced-run tables.
 struct LoopLds {
-  int live, spent, erec, cent, run, run_edge, run_tok, total;
+  int live, spent, erec, cent, run, run_edge, run_tok, emask, total;
 };
 __host__ __device__ inline int round4(int n) { return (n + 3) & ~3; }
 __host__ __device__ inline LoopLds loop_lds_layout(const DevTrie& tr, const DevState& st, bool trie) {
@@ -605,7 +628,8 @@ __host__ __device__ inline LoopLds loop_lds_layout(const DevTrie& tr, const DevS
   o.run = o.cent + (trie ? tr.live_stride : 0);
   o.run_edge = o.run + (trie ? tr.live_stride : 0);
   o.run_tok = o.run_edge + (trie ? round4(tr.n_run) : 0);
-  o.total = o.run_tok + (trie ? round4(tr.n_run) : 0);
+  o.emask = o.run_tok + (trie ? round4(tr.n_run) : 0);
+  o.total = o.emask + (trie && tr.emask ? 4 * tr.n_edges : 0);
   return o;
 }
 
@@ -647,10 +671,15 @@ __device__ __forceinline__ void copy2_to_lds(int32_t* d0, const int32_t* s0, int
 // SMALL: path, completed entries and spent flags are known to fit the
 // register-held lists (depth, k and spent words at most 64); the general
 // instantiations decide at run time.
-template <int DT, int NC, int META, bool LDS_LIVE, bool SMALL>
+// MASK: the bitmask no-repeat state replaces the live counts inside the loop
+// (legality from the edges' entry masks and the banned set; no counts to
+// copy in or release); the counts are rewritten from the masks at the end.
+template <int DT, int NC, int META, bool LDS_LIVE, bool SMALL, bool MASK>
 __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState st, LoopIO io) {
   constexpr int EL = DT == 0 ? 4 : 8;
   constexpr bool TRIE_LDS = META == kMetaLds;
+  static_assert(!MASK || (TRIE_LDS && SMALL), "the bitmask state comes with the LDS trie and register lists");
+  constexpr int LIVE_KIND = MASK ? kLiveMask : (LDS_LIVE ? kLiveLds : kLiveVector);
   // With the trie in LDS the winner's record is read again from LDS after the
   // barrier; otherwise each wavefront's best candidate carries it (PAYLOAD).
   constexpr bool PAYLOAD = !TRIE_LDS;
@@ -685,7 +714,7 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
   TrieView tv{tr.erec, tr.cent, tr.run, tr.run_edge, tr.run_tok};
   if constexpr (LDS_LIVE) {
     // live counts, and the trie image when it is kept in LDS
-    copy2_to_lds(lds + lay.live, rst ? tr.live0 : g_live, (int)ls, lds + lay.erec,
+    copy2_to_lds(lds + lay.live, rst ? tr.live0 : g_live, MASK ? 0 : (int)ls, lds + lay.erec,
                  reinterpret_cast<const int32_t*>(tr.erec), TRIE_LDS ? tr.image_words : 0);
     if (!sreg_ok)
       for (int i = threadIdx.x; i < st.spent_words; i += kLoopBlock) spent[i] = rst ? 0u : g_spent[i];
@@ -752,6 +781,12 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
                                : (uint32_t)__builtin_amdgcn_readfirstlane(spent[ent >> 5]);
     return ((w >> (ent & 31)) & 1u) != 0u;
   };
+  // the banned set of the bitmask state: spent words 0..3 (uniform)
+  Ban ban{0u, 0u, 0u, 0u};
+  if constexpr (MASK)
+    ban = Ban{(uint32_t)__builtin_amdgcn_readlane((int)sreg, 0), (uint32_t)__builtin_amdgcn_readlane((int)sreg, 1),
+              (uint32_t)__builtin_amdgcn_readlane((int)sreg, 2), (uint32_t)__builtin_amdgcn_readlane((int)sreg, 3)};
+  const int32_t* lsrc = MASK ? lds + lay.emask : live;  // what scans read for liveness
   bool ctl0 = rec.ent >= 0 && !is_spent(rec.ent);
   bool sep_ok = ctl0 && done + 1 < st.k, stop_ok = ctl0 && done + 1 >= st.k;
   const uint4* hid = (const uint4*)io.hidden_seq;
@@ -769,10 +804,18 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
       else __syncthreads();
     }
     const int ent = rec.ent;
+    if constexpr (MASK) {
+      const uint32_t bit = 1u << (ent & 31);
+      const int w = ent >> 5;
+      ban.w0 |= w == 0 ? bit : 0u;
+      ban.w1 |= w == 1 ? bit : 0u;
+      ban.w2 |= w == 2 ? bit : 0u;
+      ban.w3 |= w == 3 ? bit : 0u;
+    }
     if (wv == 0) {
       if (lane == 0) tokens[t] = tok;
       if (reg_lists) {
-        if (lane < depth) atomicSub(&live[my_path], 1);  // distinct edges; no value returned
+        if (!MASK && lane < depth) atomicSub(&live[my_path], 1);  // distinct edges; no value returned
         if (lane == done) my_ent = ent;
       } else {
         for (int i = lane; i < depth; i += kWave) atomicSub(&live[path[i]], 1);
@@ -889,7 +932,7 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
     q.sep_ok = sep_ok;
     q.stop_ok = stop_ok;
     Cand fc;
-    const int fe = forced_edge(tv, live, q, lane, fc);
+    const int fe = forced_edge<MASK>(tv, lsrc, q, lane, fc, ban);
     if (fe >= 0) {
       // forced: no rows, no reduction and no barrier unless a pointer
       // completes (forced steps have no barrier of their own, so a release
@@ -905,8 +948,8 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
     const int slot = nhead % 3;
     if (threadIdx.x == 0) s_key[(nhead + 1) % 3] = 0ull;  // the next head step's slot
     Cand cand{0, 0, 0, 0, 0, 0};
-    const unsigned long long best = scan_node<DT, NC, META, LDS_LIVE ? kLiveLds : kLiveVector, PAYLOAD>(
-        tr, tv, q, live, emb, nq, hq, wv, W, lane, cand);
+    const unsigned long long best = scan_node<DT, NC, META, LIVE_KIND, PAYLOAD>(
+        tr, tv, q, lsrc, emb, nq, hq, wv, W, lane, cand, ban);
     if (lane == 0) {
       if (best) __hip_atomic_fetch_max(&s_key[slot], best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       if constexpr (PAYLOAD) s_cand[nhead & 1][wv] = cand;
@@ -959,7 +1002,18 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
     for (int j = lane; j < st.k; j += kWave)
       io.entries[(int64_t)s * st.k + j] = (reg_lists && j < kWave) ? (j < done ? my_ent : entries[j]) : entries[j];
   }
-  if constexpr (LDS_LIVE) {
+  if constexpr (MASK) {
+    // live counts from the masks: entries below each edge not yet spent
+    const uint4* em = reinterpret_cast<const uint4*>(lds + lay.emask);
+    for (int e = threadIdx.x; e < (int)ls; e += kLoopBlock) {
+      int c = 0;
+      if (e < tr.n_edges) {
+        const uint4 m = em[e];
+        c = __popc(m.x & ~ban.w0) + __popc(m.y & ~ban.w1) + __popc(m.z & ~ban.w2) + __popc(m.w & ~ban.w3);
+      }
+      g_live[e] = c;
+    }
+  } else if constexpr (LDS_LIVE) {
     __syncthreads();
     int4* dst = reinterpret_cast<int4*>(g_live);
     for (int i = threadIdx.x; i < (int)(ls / 4); i += kLoopBlock) dst[i] = reinterpret_cast<const int4*>(live)[i];
@@ -1560,10 +1614,10 @@ struct StepLaunch {
 
 template <int DT, int NC>
 struct LoopLaunch {
-  template <int META, bool LIVE, bool SMALL>
+  template <int META, bool LIVE, bool SMALL, bool MASK = false>
   static hipError_t go(const DevTrie& tr, const DevState& st, const LoopIO& io, hipStream_t s) {
     const size_t lds = LIVE ? sizeof(int32_t) * (size_t)loop_lds_layout(tr, st, META == kMetaLds).total : 0;
-    auto* k = &loop_kernel<DT, NC, META, LIVE, SMALL>;
+    auto* k = &loop_kernel<DT, NC, META, LIVE, SMALL, MASK>;
     static size_t allowed = 65536;  // per instantiation; raised once as needed
     if (lds > allowed) {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
@@ -1577,6 +1631,9 @@ struct LoopLaunch {
   static hipError_t run(const DevTrie& tr, const DevState& st, const LoopIO& io, int mode, hipStream_t s) {
     const bool small = st.path_stride <= kWave && st.k <= kWave && st.spent_words <= kWave;
     switch (mode) {
+      case kLoopTrieMask:
+        if (small && tr.emask) return go<kMetaLds, true, true, true>(tr, st, io, s);
+        [[fallthrough]];
       case kLoopTrieLds:
         return small ? go<kMetaLds, true, true>(tr, st, io, s) : go<kMetaLds, true, false>(tr, st, io, s);
       case kLoopFastGlobal: return go<kMetaScalar, false, false>(tr, st, io, s);
