@@ -65,6 +65,9 @@ class Workload:
         self.hid_np = hidden_states(cid, self.T, self.B)
         self.hid = _to_dev(self.hid_np)
         self.state = tms.State(self.trie, self.B, c.k, self.emb)
+        begin = self.trie.csr()["begin"]
+        # the library groups root steps across sequences for B >= 8 and a root of >= 64 edges
+        self.grouped = self.B >= 8 and int(begin[1] - begin[0]) >= 64
         self.tokens = torch.empty((self.B, self.T), dtype=torch.int32, device="cuda")
         self.len = torch.empty(self.B, dtype=torch.int32, device="cuda")
         self.entries = torch.empty((self.B, c.k), dtype=torch.int32, device="cuda")
@@ -233,6 +236,41 @@ def copy_reference(reps: int = 5):
     return {"bytes_read": src.numel(), "bytes_written": dst.numel(), "reps": reps}
 
 
+def mask_fed_head_us(w: Workload, reps=20):
+    """The bitmask-fed head at the reset state (every sequence at the root):
+    vocabulary mask of the legal sets, popcount-scan materialiser, gather-GEMV
+    over the materialised rows; each timed on its own over reps launches."""
+    import torch
+
+    import trie_masked_sparse_amd as tms
+    B, V, cap = w.B, w.c.vocab, w.info["cap"]
+    W = (V + 31) // 32
+    mask = torch.empty((B, W), dtype=torch.int32, device="cuda")
+    rows = torch.empty((B, cap), dtype=torch.int32, device="cuda")
+    n = torch.empty(B, dtype=torch.int32, device="cuda")
+    out = torch.empty((B, cap), dtype=torch.float32, device="cuda")
+    w.state.reset()
+    calls = {
+        "legal_mask": lambda: tms.legal_mask(w.state.h, mask),
+        "mask_to_rows": lambda: tms.mask_to_rows(mask, V, rows, n),
+        "gather_gemv": lambda: tms.gather_gemv(w.emb, w.hid[0], rows, n, out),
+    }
+    res = {"B": B, "V": V, "mask_bytes": B * W * 4}
+    for name, f in calls.items():
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        res[f"{name}_us"] = e0.elapsed_time(e1) * 1e3 / reps
+    res["rows_per_seq"] = float(n.float().mean().item())
+    res["mask_to_rows_GBps"] = res["mask_bytes"] / (res["mask_to_rows_us"] * 1e-6) / 1e9
+    return res
+
+
 def dense_step_us(w: Workload, reps=5):
     import torch
 
@@ -345,6 +383,8 @@ def main():
         wd = Workload("structured")
         also["dense_masked_structured_B64"] = dense_step_us(wd)
         _log(f"dense B=64 {also['dense_masked_structured_B64']}")
+        also["mask_fed_head_structured_B64"] = mask_fed_head_us(wd)
+        _log(f"mask-fed head B=64 {also['mask_fed_head_structured_B64']}")
         wd.close()
     if want("stress"):
         for rows in (256, 887):
@@ -362,6 +402,7 @@ def main():
             also[f"{cid}_B64"] = {"steps_per_s": rb["steps_per_s"], "tokens_per_s": rb["tokens_per_s"],
                                   "ms_per_call": rb["ms_per_call"], "steps_per_call": rb["steps_per_call"],
                                   "path": "fast" if wb.info["path"] == tms.PATH_FAST else "global",
+                                  "root_steps": "grouped" if wb.grouped else "per sequence",
                                   "loop_kernel": {k: v for k, v in rfb.items() if k != "rows_per_step"},
                                   "graph_mode": graph_mode(wb, nb, args.warmup)}
             _log(f"{cid} {also[f'{cid}_B64']['steps_per_s']:.0f} steps/s")

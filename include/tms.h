@@ -188,6 +188,22 @@ tms_status tms_advance_forced(tms_state* st, const int32_t* tok, void* stream);
  * token order; n_legal: dev int32 [B], -1 for an inactive sequence. */
 tms_status tms_legal_set(tms_state* st, int32_t* legal_tok, int32_t* n_legal, void* stream);
 
+/* The legal set of every sequence as a vocabulary bitmask ("Understanding
+ * Inference for Systems Engineers", Part 7's masked head; the next-token mask
+ * of "GLRMask"): mask dev uint32 [B][ceil(V/32)], bit t of sequence s set iff
+ * token t is legal; all zero for an inactive sequence.  V up to 2^19 (one mask in 64 KiB). */
+tms_status tms_legal_mask(tms_state* st, uint32_t* mask, void* stream);
+
+/* Bitmask-fed materialiser (same page, Part 7: a popcount scan over the V/32
+ * words gives the sorted row list the head then reads): for each of B rows of
+ * mask (dev uint32 [B][ceil(V/32)], bits at or past V ignored), rows[s][j] =
+ * the j-th set bit's token id in ascending order for j < min(n, cap), and
+ * n_rows[s] = n, the number of set bits (which may exceed cap; slots past n
+ * are not written).  rows dev int32 [B][cap]; n_rows dev int32 [B].  Feeds
+ * tms_gather_gemv directly.  V up to 2^19 (INVALID_ARG above). */
+tms_status tms_mask_to_rows(const uint32_t* mask, int32_t B, int32_t V, int32_t cap, int32_t* rows,
+                            int32_t* n_rows, void* stream);
+
 /* The sparse head on its own (a gather-GEMV over explicit row lists, as for a
  * restricted vocabulary projection): out[s][j] = sum_i hidden[s][i] *
  * emb[rows[s][j]][i] for j < min(n_rows[s], cap), same fp32 arithmetic and

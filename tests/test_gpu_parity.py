@@ -749,3 +749,79 @@ def test_bitmask_state_matches_live_counts(cid, monkeypatch):
                     where=cid + "/mask")
     st.close()
     trie.close()
+
+
+# ---------------------------------------------------------------------------
+# Bitmask-fed materialiser: vocabulary mask -> sorted rows -> head
+# ---------------------------------------------------------------------------
+
+def test_mask_to_rows_random_masks():
+    """Popcount scan against numpy: ascending ids of the set bits, bits at or
+    past V ignored, truncation at cap with the full count reported."""
+    rng = np.random.Generator(np.random.PCG64(70))
+    for V, B, dens in ((1000, 5, 0.05), (4096, 3, 0.5), (151936, 4, 0.003), (33, 2, 0.9), (1, 1, 1.0)):
+        W = (V + 31) // 32
+        bits = rng.random((B, W * 32)) < dens
+        words = np.packbits(bits.reshape(B, W, 32)[:, :, ::-1], axis=-1, bitorder="big").view(">u4")
+        mask = words.reshape(B, W).astype(np.uint32).view(np.int32)
+        want = [np.flatnonzero(bits[s, :V]) for s in range(B)]
+        for cap in (max(1, max(len(w) for w in want)), 3):
+            rows = torch.full((B, cap), -5, dtype=torch.int32, device="cuda")
+            n = torch.full((B,), -5, dtype=torch.int32, device="cuda")
+            tms.mask_to_rows(to_dev(np.ascontiguousarray(mask)), V, rows, n)
+            torch.cuda.synchronize()
+            r, nn = rows.cpu().numpy(), n.cpu().numpy()
+            for s in range(B):
+                assert nn[s] == len(want[s]), (V, s)
+                m = min(cap, len(want[s]))
+                assert np.array_equal(r[s, :m], want[s][:m]), (V, s, cap)
+                assert (r[s, m:] == -5).all()
+
+
+@pytest.mark.parametrize("cid,B", [("tiny", 3), ("structured", 8)])
+def test_mask_fed_head_matches_sparse_step(cid, B):
+    """Along each answer: the legal mask has exactly the oracle's legal tokens;
+    the materialised rows equal the library's legal set; the head over those
+    rows (the same per-row arithmetic) picks the sparse step's token with a
+    bit-identical logit."""
+    c, otr, T, hid = config_case(cid, B=B)
+    trie = tms.Trie(catalog(cid), c.vocab, c.sep, c.stop)
+    st = tms.State(trie, B, c.k, dev_embedding(cid))
+    emb = dev_embedding(cid)
+    W = (c.vocab + 31) // 32
+    cap = trie.info["cap"]
+    mask = torch.empty((B, W), dtype=torch.int32, device="cuda")
+    rows = torch.empty((B, cap), dtype=torch.int32, device="cuda")
+    n = torch.empty(B, dtype=torch.int32, device="cuda")
+    lt = torch.empty((B, cap), dtype=torch.int32, device="cuda")
+    ln = torch.empty(B, dtype=torch.int32, device="cuda")
+    out = torch.empty((B, cap), dtype=torch.float32, device="cuda")
+    tok = torch.empty(B, dtype=torch.int32, device="cuda")
+    lg = torch.empty(B, dtype=torch.float32, device="cuda")
+    ostates = [oracle.State(otr, c.k) for _ in range(B)]
+    st.reset()
+    for t in range(T):
+        hd = to_dev(np.ascontiguousarray(hid[t]))
+        tms.legal_mask(st.h, mask)
+        tms.legal_set(st.h, lt, ln)
+        tms.mask_to_rows(mask, c.vocab, rows, n)
+        tms.gather_gemv(emb, hd, rows, n, out)
+        tms.decode_step_sparse(st.h, hd, tok, lg)
+        torch.cuda.synchronize()
+        m = mask.cpu().numpy().view(np.uint32)
+        r, nn, ltn, lnn = rows.cpu().numpy(), n.cpu().numpy(), lt.cpu().numpy(), ln.cpu().numpy()
+        o, tk, lgv = out.cpu().numpy(), tok.cpu().numpy(), lg.cpu().numpy()
+        for s in range(B):
+            ol = ostates[s].legal()
+            legal = [] if ol is None else sorted(int(x) for x in ol[0])
+            bits = np.flatnonzero(np.unpackbits(m[s].view(np.uint8), bitorder="little"))
+            assert list(bits) == legal, (cid, t, s)
+            if lnn[s] < 0:  # finished or in error
+                assert nn[s] == 0 and tk[s] == -1
+                continue
+            assert nn[s] == lnn[s] and list(r[s, : nn[s]]) == list(ltn[s, : lnn[s]]) == legal, (cid, t, s)
+            j = int(np.argmax(o[s, : nn[s]]))  # first maximum: the lowest token id among ties
+            assert r[s, j] == tk[s] and o[s, j] == lgv[s], (cid, t, s)
+            ostates[s].advance(int(tk[s]))
+    st.close()
+    trie.close()

@@ -31,7 +31,8 @@ EXPORTS = (
     "tms_trie_build", "tms_trie_upload", "tms_trie_info_get", "tms_trie_export_csr", "tms_trie_free",
     "tms_state_create", "tms_state_reset", "tms_state_sync_status", "tms_state_export", "tms_state_free",
     "tms_decode_step_sparse", "tms_decode_step_dense_masked", "tms_decode_k_pointers",
-    "tms_advance_forced", "tms_legal_set", "tms_gather_gemv", "tms_debug_set_live",
+    "tms_advance_forced", "tms_legal_set", "tms_legal_mask", "tms_mask_to_rows", "tms_gather_gemv",
+    "tms_debug_set_live",
     "tms_state_set_split", "tms_state_set_loop", "tms_state_get_launch", "tms_status_str", "tms_last_error",
 )
 
@@ -75,6 +76,8 @@ def lib():
             "tms_decode_k_pointers": [P, P, i32, P, P, P, P],
             "tms_advance_forced": [P, P, P],
             "tms_legal_set": [P, P, P, P],
+            "tms_legal_mask": [P, P, P],
+            "tms_mask_to_rows": [P, i32, i32, i32, P, P, P],
             "tms_gather_gemv": [P, C.c_int, i32, i32, P, P, P, i32, i32, P, P],
             "tms_debug_set_live": [P, i32, i32, i32, P],
             "tms_state_set_split": [P, i32],
@@ -269,6 +272,16 @@ def advance_forced(st, tok, stream=None):
 def legal_set(st, legal_tok, n_legal, stream=None):
     _check(lib().tms_legal_set(st, _dev(legal_tok, torch.int32, "legal_tok"), _dev(n_legal, torch.int32, "n_legal"),
                                _stream(stream)), "legal_set")
+
+
+def legal_mask(st, mask, stream=None):
+    _check(lib().tms_legal_mask(st, _dev(mask, torch.int32, "mask"), _stream(stream)), "legal_mask")
+
+
+def mask_to_rows(mask, V: int, rows, n_rows, stream=None):
+    B, cap = rows.shape
+    _check(lib().tms_mask_to_rows(_dev(mask, torch.int32, "mask"), B, V, cap, _dev(rows, torch.int32, "rows"),
+                                  _dev(n_rows, torch.int32, "n_rows"), _stream(stream)), "mask_to_rows")
 
 
 def gather_gemv(emb, hidden, rows, n_rows, out, stream=None):

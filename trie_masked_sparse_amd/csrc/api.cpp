@@ -687,6 +687,23 @@ tms_status tms_legal_set(tms_state* st, int32_t* legal_tok, int32_t* n_legal, vo
   return TMS_OK;
 }
 
+tms_status tms_legal_mask(tms_state* st, uint32_t* mask, void* stream) {
+  if (!st || !mask) return fail(TMS_ERR_INVALID_ARG, "null argument");
+  if (size_t(st->dev.mask_words) * 4 > 65536) return fail(TMS_ERR_INVALID_ARG, "vocabulary too large for the mask");
+  TMS_FLUSH_RESET(st, stream);
+  TMS_HIP(tms::launch_legal_mask(st->trie->dev, st->dev, mask, static_cast<hipStream_t>(stream)), "legal mask launch");
+  return TMS_OK;
+}
+
+tms_status tms_mask_to_rows(const uint32_t* mask, int32_t B, int32_t V, int32_t cap, int32_t* rows,
+                            int32_t* n_rows, void* stream) {
+  if (!mask || !rows || !n_rows) return fail(TMS_ERR_INVALID_ARG, "null argument");
+  if (B < 1 || V < 1 || cap < 0) return fail(TMS_ERR_INVALID_ARG, "B and V must be positive, cap not negative");
+  if (V > (1 << 19)) return fail(TMS_ERR_INVALID_ARG, "V above 2^19 (a mask row is staged in 64 KiB of LDS)");
+  TMS_HIP(tms::launch_mask_rows(mask, B, V, cap, rows, n_rows, static_cast<hipStream_t>(stream)), "mask rows launch");
+  return TMS_OK;
+}
+
 tms_status tms_gather_gemv(const void* emb, tms_dtype dtype, int32_t V, int32_t H, const void* hidden,
                            const int32_t* rows, const int32_t* n_rows, int32_t B, int32_t cap, float* out,
                            void* stream) {

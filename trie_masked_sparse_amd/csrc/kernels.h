@@ -136,6 +136,11 @@ size_t loop_lds_bytes(const DevTrie& tr, const DevState& st, bool trie);
 hipError_t launch_dense_step(const DevTrie& tr, const DevState& st, const StepIO& io, int dtype,
                              float* full_logits, int grid, bool mfma, hipStream_t s);
 bool dense_uses_mfma(int dtype, int B, int H);
+// The vocabulary bitmask of each sequence's legal set ([B][ceil(V/32)]).
+hipError_t launch_legal_mask(const DevTrie& tr, const DevState& st, uint32_t* out, hipStream_t s);
+// Sorted token ids of the set bits of each mask row, at most cap of them.
+hipError_t launch_mask_rows(const uint32_t* mask, int B, int V, int cap, int32_t* rows, int32_t* n_rows,
+                            hipStream_t s);
 hipError_t launch_forced(const DevTrie& tr, const DevState& st, const int32_t* forced, hipStream_t s);
 hipError_t launch_legal_set(const DevTrie& tr, const DevState& st, int32_t* legal_tok,
                             int32_t* n_legal, hipStream_t s);

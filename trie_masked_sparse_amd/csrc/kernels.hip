@@ -1149,7 +1149,7 @@ __global__ __launch_bounds__(kBlock) void root_head_kernel(DevTrie tr, DevState 
 // ---------------------------------------------------------------------------
 
 // One workgroup per sequence builds its V-bit mask in LDS, then stores it.
-__global__ __launch_bounds__(kBlock) void dense_mask_kernel(DevTrie tr, DevState st) {
+__global__ __launch_bounds__(kBlock) void dense_mask_kernel(DevTrie tr, DevState st, uint32_t* out) {
   extern __shared__ uint32_t smask[];
   const int s = blockIdx.x;
   const int mw = st.mask_words;
@@ -1167,8 +1167,69 @@ __global__ __launch_bounds__(kBlock) void dense_mask_kernel(DevTrie tr, DevState
     }
   }
   __syncthreads();
-  uint32_t* dst = st.mask + (int64_t)s * mw;
+  uint32_t* dst = (out ? out : st.mask) + (int64_t)s * mw;
   for (int i = threadIdx.x; i < mw; i += kBlock) dst[i] = smask[i];
+}
+
+// Bitmask-fed materialiser ("Understanding Inference for Systems Engineers",
+// the masked head of Part 7: the legal rows are read off a vocabulary bitmask
+// with a popcount scan, then only those rows go through the head).  One
+// workgroup per sequence: thread i counts the set bits of its run of words,
+// an exclusive scan over the workgroup gives each run's first slot, and the
+// runs write their token ids in ascending order.  Bits at or past V are not
+// tokens and are ignored.
+__global__ __launch_bounds__(kBlock) void mask_rows_kernel(const uint32_t* mask, int W, int V, int cap,
+                                                           int32_t* rows, int32_t* n_rows) {
+  __shared__ int s_scan[kBlock];
+  extern __shared__ uint32_t s_words[];  // the sequence's mask row, staged with coalesced loads
+  const int s = blockIdx.x;
+  {
+    const uint32_t* g = mask + (int64_t)s * W;
+    constexpr int L = 16;  // loads per thread in flight
+    for (int base = 0; base < W; base += L * kBlock) {
+      uint32_t v[L];
+#pragma unroll
+      for (int u = 0; u < L; ++u) {
+        const int w = base + u * kBlock + (int)threadIdx.x;
+        v[u] = w < W ? g[w] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < L; ++u) {
+        const int w = base + u * kBlock + (int)threadIdx.x;
+        if (w < W) s_words[w] = v[u];
+      }
+    }
+    __syncthreads();
+  }
+  const uint32_t* m = s_words;
+  const int per = (W + kBlock - 1) / kBlock;
+  const int w0 = min(W, (int)threadIdx.x * per), w1 = min(W, w0 + per);
+  auto word = [&](int w) -> uint32_t {
+    uint32_t x = m[w];
+    const int lo = w * 32;
+    if (lo + 32 > V) x &= (V - lo) >= 32 ? 0xFFFFFFFFu : ((1u << (V - lo)) - 1u);
+    return x;
+  };
+  int c = 0;
+  for (int w = w0; w < w1; ++w) c += __popc(word(w));
+  s_scan[threadIdx.x] = c;
+  __syncthreads();
+  for (int d = 1; d < kBlock; d <<= 1) {  // inclusive scan
+    const int v = threadIdx.x >= (unsigned)d ? s_scan[threadIdx.x - d] : 0;
+    __syncthreads();
+    s_scan[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int off = s_scan[threadIdx.x] - c;
+  int32_t* out = rows + (int64_t)s * cap;
+  for (int w = w0; w < w1 && off < cap; ++w) {
+    uint32_t x = word(w);
+    while (x && off < cap) {
+      out[off++] = w * 32 + __builtin_ctz(x);
+      x &= x - 1u;
+    }
+  }
+  if (threadIdx.x == kBlock - 1) n_rows[s] = s_scan[kBlock - 1];
 }
 
 // Every logit of every sequence; masked-in ones feed the per-sequence key.
@@ -1776,7 +1837,8 @@ bool dense_uses_mfma(int dtype, int B, int H) { return dtype == 1 && B >= 2 && B
 
 hipError_t launch_dense_step(const DevTrie& tr, const DevState& st, const StepIO& io, int dtype, float* full,
                              int grid, bool mfma, hipStream_t s) {
-  hipLaunchKernelGGL(dense_mask_kernel, dim3(st.B), dim3(kBlock), st.mask_words * sizeof(uint32_t), s, tr, st);
+  hipLaunchKernelGGL(dense_mask_kernel, dim3(st.B), dim3(kBlock), st.mask_words * sizeof(uint32_t), s, tr, st,
+                     nullptr);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (mfma && dense_uses_mfma(dtype, st.B, io.H)) {
@@ -1790,6 +1852,19 @@ hipError_t launch_dense_step(const DevTrie& tr, const DevState& st, const StepIO
   }
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dense_advance_kernel, dim3(st.B), dim3(kWave), 0, s, tr, st, io);
+  return hipGetLastError();
+}
+
+hipError_t launch_legal_mask(const DevTrie& tr, const DevState& st, uint32_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(dense_mask_kernel, dim3(st.B), dim3(kBlock), st.mask_words * sizeof(uint32_t), s, tr, st, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_mask_rows(const uint32_t* mask, int B, int V, int cap, int32_t* rows, int32_t* n_rows,
+                            hipStream_t s) {
+  const int W = (V + 31) / 32;
+  hipLaunchKernelGGL(mask_rows_kernel, dim3((unsigned)B), dim3(kBlock), sizeof(uint32_t) * (size_t)W, s, mask, W, V,
+                     cap, rows, n_rows);
   return hipGetLastError();
 }
 
