@@ -1481,6 +1481,122 @@ __global__ __launch_bounds__(kBlock) void root_mfma_kernel(DevTrie tr, DevState 
   if (lane < cnt) st.rkey[(int64_t)blockIdx.x * st.B + s_mem[m0 + lane]] = best;
 }
 
+// The same contraction with the K loop outside (H a multiple of 128): each
+// wavefront keeps T row tiles of 16 in accumulators for the whole of H, so a
+// workgroup stages each 128-wide K block of the hidden vectors once for its
+// 64*T rows (double-buffered: the next block's slice and table data are in
+// flight while the current one is multiplied, one barrier per block).  A lane
+// reads four consecutive K steps of its row per block, i.e. 64 bytes; the
+// four lanes of a row cover a full 256-byte run, so no line is read twice.
+// Sums in the same K order as dense_mfma_kernel.
+template <int MAXT, int T>
+__global__ __launch_bounds__(kBlock) void dense_mfma_kstream_kernel(DevState st, StepIO io, float* full_logits,
+                                                                     int ntiles, int nblk) {
+  extern __shared__ uint4 sh[];  // two buffers of [ntiles*16][kDenseStride]
+  const int lane = __lane_id();
+  const int wv = wave_id();
+  const int V = io.V, H = io.H, B = st.B;
+  const int nq = H / 8;
+  const uint4* emb = (const uint4*)io.emb;
+  const uint4* hid = (const uint4*)io.hidden;
+  const int nseq = ntiles * 16;
+  const int bufsz = nseq * kDenseStride;
+  constexpr int kRows = 4 * T * 16;
+  const int nkb = H / kDenseKB;
+  uint4 hv[MAXT];  // this thread's share of a staged block: entries tid + 256u
+  auto hload = [&](int kb) {
+#pragma unroll
+    for (int u = 0; u < MAXT; ++u) {
+      const int idx = u * kBlock + (int)threadIdx.x;
+      const int sq = idx >> 4, qq = idx & 15;
+      hv[u] = (idx < nseq * 16 && sq < B) ? hid[(int64_t)sq * nq + kb * 16 + qq] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto hstore = [&](uint4* buf) {
+#pragma unroll
+    for (int u = 0; u < MAXT; ++u) {
+      const int idx = u * kBlock + (int)threadIdx.x;
+      if (idx < nseq * 16) buf[(idx >> 4) * kDenseStride + (idx & 15)] = hv[u];
+    }
+  };
+  for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    const int m0 = blk * kRows + wv * (T * 16);
+    const uint4* rp[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) rp[t] = emb + (int64_t)min(m0 + t * 16 + (lane & 15), V - 1) * nq + (lane >> 4);
+    f32x4_t acc[T][MAXT];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int m = 0; m < MAXT; ++m) acc[t][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    u32x4_t a[T][4];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[t][j] = *reinterpret_cast<const u32x4_t*>(rp[t] + j * 4);
+    hload(0);
+    __syncthreads();  // the buffers of the previous row block are consumed
+    hstore(sh);
+    int cur = 0;
+    for (int kb = 0; kb < nkb; ++kb) {
+      const bool more = kb + 1 < nkb;
+      u32x4_t an[T][4];
+      if (more) {
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) an[t][j] = *reinterpret_cast<const u32x4_t*>(rp[t] + (kb + 1) * 16 + j * 4);
+        hload(kb + 1);
+      }
+      lds_barrier();  // block kb staged; every wavefront is done with the other buffer
+      const uint4* hb = sh + cur * bufsz;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int m = 0; m < MAXT; ++m) {
+          if (m < ntiles) {
+            const bf16x8_t b =
+                __builtin_bit_cast(bf16x8_t, hb[(m * 16 + (lane & 15)) * kDenseStride + j * 4 + (lane >> 4)]);
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+              acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[t][j]), b, acc[t][m],
+                                                                   0, 0, 0);
+          }
+        }
+      }
+      if (more) {
+        hstore(sh + (cur ^ 1) * bufsz);
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) a[t][j] = an[t][j];
+      }
+      cur ^= 1;
+    }
+    // epilogue: tile t, sequence m*16 + lane%16, rows m0 + t*16 + 4*(lane/16) + i
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int r0 = m0 + t * 16 + 4 * (lane >> 4);
+#pragma unroll
+      for (int m = 0; m < MAXT; ++m) {
+        if (m >= ntiles) continue;
+        const int sq = m * 16 + (lane & 15);
+        if (sq >= B) continue;
+        const uint32_t word = r0 < V ? st.mask[(int64_t)sq * st.mask_words + (r0 >> 5)] : 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = r0 + i;
+          if (r >= V) continue;
+          const float l = acc[t][m][i];
+          if (full_logits) full_logits[(int64_t)sq * V + r] = l;
+          if ((word >> ((r0 & 31) + i)) & 1u)
+            __hip_atomic_fetch_max(&st.key[sq], pack_key(l, (uint32_t)r), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+  }
+}
+
 // One wavefront per sequence: winner token from the key, its edge, advance.
 __global__ __launch_bounds__(kWave) void dense_advance_kernel(DevTrie tr, DevState st, StepIO io) {
   const int s = blockIdx.x;
@@ -1833,6 +1949,23 @@ hipError_t launch_dense_mfma(const DevState& st, const StepIO& io, float* full, 
   return hipGetLastError();
 }
 
+template <int MAXT, int T>
+hipError_t launch_dense_kstream(const DevState& st, const StepIO& io, float* full, hipStream_t s) {
+  const int ntiles = (st.B + 15) / 16;
+  const size_t lds = 2 * sizeof(uint4) * (size_t)ntiles * 16 * kDenseStride;  // double buffer
+  auto* k = &dense_mfma_kstream_kernel<MAXT, T>;
+  static size_t allowed = 65536;
+  if (lds > allowed) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+    allowed = lds;
+  }
+  const int nblk = (io.V + 64 * T - 1) / (64 * T);
+  hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(kBlock), lds, s, st, io, full, ntiles, nblk);
+  return hipGetLastError();
+}
+
 bool dense_uses_mfma(int dtype, int B, int H) { return dtype == 1 && B >= 2 && B <= 256 && H % 32 == 0; }
 
 hipError_t launch_dense_step(const DevTrie& tr, const DevState& st, const StepIO& io, int dtype, float* full,
@@ -1844,9 +1977,15 @@ hipError_t launch_dense_step(const DevTrie& tr, const DevState& st, const StepIO
   if (mfma && dense_uses_mfma(dtype, st.B, io.H)) {
     // one 16-row tile per wavefront keeps many workgroups (2374 at V = 151936)
     // for balance and latency hiding
-    err = st.B <= 64 ? launch_dense_mfma<4, 1>(st, io, full, s)
-        : st.B <= 128 ? launch_dense_mfma<8, 1>(st, io, full, s)
-                      : launch_dense_mfma<16, 1>(st, io, full, s);
+    if (io.H % kDenseKB == 0)
+      // two row tiles per wavefront: measured best (1/2/3/4/8 swept at B = 64)
+      err = st.B <= 64 ? launch_dense_kstream<4, 2>(st, io, full, s)
+          : st.B <= 128 ? launch_dense_kstream<8, 2>(st, io, full, s)
+                        : launch_dense_kstream<16, 1>(st, io, full, s);
+    else
+      err = st.B <= 64 ? launch_dense_mfma<4, 1>(st, io, full, s)
+          : st.B <= 128 ? launch_dense_mfma<8, 1>(st, io, full, s)
+                        : launch_dense_mfma<16, 1>(st, io, full, s);
   } else {
     err = dispatch<DenseLaunch>(dtype, chunks_for(dtype, io.H), st, io, full, grid, s);
   }
