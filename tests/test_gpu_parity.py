@@ -825,3 +825,41 @@ def test_mask_fed_head_matches_sparse_step(cid, B):
             ostates[s].advance(int(tk[s]))
     st.close()
     trie.close()
+
+
+@pytest.mark.parametrize("dtype,H", [("bf16", 4096), ("bf16", 1024), ("fp32", 512), ("bf16", 2048)])
+def test_grouped_root_random_tables(dtype, H):
+    """Grouped root heads on catalogs with a wide root: the matrix-core head
+    for bf16 with H = 2048 or 4096 (16 and 32 steps per quarter), the vector
+    head otherwise; B = 24 gives a full and a partial member tile.  Checked
+    against the oracle (tie depth H + 1 for the matrix cores) and against the
+    per-sequence loop (bit-identical for the vector head)."""
+    rng = np.random.Generator(np.random.PCG64(80 + H))
+    V, B, k = 2000, 24, 3
+    cat = random_catalog(90 + H, 400, 5, V - 2, min_len=2)
+    otr = oracle.Trie(cat, V, V - 2, V - 1)
+    b = otr.csr()["begin"]
+    assert b[1] - b[0] >= 64  # a wide root
+    T = k * (otr.max_depth + 1)
+    emb = _rand_table(rng, V, H, dtype)
+    hid = _rand_hidden(rng, T, B, H, dtype)
+    ref = oracle.decode(otr, k, emb, hid)
+    mfma = dtype == "bf16" and H in (2048, 4096)
+    trie = tms.Trie(cat, V, V - 2, V - 1)
+    st = tms.State(trie, B, k, to_dev(emb))
+    hd = to_dev(hid)
+    out = {}
+    for mode in (tms.LOOP_RESIDENT_GROUPED, tms.LOOP_RESIDENT_SOLO):
+        tms.state_set_loop(st.h, mode)
+        st.reset()
+        out[mode] = run_k_pointers(st, hd) + (st.export(live=True),)
+    tg, lg, eg, exg = out[tms.LOOP_RESIDENT_GROUPED]
+    ts, ls, es, exs = out[tms.LOOP_RESIDENT_SOLO]
+    fg = compare(tg, ref, H, None, lg, eg, where=f"grouped {dtype} H={H}", depth=H + 1 if mfma else None)
+    fs = compare(ts, ref, H, None, ls, es, where=f"solo {dtype} H={H}")
+    if not mfma or (not fg and not fs):
+        assert np.array_equal(tg, ts) and np.array_equal(eg, es)
+        for key in ("node", "depth", "done", "status", "finished", "n_emitted", "entries", "live"):
+            assert np.array_equal(exg[key], exs[key]), key
+    st.close()
+    trie.close()
