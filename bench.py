@@ -313,6 +313,52 @@ def cpu_baseline(w: Workload, min_seconds: float):
                       f"{int(out['len'].sum())} tokens each), {el:.1f} s, single thread, gcc -O2 fp64"}
 
 
+def cpu_baseline_threads(w: Workload, seq_sample=None):
+    """The oracle decoding the same batch once: on one thread, and with the
+    sequences split over the host's threads (ctypes releases the GIL around
+    each call).  seq_sample: decode only these sequences (large batches)."""
+    import concurrent.futures as cf
+
+    import numpy as np
+
+    import oracle
+    otr = oracle.Trie(__import__("synth").catalog(w.cid), w.c.vocab, w.c.sep, w.c.stop)
+    hid = w.hid_np if seq_sample is None else np.ascontiguousarray(w.hid_np[:, seq_sample, :])
+    t0 = time.perf_counter()
+    oracle.decode(otr, w.c.k, w.emb_np, hid)
+    one = time.perf_counter() - t0
+    n = min(os.cpu_count() or 1, hid.shape[1])
+    parts = [np.ascontiguousarray(hid[:, i::n, :]) for i in range(n)]
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(n) as ex:
+        list(ex.map(lambda h: oracle.decode(otr, w.c.k, w.emb_np, h), parts))
+    many = time.perf_counter() - t0
+    return {"seconds_1_thread": one, "seconds_n_threads": many, "threads": n, "sequences": int(hid.shape[1])}
+
+
+def config_table(steps: int, warmup: int):
+    """Every workload: the resident decode's steps/s and tokens/s, gathered
+    bytes per second, the dense+mask step, and the oracle's time for the
+    same batch (the results table of the bench's plan)."""
+    import numpy as np
+    out = {}
+    for cid in ("tiny", "product", "product_deep", "structured", "unstructured", "large"):
+        _log(f"table: {cid}")
+        w = Workload(cid)
+        r = time_decode(w, steps, warmup)
+        n_rows, n_act, _ = w.legal_profile()
+        gathered = float(((n_rows + n_act) * w.c.hidden * w.esz).sum())
+        sample = None if w.B <= 64 else list(range(0, w.B, w.B // 24))[:24]
+        row = {"B": w.B, "steps_per_s": r["steps_per_s"], "tokens_per_s": r["tokens_per_s"],
+               "ms_per_call": r["ms_per_call"], "gathered_TBps": gathered / (r["gpu_ms"] * 1e-3 / steps) / 1e12,
+               "dense_mask_step_us": dense_step_us(w)["us_per_step"],
+               "oracle": cpu_baseline_threads(w, sample)}
+        out[cid] = row
+        _log(f"table: {cid} {row}")
+        w.close()
+    return out
+
+
 def _pmc_traffic(kernel: str, workload: str):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it
     was taken with the current kernel sources."""
@@ -333,7 +379,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--only", default="",
-                    help="comma list of headline,b64,stress,dense,cpu,copyref (default: all but copyref)")
+                    help="comma list of headline,b64,stress,dense,cpu,copyref,configs (default: all but copyref, configs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
@@ -407,6 +453,8 @@ def main():
                                   "graph_mode": graph_mode(wb, nb, args.warmup)}
             _log(f"{cid} {also[f'{cid}_B64']['steps_per_s']:.0f} steps/s")
             wb.close()
+    if args.only and "configs" in args.only.split(","):
+        also["configs"] = config_table(args.steps, args.warmup)
     if want("cpu"):
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
         _log(f"cpu {line['cpu_baseline']}")
