@@ -174,6 +174,7 @@ def loop_roofline(w: Workload, timed: dict, steps: int):
         "kernel": "loop_kernel", "avg_launch_us": launch_us, "event_pair_us": timed["decode_launch_us"],
         "alg_bytes_per_launch": gathered, "unique_bytes_per_launch": unique,
         "achieved_GBps": gathered / (launch_us * 1e-6) / 1e9, "unique_GBps": unique / (launch_us * 1e-6) / 1e9,
+        "flops_per_launch": float(2 * H * n_rows.sum()),
         "rows_per_step": [int(x) for x in n_rows],
     }
 
@@ -234,6 +235,63 @@ def copy_reference(reps: int = 5):
         dst.copy_(src)
     torch.cuda.synchronize()
     return {"bytes_read": src.numel(), "bytes_written": dst.numel(), "reps": reps}
+
+
+def streaming_read_reference(nbytes: int = 604 << 20, reps: int = 5):
+    """A plain streaming read of a buffer the size of the stress working set,
+    the reference the gathers are compared with: torch's row sums over a
+    [n / 4096, 4096] fp32 view (the fastest of the library's plain reductions
+    measured here: sum, amax and row sums in bf16/fp32; full sums reach only
+    3.3-3.8 TB/s)."""
+    import torch
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda").view(-1, 4096)
+    x.sum(dim=1)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        x.sum(dim=1)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    return {"bytes": nbytes, "us": us, "GBps": nbytes / (us * 1e-6) / 1e9, "kernel": "torch row sums (fp32)"}
+
+
+def launch_floor(w: Workload, reps: int = 20):
+    """Per-launch cost of the step kernel when it has nothing to do: the
+    hipGraph of T step kernels replayed on a finished state."""
+    import torch
+
+    import trie_masked_sparse_amd as tms
+    tms.state_set_loop(w.state.h, tms.LOOP_GRAPH)
+    w.decode()  # build the graph; every sequence finishes
+    tms.decode_k_pointers(w.state.h, w.hid, w.tokens, w.len, w.entries)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        tms.decode_k_pointers(w.state.h, w.hid, w.tokens, w.len, w.entries)
+    e1.record()
+    torch.cuda.synchronize()
+    tms.state_set_loop(w.state.h, tms.LOOP_RESIDENT)
+    per_call = e0.elapsed_time(e1) * 1e3 / reps
+    return {"us_per_step_kernel": per_call / (w.T + 1), "launches_per_call": w.T + 1, "us_per_call": per_call}
+
+
+def environment():
+    import platform
+
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None), "gpu": p.name,
+            "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+            "host_cpu": cpu, "host_threads": os.cpu_count(), "python": platform.python_version()}
 
 
 def mask_fed_head_us(w: Workload, reps=20):
@@ -422,6 +480,7 @@ def main():
                             "avg_launch_us": rf["avg_launch_us"]}
         also["product_loop_detail"] = rf
         also["product_graph_mode"] = graph_mode(w, args.steps, args.warmup)
+        also["product_launch_floor"] = launch_floor(w)
         _log(f"roofline {line['roofline']}; graph {also['product_graph_mode']}")
     if want("dense"):
         also["dense_masked_product_B1"] = dense_step_us(w)
@@ -436,6 +495,12 @@ def main():
         for rows in (256, 887):
             also[f"gather_gemv_stress_64x{rows}"] = stress_gemv(max(3, args.steps // 5), 2, w.emb, w.emb_np, rows)
             _log(f"stress {also[f'gather_gemv_stress_64x{rows}']}")
+        ref = streaming_read_reference()
+        also["streaming_read_reference"] = ref
+        for rows in (256, 887):
+            d = also[f"gather_gemv_stress_64x{rows}"]
+            d["frac_of_streaming_read"] = d["achieved_GBps"] / ref["GBps"]
+        _log(f"streaming read {ref}")
     if want("copyref"):
         also["copy_reference"] = copy_reference()
     if want("b64"):
@@ -458,6 +523,7 @@ def main():
     if want("cpu"):
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
         _log(f"cpu {line['cpu_baseline']}")
+    also["environment"] = environment()
     line["also"] = also
     w.close()
     print(json.dumps(line), flush=True)
