@@ -1,7 +1,9 @@
 // C ABI of the trie-constrained sparse decode library (declared in include/tms.h).
 // Handles own their device memory; decode calls only enqueue kernels on the
-// caller's stream.  The device loop is a hipGraph of T step kernels captured on
-// a private stream and replayed on the caller's stream.
+// caller's stream.  The device loop runs as one resident kernel (or one grouped
+// root head plus one resident kernel per pointer), or as T step kernels, either
+// launched directly or as a hipGraph captured on a private stream and replayed
+// on the caller's stream.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>

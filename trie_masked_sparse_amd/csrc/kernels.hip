@@ -1,5 +1,5 @@
 // HIP kernels for gfx950 (CDNA4, 64-wide wavefronts): the trie-constrained
-// sparse decode step and its dense-plus-mask cross-check.
+// sparse decode step, its device loop, and the dense-plus-mask cross-check.
 //
 // Sources (web page "Constraint made cheaper than no constraint"):
 //   section "The grammar as a trie over tokens"  - CSR trie, sentinel children;
@@ -8,23 +8,27 @@
 //     an unwalkable winner, exactly-k rule, live counts decremented along the
 //     completed pointer's path, per-terminal spent flag;
 //   section "The sparse output layer" - one dot product per legal token against
-//     the tied embedding on a fixed grid; the dense head kept as a cross-check
-//     with the same tie rule and transitions;
-//   section "The whole loop on the device" - step kernels that read token,
-//     node and no-repeat state from device memory.
-// Dense-plus-mask semantics: page "Constrained decoding with weighted
-// automata" (mask the logits, then take the argmax) and page "Understanding
-// inference for systems engineers", section 7 (the post-logit bitmask pipeline).
+//     the tied embedding; the dense head kept as a cross-check with the same
+//     tie rule and transitions; no head on steps with a single legal token;
+//   section "The whole loop on the device" - the steps run on the device with
+//     token, node and no-repeat state in device memory;
+//   section "The batched engine" - rows shared by sequences at the same node
+//     read once (the grouped root head); the bitmask no-repeat state.
+// Dense-plus-mask semantics: page "GLRMask" (mask the logits, then take the
+// argmax) and page "Understanding Inference for Systems Engineers", Part 7
+// (the post-logit bitmask and the row list read off it).
 //
-// Arithmetic contract (identical in every kernel that produces a logit):
+// Arithmetic contract of the vector kernels (every logit of the sparse
+// paths, the B = 1 dense head, the vector grouped root head):
 //   lane l of a wavefront owns 16-byte chunks c = 0,1,.. of a row, i.e. the
 //   elements [c*CH + l*EL, c*CH + l*EL + EL) with EL = 4 (fp32) or 8 (bf16) and
 //   CH = 64*EL; it accumulates h[i]*E[v][i] in fp32 in ascending element order
 //   (fp32: one fused multiply-add per element; bf16: one v_dot2_f32_bf16 per
 //   pair of adjacent elements); the 64 partial sums are then combined by a fixed
-//   6-level tree (see wave_sum).  The order depends only on
-//   H, never on the workgroup, slot, batch size or path, so equal rows give
-//   equal logits and every path gives bit-identical logits.
+//   6-level tree (see wave_sum).  The order depends only on H, never on the
+//   workgroup, slot, batch size or path, so these kernels give bit-identical
+//   logits.  The matrix-core heads (dense at B > 1, grouped root for bf16 with
+//   H = 2048 or 4096) sum in the hardware's order, fixed for a given shape.
 //
 // Argmax: a 64-bit key (order-preserving fp32 bits, -0 folded into +0, in the
 // high word; 0xFFFFFFFF - id in the low word) so that an unsigned max picks
