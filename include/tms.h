@@ -20,9 +20,9 @@
  *   - section "The whole loop on the device": the decode loop runs without the
  *     host between steps.
  * The mask semantics are Mask(u) = {v : some w makes u v w an answer} (page
- * "Constrained decoding with weighted automata", the next-token mask), and the
- * greedy tie rule is the one of page "Understanding inference for systems
- * engineers", section 3.8.
+ * "GLRMask - constrained decoding with weighted automata", the next-token
+ * mask), and the greedy tie rule is the one of page "Understanding Inference
+ * for Systems Engineers", section 3.8.
  *
  * Conventions for every call:
  *   - Every function returns a tms_status and never throws.  On failure
@@ -31,7 +31,8 @@
  *     torch.Tensor.data_ptr()); "host" pointers are host memory owned by the
  *     caller.  The library never frees caller memory.
  *   - stream is a hipStream_t (NULL = the legacy default stream).  Decode
- *     calls only enqueue work on it and return; they allocate nothing.
+ *     calls only enqueue work on it and return; they allocate nothing (the
+ *     GRAPH loop form instantiates its graph on its first call).
  *   - Device-detected errors (EMPTY_MASK, NOT_WALKABLE, NOT_DONE) are recorded
  *     per sequence and are sticky: that sequence stops, the others continue.
  *     tms_state_sync_status() synchronises the stream and reports them.
@@ -168,13 +169,18 @@ tms_status tms_decode_step_dense_masked(tms_state* st, const void* hidden, int32
 /* The device-resident loop (section "The whole loop on the device"): T sparse
  * steps from the current state with no host work in between.  By default one
  * kernel runs the whole loop with one workgroup per sequence (state kept on
- * chip between steps); see tms_state_set_loop for the other forms.  hidden_seq: dev
+ * chip between steps), or, for B >= 8 and a root of at least 64 edges, one
+ * grouped root head plus one such kernel per pointer; see tms_state_set_loop
+ * for the other forms.  hidden_seq: dev
  * [T][B][H], step t uses hidden_seq[t].  Outputs: tokens dev int32 [B][T]
  * (token of step t, -1 where a sequence was inactive), len dev int32 [B]
  * (tokens emitted since the last reset), entries dev int32 [B][k] (catalog
  * index of each completed pointer, -1 if missing).  Sequences still unfinished
  * after T steps get NOT_DONE.  T must be >= k*(max_depth+1) (INVALID_ARG).
- * Bit-identical to T calls of tms_decode_step_sparse. */
+ * Bit-identical to T calls of tms_decode_step_sparse, except that a grouped
+ * root head on the matrix cores (bf16, H = 2048 or 4096) sums the root steps'
+ * logits in the matrix cores' order: the same tokens unless two root logits
+ * are closer than that order's rounding. */
 tms_status tms_decode_k_pointers(tms_state* st, const void* hidden_seq, int32_t T, int32_t* tokens,
                                  int32_t* len, int32_t* entries, void* stream);
 
@@ -222,7 +228,8 @@ tms_status tms_debug_set_live(tms_state* st, int32_t s, int32_t edge, int32_t va
  * workgroups per sequence in the fused step; 0 restores the default. */
 tms_status tms_state_set_split(tms_state* st, int32_t split);
 
-/* How tms_decode_k_pointers runs its T steps (all bit-identical):
+/* How tms_decode_k_pointers runs its T steps (all bit-identical, up to the
+ * matrix-core root head noted at tms_decode_k_pointers):
  * RESIDENT_SOLO: one launch, one workgroup per sequence loops over the steps;
  * RESIDENT_GROUPED: one phase per pointer; each phase first takes the root
  *   step of every sequence standing at the root in one grouped launch (each
