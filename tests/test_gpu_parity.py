@@ -631,6 +631,55 @@ def test_deferred_reset_is_applied_by_every_next_call():
     trie.close()
 
 
+@pytest.mark.parametrize("mode", ["grouped", "solo", "stream"])
+def test_reset_restores_released_paths(mode):
+    """A reset after decoding restores only the live counts on the completed
+    entries' root paths (all that completions take off); after
+    tms_debug_set_live, or on a fresh state, it rewrites whole rows.  Both,
+    inside the resident loop and as a reset kernel, leave every sequence's
+    state equal to a fresh one's, and a decode after them repeats the first."""
+    B = 64
+    c, otr, T, hid = config_case("structured", B=B)
+    trie = tms.Trie(catalog("structured"), c.vocab, c.sep, c.stop)
+    st = tms.State(trie, B, c.k, dev_embedding("structured"))
+    tms.state_set_loop(st.h, {"grouped": tms.LOOP_RESIDENT_GROUPED, "solo": tms.LOOP_RESIDENT_SOLO,
+                              "stream": tms.LOOP_STREAM}[mode])
+    hd = to_dev(hid)
+    keys = ("node", "depth", "done", "status", "finished", "n_emitted", "entries", "live", "spent")
+    fresh = st.export(live=True)
+    r0 = run_k_pointers(st, hd)
+    ex0 = st.export(live=True)
+    assert (ex0["live"] != fresh["live"]).any() and (ex0["done"] == c.k).all()
+
+    def same(a, b, where):
+        for key in keys:
+            if key in a:
+                assert np.array_equal(a[key], b[key]), (mode, where, key)
+
+    st.reset()  # carried out by the next decode
+    r1 = run_k_pointers(st, hd)
+    for x, y in zip(r0, r1):
+        assert np.array_equal(x, y), (mode, "decode after reset")
+    same(st.export(live=True), ex0, "state after reset and decode")
+    st.reset()  # carried out by the export (reset kernel)
+    same(st.export(live=True), fresh, "reset kernel")
+    root = trie.csr()
+    e = int(root["begin"][0])
+    run_k_pointers(st, hd)
+    tms.debug_set_live(st.h, 3, e, 0)
+    st.reset()
+    same(st.export(live=True), fresh, "reset kernel after set_live")
+    run_k_pointers(st, hd)
+    tms.debug_set_live(st.h, 5, e + 1, 0)
+    st.reset()
+    r2 = run_k_pointers(st, hd)
+    for x, y in zip(r0, r2):
+        assert np.array_equal(x, y), (mode, "decode after set_live and reset")
+    same(st.export(live=True), ex0, "state after set_live, reset and decode")
+    st.close()
+    trie.close()
+
+
 # ---------------------------------------------------------------------------
 # Root steps grouped across sequences (one phase per pointer)
 # ---------------------------------------------------------------------------

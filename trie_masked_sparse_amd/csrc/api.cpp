@@ -44,6 +44,10 @@ struct tms_state {
   // live counts changed by tms_debug_set_live since the last reset: the
   // bitmask state (which derives liveness from the spent set) does not apply
   bool live_dirty = false;
+  // every live row equals live0 except on the root paths of the row's stored
+  // completed entries (false until the first reset has run, and after
+  // tms_debug_set_live): a reset may then restore just those paths
+  bool live_by_paths = false;
   hipStream_t capture = nullptr;
   hipGraph_t graph = nullptr;
   hipGraphExec_t gexec = nullptr;
@@ -229,17 +233,25 @@ tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_
   // below each content edge (the edges of each entry's root path)
   const bool with_mask = h.n_entries <= 128;
   std::vector<uint32_t> emask(with_mask ? size_t(h.n_edges) * 4 : 0, 0u);
-  if (with_mask) {
+  // each entry's root path, for resets that restore only what completions
+  // released (int32 offsets: at most 2^31 - 1 catalog tokens)
+  const int64_t n_path = offsets[K] - offsets[0];
+  const bool with_paths = n_path < (int64_t(1) << 31);
+  std::vector<int32_t> ent_off(with_paths ? size_t(K) + 1 : 0, 0), ent_path(with_paths ? size_t(n_path) : 0, 0);
+  if (with_mask || with_paths) {
     for (int32_t j = 0; j < K; ++j) {
       int32_t n = 0;
+      if (with_paths) ent_off[j] = static_cast<int32_t>(offsets[j] - offsets[0]);
       for (int64_t p = offsets[j]; p < offsets[j + 1]; ++p) {
         const int32_t* lo = h.tok.data() + h.begin[n];
         const int32_t* hi = h.tok.data() + h.begin[n + 1];
         const int32_t x = static_cast<int32_t>(std::lower_bound(lo, hi, tokens[p]) - h.tok.data());
-        emask[4 * size_t(x) + (j >> 5)] |= 1u << (j & 31);
+        if (with_mask) emask[4 * size_t(x) + (j >> 5)] |= 1u << (j & 31);
+        if (with_paths) ent_path[size_t(p - offsets[0])] = x;
         n = h.child[x];
       }
     }
+    if (with_paths) ent_off[K] = static_cast<int32_t>(n_path);
   }
   // edge records, children's entries and run tables in one block, in the
   // order (and word offsets) the resident loop keeps them in LDS, so that
@@ -251,6 +263,7 @@ tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_
   const size_t o_erec = o_image + 4 * w_erec, o_cent = o_image + 4 * w_cent, o_run = o_image + 4 * w_run,
                o_run_edge = o_image + 4 * w_run_edge, o_run_tok = o_image + 4 * w_run_tok,
                o_emask = o_image + 4 * w_emask;
+  const size_t o_ent_off = c.take<int32_t>(ent_off.size()), o_ent_path = c.take<int32_t>(ent_path.size());
   run_edge.resize((n_run + 3) & ~3, 0);
   run_tok.resize((n_run + 3) & ~3, 0);
   hipError_t e = hipGetDevice(&t->device);
@@ -297,6 +310,10 @@ tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_
     e = hipMemcpyAsync(base + o_run_tok, run_tok.data(), 4 * run_tok.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess && with_mask)
     e = hipMemcpyAsync(base + o_emask, emask.data(), 4 * emask.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && with_paths)
+    e = hipMemcpyAsync(base + o_ent_off, ent_off.data(), 4 * ent_off.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && with_paths && !ent_path.empty())
+    e = hipMemcpyAsync(base + o_ent_path, ent_path.data(), 4 * ent_path.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     (void)hipFree(t->dmem);
@@ -317,6 +334,8 @@ tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_
   d.run_tok = reinterpret_cast<const int32_t*>(base + o_run_tok);
   d.image_words = static_cast<int32_t>(w_image);
   d.emask = with_mask ? reinterpret_cast<const uint32_t*>(base + o_emask) : nullptr;
+  d.ent_off = with_paths ? reinterpret_cast<const int32_t*>(base + o_ent_off) : nullptr;
+  d.ent_path = with_paths ? reinterpret_cast<const int32_t*>(base + o_ent_path) : nullptr;
   d.n_run = n_run;
   d.n_nodes = h.n_nodes;
   d.n_edges = h.n_edges;
@@ -471,10 +490,25 @@ tms_status tms_state_create(tms_trie* trie, int32_t B, int32_t k, const void* em
 }
 
 // Carries out a pending reset before another call reads or writes the state.
+// The kind of reset a pending reset takes.
+static int reset_kind(const tms_state* st) {
+  if (!st->reset_pending) return tms::kResetNone;
+  return st->live_by_paths && st->trie->dev.ent_path ? tms::kResetPaths : tms::kResetFull;
+}
+
+// A pending reset was enqueued: afterwards the live rows follow the stored
+// entries again.
+static void reset_enqueued(tms_state* st) {
+  st->reset_pending = false;
+  st->live_by_paths = true;
+}
+
+// Carries out a pending reset before another call reads or writes the state.
 static tms_status flush_reset(tms_state* st, void* stream) {
   if (!st->reset_pending) return TMS_OK;
-  TMS_HIP(tms::launch_reset(st->trie->dev, st->dev, static_cast<hipStream_t>(stream)), "reset launch");
-  st->reset_pending = false;
+  TMS_HIP(tms::launch_reset(st->trie->dev, st->dev, reset_kind(st), static_cast<hipStream_t>(stream)),
+          "reset launch");
+  reset_enqueued(st);
   return TMS_OK;
 }
 
@@ -589,7 +623,8 @@ tms_status tms_decode_k_pointers(tms_state* st, const void* hidden_seq, int32_t 
     io.tokens_bt = tokens;
     io.len = len;
     io.entries = entries;
-    io.reset = st->reset_pending ? 1 : 0;  // the kernel resets its sequence first
+    const bool fresh = st->reset_pending;  // every sequence starts at the root
+    io.reset = reset_kind(st);             // the kernel resets its sequence first
     // LDS budget per workgroup for the loop's on-chip copy (the part offers
     // 160 KiB; a little is left for the kernel's own shared variables)
     const size_t budget = 160 * 1024 - 2048;
@@ -619,17 +654,17 @@ tms_status tms_decode_k_pointers(tms_state* st, const void* hidden_seq, int32_t 
       // after a grouped root step a phase reads few live counts: keep them
       // in device memory rather than copying them through LDS every phase
       if (mode == tms::kLoopVectorLds) mode = tms::kLoopVectorGlobal;
-      const bool fresh = st->reset_pending;  // every sequence starts at the root
+      const int reset = io.reset;
       const int phases = fresh ? st->k : st->k + 1;
       for (int p = 0; p < phases; ++p) {
-        io.reset = p == 0 && fresh ? 1 : 0;
+        io.reset = p == 0 ? reset : tms::kResetNone;
         io.flags = (p > 0 ? tms::kLoopLater : 0) | (p + 1 < phases ? tms::kLoopExitAtRoot : 0) | tms::kLoopRootKey;
         io.root_tiles = tms::root_head_tiles(st->dtype, st->H, root_edges);
         TMS_HIP(tms::launch_root_head(st->trie->dev, st->dev, io, st->dtype, root_edges, s), "root head launch");
         TMS_HIP(tms::launch_loop(st->trie->dev, st->dev, io, st->dtype, mode, s), "loop launch");
       }
     }
-    st->reset_pending = false;
+    if (fresh) reset_enqueued(st);
     return TMS_OK;
   }
   TMS_FLUSH_RESET(st, stream);
@@ -734,6 +769,7 @@ tms_status tms_debug_set_live(tms_state* st, int32_t s, int32_t edge, int32_t va
     return fail(TMS_ERR_INVALID_ARG, "sequence or edge out of range");
   TMS_FLUSH_RESET(st, stream);
   st->live_dirty = true;
+  st->live_by_paths = false;
   TMS_HIP(tms::launch_set_live(st->trie->dev, st->dev, s, edge, value, static_cast<hipStream_t>(stream)),
           "set live launch");
   return TMS_OK;

@@ -45,6 +45,11 @@ struct DevTrie {
   // Bitmask no-repeat state (catalogs of at most 128 entries, else null): for
   // each edge the set of entries below it, 4 words, bit j = entry j.
   const uint32_t* emask;    // [n_edges][4]
+  // Root path of every entry (its content edges from the root to its terminal,
+  // in order): entry j's edges are ent_path[ent_off[j] .. ent_off[j+1]).  Null
+  // when the catalog's tokens do not fit int32 offsets.
+  const int32_t* ent_off;   // [n_entries + 1]
+  const int32_t* ent_path;  // [ent_off[n_entries]]
   // erec, cent, run, run_edge, run_tok and emask (when present) are laid out
   // back to back from erec (each part a multiple of 16 bytes): image_words
   // int32 words in all
@@ -96,7 +101,7 @@ struct LoopIO {
   int32_t* tokens_bt;      // [B][T]
   int32_t* len;            // [B] or null
   int32_t* entries;        // [B][k] or null
-  int32_t reset;           // 1: reset each sequence's state before the first step
+  int32_t reset;           // kReset*: reset each sequence's state before the first step
   int32_t flags;           // kLoop* bits (phased runs of the resident loop)
   int32_t root_tiles;      // row tiles written by the last grouped root head (kLoopRootKey)
 };
@@ -108,8 +113,14 @@ struct LoopIO {
 // root step of every sequence standing at the root was computed into key[s].
 enum { kLoopLater = 1, kLoopExitAtRoot = 2, kLoopRootKey = 4 };
 
+// Reset kinds.  kResetFull copies every live count from live0; kResetPaths
+// relies on the stored live counts differing from live0 only on the root
+// paths of the stored completed entries (what completions release), and
+// restores just those edges and the entries' spent words.
+enum { kResetNone = 0, kResetFull = 1, kResetPaths = 2 };
+
 // dtype: 0 fp32, 1 bf16.  Every launcher returns hipGetLastError().
-hipError_t launch_reset(const DevTrie& tr, const DevState& st, hipStream_t s);
+hipError_t launch_reset(const DevTrie& tr, const DevState& st, int kind, hipStream_t s);
 hipError_t launch_step_sparse(const DevTrie& tr, const DevState& st, const StepIO& io, int dtype,
                               bool fast, int split, hipStream_t s);
 // Variants of the resident loop: trie, live counts and spent bits in LDS

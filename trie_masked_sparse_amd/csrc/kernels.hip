@@ -637,6 +637,29 @@ __host__ __device__ inline LoopLds loop_lds_layout(const DevTrie& tr, const DevS
   return o;
 }
 
+// Reset of sequence s by its completed entries (kResetPaths): each completion
+// took one live count off every edge of the entry's root path and set the
+// entry's spent bit, so giving those edges their live0 counts back and
+// clearing those spent words restores the initial state.  An edge on several
+// paths gets the same value from each writer.  Wavefront wv of nw.  The
+// caller orders these stores before anything reads the counts or clears the
+// stored entries.
+__device__ __forceinline__ void restore_paths(const DevTrie& tr, const DevState& st, int s, int32_t* g_live,
+                                              uint32_t* g_spent, int wv, int nw, int lane) {
+  const int32_t* ent = st.entries + (int64_t)s * st.k;
+  const int od = min(max(st.done[s], 0), st.k);
+  for (int j = wv; j < od; j += nw) {
+    const int x = __builtin_amdgcn_readfirstlane(ent[j]);
+    if (x < 0 || x >= tr.n_entries) continue;
+    const int p1 = tr.ent_off[x + 1];
+    for (int p = tr.ent_off[x] + lane; p < p1; p += kWave) {
+      const int e = tr.ent_path[p];
+      g_live[e] = tr.live0[e];
+    }
+    if (lane == 0) g_spent[x >> 5] = 0u;
+  }
+}
+
 // Two blocks of n0 and n1 int32 words from device memory into LDS as
 // 16-byte moves, every load of a round issued before its stores (the device
 // buffers are padded to 256 bytes and the LDS parts to 4 words).
@@ -722,6 +745,9 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
                  reinterpret_cast<const int32_t*>(tr.erec), TRIE_LDS ? tr.image_words : 0);
     if (!sreg_ok)
       for (int i = threadIdx.x; i < st.spent_words; i += kLoopBlock) spent[i] = rst ? 0u : g_spent[i];
+  } else if (io.reset == kResetPaths) {
+    restore_paths(tr, st, s, g_live, g_spent, wv, W, lane);
+    __syncthreads();  // the stored entries are read before they are cleared below
   } else if (rst) {
     for (int i = threadIdx.x; i < (int)(ls / 4); i += kLoopBlock)
       reinterpret_cast<int4*>(g_live)[i] = reinterpret_cast<const int4*>(tr.live0)[i];
@@ -1732,15 +1758,22 @@ __global__ __launch_bounds__(kBlock) void gather_gemv_kernel(const uint4* __rest
 // State maintenance
 // ---------------------------------------------------------------------------
 
-// grid (x, B): row s = blockIdx.y; live row copied from live0 with 16-byte stores.
-__global__ __launch_bounds__(kBlock) void reset_kernel(DevTrie tr, DevState st) {
+// grid (x, B): row s = blockIdx.y.  kResetFull: live row copied from live0
+// with 16-byte stores, spent row cleared; kResetPaths (grid x = 1): only the
+// root paths of the stored entries.
+__global__ __launch_bounds__(kBlock) void reset_kernel(DevTrie tr, DevState st, int kind) {
   const int s = blockIdx.y;
-  const int q4 = tr.live_stride / 4;
-  const int4* src = (const int4*)tr.live0;
-  int4* dst = (int4*)(st.live + (int64_t)s * tr.live_stride);
-  for (int i = blockIdx.x * kBlock + threadIdx.x; i < q4; i += gridDim.x * kBlock) dst[i] = src[i];
   uint32_t* sp = st.spent + (int64_t)s * st.spent_words;
-  for (int i = blockIdx.x * kBlock + threadIdx.x; i < st.spent_words; i += gridDim.x * kBlock) sp[i] = 0u;
+  if (kind == kResetPaths) {
+    restore_paths(tr, st, s, st.live + (int64_t)s * tr.live_stride, sp, wave_id(), kWavesPerBlock, __lane_id());
+    __syncthreads();  // the stored entries are read before they are cleared below
+  } else {
+    const int q4 = tr.live_stride / 4;
+    const int4* src = (const int4*)tr.live0;
+    int4* dst = (int4*)(st.live + (int64_t)s * tr.live_stride);
+    for (int i = blockIdx.x * kBlock + threadIdx.x; i < q4; i += gridDim.x * kBlock) dst[i] = src[i];
+    for (int i = blockIdx.x * kBlock + threadIdx.x; i < st.spent_words; i += gridDim.x * kBlock) sp[i] = 0u;
+  }
   if (blockIdx.x == 0) {
     for (int i = threadIdx.x; i < st.k; i += kBlock) st.entries[(int64_t)s * st.k + i] = -1;
     if (threadIdx.x == 0) {
@@ -1856,11 +1889,11 @@ int chunks_for(int dtype, int H) {
   return 0;
 }
 
-hipError_t launch_reset(const DevTrie& tr, const DevState& st, hipStream_t s) {
+hipError_t launch_reset(const DevTrie& tr, const DevState& st, int kind, hipStream_t s) {
   const int q4 = tr.live_stride / 4;
   int gx = (q4 + kBlock * 8 - 1) / (kBlock * 8);
-  gx = gx < 1 ? 1 : (gx > 256 ? 256 : gx);
-  hipLaunchKernelGGL(reset_kernel, dim3(gx, st.B), dim3(kBlock), 0, s, tr, st);
+  gx = kind == kResetPaths || gx < 1 ? 1 : (gx > 256 ? 256 : gx);
+  hipLaunchKernelGGL(reset_kernel, dim3(gx, st.B), dim3(kBlock), 0, s, tr, st, kind);
   return hipGetLastError();
 }
 
