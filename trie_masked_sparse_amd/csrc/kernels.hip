@@ -569,37 +569,79 @@ __global__ __launch_bounds__(kBlock) void step_sparse_kernel(DevTrie tr, DevStat
   }
 }
 
-// A forced step (sections "Masked sampling inside the sampler" and "The
-// sparse output layer": with a single legal token the argmax over the legal
-// set is that token whatever the logits).  Returns the node's one legal edge
-// when the node has at most 64 edges and exactly one of them is legal, else
-// -1 (more than one, none, or a node too wide to check in one pass: the full
-// step handles those, including the empty-mask error).  Every wavefront of
-// the resident loop evaluates it from the same state, so all of them take the
-// same branch without a barrier.
+// The edges of a node of at most 64 edges, one lane per edge (lane i: edge
+// b0+i; lanes past the range hold a record that matches no edge kind), and
+// the ballot of the legal ones.  Every wavefront of the resident loop loads
+// the same copy, so all of them take the same decisions from it without a
+// barrier.
+struct NodeLanes {
+  EdgeRec r;
+  int lv, ce, rn;
+  unsigned long long m;  // bit i: edge b0+i is legal
+};
+
 template <bool MASK>
-__device__ __forceinline__ int forced_edge(const TrieView& tv, const int32_t* live, const Seq& q, int lane,
-                                           Cand& c, const Ban& ban) {
+__device__ __forceinline__ NodeLanes node_lanes(const TrieView& tv, const int32_t* live, const Seq& q, int lane,
+                                                const Ban& ban) {
   const int f = q.b1 - q.b0;
-  if (f > kWave) return -1;
   const int e = q.b0 + lane;
-  EdgeRec r{kChildSep - 8, 0, 0, 0};  // lanes past the range: matches no edge kind
-  int lv = 0, ce = -1, rn = 0;
+  NodeLanes n{EdgeRec{kChildSep - 8, 0, 0, 0}, 0, -1, 0, 0ull};
   if (lane < f) {
-    r = tv.erec[e];
+    n.r = tv.erec[e];
     // read for every edge (in range of the live array), used for content edges
-    if constexpr (MASK) lv = mask_live(reinterpret_cast<const uint4*>(live)[e], ban) ? 1 : 0;
-    else lv = live[e];
-    ce = tv.cent[e];
-    rn = tv.run[e];
+    if constexpr (MASK) n.lv = mask_live(reinterpret_cast<const uint4*>(live)[e], ban) ? 1 : 0;
+    else n.lv = live[e];
+    n.ce = tv.cent[e];
+    n.rn = tv.run[e];
   }
-  const unsigned long long m = __ballot(edge_ok_bits(r.child, lv, q));
-  if (__popcll(m) != 1) return -1;
-  const int w = (int)__builtin_ctzll(m);
-  c = Cand{__builtin_amdgcn_readlane(r.child, w), __builtin_amdgcn_readlane(r.tok, w),
-           __builtin_amdgcn_readlane(r.b0, w), __builtin_amdgcn_readlane(r.b1, w), __builtin_amdgcn_readlane(ce, w),
-           __builtin_amdgcn_readlane(rn, w)};
-  return q.b0 + w;
+  n.m = __ballot(edge_ok_bits(n.r.child, n.lv, q));
+  return n;
+}
+
+__device__ __forceinline__ Cand lane_cand(const NodeLanes& n, int w) {
+  return Cand{__builtin_amdgcn_readlane(n.r.child, w), __builtin_amdgcn_readlane(n.r.tok, w),
+              __builtin_amdgcn_readlane(n.r.b0, w),    __builtin_amdgcn_readlane(n.r.b1, w),
+              __builtin_amdgcn_readlane(n.ce, w),      __builtin_amdgcn_readlane(n.rn, w)};
+}
+
+// Head scan of a node held as NodeLanes (sections "The sparse output layer"
+// and "The batched engine": logits of the legal edges only): wavefront wv
+// takes lanes wv, wv+W, ..., U per pass, and requests their rows straight
+// from the lanes' records, with no second read of records or live counts.
+// Same keys as scan_node, so the winner does not depend on which scan ran.
+template <int DT, int NC, bool CAND>
+__device__ __forceinline__ unsigned long long scan_lanes(const Seq& q, const NodeLanes& n,
+                                                         const uint4* __restrict__ emb, int nq,
+                                                         const uint4 (&hq)[NC], int wv, int W, int lane,
+                                                         Cand& cand) {
+  constexpr int U = rows_per_pass(NC);
+  const int f = q.b1 - q.b0;
+  unsigned long long best = 0;
+  for (int j0 = wv; j0 < f; j0 += U * W) {
+    int rows[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * W;
+      const bool ok = j < f && ((n.m >> (j & 63)) & 1ull);
+      rows[u] = ok ? __builtin_amdgcn_readlane(n.r.tok, j & 63) : -1;
+    }
+    uint4 raw[U][NC];
+    issue_rows<NC, U>(emb, nq, rows, raw, lane);
+    float l[U];
+    finish_rows<DT, NC, U>(nq, rows, raw, hq, l, lane);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (rows[u] < 0) continue;
+      const int j = j0 + u * W;
+      const uint32_t e = (uint32_t)(q.b0 + j);
+      const unsigned long long k = CAND ? pack_key_wave(l[u], e, wv) : pack_key(l[u], e);
+      if (k > best) {
+        best = k;
+        if constexpr (CAND) cand = lane_cand(n, j);
+      }
+    }
+  }
+  return best;
 }
 
 // ---------------------------------------------------------------------------
@@ -961,14 +1003,22 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
     q.b1 = rec.b1;
     q.sep_ok = sep_ok;
     q.stop_ok = stop_ok;
-    Cand fc;
-    const int fe = forced_edge<MASK>(tv, lsrc, q, lane, fc, ban);
-    if (fe >= 0) {
-      // forced: no rows, no reduction and no barrier unless a pointer
-      // completes (forced steps have no barrier of their own, so a release
-      // first waits for every wavefront)
-      take(fe, fc, true);
-      continue;
+    // A node of at most 64 edges is loaded once, one lane per edge: with a
+    // single legal edge the step is forced (sections "Masked sampling inside
+    // the sampler" and "The sparse output layer": the argmax over one legal
+    // token is that token whatever the logits) and takes no rows, no
+    // reduction and no barrier unless a pointer completes (forced steps have
+    // no barrier of their own, so a release first waits for every
+    // wavefront); otherwise the head scan starts from the same lanes.
+    const bool narrow = q.b1 - q.b0 <= kWave;
+    NodeLanes nl{};
+    if (narrow) {
+      nl = node_lanes<MASK>(tv, lsrc, q, lane, ban);
+      if (__popcll(nl.m) == 1) {
+        const int w = (int)__builtin_ctzll(nl.m);
+        take(q.b0 + w, lane_cand(nl, w), true);
+        continue;
+      }
     }
     // this step's hidden vector, requested before the edge records and rows:
     // it arrives alongside them (a copy carried from earlier steps would have
@@ -978,8 +1028,9 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
     const int slot = nhead % 3;
     if (threadIdx.x == 0) s_key[(nhead + 1) % 3] = 0ull;  // the next head step's slot
     Cand cand{0, 0, 0, 0, 0, 0};
-    const unsigned long long best = scan_node<DT, NC, META, LIVE_KIND, PAYLOAD>(
-        tr, tv, q, lsrc, emb, nq, hq, wv, W, lane, cand, ban);
+    const unsigned long long best =
+        narrow ? scan_lanes<DT, NC, PAYLOAD>(q, nl, emb, nq, hq, wv, W, lane, cand)
+               : scan_node<DT, NC, META, LIVE_KIND, PAYLOAD>(tr, tv, q, lsrc, emb, nq, hq, wv, W, lane, cand, ban);
     if (lane == 0) {
       if (best) __hip_atomic_fetch_max(&s_key[slot], best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       if constexpr (PAYLOAD) s_cand[nhead & 1][wv] = cand;
