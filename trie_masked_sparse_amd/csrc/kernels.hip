@@ -656,6 +656,24 @@ __device__ __forceinline__ unsigned long long scan_lanes(const Seq& q, const Nod
 // they stay in device memory.
 // ---------------------------------------------------------------------------
 constexpr int kLoopBlock = 512;
+
+// A 64-bit uniform value parked in lanes 2I and 2I+1 of a vector register
+// while the resident loop runs, and read back after it: values used only
+// before and after the loop then leave the scalar registers to the loop's
+// own state (which otherwise gets spilled inside the loop).
+template <int I>
+__device__ __forceinline__ void park64(int& reg, const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  asm volatile("s_nop 4\n\tv_writelane_b32 %0, %1, %2" : "+v"(reg) : "s"(lo), "n"(2 * I));
+  asm volatile("s_nop 4\n\tv_writelane_b32 %0, %1, %2" : "+v"(reg) : "s"(hi), "n"(2 * I + 1));
+}
+template <typename T, int I>
+__device__ __forceinline__ T* unpark64(int reg) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane(reg, 2 * I);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane(reg, 2 * I + 1);
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
 constexpr int kLoopWaves = kLoopBlock / kWave;
 
 // LDS layout of the resident loop (in int32 words, each part a multiple of 4):
@@ -848,6 +866,20 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
     if (lane == 0) s_pre_key = m;
   }
   __syncthreads();  // also orders the reset's stores before their first reads
+  int parked = 0;
+  park64<0>(parked, path);
+  park64<1>(parked, entries);
+  park64<2>(parked, g_spent);
+  park64<3>(parked, g_live);
+  park64<4>(parked, st.tstep + s);
+  park64<5>(parked, st.node + s);
+  park64<6>(parked, st.depth + s);
+  park64<7>(parked, st.done + s);
+  park64<8>(parked, st.status + s);
+  park64<9>(parked, st.finished + s);
+  park64<10>(parked, st.nemit + s);
+  park64<11>(parked, io.len ? io.len + s : nullptr);
+  park64<12>(parked, io.entries ? io.entries + (int64_t)s * st.k : nullptr);
   auto is_spent = [&](int ent) -> bool {
     const uint32_t w = sreg_ok ? (uint32_t)__builtin_amdgcn_readlane((int)sreg, ent >> 5)
                                : (uint32_t)__builtin_amdgcn_readfirstlane(spent[ent >> 5]);
@@ -1058,31 +1090,39 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
       take(e, c, false);
     }
   }
-  if (wv == 0) {
-    if (reg_lists) {
-      if (lane < depth) path[lane] = my_path;
-      if (lane < done) entries[lane] = my_ent;
+  {
+    int32_t* const p_path = unpark64<int32_t, 0>(parked);
+    int32_t* const p_entries = unpark64<int32_t, 1>(parked);
+    uint32_t* const p_spent = unpark64<uint32_t, 2>(parked);
+    if (wv == 0) {
+      if (reg_lists) {
+        if (lane < depth) p_path[lane] = my_path;
+        if (lane < done) p_entries[lane] = my_ent;
+      }
+      if (sreg_ok && lane < st.spent_words) p_spent[lane] = sreg;
     }
-    if (sreg_ok && lane < st.spent_words) g_spent[lane] = sreg;
+    if (!exit_root) {
+      for (int i = t + threadIdx.x; i < io.T; i += kLoopBlock) tokens[i] = -1;
+      if (status == kSeqOk && !fin) status = kSeqNotDone;
+    }
+    if (threadIdx.x == 0) {
+      *unpark64<int32_t, 4>(parked) = t;
+      *unpark64<int32_t, 5>(parked) = node;
+      *unpark64<int32_t, 6>(parked) = depth;
+      *unpark64<int32_t, 7>(parked) = done;
+      *unpark64<int32_t, 8>(parked) = status;
+      *unpark64<int32_t, 9>(parked) = fin;
+      *unpark64<int32_t, 10>(parked) = nemit;
+      int32_t* const p_len = unpark64<int32_t, 11>(parked);
+      if (p_len) *p_len = nemit;
+    }
+    int32_t* const p_out = unpark64<int32_t, 12>(parked);
+    if (wv == 0 && p_out) {
+      for (int j = lane; j < st.k; j += kWave)
+        p_out[j] = (reg_lists && j < kWave) ? (j < done ? my_ent : p_entries[j]) : p_entries[j];
+    }
   }
-  if (!exit_root) {
-    for (int i = t + threadIdx.x; i < io.T; i += kLoopBlock) tokens[i] = -1;
-    if (status == kSeqOk && !fin) status = kSeqNotDone;
-  }
-  if (threadIdx.x == 0) {
-    st.tstep[s] = t;
-    st.node[s] = node;
-    st.depth[s] = depth;
-    st.done[s] = done;
-    st.status[s] = status;
-    st.finished[s] = fin;
-    st.nemit[s] = nemit;
-    if (io.len) io.len[s] = nemit;
-  }
-  if (wv == 0 && io.entries) {
-    for (int j = lane; j < st.k; j += kWave)
-      io.entries[(int64_t)s * st.k + j] = (reg_lists && j < kWave) ? (j < done ? my_ent : entries[j]) : entries[j];
-  }
+  int32_t* const g_live_out = unpark64<int32_t, 3>(parked);
   if constexpr (MASK) {
     // live counts from the masks: entries below each edge not yet spent
     const uint4* em = reinterpret_cast<const uint4*>(lds + lay.emask);
@@ -1092,11 +1132,11 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
         const uint4 m = em[e];
         c = __popc(m.x & ~ban.w0) + __popc(m.y & ~ban.w1) + __popc(m.z & ~ban.w2) + __popc(m.w & ~ban.w3);
       }
-      g_live[e] = c;
+      g_live_out[e] = c;
     }
   } else if constexpr (LDS_LIVE) {
     __syncthreads();
-    int4* dst = reinterpret_cast<int4*>(g_live);
+    int4* dst = reinterpret_cast<int4*>(g_live_out);
     for (int i = threadIdx.x; i < (int)(ls / 4); i += kLoopBlock) dst[i] = reinterpret_cast<const int4*>(live)[i];
     if (!sreg_ok)
       for (int i = threadIdx.x; i < st.spent_words; i += kLoopBlock) g_spent[i] = spent[i];
