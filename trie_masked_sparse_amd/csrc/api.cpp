@@ -258,12 +258,27 @@ tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_
   // one copy loop brings them on chip
   const size_t w_erec = 0, w_cent = w_erec + 4 * size_t(h.n_edges), w_run = w_cent + live_stride,
                w_run_edge = w_run + live_stride, w_run_tok = w_run_edge + ((n_run + 3) & ~3),
-               w_emask = w_run_tok + ((n_run + 3) & ~3), w_image = w_emask + emask.size();
+               w_run_land = w_run_tok + ((n_run + 3) & ~3), w_emask = w_run_land + 4 * size_t(n_run),
+               w_image = w_emask + emask.size();
   const size_t o_image = c.take<int32_t>(w_image);
   const size_t o_erec = o_image + 4 * w_erec, o_cent = o_image + 4 * w_cent, o_run = o_image + 4 * w_run,
                o_run_edge = o_image + 4 * w_run_edge, o_run_tok = o_image + 4 * w_run_tok,
+               o_run_land = o_image + 4 * w_run_land,
                o_emask = o_image + 4 * w_emask;
   const size_t o_ent_off = c.take<int32_t>(ent_off.size()), o_ent_path = c.take<int32_t>(ent_path.size());
+  // where each run position lands: the child of run_edge[p] and its record
+  std::vector<int32_t> run_land(4 * size_t(n_run), 0);
+  for (int32_t p = 0; p < n_run; ++p) {
+    const int32_t ch = h.child[run_edge[p]];
+    run_land[4 * size_t(p)] = ch;
+    if (ch >= 0) {
+      run_land[4 * size_t(p) + 1] = h.begin[ch];
+      run_land[4 * size_t(p) + 2] = h.begin[ch + 1];
+      run_land[4 * size_t(p) + 3] = h.entry[ch];
+    } else {
+      run_land[4 * size_t(p) + 3] = -1;
+    }
+  }
   run_edge.resize((n_run + 3) & ~3, 0);
   run_tok.resize((n_run + 3) & ~3, 0);
   hipError_t e = hipGetDevice(&t->device);
@@ -308,6 +323,8 @@ tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_
     e = hipMemcpyAsync(base + o_run_edge, run_edge.data(), 4 * run_edge.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess && !run_tok.empty())
     e = hipMemcpyAsync(base + o_run_tok, run_tok.data(), 4 * run_tok.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && !run_land.empty())
+    e = hipMemcpyAsync(base + o_run_land, run_land.data(), 4 * run_land.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess && with_mask)
     e = hipMemcpyAsync(base + o_emask, emask.data(), 4 * emask.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess && with_paths)
@@ -332,6 +349,7 @@ tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_
   d.run = reinterpret_cast<const int32_t*>(base + o_run);
   d.run_edge = reinterpret_cast<const int32_t*>(base + o_run_edge);
   d.run_tok = reinterpret_cast<const int32_t*>(base + o_run_tok);
+  d.run_land = reinterpret_cast<const int4*>(base + o_run_land);
   d.image_words = static_cast<int32_t>(w_image);
   d.emask = with_mask ? reinterpret_cast<const uint32_t*>(base + o_emask) : nullptr;
   d.ent_off = with_paths ? reinterpret_cast<const int32_t*>(base + o_ent_off) : nullptr;

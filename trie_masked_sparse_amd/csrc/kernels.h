@@ -41,6 +41,9 @@ struct DevTrie {
   const int32_t* run;       // [live_stride]
   const int32_t* run_edge;  // [n_run]
   const int32_t* run_tok;   // [n_run]
+  // Where a run ends: for run position p, {child, child's first edge, child's
+  // end edge, entry at the child} of run_edge[p] (one read lands a whole run).
+  const int4* run_land;     // [n_run]
   int32_t n_run;            // nodes with a single edge
   // Bitmask no-repeat state (catalogs of at most 128 entries, else null): for
   // each edge the set of entries below it, 4 words, bit j = entry j.
@@ -50,7 +53,7 @@ struct DevTrie {
   // when the catalog's tokens do not fit int32 offsets.
   const int32_t* ent_off;   // [n_entries + 1]
   const int32_t* ent_path;  // [ent_off[n_entries]]
-  // erec, cent, run, run_edge, run_tok and emask (when present) are laid out
+  // erec, cent, run, run_edge, run_tok, run_land and emask (when present) are laid out
   // back to back from erec (each part a multiple of 16 bytes): image_words
   // int32 words in all
   int32_t image_words;

@@ -351,6 +351,7 @@ struct TrieView {
   const int32_t* run;
   const int32_t* run_edge;
   const int32_t* run_tok;
+  const int4* run_land;
 };
 
 // A wave-uniform edge record: scalar loads (kMetaScalar) or one 16-byte read
@@ -535,7 +536,7 @@ __global__ __launch_bounds__(kBlock) void step_sparse_kernel(DevTrie tr, DevStat
   load_hidden<NC>((const uint4*)io.hidden + (int64_t)s * nq, nq, hq, lane);
   const int32_t* live = st.live + (int64_t)s * tr.live_stride;
   Cand unused;
-  const TrieView tv{tr.erec, tr.cent, tr.run, tr.run_edge, tr.run_tok};
+  const TrieView tv{tr.erec, tr.cent, tr.run, tr.run_edge, tr.run_tok, tr.run_land};
   const unsigned long long best = scan_node<DT, NC, FAST ? kMetaScalar : kMetaVector, kLiveScalar, false>(
       tr, tv, q, live, (const uint4*)io.emb, nq, hq, wv, W, lane, unused);
 
@@ -680,7 +681,7 @@ constexpr int kLoopWaves = kLoopBlock / kWave;
 // live counts, spent bits and, with the trie in LDS, edge records, the
 // entries of the edges' children and the forced-run tables.
 struct LoopLds {
-  int live, spent, erec, cent, run, run_edge, run_tok, emask, total;
+  int live, spent, erec, cent, run, run_edge, run_tok, land, emask, total;
 };
 __host__ __device__ inline int round4(int n) { return (n + 3) & ~3; }
 __host__ __device__ inline LoopLds loop_lds_layout(const DevTrie& tr, const DevState& st, bool trie) {
@@ -692,7 +693,8 @@ __host__ __device__ inline LoopLds loop_lds_layout(const DevTrie& tr, const DevS
   o.run = o.cent + (trie ? tr.live_stride : 0);
   o.run_edge = o.run + (trie ? tr.live_stride : 0);
   o.run_tok = o.run_edge + (trie ? round4(tr.n_run) : 0);
-  o.emask = o.run_tok + (trie ? round4(tr.n_run) : 0);
+  o.land = o.run_tok + (trie ? round4(tr.n_run) : 0);
+  o.emask = o.land + (trie ? 4 * tr.n_run : 0);
   o.total = o.emask + (trie && tr.emask ? 4 * tr.n_edges : 0);
   return o;
 }
@@ -798,7 +800,7 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
   __shared__ unsigned long long s_pre_key;
   uint32_t sreg = 0u;
   if (sreg_ok && lane < st.spent_words && !rst) sreg = g_spent[lane];
-  TrieView tv{tr.erec, tr.cent, tr.run, tr.run_edge, tr.run_tok};
+  TrieView tv{tr.erec, tr.cent, tr.run, tr.run_edge, tr.run_tok, tr.run_land};
   if constexpr (LDS_LIVE) {
     // live counts, and the trie image when it is kept in LDS
     copy2_to_lds(lds + lay.live, rst ? tr.live0 : g_live, MASK ? 0 : (int)ls, lds + lay.erec,
@@ -816,7 +818,7 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
   }
   if constexpr (TRIE_LDS) {
     tv = TrieView{reinterpret_cast<const EdgeRec*>(lds + lay.erec), lds + lay.cent, lds + lay.run,
-                  lds + lay.run_edge, lds + lay.run_tok};
+                  lds + lay.run_edge, lds + lay.run_tok, reinterpret_cast<const int4*>(lds + lay.land)};
   }
   int node = 0, depth = 0, done = 0, status = kSeqOk, fin = 0, nemit = 0;
   if (!rst) {
@@ -981,16 +983,26 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // read back by this wavefront
           }
         }
-        const int el = __builtin_amdgcn_readfirstlane(tv.run_edge[ra + L - 1]);
-        const EdgeRec r = tv.erec[el];
-        const int ce = __builtin_amdgcn_readfirstlane(tv.cent[el]);
-        const int rn = __builtin_amdgcn_readfirstlane(tv.run[el]);
-        node = __builtin_amdgcn_readfirstlane(r.child);
-        rec = NodeRec{__builtin_amdgcn_readfirstlane(r.b0), __builtin_amdgcn_readfirstlane(r.b1), ce, 0};
+        if (L == rl && rl < 64) {
+          // the whole run, and it ends the chain (a run of 64 may continue):
+          // land on the child of its last edge in one read
+          const int4 d = tv.run_land[ra + rl - 1];
+          node = __builtin_amdgcn_readfirstlane(d.x);
+          rec = NodeRec{__builtin_amdgcn_readfirstlane(d.y), __builtin_amdgcn_readfirstlane(d.z),
+                        __builtin_amdgcn_readfirstlane(d.w), 0};
+          ri = 0;
+        } else {
+          const int el = __builtin_amdgcn_readfirstlane(tv.run_edge[ra + L - 1]);
+          const EdgeRec r = tv.erec[el];
+          const int ce = __builtin_amdgcn_readfirstlane(tv.cent[el]);
+          const int rn = __builtin_amdgcn_readfirstlane(tv.run[el]);
+          node = __builtin_amdgcn_readfirstlane(r.child);
+          rec = NodeRec{__builtin_amdgcn_readfirstlane(r.b0), __builtin_amdgcn_readfirstlane(r.b1), ce, 0};
+          ri = L == rl ? rn : 0;
+        }
         depth += L;
         t += L;
         nemit += L;
-        ri = L == rl ? rn : 0;
       }
       if (rec.ent >= 0 && rec.b1 - rec.b0 == 2 && t + 1 < io.T && !is_spent(rec.ent)) {
         t += 1;
