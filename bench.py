@@ -394,21 +394,25 @@ def cpu_baseline_threads(w: Workload, seq_sample=None):
     return {"seconds_1_thread": one, "seconds_n_threads": many, "threads": n, "sequences": int(hid.shape[1])}
 
 
-def config_table(steps: int, warmup: int):
+def config_table(steps: int, warmup: int, cids=("tiny", "product", "product_deep", "structured", "unstructured",
+                                                 "large")):
     """Every workload: the resident decode's steps/s and tokens/s, gathered
     bytes per second, the dense+mask step, and the oracle's time for the
     same batch (the results table of the bench's plan)."""
     import numpy as np
     out = {}
-    for cid in ("tiny", "product", "product_deep", "structured", "unstructured", "large"):
+    for cid in cids:
         _log(f"table: {cid}")
         w = Workload(cid)
         r = time_decode(w, steps, warmup)
-        n_rows, n_act, _ = w.legal_profile()
+        n_rows, n_act, n_uniq = w.legal_profile()
         gathered = float(((n_rows + n_act) * w.c.hidden * w.esz).sum())
+        unique = float(((n_uniq + n_act) * w.c.hidden * w.esz).sum())
         sample = None if w.B <= 64 else list(range(0, w.B, w.B // 24))[:24]
         row = {"B": w.B, "steps_per_s": r["steps_per_s"], "tokens_per_s": r["tokens_per_s"],
                "ms_per_call": r["ms_per_call"], "gathered_TBps": gathered / (r["gpu_ms"] * 1e-3 / steps) / 1e12,
+               "unique_TBps": unique / (r["gpu_ms"] * 1e-3 / steps) / 1e12,
+               "gathered_bytes_per_call": gathered, "unique_bytes_per_call": unique,
                "dense_mask_step_us": dense_step_us(w)["us_per_step"],
                "oracle": cpu_baseline_threads(w, sample)}
         out[cid] = row
@@ -436,6 +440,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--configs", default="tiny,product,product_deep,structured,unstructured,large",
+                    help="workloads of the --only configs table")
     ap.add_argument("--only", default="",
                     help="comma list of headline,b64,stress,dense,cpu,copyref,configs (default: all but copyref, configs)")
     args = ap.parse_args()
@@ -519,7 +525,7 @@ def main():
             _log(f"{cid} {also[f'{cid}_B64']['steps_per_s']:.0f} steps/s")
             wb.close()
     if args.only and "configs" in args.only.split(","):
-        also["configs"] = config_table(args.steps, args.warmup)
+        also["configs"] = config_table(args.steps, args.warmup, tuple(filter(None, args.configs.split(","))))
     if want("cpu"):
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
         _log(f"cpu {line['cpu_baseline']}")
