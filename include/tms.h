@@ -131,7 +131,12 @@ tms_status tms_state_create(tms_trie* trie, int32_t B, int32_t k, const void* em
  * done, status OK, nothing emitted.  The reset is deferred: the next call on
  * st carries it out on that call's stream before its own work (the resident
  * device loop of tms_decode_k_pointers does it inside its kernel; every other
- * call enqueues a reset kernel first, no memset).  stream is not used. */
+ * call enqueues a reset kernel first, no memset).  stream is not used.
+ * Cost: a completed pointer only ever lowers the live counts on its entry's
+ * root path (section "Masked sampling inside the sampler" of the page above),
+ * so the reset of a decoded state rewrites just those edges from live0 and
+ * clears just those spent words; whole rows are rewritten on a new state and
+ * after tms_debug_set_live. */
 tms_status tms_state_reset(tms_state* st, void* stream);
 
 /* Synchronise stream, copy per-sequence status to host_status [B] (may be
