@@ -1730,6 +1730,130 @@ __global__ __launch_bounds__(kBlock) void dense_mfma_kstream_kernel(DevState st,
   }
 }
 
+// The K-streamed contraction with every load requested two K blocks ahead
+// (B <= 64): table fragments in a ring of three register slots and hidden
+// slices in a ring of two per wavefront.  The K loop is fully unrolled (NKB
+// blocks of KB: H fixed per instantiation), so each slot keeps its role
+// without copies (a copy of a fragment still in flight would wait for it) and
+// every wait counts exactly how many younger loads may stay in flight (loads
+// complete in issue order): the products of block kb wait only for loads
+// issued two blocks earlier.  All MAXT member tiles are computed (missing
+// members are zeros), which keeps the unrolled body free of branches.  Same
+// products and K order as the kernel above, so bit-identical logits.
+template <int MAXT, int T, int KB, int NKB>
+__global__ __launch_bounds__(kBlock) void dense_mfma_kring_kernel(DevState st, StepIO io, float* full_logits,
+                                                                   int ntiles, int nblk) {
+  extern __shared__ uint4 sh[];  // two buffers of [ntiles*16][KS]
+  constexpr int KQ = KB / 8;     // uint4 per staged row
+  constexpr int KS = KQ + 1;     // staged row stride (+1 against bank conflicts)
+  constexpr int KJ = KB / 32;    // matrix-core K steps per block
+  const int lane = __lane_id();
+  const int wv = wave_id();
+  const int V = io.V, H = io.H, B = st.B;
+  const int nq = H / 8;
+  const uint4* emb = (const uint4*)io.emb;
+  const uint4* hid = (const uint4*)io.hidden;
+  constexpr int nseq = MAXT * 16;  // every member tile is computed (missing members are zeros): no branches
+  (void)ntiles;
+  const int bufsz = nseq * KS;
+  constexpr int kRows = 4 * T * 16;
+  constexpr int nkb = NKB;  // H / KB, fixed so that the K loop unrolls fully
+  typedef u32x4_t Frag[T][KJ];
+  constexpr int HV = MAXT * KQ / 16;  // this thread's share of a staged block
+  typedef uint4 Slice[HV];
+  Slice hv0, hv1;  // hidden slices, two blocks in flight
+  auto hload = [&](Slice& hv, int kb) {
+#pragma unroll
+    for (int u = 0; u < HV; ++u) {
+      const int idx = u * kBlock + (int)threadIdx.x;
+      const int sq = idx / KQ, qq = idx % KQ;
+      hv[u] = (idx < nseq * KQ && sq < B) ? hid[(int64_t)sq * nq + kb * KQ + qq] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto hstore = [&](uint4* buf, const Slice& hv) {
+#pragma unroll
+    for (int u = 0; u < HV; ++u) {
+      const int idx = u * kBlock + (int)threadIdx.x;
+      if (idx < nseq * KQ) buf[(idx / KQ) * KS + idx % KQ] = hv[u];
+    }
+  };
+  for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    const int m0 = blk * kRows + wv * (T * 16);
+    const uint4* rp[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) rp[t] = emb + (int64_t)min(m0 + t * 16 + (lane & 15), V - 1) * nq + (lane >> 4);
+    f32x4_t acc[T][MAXT];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int m = 0; m < MAXT; ++m) acc[t][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto fetch = [&](Frag& f, int kb) {
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int j = 0; j < KJ; ++j) f[t][j] = *reinterpret_cast<const u32x4_t*>(rp[t] + kb * KQ + j * 4);
+    };
+    Frag f0, f1, f2;
+    hload(hv0, 0);
+    fetch(f0, 0);
+    if (nkb > 1) {
+      hload(hv1, 1);
+      fetch(f1, 1);
+    }
+    __syncthreads();  // the buffers of the previous row block are consumed
+    hstore(sh, hv0);
+    // block kb: its fragments are in `cur`; the hidden slice of block kb + 2
+    // goes into `hnext` (free: block kb's slice was staged in the previous
+    // step) and its table fragments into `ahead`
+    auto step = [&](const Frag& cur, Frag& ahead, Slice& hnext, const Slice& hstage, int kb) {
+      if (kb + 2 < nkb) {
+        hload(hnext, kb + 2);
+        fetch(ahead, kb + 2);
+      }
+      lds_barrier();  // block kb staged; every wavefront is done with the other buffer
+      const uint4* hb = sh + (kb & 1) * bufsz;
+#pragma unroll
+      for (int j = 0; j < KJ; ++j) {
+#pragma unroll
+        for (int m = 0; m < MAXT; ++m) {
+          const bf16x8_t b = __builtin_bit_cast(bf16x8_t, hb[(m * 16 + (lane & 15)) * KS + j * 4 + (lane >> 4)]);
+#pragma unroll
+          for (int t = 0; t < T; ++t)
+            acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur[t][j]), b, acc[t][m],
+                                                                 0, 0, 0);
+        }
+      }
+      if (kb + 1 < nkb) hstore(sh + ((kb + 1) & 1) * bufsz, hstage);
+    };
+#pragma unroll
+    for (int kb = 0; kb < nkb; ++kb) {
+      const int r = kb % 3;
+      step(r == 0 ? f0 : r == 1 ? f1 : f2, r == 0 ? f2 : r == 1 ? f0 : f1, (kb & 1) ? hv1 : hv0, (kb & 1) ? hv0 : hv1,
+           kb);
+    }
+    // epilogue: tile t, sequence m*16 + lane%16, rows m0 + t*16 + 4*(lane/16) + i
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int r0 = m0 + t * 16 + 4 * (lane >> 4);
+#pragma unroll
+      for (int m = 0; m < MAXT; ++m) {
+        const int sq = m * 16 + (lane & 15);
+        if (sq >= B) continue;
+        const uint32_t word = r0 < V ? st.mask[(int64_t)sq * st.mask_words + (r0 >> 5)] : 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = r0 + i;
+          if (r >= V) continue;
+          const float l = acc[t][m][i];
+          if (full_logits) full_logits[(int64_t)sq * V + r] = l;
+          if ((word >> ((r0 & 31) + i)) & 1u)
+            __hip_atomic_fetch_max(&st.key[sq], pack_key(l, (uint32_t)r), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+  }
+}
+
 // One wavefront per sequence: winner token from the key, its edge, advance.
 __global__ __launch_bounds__(kWave) void dense_advance_kernel(DevTrie tr, DevState st, StepIO io) {
   const int s = blockIdx.x;
@@ -2106,6 +2230,23 @@ hipError_t launch_dense_kstream(const DevState& st, const StepIO& io, float* ful
   return hipGetLastError();
 }
 
+template <int MAXT, int T, int KB, int NKB>
+hipError_t launch_dense_kring(const DevState& st, const StepIO& io, float* full, hipStream_t s) {
+  const int ntiles = (st.B + 15) / 16;
+  const size_t lds = 2 * sizeof(uint4) * (size_t)MAXT * 16 * (KB / 8 + 1);  // double buffer
+  auto* k = &dense_mfma_kring_kernel<MAXT, T, KB, NKB>;
+  static size_t allowed = 65536;
+  if (lds > allowed) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+    allowed = lds;
+  }
+  const int nblk = (io.V + 64 * T - 1) / (64 * T);
+  hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(kBlock), lds, s, st, io, full, ntiles, nblk);
+  return hipGetLastError();
+}
+
 bool dense_uses_mfma(int dtype, int B, int H) { return dtype == 1 && B >= 2 && B <= 256 && H % 32 == 0; }
 
 hipError_t launch_dense_step(const DevTrie& tr, const DevState& st, const StepIO& io, int dtype, float* full,
@@ -2117,7 +2258,11 @@ hipError_t launch_dense_step(const DevTrie& tr, const DevState& st, const StepIO
   if (mfma && dense_uses_mfma(dtype, st.B, io.H)) {
     // one 16-row tile per wavefront keeps many workgroups (2374 at V = 151936)
     // for balance and latency hiding
-    if (io.H % kDenseKB == 0)
+    if (st.B <= 64 && io.H == 16 * kDenseKB)
+      // loads two blocks ahead: 166 -> 136 us at B = 64, H = 2048 (V = 151936);
+      // at H = 4096 the unrolled body needs more than 256 registers
+      err = launch_dense_kring<4, 2, kDenseKB, 16>(st, io, full, s);
+    else if (io.H % kDenseKB == 0)
       // two row tiles per wavefront: measured best (1/2/3/4/8 swept at B = 64)
       err = st.B <= 64 ? launch_dense_kstream<4, 2>(st, io, full, s)
           : st.B <= 128 ? launch_dense_kstream<8, 2>(st, io, full, s)
