@@ -723,10 +723,10 @@ __device__ __forceinline__ void restore_paths(const DevTrie& tr, const DevState&
 }
 
 // Two blocks of n0 and n1 int32 words from device memory into LDS as
-// 16-byte moves, every load of a round issued before its stores (the device
-// buffers are padded to 256 bytes and the LDS parts to 4 words).
-__device__ __forceinline__ void copy2_to_lds(int32_t* d0, const int32_t* s0, int n0, int32_t* d1,
-                                             const int32_t* s1, int n1) {
+// 16-byte moves through registers, every load of a round issued before its
+// stores.
+__device__ __forceinline__ void copy2_regs(int32_t* d0, const int32_t* s0, int n0, int32_t* d1,
+                                           const int32_t* s1, int n1) {
   const int a = (n0 + 3) >> 2, b = (n1 + 3) >> 2;
   const int4* S0 = reinterpret_cast<const int4*>(s0);
   const int4* S1 = reinterpret_cast<const int4*>(s1);
@@ -743,6 +743,38 @@ __device__ __forceinline__ void copy2_to_lds(int32_t* d0, const int32_t* s0, int
     if (i1 < a) D0[i1] = v1;
     if (i0 < b) D1[i0] = v2;
     if (i1 < b) D1[i1] = v3;
+  }
+}
+
+// n int32 words from device memory into LDS with direct loads: each
+// wavefront moves 1 KB per instruction, lane l's 16 bytes landing at byte
+// 16 l of the chunk, with no register round trip and no LDS store
+// instruction (the caller waits for the loads).
+__device__ __forceinline__ void lds_chunks(int32_t* d, const int32_t* s, int n, int wv, int lane) {
+  const int q = (n + 3) >> 2;  // 16-byte units
+  const int4* S = reinterpret_cast<const int4*>(s);
+  for (int c = wv * kWave; c < q; c += kLoopWaves * kWave) {
+    if (c + lane < q)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(S + c + lane),
+                                       reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                           reinterpret_cast<uintptr_t>(d + 4 * c)),
+                                       16, 0, 0);
+  }
+}
+// Two blocks of n0 and n1 int32 words from device memory into LDS (the
+// device buffers are padded to 256 bytes and the LDS parts to 4 words).  A
+// large image goes with direct loads (lds_chunks); a small one (the product
+// catalog's 8 KB) through registers, measured the faster of the two there.
+// The caller's barrier follows.
+__device__ __forceinline__ void copy2_to_lds(int32_t* d0, const int32_t* s0, int n0, int32_t* d1,
+                                             const int32_t* s1, int n1) {
+  if (n0 + n1 >= 4096) {  // 16 KB
+    const int wv = wave_id(), lane = __lane_id();
+    lds_chunks(d0, s0, n0, wv, lane);
+    lds_chunks(d1, s1, n1, wv, lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    copy2_regs(d0, s0, n0, d1, s1, n1);
   }
 }
 
