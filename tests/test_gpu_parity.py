@@ -247,7 +247,8 @@ def test_two_tries_no_contamination():
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("cid,B", [("tiny", 1), ("product", 1), ("structured", 8), ("unstructured", 4),
-                                   ("structured", 64), ("large", 24), ("structured", 128), ("large", 256)])
+                                   ("structured", 24), ("structured", 64), ("large", 24), ("structured", 128),
+                                   ("large", 256)])
 def test_dense_masked_matches_sparse(cid, B, monkeypatch):
     """Dense head + mask against the sparse step and the oracle.  B = 1 (and the
     vector head at any B) uses the sparse head's per-row arithmetic, so logits
