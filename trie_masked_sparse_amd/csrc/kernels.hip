@@ -756,9 +756,7 @@ __device__ __forceinline__ void lds_chunks(int32_t* d, const int32_t* s, int n, 
   for (int c = wv * kWave; c < q; c += kLoopWaves * kWave) {
     if (c + lane < q)
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(S + c + lane),
-                                       reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                           reinterpret_cast<uintptr_t>(d + 4 * c)),
-                                       16, 0, 0);
+                                       (__attribute__((address_space(3))) void*)(d + 4 * c), 16, 0, 0);
   }
 }
 // Two blocks of n0 and n1 int32 words from device memory into LDS (the
