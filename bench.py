@@ -348,9 +348,13 @@ def dense_step_us(w: Workload, reps=5):
     us = e0.elapsed_time(e1) * 1e3 / n
     table = w.c.vocab * w.c.hidden * w.esz
     flops = 2.0 * w.B * w.c.vocab * w.c.hidden
-    return {"B": w.B, "us_per_step": us, "table_GBps": table / (us * 1e-6) / 1e9,
-            "head": "matrix cores (v_mfma_f32_16x16x32_bf16)" if w.B > 1 and w.c.dtype == "bf16" else "vector units",
-            "TFLOPs": flops / (us * 1e-6) / 1e12}
+    mfma = w.B > 1 and w.c.dtype == "bf16"
+    gbps, tflops = table / (us * 1e-6) / 1e9, flops / (us * 1e-6) / 1e12
+    # a whole dense step (mask, head, advance) against the table read once and
+    # the matrix cores' dense bf16 peak (the vector head's fp32 peak otherwise)
+    return {"B": w.B, "us_per_step": us, "table_GBps": gbps, "frac_of_8TBps": gbps / HBM_PEAK_GBPS,
+            "head": "matrix cores (v_mfma_f32_16x16x32_bf16)" if mfma else "vector units",
+            "TFLOPs": tflops, "frac_of_compute_peak": tflops / (2500.0 if mfma else 157.3)}
 
 
 def cpu_baseline(w: Workload, min_seconds: float):
