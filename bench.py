@@ -450,7 +450,7 @@ def main():
                     help="comma list of headline,b64,stress,dense,cpu,copyref,configs (default: all but copyref, configs)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}). "
               "Sequences shard across GPUs with no per-step exchange; run one process per GPU.", file=sys.stderr)
         sys.exit(2)
     only = set(filter(None, args.only.split(",")))
