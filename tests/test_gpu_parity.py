@@ -514,6 +514,39 @@ def test_loop_fast_store_live_in_memory():
     assert info["path"] == tms.PATH_FAST and info["n_edges"] * 4 > 65536
 
 
+@pytest.mark.parametrize("cat,k", [([[7]], 1), ([list(range(3, 73))], 1), ([[4, 5], [4]], 2), ([[4], [4, 5]], 1),
+                                   ([[9, 1], [9, 2], [8], [9, 1, 3], [2]], 5)])
+def test_loop_degenerate_catalogs(cat, k):
+    """Degenerate catalogs through the resident loop: one entry (every step
+    forced, one of them a run of more than 64 tokens), an entry that is a
+    prefix of the other (its terminal is not a leaf), and k equal to the
+    catalog size (the last pointer has one entry left).  Tokens, lengths,
+    entries and final state against the oracle and the per-step form."""
+    V, H, B = 128, 256, 3
+    rng = np.random.Generator(np.random.PCG64(70 + len(cat) + k))
+    otr = oracle.Trie(cat, V, V - 2, V - 1)
+    T = k * (otr.max_depth + 1)
+    emb = _rand_table(rng, V, H, "bf16")
+    hid = _rand_hidden(rng, T, B, H, "bf16")
+    ref = oracle.decode(otr, k, emb, hid)
+    for path in (tms.PATH_FAST, tms.PATH_GLOBAL):
+        trie = tms.Trie(cat, V, V - 2, V - 1, path=path)
+        st = tms.State(trie, B, k, to_dev(emb))
+        hd = to_dev(hid)
+        tok, ln, ent = run_k_pointers(st, hd)
+        compare(tok, ref, H, None, ln, ent, where=f"degenerate {cat} k={k} path={path}")
+        ex = st.export(live=True)
+        tms.state_set_loop(st.h, tms.LOOP_STREAM)
+        st.reset()
+        tok2, ln2, ent2 = run_k_pointers(st, hd)
+        assert np.array_equal(tok, tok2) and np.array_equal(ln, ln2) and np.array_equal(ent, ent2)
+        ex2 = st.export(live=True)
+        for key in ("node", "depth", "done", "status", "finished", "n_emitted", "entries", "live"):
+            assert np.array_equal(ex[key], ex2[key]), (cat, k, path, key)
+        st.close()
+        trie.close()
+
+
 def test_bf16_pair_product_rounding():
     """How one v_dot2_f32_bf16 rounds (an in-bounds check through the sparse
     head with H = 8, where lane 0 holds the whole row): 1.0 from the first
