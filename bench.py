@@ -221,7 +221,8 @@ def stress_gemv(steps: int, warmup: int, emb, emb_np, rows_per_seq: int):
     return {"shape": f"64 seq x {R} distinct rows, H={H} bf16, {S} disjoint sets ({S * B * R * H * 2 >> 20} MiB)",
             "kernel": "gather_gemv_kernel", "avg_launch_us": us, "alg_bytes_per_launch": nbytes,
             "achieved_GBps": gbps, "frac_of_8TBps": gbps / HBM_PEAK_GBPS,
-            "traffic": _pmc_traffic("gather_gemv", f"stress64x{R}")}
+            "traffic": _pmc_traffic("gather_gemv", f"stress64x{R}"),
+            "seeds": {"rows": 4242, "hidden": 5, "table": "the product-scale embedding's"}}
 
 
 def copy_reference(reps: int = 5):
@@ -413,7 +414,8 @@ def config_table(steps: int, warmup: int, cids=("tiny", "product", "product_deep
         gathered = float(((n_rows + n_act) * w.c.hidden * w.esz).sum())
         unique = float(((n_uniq + n_act) * w.c.hidden * w.esz).sum())
         sample = None if w.B <= 64 else list(range(0, w.B, w.B // 24))[:24]
-        row = {"B": w.B, "steps_per_s": r["steps_per_s"], "tokens_per_s": r["tokens_per_s"],
+        row = {"B": w.B, "seeds": {"catalog": w.c.cat_seed, "embedding": w.c.emb_seed, "hidden": w.c.hid_seed},
+               "steps_per_s": r["steps_per_s"], "tokens_per_s": r["tokens_per_s"],
                "ms_per_call": r["ms_per_call"], "gathered_TBps": gathered / (r["gpu_ms"] * 1e-3 / steps) / 1e12,
                "unique_TBps": unique / (r["gpu_ms"] * 1e-3 / steps) / 1e12,
                "gathered_bytes_per_call": gathered, "unique_bytes_per_call": unique,
@@ -480,7 +482,8 @@ def main():
                         "state reset + one whole answer from the resident device loop "
                         f"(up to {w.T} steps); bf16 inputs, fp32 accumulation",
             "path": "fast" if w.info["path"] == tms.PATH_FAST else "global",
-            "steps_per_call": r["steps_per_call"], "tokens_per_call": r["tokens_per_call"]}
+            "steps_per_call": r["steps_per_call"], "tokens_per_call": r["tokens_per_call"],
+            "seeds": {"catalog": w.c.cat_seed, "embedding": w.c.emb_seed, "hidden": w.c.hid_seed}}
         _log(f"headline {r}")
         rf = loop_roofline(w, r, args.steps)
         line["roofline"] = {"bound": "hbm", "kernel": rf["kernel"], "achieved": rf["achieved_GBps"],
