@@ -958,10 +958,11 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
         if (lane == 0) entries[done] = ent;
       }
       if (!sreg_ok && lane == 0) spent[ent >> 5] |= 1u << (ent & 31);
-      if (!LDS_LIVE || !reg_lists || !sreg_ok) {
-        // live counts, spent flags or entries in device memory are read again
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
+      // live counts in device memory are read again by this kernel unless the
+      // sequence stops here or the phase ends at the root; spent flags and
+      // entries in device memory are read back in any case
+      const bool reread = kind != kChildStop && !exit_root;
+      if ((!LDS_LIVE && reread) || !reg_lists || !sreg_ok) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     if (sreg_ok && lane == (ent >> 5)) sreg |= 1u << (ent & 31);
     if constexpr (LDS_LIVE) lds_barrier();
@@ -1304,7 +1305,7 @@ __global__ __launch_bounds__(kBlock) void root_head_kernel(DevTrie tr, DevState 
   }
   lds_barrier();
   // this tile's best per member (0: none legal); the loop takes the max over tiles
-  if (threadIdx.x < cnt) st.rkey[(int64_t)blockIdx.x * st.B + s_mem[m0 + threadIdx.x]] = s_best[threadIdx.x];
+  if ((int)threadIdx.x < cnt) st.rkey[(int64_t)blockIdx.x * st.B + s_mem[m0 + threadIdx.x]] = s_best[threadIdx.x];
 }
 
 // ---------------------------------------------------------------------------
