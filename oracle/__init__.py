@@ -116,7 +116,9 @@ class Trie:
          self.sep, self.stop, self.vocab) = (int(x) for x in info)
 
     def __del__(self):
-        if getattr(self, "_h", None):
+        # at interpreter exit the module globals (lib among them) may already
+        # be gone; the process is ending and frees the memory anyway
+        if getattr(self, "_h", None) and lib is not None:
             lib().orc_trie_free(self._h)
             self._h = None
 
