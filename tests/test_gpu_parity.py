@@ -547,6 +547,55 @@ def test_loop_degenerate_catalogs(cat, k):
         trie.close()
 
 
+def test_random_sweep_repeated_decodes():
+    """Seeded random catalogs (sizes, depths, id ranges, hidden sizes, batch
+    sizes, k, both stores, every resident loop form): three decodes on one
+    state with resets between (the later ones restore only released paths),
+    each against the oracle and with identical exported state, then the
+    per-step form."""
+    rng = np.random.Generator(np.random.PCG64(12345))
+    n = 0
+    while n < 48:
+        seed = int(rng.integers(1 << 30))
+        K, maxlen, idhi = int(rng.choice([3, 20, 150, 900])), int(rng.choice([3, 6, 12, 40, 80])), \
+            int(rng.choice([6, 30, 300, 2000]))
+        V = (max(idhi + 2, 64) + 7) // 8 * 8
+        try:
+            cat = random_catalog(seed, K, maxlen, idhi)
+        except ValueError:
+            continue  # not that many distinct strings in this id range
+        H, B = int(rng.choice([64, 256])), int(rng.choice([1, 3, 8, 17]))
+        k = int(rng.integers(1, min(len(cat), 6) + 1))
+        path = int(rng.choice([tms.PATH_AUTO, tms.PATH_GLOBAL]))
+        mode = int(rng.choice([tms.LOOP_RESIDENT, tms.LOOP_RESIDENT_SOLO, tms.LOOP_RESIDENT_GROUPED]))
+        otr = oracle.Trie(cat, V, V - 2, V - 1)
+        T = k * (otr.max_depth + 1)
+        r2 = np.random.Generator(np.random.PCG64(seed + 1))
+        emb, hid = _rand_table(r2, V, H, "bf16"), _rand_hidden(r2, T, B, H, "bf16")
+        ref = oracle.decode(otr, k, emb, hid)
+        trie = tms.Trie(cat, V, V - 2, V - 1, path=path)
+        st = tms.State(trie, B, k, to_dev(emb))
+        tms.state_set_loop(st.h, mode)
+        hd = to_dev(hid)
+        where = f"seed={seed} K={K} maxlen={maxlen} idhi={idhi} H={H} B={B} k={k} path={path} mode={mode}"
+        first = None
+        for rep in range(3):
+            st.reset()
+            tok, ln, ent = run_k_pointers(st, hd)
+            compare(tok, ref, H, None, ln, ent, where=f"{where} rep={rep}")
+            ex = st.export(live=True)
+            first = first or ex
+            for key in ("node", "depth", "done", "status", "finished", "n_emitted", "entries", "live"):
+                assert np.array_equal(ex[key], first[key]), (where, rep, key)
+        tms.state_set_loop(st.h, tms.LOOP_STREAM)
+        st.reset()
+        tok2, ln2, ent2 = run_k_pointers(st, hd)
+        assert np.array_equal(tok, tok2) and np.array_equal(ln, ln2) and np.array_equal(ent, ent2), where
+        st.close()
+        trie.close()
+        n += 1
+
+
 def test_bf16_pair_product_rounding():
     """How one v_dot2_f32_bf16 rounds (an in-bounds check through the sparse
     head with H = 8, where lane 0 holds the whole row): 1.0 from the first
