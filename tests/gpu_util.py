@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import functools
 import math
+import warnings
 
 import numpy as np
 import torch
@@ -37,9 +38,13 @@ def tree_depth(H: int) -> int:
 
 
 def to_dev(a: np.ndarray) -> torch.Tensor:
-    if a.dtype == np.uint16:
-        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
-    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    # cached inputs are read-only arrays; the host tensor wrapping them is only
+    # copied to the device, never written, so torch's warning about that is moot
+    with warnings.catch_warnings():
+        warnings.filterwarnings("ignore", message="The given NumPy array is not writable")
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
 @functools.lru_cache(maxsize=2)
