@@ -37,9 +37,11 @@ def _log(msg):
 
 
 def _kernel_hash():
+    """Kernel sources and the build script (compile flags): counters taken with
+    another build are not reported."""
     h = hashlib.sha256()
-    for f in ("kernels.hip", "kernels.h"):
-        with open(os.path.join(ROOT, "trie_masked_sparse_amd", "csrc", f), "rb") as fh:
+    for f in ("csrc/kernels.hip", "csrc/kernels.h", "build.py"):
+        with open(os.path.join(ROOT, "trie_masked_sparse_amd", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 

@@ -15,8 +15,10 @@ LIB = os.path.join(HERE, "libtms.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-# Packed fp32 instructions are disabled for all device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed fp32 instructions are disabled for all device code.  The scheduler
+# favours instruction-level parallelism (measured: the resident loop 2-3 %
+# faster on every workload, the other kernels unchanged or faster).
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-sched-strategy=max-ilp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{os.path.join(ROOT, 'include')}"]
 
 
