@@ -1885,6 +1885,152 @@ __global__ __launch_bounds__(kBlock) void dense_mfma_kring_kernel(DevState st, S
   }
 }
 
+// The contraction for 64 < B <= 256 (H a multiple of KB * R): each wavefront
+// keeps T row tiles x MAXT member tiles of accumulators for the whole of H.
+// The hidden slice of a KB-wide K block goes through registers into one of
+// two LDS buffers (requested one block ahead, stored after the products);
+// the table fragments rotate over a ring of R register slots, requested R - 1
+// blocks ahead.  The K loop is unrolled by R so that every slot keeps its
+// role without copies, and its body has no branches: the requests past the
+// last block repeat the last block (cached, unused).  All MAXT member tiles are
+// computed (missing members read a copy of the last one and are dropped).
+// At 8 member tiles the kernel fits 256 registers, so two workgroups share a
+// compute unit; at 16 the accumulators take the accumulation registers and
+// one workgroup runs per unit.  Same products and K order as the kernels
+// above, so bit-identical logits.
+template <int MAXT, int T, int KB, int R>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MAXT <= 8 ? 2 : 1, 2)))
+void dense_mfma_wide_kernel(DevState st, StepIO io, float* full_logits, int nblk) {
+  extern __shared__ uint4 sh[];  // two buffers of [MAXT*16][KS]
+  constexpr int KQ = KB / 8;     // uint4 per staged row
+  constexpr int KS = KQ + 1;     // staged row stride (+1 against bank conflicts)
+  constexpr int KJ = KB / 32;    // matrix-core K steps per block
+  constexpr int nseq = MAXT * 16;
+  constexpr int bufsz = nseq * KS;
+  constexpr int HV = nseq * KQ / kBlock;
+  constexpr int kRows = 4 * T * 16;
+  static_assert(nseq * KQ % kBlock == 0, "whole staging rounds");
+  const int lane = __lane_id();
+  const int wv = wave_id();
+  const int V = io.V, B = st.B;
+  const int nq = io.H / 8;
+  const int nkb = io.H / KB;  // a multiple of R
+  const uint4* emb = (const uint4*)io.emb;
+  const uint4* hid = (const uint4*)io.hidden;
+  typedef u32x4_t Frag[T][KJ];
+  u32x4_t hv[HV];  // a vector type: copies of uint4 (a struct) would go through private memory
+  auto hload = [&](int kb) {
+#pragma unroll
+    for (int u = 0; u < HV; ++u) {
+      const int idx = u * kBlock + (int)threadIdx.x;
+      const int sq = idx / KQ, qq = idx % KQ;
+      hv[u] = *reinterpret_cast<const u32x4_t*>(hid + (int64_t)min(sq, B - 1) * nq + kb * KQ + qq);
+    }
+  };
+  auto hstore = [&](uint4* buf) {
+#pragma unroll
+    for (int u = 0; u < HV; ++u) {
+      const int idx = u * kBlock + (int)threadIdx.x;
+      *reinterpret_cast<u32x4_t*>(buf + (idx / KQ) * KS + idx % KQ) = hv[u];
+    }
+  };
+  for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    const int m0 = blk * kRows + wv * (T * 16);
+    const uint4* rp[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) rp[t] = emb + (int64_t)min(m0 + t * 16 + (lane & 15), V - 1) * nq + (lane >> 4);
+    auto fetch = [&](Frag& f, int kb) {
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int j = 0; j < KJ; ++j) f[t][j] = *reinterpret_cast<const u32x4_t*>(rp[t] + kb * KQ + j * 4);
+    };
+    f32x4_t acc[T][MAXT];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int m = 0; m < MAXT; ++m) acc[t][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    Frag f[R];
+    hload(0);
+#pragma unroll
+    for (int r = 0; r + 1 < R; ++r) fetch(f[r], r);
+    __syncthreads();  // the buffers of the previous row block are consumed
+    hstore(sh);
+    // block kb from slot kb % R; block kb + R - 1 goes into the slot block
+    // kb - 1 used, and the hidden slice of block kb + 1 is requested first
+    for (int k0 = 0; k0 < nkb; k0 += R) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int kb = k0 + r;
+        hload(min(kb + 1, nkb - 1));
+        fetch(f[(r + R - 1) % R], min(kb + R - 1, nkb - 1));
+        lds_barrier();  // block kb staged; every wavefront is done with the other buffer
+        const uint4* hb = sh + (kb & 1) * bufsz;
+#pragma unroll
+        for (int j = 0; j < KJ; ++j) {
+#pragma unroll
+          for (int m = 0; m < MAXT; ++m) {
+            const bf16x8_t b = __builtin_bit_cast(bf16x8_t, hb[(m * 16 + (lane & 15)) * KS + j * 4 + (lane >> 4)]);
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+              acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f[r][t][j]), b,
+                                                                   acc[t][m], 0, 0, 0);
+          }
+        }
+        // schedule: kAhead LDS reads first, then one read per T products, so
+        // that at most kAhead + 1 hidden fragments occupy registers
+        constexpr int kAhead = 4;
+        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+        for (int g = 0; g < KJ * MAXT - kAhead; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, T, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kAhead * T, 0);
+        hstore(sh + ((kb + 1) & 1) * bufsz);  // after the last block: a copy into the free buffer, unused
+      }
+    }
+    // epilogue: tile t, sequence m*16 + lane%16, rows m0 + t*16 + 4*(lane/16) + i.
+    // The mask pointer passes through an empty asm statement so that the
+    // addresses below are formed here, not kept in registers across the K
+    // loop.  A lane's four rows of a tile share one mask word (r0 % 4 == 0);
+    // bits past V are never set.  Each lane combines its masked-in keys of a
+    // member tile (the unsigned max is order-independent) into one atomic.
+    const uint32_t* mask = st.mask;
+    asm volatile("" : "+s"(mask));
+    const int rl = m0 + 4 * (lane >> 4);
+#pragma unroll
+    for (int m = 0; m < MAXT; ++m) {
+      const int sq = m * 16 + (lane & 15);
+      const uint32_t* mrow = mask + (int64_t)min(sq, B - 1) * st.mask_words;
+      unsigned long long best = 0ull;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const int r0 = rl + t * 16;
+        const uint32_t bits = r0 < V ? (mrow[r0 >> 5] >> (r0 & 31)) & 15u : 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if ((bits >> i) & 1u) best = max(best, pack_key(acc[t][m][i], (uint32_t)(r0 + i)));
+      }
+      if (sq < B && best)
+        __hip_atomic_fetch_max(&st.key[sq], best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (full_logits) {
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int m = 0; m < MAXT; ++m) {
+          const int sq = m * 16 + (lane & 15);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = rl + t * 16 + i;
+            if (sq < B && r < V) full_logits[(int64_t)sq * V + r] = acc[t][m][i];
+          }
+        }
+    }
+  }
+}
+
 // One wavefront per sequence: winner token from the key, its edge, advance.
 __global__ __launch_bounds__(kWave) void dense_advance_kernel(DevTrie tr, DevState st, StepIO io) {
   const int s = blockIdx.x;
@@ -2278,6 +2424,22 @@ hipError_t launch_dense_kring(const DevState& st, const StepIO& io, float* full,
   return hipGetLastError();
 }
 
+template <int MAXT, int T, int KB, int R>
+hipError_t launch_dense_wide(const DevState& st, const StepIO& io, float* full, hipStream_t s) {
+  const size_t lds = 2 * sizeof(uint4) * (size_t)MAXT * 16 * (KB / 8 + 1);  // double buffer
+  auto* k = &dense_mfma_wide_kernel<MAXT, T, KB, R>;
+  static size_t allowed = 65536;
+  if (lds > allowed) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+    allowed = lds;
+  }
+  const int nblk = (io.V + 64 * T - 1) / (64 * T);
+  hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(kBlock), lds, s, st, io, full, nblk);
+  return hipGetLastError();
+}
+
 bool dense_uses_mfma(int dtype, int B, int H) { return dtype == 1 && B >= 2 && B <= 256 && H % 32 == 0; }
 
 hipError_t launch_dense_step(const DevTrie& tr, const DevState& st, const StepIO& io, int dtype, float* full,
@@ -2293,11 +2455,17 @@ hipError_t launch_dense_step(const DevTrie& tr, const DevState& st, const StepIO
       // loads two blocks ahead: 166 -> 136 us at B = 64, H = 2048 (V = 151936);
       // at H = 4096 the unrolled body needs more than 256 registers
       err = launch_dense_kring<4, 2, kDenseKB, 16>(st, io, full, s);
+    else if (st.B > 64 && io.H % 256 == 0)
+      // hidden slices 64 wide through registers, table fragments three blocks
+      // ahead: 939 -> 545 us at B = 256, H = 4096; 319 -> 179 us at B = 128,
+      // H = 2048 (two workgroups per compute unit fit at 8 member tiles)
+      err = st.B <= 128 ? launch_dense_wide<8, 2, 64, 4>(st, io, full, s)
+                        : launch_dense_wide<16, 2, 64, 4>(st, io, full, s);
     else if (io.H % kDenseKB == 0)
       // two row tiles per wavefront: measured best (1/2/3/4/8 swept at B = 64)
       err = st.B <= 64 ? launch_dense_kstream<4, 2>(st, io, full, s)
           : st.B <= 128 ? launch_dense_kstream<8, 2>(st, io, full, s)
-                        : launch_dense_kstream<16, 2>(st, io, full, s);  // B = 256, H = 4096: 1.50 -> 0.97 ms
+                        : launch_dense_kstream<16, 2>(st, io, full, s);
     else
       err = st.B <= 64 ? launch_dense_mfma<4, 1>(st, io, full, s)
           : st.B <= 128 ? launch_dense_mfma<8, 1>(st, io, full, s)
