@@ -1927,11 +1927,13 @@ void dense_mfma_wide_kernel(DevState st, StepIO io, float* full_logits, int nblk
       hv[u] = *reinterpret_cast<const u32x4_t*>(hid + (int64_t)min(sq, B - 1) * nq + kb * KQ + qq);
     }
   };
+  // LDS position (in uint4) of member row `row`, 16-byte column `col` of a staged block
+  auto lpos = [](int row, int col) { return row * KS + col; };
   auto hstore = [&](uint4* buf) {
 #pragma unroll
     for (int u = 0; u < HV; ++u) {
       const int idx = u * kBlock + (int)threadIdx.x;
-      *reinterpret_cast<u32x4_t*>(buf + (idx / KQ) * KS + idx % KQ) = hv[u];
+      *reinterpret_cast<u32x4_t*>(buf + lpos(idx / KQ, idx % KQ)) = hv[u];
     }
   };
   for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
@@ -1970,7 +1972,7 @@ void dense_mfma_wide_kernel(DevState st, StepIO io, float* full_logits, int nblk
         for (int j = 0; j < KJ; ++j) {
 #pragma unroll
           for (int m = 0; m < MAXT; ++m) {
-            const bf16x8_t b = __builtin_bit_cast(bf16x8_t, hb[(m * 16 + (lane & 15)) * KS + j * 4 + (lane >> 4)]);
+            const bf16x8_t b = __builtin_bit_cast(bf16x8_t, hb[lpos(m * 16 + (lane & 15), j * 4 + (lane >> 4))]);
 #pragma unroll
             for (int t = 0; t < T; ++t)
               acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f[r][t][j]), b,
