@@ -629,6 +629,43 @@ def test_dense_odd_vocab_sweep():
         trie.close()
 
 
+def test_dense_wide_batch_sweep():
+    """The matrix-core dense head for 64 < B <= 256 (H a multiple of 256):
+    batches that leave the last member tile partly empty (its lanes read a copy
+    of the last member and are dropped), both member-tile counts (8 and 16),
+    several hidden sizes and vocabularies that end inside a 128-row workgroup
+    block; seeded random catalogs.  Tokens against the oracle with the any-order
+    tie bound, full logits of the first and last sequence sampled against the
+    oracle's."""
+    rng = np.random.Generator(np.random.PCG64(4242))
+    for case in range(8):
+        seed = int(rng.integers(1 << 30))
+        H = int(rng.choice([256, 512, 1024, 2048]))
+        B = int(rng.integers(65, 257)) if case else 255
+        V = int(rng.integers(66, 3000))
+        cat = random_catalog(seed, int(rng.integers(3, 60)), 6, V - 2)
+        k = int(rng.integers(1, min(len(cat), 3) + 1))
+        otr = oracle.Trie(cat, V, V - 2, V - 1)
+        T = k * (otr.max_depth + 1)
+        r2 = np.random.Generator(np.random.PCG64(seed + 1))
+        emb, hid = _rand_table(r2, V, H, "bf16"), _rand_hidden(r2, T, B, H, "bf16")
+        ref = oracle.decode(otr, k, emb, hid)
+        trie = tms.Trie(cat, V, V - 2, V - 1)
+        st = tms.State(trie, B, k, to_dev(emb))
+        full = torch.zeros((T, B, V), dtype=torch.float32, device="cuda")
+        where = f"seed={seed} V={V} B={B} H={H} k={k}"
+        print(where, flush=True)
+        tok, lg = run_step_loop(st, to_dev(hid), dense=True, full=full)
+        compare(tok, ref, H, lg, where=where, depth=H + 1)
+        fl = full.cpu().numpy()
+        for b in (0, B - 1):
+            for v in r2.choice(V, 64, replace=False):
+                want, sa = oracle.logit(emb, int(v), hid[0, b])
+                assert abs(float(fl[0, b, v]) - want) <= 2e-3 * abs(want) + gamma(H + 1) * sa, (where, b, v)
+        st.close()
+        trie.close()
+
+
 def test_bf16_pair_product_rounding():
     """How one v_dot2_f32_bf16 rounds (an in-bounds check through the sparse
     head with H = 8, where lane 0 holds the whole row): 1.0 from the first
