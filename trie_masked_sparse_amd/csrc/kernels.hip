@@ -38,6 +38,10 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "kernels.h"
 
 namespace tms {
@@ -2232,19 +2236,30 @@ struct StepLaunch {
   }
 };
 
+// Raises a kernel's dynamic LDS limit on the current device when a launch
+// needs more than the default 64 KB.  Remembered per (kernel, device), under a
+// lock, so concurrent host threads and several devices are handled.
+hipError_t allow_lds(const void* k, size_t lds) {
+  if (lds <= 65536) return hipSuccess;
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, size_t> raised;
+  std::lock_guard<std::mutex> lock(mu);
+  size_t& have = raised[{k, dev}];
+  if (lds <= have) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e == hipSuccess) have = lds;
+  return e;
+}
+
 template <int DT, int NC>
 struct LoopLaunch {
   template <int META, bool LIVE, bool SMALL, bool MASK = false>
   static hipError_t go(const DevTrie& tr, const DevState& st, const LoopIO& io, hipStream_t s) {
     const size_t lds = LIVE ? sizeof(int32_t) * (size_t)loop_lds_layout(tr, st, META == kMetaLds).total : 0;
     auto* k = &loop_kernel<DT, NC, META, LIVE, SMALL, MASK>;
-    static size_t allowed = 65536;  // per instantiation; raised once as needed
-    if (lds > allowed) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      allowed = lds;
-    }
+    if (hipError_t e = allow_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3((unsigned)st.B), dim3(kLoopBlock), lds, s, tr, st, io);
     return hipGetLastError();
   }
@@ -2328,13 +2343,7 @@ hipError_t launch_root_mfma(const DevTrie& tr, const DevState& st, const LoopIO&
   const int nq = io.H / 8;
   const size_t lds = sizeof(uint4) * (size_t)16 * nq + (sizeof(int64_t) + sizeof(int)) * (size_t)st.B;
   auto* k = &root_mfma_kernel<KS>;
-  static size_t allowed = 65536;
-  if (lds > allowed) {
-    hipError_t e =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    allowed = lds;
-  }
+  if (hipError_t e = allow_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess) return e;
   const dim3 grid((unsigned)((root_edges + 15) / 16), (unsigned)((st.B + 15) / 16));
   hipLaunchKernelGGL(k, grid, dim3(kBlock), lds, s, tr, st, io);
   return hipGetLastError();
@@ -2349,13 +2358,7 @@ struct RootLaunch {
     const int mt = max(1, min(kRootMembers, 65536 / (nq * 16)));
     const size_t lds = sizeof(uint4) * (size_t)mt * nq + (sizeof(int64_t) + sizeof(int)) * (size_t)st.B;
     auto* k = &root_head_kernel<DT, NC>;
-    static size_t allowed = 65536;
-    if (lds > allowed) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      allowed = lds;
-    }
+    if (hipError_t e = allow_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess) return e;
     const int rows_per_wg = kWavesPerBlock * rows_per_pass(NC);
     const dim3 grid((unsigned)((root_edges + rows_per_wg - 1) / rows_per_wg), (unsigned)((st.B + mt - 1) / mt));
     hipLaunchKernelGGL(k, grid, dim3(kBlock), lds, s, tr, st, io, mt);
@@ -2380,13 +2383,7 @@ hipError_t launch_dense_mfma(const DevState& st, const StepIO& io, float* full, 
   const int ntiles = (st.B + 15) / 16;
   const size_t lds = sizeof(uint4) * (size_t)ntiles * 16 * kDenseStride;
   auto* k = &dense_mfma_kernel<MAXT, MT>;
-  static size_t allowed = 65536;
-  if (lds > allowed) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e != hipSuccess) return e;
-    allowed = lds;
-  }
+  if (hipError_t e = allow_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess) return e;
   const int nblk = (io.V + 64 * MT - 1) / (64 * MT);
   hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(kBlock), lds, s, st, io, full, ntiles);
   return hipGetLastError();
@@ -2397,13 +2394,7 @@ hipError_t launch_dense_kstream(const DevState& st, const StepIO& io, float* ful
   const int ntiles = (st.B + 15) / 16;
   const size_t lds = 2 * sizeof(uint4) * (size_t)ntiles * 16 * kDenseStride;  // double buffer
   auto* k = &dense_mfma_kstream_kernel<MAXT, T>;
-  static size_t allowed = 65536;
-  if (lds > allowed) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e != hipSuccess) return e;
-    allowed = lds;
-  }
+  if (hipError_t e = allow_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess) return e;
   const int nblk = (io.V + 64 * T - 1) / (64 * T);
   hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(kBlock), lds, s, st, io, full, ntiles, nblk);
   return hipGetLastError();
@@ -2414,13 +2405,7 @@ hipError_t launch_dense_kring(const DevState& st, const StepIO& io, float* full,
   const int ntiles = (st.B + 15) / 16;
   const size_t lds = 2 * sizeof(uint4) * (size_t)MAXT * 16 * (KB / 8 + 1);  // double buffer
   auto* k = &dense_mfma_kring_kernel<MAXT, T, KB, NKB>;
-  static size_t allowed = 65536;
-  if (lds > allowed) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e != hipSuccess) return e;
-    allowed = lds;
-  }
+  if (hipError_t e = allow_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess) return e;
   const int nblk = (io.V + 64 * T - 1) / (64 * T);
   hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(kBlock), lds, s, st, io, full, ntiles, nblk);
   return hipGetLastError();
@@ -2430,13 +2415,7 @@ template <int MAXT, int T, int KB, int R>
 hipError_t launch_dense_wide(const DevState& st, const StepIO& io, float* full, hipStream_t s) {
   const size_t lds = 2 * sizeof(uint4) * (size_t)MAXT * 16 * (KB / 8 + 1);  // double buffer
   auto* k = &dense_mfma_wide_kernel<MAXT, T, KB, R>;
-  static size_t allowed = 65536;
-  if (lds > allowed) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e != hipSuccess) return e;
-    allowed = lds;
-  }
+  if (hipError_t e = allow_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess) return e;
   const int nblk = (io.V + 64 * T - 1) / (64 * T);
   hipLaunchKernelGGL(k, dim3((unsigned)nblk), dim3(kBlock), lds, s, st, io, full, nblk);
   return hipGetLastError();
