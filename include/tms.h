@@ -165,9 +165,16 @@ tms_status tms_state_free(tms_state* st);
 tms_status tms_decode_step_sparse(tms_state* st, const void* hidden, int32_t* tok, float* logit,
                                   void* stream);
 
-/* The same step computed the post-logit way (cross-check): all V logits,
- * illegal tokens masked out, full-vocabulary argmax with the same tie rule,
- * same advance.  full_logits: dev fp32 [B][V] or NULL (written unmasked). */
+/* The same step computed the post-logit way (cross-check; section "Masked
+ * sampling inside the sampler", and section 3.8 "The head: from hidden state
+ * to token" of "Understanding Inference for Systems Engineers"): all V
+ * logits, illegal tokens masked out, full-vocabulary argmax with the same tie
+ * rule, same advance.  full_logits: dev fp32 [B][V] or NULL (written
+ * unmasked).  One sequence, or fp32 tables, use the sparse head's per-row
+ * arithmetic (bit-identical logits); bf16 with B > 1 runs on the matrix
+ * cores, whose summation order differs, so logits agree with the sparse
+ * head's within the any-order rounding bound and the argmax can differ only
+ * where two logits are within it.  Errors as for tms_decode_step_sparse. */
 tms_status tms_decode_step_dense_masked(tms_state* st, const void* hidden, int32_t* tok, float* logit,
                                         float* full_logits, void* stream);
 
