@@ -666,6 +666,40 @@ def test_dense_wide_batch_sweep():
         trie.close()
 
 
+def test_dense_large_batch_other_hidden_sizes():
+    """The matrix-core dense head for 64 < B <= 256 when H is not a multiple of
+    256: H % 128 == 0 (the K-streamed kernel) and H % 128 != 0 (the per-block
+    kernel), with partial member tiles and ragged vocabularies; tokens against
+    the oracle with the any-order tie bound, sampled full logits against the
+    oracle's."""
+    rng = np.random.Generator(np.random.PCG64(5151))
+    for H in (96, 160, 384, 640, 96, 384):
+        seed = int(rng.integers(1 << 30))
+        B = int(rng.integers(65, 257))
+        V = int(rng.integers(66, 2500))
+        cat = random_catalog(seed, int(rng.integers(3, 50)), 6, V - 2)
+        k = int(rng.integers(1, min(len(cat), 3) + 1))
+        otr = oracle.Trie(cat, V, V - 2, V - 1)
+        T = k * (otr.max_depth + 1)
+        r2 = np.random.Generator(np.random.PCG64(seed + 1))
+        emb, hid = _rand_table(r2, V, H, "bf16"), _rand_hidden(r2, T, B, H, "bf16")
+        ref = oracle.decode(otr, k, emb, hid)
+        trie = tms.Trie(cat, V, V - 2, V - 1)
+        st = tms.State(trie, B, k, to_dev(emb))
+        full = torch.zeros((T, B, V), dtype=torch.float32, device="cuda")
+        where = f"seed={seed} V={V} B={B} H={H} k={k}"
+        print(where, flush=True)
+        tok, lg = run_step_loop(st, to_dev(hid), dense=True, full=full)
+        compare(tok, ref, H, lg, where=where, depth=H + 1)
+        fl = full.cpu().numpy()
+        for b in (0, B - 1):
+            for v in r2.choice(V, 64, replace=False):
+                want, sa = oracle.logit(emb, int(v), hid[0, b])
+                assert abs(float(fl[0, b, v]) - want) <= 2e-3 * abs(want) + gamma(H + 1) * sa, (where, b, v)
+        st.close()
+        trie.close()
+
+
 def test_bf16_pair_product_rounding():
     """How one v_dot2_f32_bf16 rounds (an in-bounds check through the sparse
     head with H = 8, where lane 0 holds the whole row): 1.0 from the first
