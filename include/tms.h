@@ -252,10 +252,7 @@ tms_status tms_state_set_split(tms_state* st, int32_t split);
  * GRAPH: a hipGraph of T step kernels (as tms_decode_step_sparse), built on
  *   the first call for a given set of pointers and replayed afterwards;
  * STREAM: the same T step kernels launched directly on the stream.
- * Also read from the TMS_LOOP environment variable (0..4) at create.
- * With TMS_BITMASK=1 in the environment of a call, catalogs of at most 128
- * entries run the resident loop on the bitmask no-repeat state instead of
- * live counts (bit-identical results). */
+ * Also read from the TMS_LOOP environment variable (0..4) at create. */
 typedef enum {
   TMS_LOOP_RESIDENT = 0,
   TMS_LOOP_GRAPH = 1,
@@ -264,6 +261,20 @@ typedef enum {
   TMS_LOOP_RESIDENT_GROUPED = 4
 } tms_loop_mode;
 tms_status tms_state_set_loop(tms_state* st, int32_t mode);
+
+/* The no-repeat state the resident loop keeps (page "Constraint made cheaper
+ * than no constraint", section "The batched engine": a per-sequence set of
+ * spent pointers and, per edge, the set of pointers below it).  LIVE: the
+ * per-edge live counts of section "Masked sampling inside the sampler" (any
+ * catalog).  BITMASK: an edge is legal iff its set of entries minus the
+ * sequence's spent set is non-empty (catalogs of at most 128 entries, else
+ * INVALID_ARG); bit-identical results, live counts rewritten from the sets at
+ * the end of each call.  Default LIVE, or BITMASK when the environment holds
+ * TMS_BITMASK=1 at create and the catalog allows it.  Applies to the resident
+ * loop forms of tms_decode_k_pointers; the step kernels always use the live
+ * counts (and so does a call after tms_debug_set_live until the next reset). */
+typedef enum { TMS_NOREPEAT_LIVE = 0, TMS_NOREPEAT_BITMASK = 1 } tms_norepeat;
+tms_status tms_state_set_norepeat(tms_state* st, int32_t kind);
 
 /* Workgroups per sequence used by the fused step, and its grid size. */
 tms_status tms_state_get_launch(const tms_state* st, int32_t* split, int32_t* grid);

@@ -22,7 +22,7 @@ CHILD_SEP, CHILD_STOP = -1, -2
 
 # planted mistakes for negative-control tests
 MUT_NONE, MUT_TIE_HIGHER_ID, MUT_NO_LIVE_DECREMENT, MUT_NO_SPENT_FLAG, MUT_ROW_OFF_BY_ONE, \
-    MUT_SEP_STOP_SWAPPED, MUT_DROP_LAST_TERM = range(7)
+    MUT_SEP_STOP_SWAPPED, MUT_DROP_LAST_TERM, MUT_MARGIN_ZERO, MUT_SUMABS_WINNER, MUT_FOLLOW_IGNORED = range(10)
 
 
 def build(force: bool = True) -> str:
@@ -63,7 +63,7 @@ def lib():
         L.orc_logit.argtypes = [P, C.c_int, i32, i32, P, C.POINTER(C.c_double)]
         L.orc_logit.restype = C.c_double
         L.orc_dense_logits.argtypes = [P, C.c_int, i32, i32, P, P]
-        L.orc_decode.argtypes = [P, i32, P, C.c_int, i32, i32, P, i32, i32] + [P] * 8
+        L.orc_decode.argtypes = [P, i32, P, C.c_int, i32, i32, P, i32, i32] + [P] * 9
         L.orc_decode.restype = C.c_int
         L.orc_set_mutant.argtypes = [C.c_int]
         _lib = L
@@ -190,13 +190,22 @@ def dense_logits(emb: np.ndarray, h: np.ndarray) -> np.ndarray:
     return out
 
 
-def decode(trie: Trie, k: int, emb: np.ndarray, hidden: np.ndarray):
-    """Greedy decode of hidden [T][B][H]; returns a dict of numpy arrays."""
+def decode(trie: Trie, k: int, emb: np.ndarray, hidden: np.ndarray, follow: np.ndarray | None = None):
+    """Greedy decode of hidden [T][B][H]; returns a dict of numpy arrays.
+
+    follow: optional [B][T] int32 tokens to advance by (teacher forcing): the
+    oracle records its own greedy pick and statistics at every step, then
+    advances by follow[b][t] where that is >= 0 (NOT_WALKABLE if it is not
+    legal there) and by its own pick elsewhere."""
     emb = np.ascontiguousarray(emb)
     hidden = np.ascontiguousarray(hidden, dtype=emb.dtype)
     T, B, H = hidden.shape
     if H != emb.shape[1]:
         raise ValueError("hidden size mismatch")
+    if follow is not None:
+        follow = np.ascontiguousarray(follow, dtype=np.int32)
+        if follow.shape != (B, T):
+            raise ValueError(f"follow must be [B][T] = [{B}][{T}], got {follow.shape}")
     out = {
         "tokens": np.full((B, T), -1, np.int32),
         "len": np.zeros(B, np.int32),
@@ -208,8 +217,8 @@ def decode(trie: Trie, k: int, emb: np.ndarray, hidden: np.ndarray):
         "nlegal": np.zeros((B, T), np.int32),
     }
     rc = lib().orc_decode(trie._h, k, _ptr(emb), _dtype_code(emb), emb.shape[0], H, _ptr(hidden), B, T,
-                          *(_ptr(out[n]) for n in ("tokens", "len", "entries", "status", "best",
-                                                   "margin", "sumabs", "nlegal")))
+                          _ptr(follow), *(_ptr(out[n]) for n in ("tokens", "len", "entries", "status", "best",
+                                                                  "margin", "sumabs", "nlegal")))
     if rc != OK:
         raise OracleError(rc, "decode")
     return out

@@ -68,6 +68,9 @@ enum {
   MUT_ROW_OFF_BY_ONE = 4,   /* logit of token v is read from row v+1 */
   MUT_SEP_STOP_SWAPPED = 5, /* sep when the last pointer is due, stop otherwise */
   MUT_DROP_LAST_TERM = 6,   /* dot product skips the last hidden element */
+  MUT_MARGIN_ZERO = 7,      /* the top-two margin is reported as 0 */
+  MUT_SUMABS_WINNER = 8,    /* sum|p| is the winner's, not the larger of the top two */
+  MUT_FOLLOW_IGNORED = 9,   /* teacher forcing advances by the oracle's own pick */
 };
 static int g_mutant = 0;
 void orc_set_mutant(int m) { g_mutant = m; }
@@ -422,10 +425,11 @@ void orc_dense_logits(const void* emb, int dtype, int32_t V, int32_t H, const vo
 /* Greedy decode                                                               */
 /* ------------------------------------------------------------------------- */
 
-/* One greedy step: legal set, logits, first maximum in ascending token order
- * (ties to the lower id), advance.  Records the winner's logit, the top-two
- * margin (+inf with one candidate), the larger sum|p| of the top two, and the
- * size of the legal set.  Returns the token, or -1 when nothing was emitted. */
+/* One greedy pick: legal set, logits, first maximum in ascending token order
+ * (ties to the lower id).  Records the winner's logit, the top-two margin
+ * (+inf with one candidate), the larger sum|p| of the top two, and the size of
+ * the legal set.  Returns the token (the state is not advanced), or -1 when the
+ * sequence is inactive or its mask is empty (then EMPTY_MASK is set). */
 static int32_t greedy_step(orc_state* s, const void* emb, int dtype, int32_t H, const void* h,
                            int32_t* scratch_tok, double* best_out, double* margin_out,
                            double* sumabs_out, int32_t* nlegal_out) {
@@ -453,22 +457,29 @@ static int32_t greedy_step(orc_state* s, const void* emb, int dtype, int32_t H, 
     }
   }
   if (best_out) *best_out = best;
-  if (margin_out) *margin_out = n > 1 ? best - second : INFINITY;
-  if (sumabs_out) *sumabs_out = n > 1 && second_abs > best_abs ? second_abs : best_abs;
-  orc_state_advance(s, win);
+  if (margin_out) *margin_out = g_mutant == MUT_MARGIN_ZERO ? 0.0 : n > 1 ? best - second : INFINITY;
+  if (sumabs_out)
+    *sumabs_out = g_mutant != MUT_SUMABS_WINNER && n > 1 && second_abs > best_abs ? second_abs : best_abs;
   return win;
 }
 
 /* Greedy decode of B independent sequences over T steps.
  * hidden: [T][B][H] (fp32 or bf16 bits, same dtype as emb).
- * Outputs (any may be NULL): tokens [B][T] (-1 padded), len [B], entries [B][k],
- * status [B] (NOT_DONE when no stop was emitted within T steps), and per step
- * best logit, top-two margin, sum|p| and legal-set size, each [B][T].
+ * follow: NULL for the plain greedy decode, or [B][T] tokens to advance by
+ * (teacher forcing, "Understanding Inference for Systems Engineers", Part 8
+ * "Correctness"): at each step the oracle still records its own greedy pick
+ * and its statistics from the current state, then advances by follow[b][t]
+ * when that is >= 0 (a token that is not legal sets NOT_WALKABLE) and by its
+ * own pick otherwise.
+ * Outputs (any may be NULL): tokens [B][T] (the oracle's pick, -1 padded),
+ * len [B], entries [B][k], status [B] (NOT_DONE when no stop was emitted
+ * within T steps), and per step best logit, top-two margin, sum|p| and
+ * legal-set size, each [B][T].
  * Sequences are decoded one after another; nothing is shared between them. */
 int orc_decode(const orc_trie* t, int32_t k, const void* emb, int dtype, int32_t V, int32_t H,
-               const void* hidden, int32_t B, int32_t T, int32_t* tokens, int32_t* len,
-               int32_t* entries, int32_t* status, double* best, double* margin, double* sumabs,
-               int32_t* nlegal) {
+               const void* hidden, int32_t B, int32_t T, const int32_t* follow, int32_t* tokens,
+               int32_t* len, int32_t* entries, int32_t* status, double* best, double* margin,
+               double* sumabs, int32_t* nlegal) {
   if (k < 1 || k > t->n_entries) return ORC_ERR_K;
   if (V != t->vocab || H < 1 || B < 1 || T < 0) return ORC_ERR_INVALID_ARG;
   size_t esz = dtype == 0 ? 4 : 2;
@@ -486,7 +497,11 @@ int orc_decode(const orc_trie* t, int32_t k, const void* emb, int dtype, int32_t
         if (best) best[o] = NAN;
         if (margin) margin[o] = NAN;
         if (sumabs) sumabs[o] = NAN;
+        continue;
       }
+      int32_t take = tok;
+      if (follow && follow[o] >= 0 && g_mutant != MUT_FOLLOW_IGNORED) take = follow[o];
+      orc_state_advance(s, take);
     }
     if (s->status == ORC_OK && !s->finished) s->status = ORC_ERR_NOT_DONE;
     if (len) len[b] = s->n_emitted;

@@ -15,6 +15,12 @@ The oracle (oracle/tms_oracle.c) is trusted only because of these checks:
   * decodes that reduce to textbook results (top-k of a flat catalog via
     numpy.lexsort, lexicographic minimum of L_k(C) for a zero hidden state,
     a permutation of the catalog when k = K);
+  * the per-step statistics the GPU comparison relies on (winner, top-two
+    margin, the larger sum|p| of the top two) against a recomputation from
+    exact dot products (math.fsum) over the legal set;
+  * teacher forcing: along random answers drawn from L_k(C) itself, the
+    oracle's pick at every step is the first maximum of the exact logits over
+    Mask(u), and an illegal forced token is refused;
   * negative controls: each planted oracle mistake must fail at least one pin.
 """
 import itertools
@@ -355,6 +361,125 @@ def pin_decode_invariants():
                 assert sorted(out["entries"][b]) == list(range(6))
 
 
+def _exact_logit(ef, hf, v):
+    """(exact dot product rounded once, exact sum |p|) of token v."""
+    p = ef[v].astype(np.float64) * hf.astype(np.float64)
+    return math.fsum(p.tolist()), math.fsum(np.abs(p).tolist())
+
+
+def _top_two(cands, ef, hf):
+    """First maximum (ties to the lower id) and runner-up of exact logits over
+    the candidate tokens, with each one's exact sum |p|."""
+    vals = sorted(((-_exact_logit(ef, hf, v)[0], v) for v in cands))
+    top = vals[0][1]
+    second = vals[1][1] if len(vals) > 1 else None
+    return top, second
+
+
+def pin_step_statistics():
+    """Winner, margin and sum|p| recorded at every step of seeded decodes equal
+    a recomputation from exact dot products over the legal set (the legal set
+    itself is pinned by the brute-force mask check)."""
+    rng = np.random.Generator(np.random.PCG64(23))
+    u = 2.0 ** -53
+    cases = [("tiny", "f32", 64), ("structured", "bf16", 96)]
+    checked = 0
+    for cid, dt, H in cases:
+        c = CONFIGS[cid]
+        cat = catalog(cid)
+        trie = oracle.Trie(cat, c.vocab, c.sep, c.stop)
+        x = rng.standard_normal((c.vocab, H), dtype=np.float32) * np.float32(0.02)
+        B = 6
+        T = c.k * (trie.max_depth + 1)
+        hx = rng.standard_normal((T, B, H), dtype=np.float32)
+        if dt == "bf16":
+            emb, hid = bf16_bits_from_f32(x), bf16_bits_from_f32(hx)
+            ef, hf = bf16_bits_to_f32(emb), bf16_bits_to_f32(hid)
+        else:
+            emb, hid, ef, hf = x, hx, x, hx
+        # exact ties: a few tokens share one row
+        first = [e[0] for e in cat]
+        emb = emb.copy()
+        ef = ef.copy()
+        for v in first[1:4]:
+            emb[v] = emb[first[0]]
+            ef[v] = ef[first[0]]
+        out = oracle.decode(trie, c.k, emb, hid)
+        g = (H - 1) * u / (1 - (H - 1) * u)
+        for b in range(B):
+            st = oracle.State(trie, c.k)
+            for t in range(T):
+                lg = st.legal()
+                if lg is None:
+                    assert out["tokens"][b, t] == -1
+                    continue
+                cands = [int(v) for v in lg[0]]
+                top, second = _top_two(cands, ef, hf[t, b])
+                l1, a1 = _exact_logit(ef, hf[t, b], top)
+                assert out["tokens"][b, t] == top, (cid, b, t)
+                assert out["nlegal"][b, t] == len(cands)
+                assert abs(out["best"][b, t] - l1) <= g * a1
+                if second is None:
+                    assert out["margin"][b, t] == math.inf
+                    assert abs(out["sumabs"][b, t] - a1) <= g * a1
+                else:
+                    l2, a2 = _exact_logit(ef, hf[t, b], second)
+                    assert abs(out["margin"][b, t] - (l1 - l2)) <= 2 * g * max(a1, a2), (cid, b, t)
+                    assert abs(out["sumabs"][b, t] - max(a1, a2)) <= g * max(a1, a2), (cid, b, t)
+                checked += 1
+                assert st.advance(top) == oracle.OK
+    assert checked > 100
+
+
+def pin_teacher_forcing():
+    """Forced along random strings of L_k(C): at every step the recorded pick
+    is the first maximum of exact logits over Mask(u) (the language
+    definition), the state follows the forced string to its entries, and a
+    token outside Mask(u) is refused at the step where it is forced."""
+    rng = np.random.Generator(np.random.PCG64(31))
+    for ci, (cat, V, sep, stop) in enumerate(tiny_cases()[:24]):
+        trie = oracle.Trie(cat, V, sep, stop)
+        H = 5
+        emb = rng.standard_normal((V, H), dtype=np.float32)
+        emb[3] = emb[4]  # an exact tie between two tokens
+        for k in range(1, min(3, len(cat)) + 1):
+            L = language(cat, k, sep, stop)
+            s = L[int(rng.integers(0, len(L)))]
+            T = k * (trie.max_depth + 1)
+            hid = rng.standard_normal((T, 1, H), dtype=np.float32)
+            follow = np.full((1, T), -1, np.int32)
+            follow[0, :len(s)] = s
+            out = oracle.decode(trie, k, emb, hid, follow=follow)
+            for t in range(len(s)):
+                want = mask_by_definition(L, tuple(s[:t]))
+                top, _ = _top_two(want, emb, hid[t, 0])
+                assert out["tokens"][0, t] == top, (ci, k, t)
+            assert (out["tokens"][0, len(s):] == -1).all()
+            assert out["status"][0] == oracle.OK and out["len"][0] == len(s)
+            pieces, cur = [], []
+            for x in s[:-1]:
+                if x == sep:
+                    pieces.append(tuple(cur))
+                    cur = []
+                else:
+                    cur.append(x)
+            pieces.append(tuple(cur))
+            index = {tuple(e): i for i, e in enumerate(cat)}
+            ids = [index[p] for p in pieces]
+            assert list(out["entries"][0]) == ids, (ci, k)
+            # a token outside the mask, forced at a random step, is refused there
+            t = int(rng.integers(0, len(s)))
+            want = mask_by_definition(L, tuple(s[:t]))
+            bad = [v for v in range(V) if v not in want]
+            if bad:
+                f2 = follow.copy()
+                f2[0, t] = bad[int(rng.integers(0, len(bad)))]
+                o2 = oracle.decode(trie, k, emb, hid, follow=f2)
+                assert o2["status"][0] == oracle.ERR_NOT_WALKABLE, (ci, k, t)
+                assert (o2["tokens"][0, t + 1:] == -1).all()
+                assert np.array_equal(o2["tokens"][0, :t + 1], out["tokens"][0, :t + 1])
+
+
 # ----------------------------------------------------------------------------
 # Tests
 # ----------------------------------------------------------------------------
@@ -399,6 +524,14 @@ def test_decode_invariants():
     pin_decode_invariants()
 
 
+def test_step_statistics_exact():
+    pin_step_statistics()
+
+
+def test_teacher_forcing_follows_language():
+    pin_teacher_forcing()
+
+
 def test_catalog_validation():
     V, sep, stop = 16, 14, 15
     bad = [
@@ -423,12 +556,14 @@ def test_catalog_validation():
 
 
 ALL_PINS = [pin_mask_brute_force, pin_golden_prefix_pairs, pin_live_counts, pin_logits_exact,
-            pin_flat_topk, pin_zero_hidden_lexicographic]
+            pin_flat_topk, pin_zero_hidden_lexicographic, pin_step_statistics, pin_teacher_forcing]
 
 
 @pytest.mark.parametrize("mutant", [oracle.MUT_TIE_HIGHER_ID, oracle.MUT_NO_LIVE_DECREMENT,
                                     oracle.MUT_NO_SPENT_FLAG, oracle.MUT_ROW_OFF_BY_ONE,
-                                    oracle.MUT_SEP_STOP_SWAPPED, oracle.MUT_DROP_LAST_TERM])
+                                    oracle.MUT_SEP_STOP_SWAPPED, oracle.MUT_DROP_LAST_TERM,
+                                    oracle.MUT_MARGIN_ZERO, oracle.MUT_SUMABS_WINNER,
+                                    oracle.MUT_FOLLOW_IGNORED])
 def test_negative_controls(mutant):
     """Each planted oracle mistake must be rejected by at least one pin."""
     caught = []

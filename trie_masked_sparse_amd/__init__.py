@@ -6,6 +6,16 @@ Device buffers are torch tensors (only their data pointers are passed), the
 stream defaults to torch's current stream.  There is no fallback: if the
 library is not built, or no GPU is present, calls raise.
 
+Fail loudly (page "Constraint made cheaper than no constraint", section
+"Masked sampling inside the sampler": an empty mask or an unwalkable token is
+an error, never a silent pick): the decode calls (decode_step_sparse,
+decode_step_dense_masked, decode_k_pointers, advance_forced) synchronise the
+stream after enqueueing their work and raise TmsError when any sequence holds a
+device error (EMPTY_MASK, NOT_WALKABLE, NOT_DONE), unless called with
+check=False, which leaves them asynchronous (for timed loops and for tests of
+the error paths; State.status() then reports the per-sequence codes).  A state
+is passed as a State or as its raw handle.
+
 torch is imported before the library is loaded so that both use the same HIP
 runtime (torch ships its own libamdhip64 with the same soname).
 """
@@ -33,8 +43,10 @@ EXPORTS = (
     "tms_decode_step_sparse", "tms_decode_step_dense_masked", "tms_decode_k_pointers",
     "tms_advance_forced", "tms_legal_set", "tms_legal_mask", "tms_mask_to_rows", "tms_gather_gemv",
     "tms_debug_set_live",
-    "tms_state_set_split", "tms_state_set_loop", "tms_state_get_launch", "tms_status_str", "tms_last_error",
+    "tms_state_set_split", "tms_state_set_loop", "tms_state_set_norepeat", "tms_state_get_launch",
+    "tms_status_str", "tms_last_error",
 )
+NOREPEAT_LIVE, NOREPEAT_BITMASK = 0, 1
 
 
 class TmsError(RuntimeError):
@@ -82,6 +94,7 @@ def lib():
             "tms_debug_set_live": [P, i32, i32, i32, P],
             "tms_state_set_split": [P, i32],
             "tms_state_set_loop": [P, i32],
+            "tms_state_set_norepeat": [P, i32],
             "tms_state_get_launch": [P, P, P],
         }
         for name, args in sig.items():
@@ -198,12 +211,12 @@ def state_create(trie, B: int, k: int, emb: torch.Tensor, stream=None):
 
 
 def state_reset(st, stream=None):
-    _check(lib().tms_state_reset(st, _stream(stream)), "state_reset")
+    _check(lib().tms_state_reset(_handle(st), _stream(stream)), "state_reset")
 
 
 def state_sync_status(st, B: int, stream=None, check: bool = True) -> np.ndarray:
     out = np.zeros(B, np.int32)
-    rc = lib().tms_state_sync_status(st, out.ctypes.data, _stream(stream))
+    rc = lib().tms_state_sync_status(_handle(st), out.ctypes.data, _stream(stream))
     if rc not in (OK, ERR_EMPTY_MASK, ERR_NOT_WALKABLE, ERR_NOT_DONE) or (check and rc != OK):
         _check(rc, "state_sync_status")
     return out
@@ -213,7 +226,7 @@ def state_export(st, B: int, k: int, n_edges: int, live: bool = False, stream=No
     out = {n: np.zeros(B, np.int32) for n in ("node", "depth", "done", "status", "finished", "n_emitted")}
     out["entries"] = np.zeros((B, k), np.int32)
     lv = np.zeros((B, n_edges), np.int32) if live else None
-    _check(lib().tms_state_export(st, *(out[n].ctypes.data for n in ("node", "depth", "done", "status", "finished",
+    _check(lib().tms_state_export(_handle(st), *(out[n].ctypes.data for n in ("node", "depth", "done", "status", "finished",
                                                                       "n_emitted", "entries")),
                                   lv.ctypes.data if live else None, _stream(stream)), "state_export")
     if live:
@@ -222,20 +235,24 @@ def state_export(st, B: int, k: int, n_edges: int, live: bool = False, stream=No
 
 
 def state_free(st):
-    _check(lib().tms_state_free(st), "state_free")
+    _check(lib().tms_state_free(_handle(st)), "state_free")
 
 
 def state_set_split(st, split: int):
-    _check(lib().tms_state_set_split(st, split), "state_set_split")
+    _check(lib().tms_state_set_split(_handle(st), split), "state_set_split")
 
 
 def state_set_loop(st, mode: int):
-    _check(lib().tms_state_set_loop(st, mode), "state_set_loop")
+    _check(lib().tms_state_set_loop(_handle(st), mode), "state_set_loop")
+
+
+def state_set_norepeat(st, kind: int):
+    _check(lib().tms_state_set_norepeat(_handle(st), kind), "state_set_norepeat")
 
 
 def state_get_launch(st):
     s, g = C.c_int32(), C.c_int32()
-    _check(lib().tms_state_get_launch(st, C.byref(s), C.byref(g)), "state_get_launch")
+    _check(lib().tms_state_get_launch(_handle(st), C.byref(s), C.byref(g)), "state_get_launch")
     return s.value, g.value
 
 
@@ -244,38 +261,65 @@ def state_get_launch(st):
 _HID = (torch.float32, torch.bfloat16, torch.int16, torch.uint16)
 
 
-def decode_step_sparse(st, hidden, tok, logit=None, stream=None):
-    _check(lib().tms_decode_step_sparse(st, _dev(hidden, _HID, "hidden"), _dev(tok, torch.int32, "tok"),
+def _handle(st):
+    return st.h if isinstance(st, State) else st
+
+
+def _raise_device_errors(st, stream, where: str):
+    """Synchronise the stream and raise TmsError if any sequence of st holds a
+    device error; the message names the first such sequence and, for a State,
+    lists every sequence's status."""
+    B = st.B if isinstance(st, State) else 0
+    buf = np.zeros(max(B, 1), np.int32)
+    rc = lib().tms_state_sync_status(_handle(st), buf.ctypes.data if B else None, _stream(stream))
+    if rc != OK:
+        detail = lib().tms_last_error().decode()
+        if B:
+            bad = {i: int(x) for i, x in enumerate(buf) if x != OK}
+            detail += f"; {len(bad)} of {B} sequences in error: {dict(list(bad.items())[:16])}"
+        raise TmsError(rc, where, detail)
+
+
+def decode_step_sparse(st, hidden, tok, logit=None, stream=None, check: bool = True):
+    _check(lib().tms_decode_step_sparse(_handle(st), _dev(hidden, _HID, "hidden"), _dev(tok, torch.int32, "tok"),
                                         _dev(logit, torch.float32, "logit"), _stream(stream)),
            "decode_step_sparse")
+    if check:
+        _raise_device_errors(st, stream, "decode_step_sparse")
 
 
-def decode_step_dense_masked(st, hidden, tok, logit=None, full_logits=None, stream=None):
-    _check(lib().tms_decode_step_dense_masked(st, _dev(hidden, _HID, "hidden"), _dev(tok, torch.int32, "tok"),
-                                              _dev(logit, torch.float32, "logit"),
+def decode_step_dense_masked(st, hidden, tok, logit=None, full_logits=None, stream=None, check: bool = True):
+    _check(lib().tms_decode_step_dense_masked(_handle(st), _dev(hidden, _HID, "hidden"),
+                                              _dev(tok, torch.int32, "tok"), _dev(logit, torch.float32, "logit"),
                                               _dev(full_logits, torch.float32, "full_logits"), _stream(stream)),
            "decode_step_dense_masked")
+    if check:
+        _raise_device_errors(st, stream, "decode_step_dense_masked")
 
 
-def decode_k_pointers(st, hidden_seq, tokens, len=None, entries=None, stream=None):  # noqa: A002
+def decode_k_pointers(st, hidden_seq, tokens, len=None, entries=None, stream=None, check: bool = True):  # noqa: A002
     T = hidden_seq.shape[0]
-    _check(lib().tms_decode_k_pointers(st, _dev(hidden_seq, _HID, "hidden_seq"), T,
+    _check(lib().tms_decode_k_pointers(_handle(st), _dev(hidden_seq, _HID, "hidden_seq"), T,
                                        _dev(tokens, torch.int32, "tokens"), _dev(len, torch.int32, "len"),
                                        _dev(entries, torch.int32, "entries"), _stream(stream)),
            "decode_k_pointers")
+    if check:
+        _raise_device_errors(st, stream, "decode_k_pointers")
 
 
-def advance_forced(st, tok, stream=None):
-    _check(lib().tms_advance_forced(st, _dev(tok, torch.int32, "tok"), _stream(stream)), "advance_forced")
+def advance_forced(st, tok, stream=None, check: bool = True):
+    _check(lib().tms_advance_forced(_handle(st), _dev(tok, torch.int32, "tok"), _stream(stream)), "advance_forced")
+    if check:
+        _raise_device_errors(st, stream, "advance_forced")
 
 
 def legal_set(st, legal_tok, n_legal, stream=None):
-    _check(lib().tms_legal_set(st, _dev(legal_tok, torch.int32, "legal_tok"), _dev(n_legal, torch.int32, "n_legal"),
+    _check(lib().tms_legal_set(_handle(st), _dev(legal_tok, torch.int32, "legal_tok"), _dev(n_legal, torch.int32, "n_legal"),
                                _stream(stream)), "legal_set")
 
 
 def legal_mask(st, mask, stream=None):
-    _check(lib().tms_legal_mask(st, _dev(mask, torch.int32, "mask"), _stream(stream)), "legal_mask")
+    _check(lib().tms_legal_mask(_handle(st), _dev(mask, torch.int32, "mask"), _stream(stream)), "legal_mask")
 
 
 def mask_to_rows(mask, V: int, rows, n_rows, stream=None):
@@ -293,7 +337,7 @@ def gather_gemv(emb, hidden, rows, n_rows, out, stream=None):
 
 
 def debug_set_live(st, s: int, edge: int, value: int, stream=None):
-    _check(lib().tms_debug_set_live(st, s, edge, value, _stream(stream)), "debug_set_live")
+    _check(lib().tms_debug_set_live(_handle(st), s, edge, value, _stream(stream)), "debug_set_live")
 
 
 # --------------------------------------------------------------------------- handles

@@ -12,50 +12,7 @@
 #include <string>
 #include <vector>
 
-#include "tms.h"
-#include "kernels.h"
-#include "trie_build.h"
-
-struct tms_trie {
-  tms::HostTrie host;
-  int path = TMS_PATH_AUTO;  // FAST or GLOBAL once uploaded
-  int device = -1;
-  void* dmem = nullptr;
-  size_t dbytes = 0;
-  tms::DevTrie dev{};
-  int refs = 0;
-};
-
-struct tms_state {
-  tms_trie* trie = nullptr;
-  int B = 0, k = 0, H = 0, dtype = 0, device = -1;
-  const void* emb = nullptr;
-  void* dmem = nullptr;
-  size_t dbytes = 0;
-  tms::DevState dev{};
-  int split = 1, split_default = 1;
-  bool fast = false;
-  int loop_mode = TMS_LOOP_RESIDENT;
-  bool dense_mfma = true;  // matrix-core dense head where it applies
-  // A reset asked for and not yet carried out: the next call on the state
-  // applies it on that call's stream (inside the resident loop's kernel when
-  // that is the next call, otherwise as a reset kernel launched first).
-  bool reset_pending = false;
-  // live counts changed by tms_debug_set_live since the last reset: the
-  // bitmask state (which derives liveness from the spent set) does not apply
-  bool live_dirty = false;
-  // every live row equals live0 except on the root paths of the row's stored
-  // completed entries (false until the first reset has run, and after
-  // tms_debug_set_live): a reset may then restore just those paths
-  bool live_by_paths = false;
-  hipStream_t capture = nullptr;
-  hipGraph_t graph = nullptr;
-  hipGraphExec_t gexec = nullptr;
-  const void* g_hidden = nullptr;
-  int32_t g_T = 0;
-  int32_t *g_tokens = nullptr, *g_len = nullptr, *g_entries = nullptr;
-  std::vector<int32_t> host_status;
-};
+#include "handles.h"
 
 namespace {
 
@@ -130,6 +87,51 @@ tms::StepIO make_io(const tms_state* st, const void* hidden) {
 }
 
 }  // namespace
+
+namespace tms {
+
+tms_status api_fail(tms_status s, const std::string& msg) { return fail(s, msg); }
+tms_status api_hip_fail(hipError_t e, const char* what) { return hip_fail(e, what); }
+
+hipError_t enqueue_resident(const tms_trie* trie, const DevState& dev, LoopIO io, int dtype, bool fast,
+                            int loop_mode, bool fresh, bool bitmask, hipStream_t s) {
+  // LDS budget per workgroup for the loop's on-chip copy (the part offers
+  // 160 KiB; a little is left for the kernel's own shared variables)
+  const size_t budget = 160 * 1024 - 2048;
+  int mode;
+  if (fast) {
+    mode = loop_lds_bytes(trie->dev, dev, true) <= budget ? kLoopTrieLds : kLoopFastGlobal;
+    // the bitmask no-repeat state, on request (measured slower than the live
+    // counts for the product catalog: 17.4 vs 15.6 us per answer)
+    if (mode == kLoopTrieLds && trie->dev.emask && bitmask) mode = kLoopTrieMask;
+  } else {
+    mode = loop_lds_bytes(trie->dev, dev, false) <= budget ? kLoopVectorLds : kLoopVectorGlobal;
+  }
+  // Root steps grouped across sequences: one phase per pointer (every
+  // pointer starts at the root), each a grouped root head then the loop up
+  // to the next return to the root; the last phase runs to the end.  Worth
+  // it where the root is wide and shared by many sequences.
+  const HostTrie& h = trie->host;
+  const int root_edges = h.begin[1] - h.begin[0];
+  const bool group = loop_mode == TMS_LOOP_RESIDENT_GROUPED ||
+                     (loop_mode == TMS_LOOP_RESIDENT && dev.B >= 8 && root_edges >= 64);
+  if (!group) return launch_loop(trie->dev, dev, io, dtype, mode, s);
+  // after a grouped root step a phase reads few live counts: keep them in
+  // device memory rather than copying them through LDS every phase
+  if (mode == kLoopVectorLds) mode = kLoopVectorGlobal;
+  const int reset = io.reset;
+  const int phases = fresh ? dev.k : dev.k + 1;
+  for (int p = 0; p < phases; ++p) {
+    io.reset = p == 0 ? reset : kResetNone;
+    io.flags = (p > 0 ? kLoopLater : 0) | (p + 1 < phases ? kLoopExitAtRoot : 0) | kLoopRootKey;
+    io.root_tiles = root_head_tiles(dtype, io.H, root_edges);
+    if (hipError_t e = launch_root_head(trie->dev, dev, io, dtype, root_edges, s); e != hipSuccess) return e;
+    if (hipError_t e = launch_loop(trie->dev, dev, io, dtype, mode, s); e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace tms
 
 extern "C" {
 
@@ -489,6 +491,8 @@ tms_status tms_state_create(tms_trie* trie, int32_t B, int32_t k, const void* em
     const int v = std::atoi(env);
     if (v >= TMS_LOOP_RESIDENT && v <= TMS_LOOP_RESIDENT_GROUPED) st->loop_mode = v;
   }
+  if (const char* env = std::getenv("TMS_BITMASK"))
+    if (env[0] == '1' && trie->dev.emask) st->norepeat = TMS_NOREPEAT_BITMASK;
   st->host_status.assign(B, 0);
   e = hipStreamCreateWithFlags(&st->capture, hipStreamNonBlocking);
   if (e != hipSuccess) {
@@ -643,45 +647,9 @@ tms_status tms_decode_k_pointers(tms_state* st, const void* hidden_seq, int32_t 
     io.entries = entries;
     const bool fresh = st->reset_pending;  // every sequence starts at the root
     io.reset = reset_kind(st);             // the kernel resets its sequence first
-    // LDS budget per workgroup for the loop's on-chip copy (the part offers
-    // 160 KiB; a little is left for the kernel's own shared variables)
-    const size_t budget = 160 * 1024 - 2048;
-    int mode;
-    if (st->fast) {
-      mode = tms::loop_lds_bytes(st->trie->dev, st->dev, true) <= budget ? tms::kLoopTrieLds : tms::kLoopFastGlobal;
-      // the bitmask no-repeat state, on request (measured slower than the
-      // live counts for the product catalog: 17.4 vs 15.6 us per answer)
-      const char* bm = std::getenv("TMS_BITMASK");
-      if (mode == tms::kLoopTrieLds && st->trie->dev.emask && !st->live_dirty && bm && bm[0] == '1')
-        mode = tms::kLoopTrieMask;
-    } else {
-      mode = tms::loop_lds_bytes(st->trie->dev, st->dev, false) <= budget ? tms::kLoopVectorLds
-                                                                           : tms::kLoopVectorGlobal;
-    }
-    // Root steps grouped across sequences: one phase per pointer (every
-    // pointer starts at the root), each a grouped root head then the loop up
-    // to the next return to the root; the last phase runs to the end.  Worth
-    // it where the root is wide and shared by many sequences.
-    const tms::HostTrie& h = st->trie->host;
-    const int root_edges = h.begin[1] - h.begin[0];
-    const bool group = st->loop_mode == TMS_LOOP_RESIDENT_GROUPED ||
-                       (st->loop_mode == TMS_LOOP_RESIDENT && st->B >= 8 && root_edges >= 64);
-    if (!group) {
-      TMS_HIP(tms::launch_loop(st->trie->dev, st->dev, io, st->dtype, mode, s), "loop launch");
-    } else {
-      // after a grouped root step a phase reads few live counts: keep them
-      // in device memory rather than copying them through LDS every phase
-      if (mode == tms::kLoopVectorLds) mode = tms::kLoopVectorGlobal;
-      const int reset = io.reset;
-      const int phases = fresh ? st->k : st->k + 1;
-      for (int p = 0; p < phases; ++p) {
-        io.reset = p == 0 ? reset : tms::kResetNone;
-        io.flags = (p > 0 ? tms::kLoopLater : 0) | (p + 1 < phases ? tms::kLoopExitAtRoot : 0) | tms::kLoopRootKey;
-        io.root_tiles = tms::root_head_tiles(st->dtype, st->H, root_edges);
-        TMS_HIP(tms::launch_root_head(st->trie->dev, st->dev, io, st->dtype, root_edges, s), "root head launch");
-        TMS_HIP(tms::launch_loop(st->trie->dev, st->dev, io, st->dtype, mode, s), "loop launch");
-      }
-    }
+    const bool bitmask = st->norepeat == TMS_NOREPEAT_BITMASK && !st->live_dirty;
+    TMS_HIP(tms::enqueue_resident(st->trie, st->dev, io, st->dtype, st->fast, st->loop_mode, fresh, bitmask, s),
+            "loop launch");
     if (fresh) reset_enqueued(st);
     return TMS_OK;
   }
@@ -805,6 +773,15 @@ tms_status tms_state_set_loop(tms_state* st, int32_t mode) {
     return fail(TMS_ERR_INVALID_ARG, "unknown loop mode");
   st->loop_mode = mode;
   destroy_graph(st);
+  return TMS_OK;
+}
+
+tms_status tms_state_set_norepeat(tms_state* st, int32_t kind) {
+  if (!st || (kind != TMS_NOREPEAT_LIVE && kind != TMS_NOREPEAT_BITMASK))
+    return fail(TMS_ERR_INVALID_ARG, "unknown no-repeat state");
+  if (kind == TMS_NOREPEAT_BITMASK && !st->trie->dev.emask)
+    return fail(TMS_ERR_INVALID_ARG, "the bitmask no-repeat state needs a catalog of at most 128 entries");
+  st->norepeat = kind;
   return TMS_OK;
 }
 
