@@ -279,6 +279,33 @@ tms_status tms_state_set_norepeat(tms_state* st, int32_t kind);
 /* Workgroups per sequence used by the fused step, and its grid size. */
 tms_status tms_state_get_launch(const tms_state* st, int32_t* split, int32_t* grid);
 
+/* ------------------------------------------------------ no allocation -- */
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): one whole
+ * answer per sequence, exactly as tms_state_create + tms_decode_k_pointers on
+ * a reset state (same kernels, bit-identical outputs), but with no state
+ * handle: the per-sequence decode state (live counts, spent flags, path,
+ * entries, argmax slots) lives in a device array of the library,
+ * TMS_NOALLOC_SCRATCH_BYTES per GPU, allocated with the code object when the
+ * library is first used on a GPU and held until the process ends.  The call
+ * allocates nothing; the kernels initialise every word of the scratch they
+ * read, so nothing carries over from an earlier call.
+ * trie: uploaded on the current device; emb dev [V][H] (dtype, H as for
+ * tms_state_create); hidden_seq dev [T][B][H]; outputs as for
+ * tms_decode_k_pointers plus status dev int32 [B] (required: the per-sequence
+ * tms_status, the only error report of the device for this call).
+ * Errors: INVALID_ARG (as tms_state_create / tms_decode_k_pointers, null
+ * status, or a batch whose state needs more than TMS_NOALLOC_SCRATCH_BYTES:
+ * about B * (4 * n_edges + 4 * max_depth + 8 * k + 2 * root edges + 64)
+ * bytes), K, HIP.  All calls on one GPU share its scratch: calls that overlap
+ * on that GPU (other streams, other host threads) race, so serialise them. */
+#define TMS_NOALLOC_SCRATCH_BYTES (32ll << 20)
+tms_status tms_decode_k_pointers_noalloc(const tms_trie* trie, const void* emb, tms_dtype dtype, int32_t H,
+                                         int32_t B, int32_t k, const void* hidden_seq, int32_t T,
+                                         int32_t* tokens, int32_t* len, int32_t* entries, int32_t* status,
+                                         void* stream);
+
 const char* tms_status_str(tms_status s);
 const char* tms_last_error(void);
 

@@ -44,9 +44,10 @@ EXPORTS = (
     "tms_advance_forced", "tms_legal_set", "tms_legal_mask", "tms_mask_to_rows", "tms_gather_gemv",
     "tms_debug_set_live",
     "tms_state_set_split", "tms_state_set_loop", "tms_state_set_norepeat", "tms_state_get_launch",
-    "tms_status_str", "tms_last_error",
+    "tms_decode_k_pointers_noalloc", "tms_status_str", "tms_last_error",
 )
 NOREPEAT_LIVE, NOREPEAT_BITMASK = 0, 1
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class TmsError(RuntimeError):
@@ -95,6 +96,7 @@ def lib():
             "tms_state_set_split": [P, i32],
             "tms_state_set_loop": [P, i32],
             "tms_state_set_norepeat": [P, i32],
+            "tms_decode_k_pointers_noalloc": [P, P, C.c_int, i32, i32, i32, P, i32, P, P, P, P, P],
             "tms_state_get_launch": [P, P, P],
         }
         for name, args in sig.items():
@@ -305,6 +307,29 @@ def decode_k_pointers(st, hidden_seq, tokens, len=None, entries=None, stream=Non
            "decode_k_pointers")
     if check:
         _raise_device_errors(st, stream, "decode_k_pointers")
+
+
+def decode_k_pointers_noalloc(trie, emb, k: int, hidden_seq, tokens, status, len=None, entries=None,  # noqa: A002
+                              stream=None, check: bool = True):
+    """One whole answer per sequence with the decode state in the library's
+    per-GPU scratch (no state handle, no allocation).  status: dev int32 [B].
+    check: synchronise and raise TmsError on any per-sequence device error."""
+    T, B, H = hidden_seq.shape
+    if emb.dim() != 2 or emb.shape[1] != H:
+        raise ValueError("emb must be [V][H] with the hidden size of hidden_seq")
+    _check(lib().tms_decode_k_pointers_noalloc(trie.h if isinstance(trie, Trie) else trie, _dev(emb, name="emb"),
+                                               _dtype_code(emb), H, B, k, _dev(hidden_seq, _HID, "hidden_seq"), T,
+                                               _dev(tokens, torch.int32, "tokens"), _dev(len, torch.int32, "len"),
+                                               _dev(entries, torch.int32, "entries"),
+                                               _dev(status, torch.int32, "status"), _stream(stream)),
+           "decode_k_pointers_noalloc")
+    if check:
+        torch.cuda.synchronize()
+        bad = status.cpu().numpy()
+        if (bad != OK).any():
+            first = int(np.nonzero(bad != OK)[0][0])
+            raise TmsError(int(bad[first]), "decode_k_pointers_noalloc",
+                           f"sequence {first}; {int((bad != OK).sum())} of {B} sequences in error")
 
 
 def advance_forced(st, tok, stream=None, check: bool = True):
