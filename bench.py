@@ -1,20 +1,26 @@
 """Benchmark of the trie-constrained sparse decode on one MI355X.
 
 One bench step = one whole answer for one batch of the product-scale workload
-(V=151936, H=2048 bf16 tied embedding, 42-tool catalog, k=3, B=1): reset the
-decode state, then the device-resident loop (one kernel, one workgroup per
-sequence) until every sequence has emitted exactly k pointers.  value = decode
-steps per second (lockstep steps that emitted a token), over K timed steps
-after W warmup steps, bracketed by device synchronisations.
+(V=151936, H=2048 bf16 tied embedding, 42-tool catalog, k=3, B=1): the decode
+state is reset and the device-resident loop (one kernel, one workgroup per
+sequence, the reset applied inside it) runs until every sequence has emitted
+exactly k pointers.  The K timed answers are captured once into a HIP graph
+(as a serving loop would) and replayed; each replay is bracketed by HIP events
+on the stream the kernels run on, and by device synchronisations.  value =
+decode steps per second = steps per answer / median time per answer; the
+eager per-call figures (Python launches, host in the loop) are reported beside
+it.  The graph's outputs are checked against an eager answer before any number
+is reported.
 
-Also reported on the same line: the loop kernel's roofline (algorithmic bytes
-of one answer / that launch's duration, timed with HIP events on the launch
-stream), the same answers through the hipGraph of per-step kernels, the
-batch-64 workloads, the gather-GEMV bandwidth stress shapes (64 sequences x
-256 or x 887 distinct rows per launch, cycling through disjoint row sets of
-the 622 MB table), the dense+mask step, and the CPU oracle timed on this host
-(cpu_baseline leg, the only place the oracle is used here).  --only copyref
-runs a 256 MiB device copy that calibrates the HBM byte counters.
+Also on the same line: the loop kernel's roofline (the unique rows and hidden
+vectors the head steps must read, over the kernel's duration), the batch-64
+and batch-256 workloads (unique-row rates: rows shared by sequences are read
+once), the per-step kernel graph (the form a caller with its own forward pass
+uses), the gather-GEMV bandwidth stress shapes next to a hand-written
+streaming-read kernel timed on the same byte counts, the dense+mask step, and
+the CPU oracle on every host thread (cpu_baseline, the only place the oracle
+is used here).  --only copyref runs a 256 MiB device copy that calibrates the
+HBM byte counters.
 """
 from __future__ import annotations
 
@@ -22,6 +28,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -46,11 +53,43 @@ def _kernel_hash():
     return h.hexdigest()[:16]
 
 
+def _to_dev(a):
+    import numpy as np
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _graph_time(fn, n_inner: int, reps: int):
+    """Capture n_inner calls of fn into one HIP graph and replay it reps times,
+    each replay between two events on the replay stream; returns (median
+    microseconds per inner call, every replay's per-call microseconds)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        for _ in range(n_inner):
+            fn()
+    torch.cuda.synchronize()
+    g.replay()  # first replay: uploads the graph
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) * 1e3 / n_inner)
+    return statistics.median(per), per, g
+
+
 class Workload:
     """Device copies of one seeded workload plus a state for it."""
 
     def __init__(self, cid, B=None):
-        import numpy as np
         import torch
 
         import trie_masked_sparse_amd as tms
@@ -74,126 +113,214 @@ class Workload:
         self.len = torch.empty(self.B, dtype=torch.int32, device="cuda")
         self.entries = torch.empty((self.B, c.k), dtype=torch.int32, device="cuda")
         self.esz = 2 if c.dtype == "bf16" else 4
-        self.np = np
 
-    def decode(self, ev=None):
-        """One bench step: reset, then the whole answer.  ev: optional pair of
-        events recorded around the decode launch (after the reset)."""
+    def decode(self):
+        """One bench step: reset (applied inside the loop kernel), then the
+        whole answer; asynchronous."""
         import trie_masked_sparse_amd as tms
         self.state.reset()
-        if ev:
-            ev[0].record()
-        tms.decode_k_pointers(self.state.h, self.hid, self.tokens, self.len, self.entries, check=False)
-        if ev:
-            ev[1].record()
+        tms.decode_k_pointers(self.state, self.hid, self.tokens, self.len, self.entries, check=False)
 
-    def legal_profile(self):
-        """Per step: legal-set sizes and unique rows, from the library's own
-        materialiser, along the decode's own path (host-driven steps)."""
+    def outputs(self):
+        return self.tokens.cpu().numpy().copy(), self.len.cpu().numpy().copy(), self.entries.cpu().numpy().copy()
+
+    def byte_profile(self):
+        """Bytes per answer along the decode's own path, from the library's
+        materialiser over host-driven steps.  Per step and sequence with legal
+        set L: a head step (|L| >= 2) reads |L| rows and one hidden vector; a
+        forced step (|L| = 1) reads nothing (its token is determined).
+        head_gathered: every sequence reads its own rows; head_unique: a row
+        needed by several sequences in the same step counted once (the union of
+        the legal sets, the least that must come from memory); sec8d_gathered:
+        every step counted, forced ones included."""
+        import numpy as np
         import torch
 
         import trie_masked_sparse_amd as tms
-        np = self.np
         cap = self.info["cap"]
         legal = torch.empty((self.B, cap), dtype=torch.int32, device="cuda")
         nleg = torch.empty(self.B, dtype=torch.int32, device="cuda")
         tok = torch.empty(self.B, dtype=torch.int32, device="cuda")
         self.state.reset()
-        n_rows, n_active, n_unique = [], [], []
+        row = self.c.hidden * self.esz
+        g_head = u_head = g_all = 0
+        head_steps = rows_head = 0
         for t in range(self.T):
-            tms.legal_set(self.state.h, legal, nleg)
+            tms.legal_set(self.state, legal, nleg)
             lg, nl = legal.cpu().numpy(), nleg.cpu().numpy()
             act = nl >= 0
-            n_active.append(int(act.sum()))
-            n_rows.append(int(nl[act].sum()))
+            g_all += int(nl[act].sum()) + int(act.sum())
+            head = np.nonzero(nl >= 2)[0]
             u = set()
-            for b in np.nonzero(act)[0]:
+            for b in head:
                 u.update(lg[b, :nl[b]].tolist())
-            n_unique.append(len(u))
-            tms.decode_step_sparse(self.state.h, self.hid[t], tok)
+            g_head += int(nl[head].sum()) + len(head)
+            rows_head += int(nl[head].sum())
+            u_head += len(u) + len(head)
+            head_steps += len(head)
+            tms.decode_step_sparse(self.state, self.hid[t], tok, check=False)
         torch.cuda.synchronize()
-        return np.array(n_rows), np.array(n_active), np.array(n_unique)
+        return {"head_gathered": g_head * row, "head_unique": u_head * row, "sec8d_gathered": g_all * row,
+                "head_steps": head_steps, "head_rows": rows_head, "flops": 2 * self.c.hidden * rows_head}
 
     def close(self):
         self.state.close()
         self.trie.close()
 
 
-def _to_dev(a):
+def time_answers(w: Workload, steps: int, warmup: int, reps: int = 5):
+    """Eager answers (host launch per call) and graph-replayed answers."""
     import numpy as np
-    import torch
-    if a.dtype == np.uint16:
-        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
-    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
-
-
-def time_decode(w: Workload, steps: int, warmup: int):
     import torch
     for _ in range(warmup):
         w.decode()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ref = w.outputs()
+    assert (w.state.status() == 0).all(), "decode reported a device error"
+    # eager: one event pair per call, and the wall clock over all of them
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0.record()
-    for i in range(steps):
+    for a, b in evs:
+        a.record()
         w.decode()
-    e1.record()
+        b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gpu_ms = e0.elapsed_time(e1)
-    # a second pass of the same bench steps with an event pair around each
-    # decode launch: the loop kernel's own duration, for the roofline (kept out
-    # of the region above, where the extra markers would lengthen the timeline)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i in range(steps):
-        w.decode(evs[i])
+    eager_us = statistics.median(a.elapsed_time(b) * 1e3 for a, b in evs)
+    # graph: the same K answers captured once, replayed
+    per_answer_us, per_rep, g = _graph_time(w.decode, steps, reps)
     torch.cuda.synchronize()
-    decode_us = sum(a.elapsed_time(b) for a, b in evs) * 1e3 / steps
-    ln = w.len.cpu().numpy()
+    got = w.outputs()
+    for x, y in zip(ref, got):
+        assert np.array_equal(x, y), "graph-replayed answers differ from the eager answer"
     assert (w.state.status() == 0).all(), "decode reported a device error"
-    steps_per_call = int(ln.max())  # lockstep steps that emitted a token
-    tokens_per_call = int(ln.sum())
+    del g
+    steps_per_call = int(ref[1].max())  # lockstep steps that emitted a token
+    tokens_per_call = int(ref[1].sum())
     return {
-        "wall_s": wall, "gpu_ms": gpu_ms, "ms_per_call": wall * 1e3 / steps, "decode_launch_us": decode_us,
-        "steps_per_s": steps_per_call * steps / wall, "tokens_per_s": tokens_per_call * steps / wall,
-        "steps_per_call": steps_per_call, "tokens_per_call": tokens_per_call, "launches_per_call": w.T,
+        "us_per_answer": per_answer_us, "us_per_answer_each_replay": per_rep,
+        "steps_per_s": steps_per_call / (per_answer_us * 1e-6), "tokens_per_s": tokens_per_call / (per_answer_us * 1e-6),
+        "eager_event_median_us": eager_us, "eager_wall_us_per_call": wall * 1e6 / steps,
+        "eager_steps_per_s": steps_per_call * steps / wall,
+        "steps_per_call": steps_per_call, "tokens_per_call": tokens_per_call,
+        "launches_per_answer": 2 * w.c.k if w.grouped else 1,
     }
 
 
-def loop_roofline(w: Workload, timed: dict, steps: int):
-    """Algorithmic bytes of one whole answer (the resident loop kernel's launch)
-    over that launch's average duration.  A bench step is exactly one launch of
-    the loop kernel (the state reset is carried out inside it), so the duration
-    is the timed region's GPU time (HIP events on the launch stream) over the
-    number of steps; the event pairs recorded around single launches in a
-    second pass are reported beside it (they also count the dispatch)."""
-    n_rows, n_act, n_uni = w.legal_profile()
-    H, esz = w.c.hidden, w.esz
-    gathered = float(((n_rows + n_act) * H * esz).sum())   # legal rows + hidden vectors
-    unique = float(((n_uni + n_act) * H * esz).sum())
-    launch_us = timed["gpu_ms"] * 1e3 / steps
-    return {
-        "kernel": "loop_kernel", "avg_launch_us": launch_us, "event_pair_us": timed["decode_launch_us"],
-        "alg_bytes_per_launch": gathered, "unique_bytes_per_launch": unique,
-        "achieved_GBps": gathered / (launch_us * 1e-6) / 1e9, "unique_GBps": unique / (launch_us * 1e-6) / 1e9,
-        "flops_per_launch": float(2 * H * n_rows.sum()),
-        "rows_per_step": [int(x) for x in n_rows],
-    }
+def loop_rates(w: Workload, r: dict, prof: dict):
+    t = r["us_per_answer"] * 1e-6
+    return {"unique_GBps": prof["head_unique"] / t / 1e9, "gathered_GBps": prof["head_gathered"] / t / 1e9,
+            "unique_bytes_per_answer": prof["head_unique"], "gathered_bytes_per_answer": prof["head_gathered"],
+            "sec8d_gathered_bytes_per_answer": prof["sec8d_gathered"], "head_steps_per_answer": prof["head_steps"],
+            "flops_per_answer": prof["flops"]}
 
 
 def graph_mode(w: Workload, steps: int, warmup: int):
-    """The same answers through the hipGraph of per-step kernels."""
+    """The same answers through the hipGraph of per-step kernels (one launch
+    per step, the form a caller whose forward pass sits between steps uses)."""
+    import torch
+
     import trie_masked_sparse_amd as tms
-    tms.state_set_loop(w.state.h, tms.LOOP_GRAPH)
-    r = time_decode(w, steps, warmup)
-    tms.state_set_loop(w.state.h, tms.LOOP_RESIDENT)
-    return {"steps_per_s": r["steps_per_s"], "ms_per_call": r["ms_per_call"],
-            "step_kernel_launches_per_call": w.T}
+    tms.state_set_loop(w.state, tms.LOOP_GRAPH)
+    for _ in range(warmup):
+        w.decode()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        w.decode()
+    e1.record()
+    torch.cuda.synchronize()
+    tms.state_set_loop(w.state, tms.LOOP_RESIDENT)
+    per = e0.elapsed_time(e1) * 1e3 / steps
+    spc = int(w.len.max().item())
+    return {"us_per_answer": per, "steps_per_s": spc / (per * 1e-6), "us_per_step_kernel": per / w.T,
+            "step_kernel_launches_per_answer": w.T}
 
 
-def stress_gemv(steps: int, warmup: int, emb, emb_np, rows_per_seq: int):
+def launch_floor(w: Workload, reps: int = 20):
+    """Per-launch cost of the step kernel when it has nothing to do: the
+    hipGraph of T step kernels replayed on a finished state."""
+    import torch
+
+    import trie_masked_sparse_amd as tms
+    tms.state_set_loop(w.state, tms.LOOP_GRAPH)
+    w.decode()  # build the graph; every sequence finishes
+    tms.decode_k_pointers(w.state, w.hid, w.tokens, w.len, w.entries, check=False)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        tms.decode_k_pointers(w.state, w.hid, w.tokens, w.len, w.entries, check=False)
+    e1.record()
+    torch.cuda.synchronize()
+    tms.state_set_loop(w.state, tms.LOOP_RESIDENT)
+    per_call = e0.elapsed_time(e1) * 1e3 / reps
+    return {"us_per_step_kernel": per_call / (w.T + 1), "launches_per_call": w.T + 1, "us_per_call": per_call}
+
+
+READ_REF = {"grid": 0, "unroll": 4}  # set by streaming_read_reference's sweep
+
+
+def stress_sizes(V: int, H: int, esz: int = 2):
+    """Row bytes per launch of the two stress shapes (64 sequences x 256 or
+    x 887 distinct rows), and the byte counts the streaming reference reads:
+    the same two, plus the 64 x 256 shape's whole working set (its disjoint
+    row sets together), every one within the V x H table."""
+    sizes = {R: 64 * R * H * esz for R in (256, 887)}
+    working_set = (V // (64 * 256)) * sizes[256]
+    ref = sorted(set(sizes.values())) + [working_set]
+    assert max(ref) <= V * H * esz
+    return sizes, ref
+
+
+def streaming_read_reference(table, sizes, reps: int = 5):
+    """The in-tree streaming-read kernel (tms_read_reference) on contiguous
+    slices of the table, cycling through disjoint slices as the stress gathers
+    cycle through disjoint row sets.  The launch shape (workgroups, loads in
+    flight) is the best of a small sweep at the largest size."""
+    import torch
+
+    import trie_masked_sparse_amd as tms
+    flat = table.view(-1)
+    total = flat.numel() * flat.element_size()
+    out = torch.zeros(1024, dtype=torch.int32, device="cuda")
+
+    def run(nbytes, grid, unroll):
+        n_sl = max(1, total // nbytes)
+        el = nbytes // flat.element_size()
+        slices = [flat[i * el:(i + 1) * el] for i in range(n_sl)]
+        assert all(x.numel() == el for x in slices), "a slice runs past the table"
+        it = iter(range(1 << 30))
+
+        def one():
+            tms.read_reference(slices[next(it) % n_sl], out, grid, unroll, nbytes)
+        us, _, g = _graph_time(one, n_sl * 2, reps)
+        del g
+        return us, nbytes / (us * 1e-6) / 1e9, n_sl
+
+    for n in sizes:
+        if n > total:
+            raise ValueError(f"reference size {n} exceeds the {total}-byte table")
+    big = max(sizes)
+    sweep = {}
+    for grid in (0, 1024, 2048, 4096, 8192):
+        for unroll in (2, 4, 8):
+            sweep[f"grid={grid},unroll={unroll}"] = run(big, grid, unroll)[1]
+    best = max(sweep, key=sweep.get)
+    READ_REF["grid"], READ_REF["unroll"] = (int(x.split("=")[1]) for x in best.split(","))
+    res = {"kernel": "read_ref_kernel (tms_read_reference)", "launch": dict(READ_REF), "sweep_GBps": sweep}
+    for n in sizes:
+        us, gbps, n_sl = run(n, READ_REF["grid"], READ_REF["unroll"])
+        res[f"{n}"] = {"bytes": n, "us": us, "GBps": gbps, "disjoint_slices": n_sl}
+    return res
+
+
+def stress_gemv(steps: int, emb, emb_np, rows_per_seq: int, reps: int = 5):
     """64 sequences x rows_per_seq distinct rows per launch, cycling through
-    disjoint row sets so that no launch re-reads a row of the previous one."""
+    disjoint row sets so that no launch re-reads a row of the previous one;
+    the launches are graph-replayed (no host gap between them)."""
     import numpy as np
     import torch
 
@@ -207,17 +334,12 @@ def stress_gemv(steps: int, warmup: int, emb, emb_np, rows_per_seq: int):
     hid = _to_dev(bf16_bits_from_f32(rng.standard_normal((B, H), dtype=np.float32)))
     n = torch.full((B,), R, dtype=torch.int32, device="cuda")
     out = torch.empty((B, R), dtype=torch.float32, device="cuda")
-    for i in range(warmup * S):
-        tms.gather_gemv(emb, hid, sets[i % S], n, out)
-    torch.cuda.synchronize()
-    iters = max(steps, 1) * S
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(iters):
-        tms.gather_gemv(emb, hid, sets[i % S], n, out)
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / iters  # back-to-back launches on the launch stream
+    it = iter(range(1 << 30))
+
+    def one():
+        tms.gather_gemv(emb, hid, sets[next(it) % S], n, out)
+    us, per, g = _graph_time(one, S * max(2, steps // 10), reps)
+    del g
     nbytes = B * R * H * 2 + B * H * 2
     gbps = nbytes / (us * 1e-6) / 1e9
     return {"shape": f"64 seq x {R} distinct rows, H={H} bf16, {S} disjoint sets ({S * B * R * H * 2 >> 20} MiB)",
@@ -238,47 +360,6 @@ def copy_reference(reps: int = 5):
         dst.copy_(src)
     torch.cuda.synchronize()
     return {"bytes_read": src.numel(), "bytes_written": dst.numel(), "reps": reps}
-
-
-def streaming_read_reference(nbytes: int = 604 << 20, reps: int = 5):
-    """A plain streaming read of a buffer the size of the stress working set,
-    the reference the gathers are compared with: torch's row sums over a
-    [n / 4096, 4096] fp32 view (the fastest of the library's plain reductions
-    measured here: sum, amax and row sums in bf16/fp32; full sums reach only
-    3.3-3.8 TB/s)."""
-    import torch
-    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda").view(-1, 4096)
-    x.sum(dim=1)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        x.sum(dim=1)
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / reps
-    return {"bytes": nbytes, "us": us, "GBps": nbytes / (us * 1e-6) / 1e9, "kernel": "torch row sums (fp32)"}
-
-
-def launch_floor(w: Workload, reps: int = 20):
-    """Per-launch cost of the step kernel when it has nothing to do: the
-    hipGraph of T step kernels replayed on a finished state."""
-    import torch
-
-    import trie_masked_sparse_amd as tms
-    tms.state_set_loop(w.state.h, tms.LOOP_GRAPH)
-    w.decode()  # build the graph; every sequence finishes
-    tms.decode_k_pointers(w.state.h, w.hid, w.tokens, w.len, w.entries, check=False)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        tms.decode_k_pointers(w.state.h, w.hid, w.tokens, w.len, w.entries, check=False)
-    e1.record()
-    torch.cuda.synchronize()
-    tms.state_set_loop(w.state.h, tms.LOOP_RESIDENT)
-    per_call = e0.elapsed_time(e1) * 1e3 / reps
-    return {"us_per_step_kernel": per_call / (w.T + 1), "launches_per_call": w.T + 1, "us_per_call": per_call}
 
 
 def environment():
@@ -312,7 +393,7 @@ def mask_fed_head_us(w: Workload, reps=20):
     out = torch.empty((B, cap), dtype=torch.float32, device="cuda")
     w.state.reset()
     calls = {
-        "legal_mask": lambda: tms.legal_mask(w.state.h, mask),
+        "legal_mask": lambda: tms.legal_mask(w.state, mask),
         "mask_to_rows": lambda: tms.mask_to_rows(mask, V, rows, n),
         "gather_gemv": lambda: tms.gather_gemv(w.emb, w.hid[0], rows, n, out),
     }
@@ -338,14 +419,14 @@ def dense_step_us(w: Workload, reps=5):
     import trie_masked_sparse_amd as tms
     tok = torch.empty(w.B, dtype=torch.int32, device="cuda")
     w.state.reset()
-    tms.decode_step_dense_masked(w.state.h, w.hid[0], tok)
+    tms.decode_step_dense_masked(w.state, w.hid[0], tok, check=False)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     w.state.reset()
     e0.record()
     n = min(reps, w.T)
     for t in range(n):
-        tms.decode_step_dense_masked(w.state.h, w.hid[t], tok, check=False)
+        tms.decode_step_dense_masked(w.state, w.hid[t], tok, check=False)
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / n
@@ -360,73 +441,44 @@ def dense_step_us(w: Workload, reps=5):
             "TFLOPs": tflops, "frac_of_compute_peak": tflops / (2500.0 if mfma else 157.3)}
 
 
-def cpu_baseline(w: Workload, min_seconds: float):
-    """The oracle (plain C, fp64, one thread) decoding the same batch, repeated."""
-    import oracle
-    otr = oracle.Trie(__import__("synth").catalog(w.cid), w.c.vocab, w.c.sep, w.c.stop)
-    reps, t0 = 0, time.perf_counter()
-    steps = 0
-    while True:
-        out = oracle.decode(otr, w.c.k, w.emb_np, w.hid_np)
-        reps += 1
-        steps += int(out["len"].max())
-        el = time.perf_counter() - t0
-        if el >= min_seconds:
-            break
-    return {"value": steps / el, "unit": "steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} repetitions of the full {w.cid} decode (B={w.B}, {int(out['len'].max())} steps, "
-                      f"{int(out['len'].sum())} tokens each), {el:.1f} s, single thread, gcc -O2 fp64"}
-
-
-def cpu_baseline_threads(w: Workload, seq_sample=None):
-    """The oracle decoding the same batch once: on one thread, and with the
-    sequences split over the host's threads (ctypes releases the GIL around
-    each call).  seq_sample: decode only these sequences (large batches)."""
+def cpu_baseline(w: Workload, seconds: float, copies: int = 64):
+    """The oracle (plain C, fp64) decoding the bench's answer on every host
+    thread: each thread decodes batches of `copies` copies of the same
+    sequence (one C call per batch, so the interpreter lock is not the
+    limit) until `seconds` of wall time have passed; value = steps over all
+    threads / wall time.  The single-thread rate is measured the same way."""
     import concurrent.futures as cf
 
     import numpy as np
 
     import oracle
-    otr = oracle.Trie(__import__("synth").catalog(w.cid), w.c.vocab, w.c.sep, w.c.stop)
-    hid = w.hid_np if seq_sample is None else np.ascontiguousarray(w.hid_np[:, seq_sample, :])
-    t0 = time.perf_counter()
-    oracle.decode(otr, w.c.k, w.emb_np, hid)
-    one = time.perf_counter() - t0
-    n = min(os.cpu_count() or 1, hid.shape[1])
-    parts = [np.ascontiguousarray(hid[:, i::n, :]) for i in range(n)]
-    t0 = time.perf_counter()
-    with cf.ThreadPoolExecutor(n) as ex:
-        list(ex.map(lambda h: oracle.decode(otr, w.c.k, w.emb_np, h), parts))
-    many = time.perf_counter() - t0
-    return {"seconds_1_thread": one, "seconds_n_threads": many, "threads": n, "sequences": int(hid.shape[1])}
+    from synth import catalog
+    otr = oracle.Trie(catalog(w.cid), w.c.vocab, w.c.sep, w.c.stop)
+    hid = np.ascontiguousarray(np.repeat(w.hid_np, copies, axis=1))
+    one = oracle.decode(otr, w.c.k, w.emb_np, w.hid_np[:, :1])
+    steps_per_answer = int(one["len"][0])
 
+    def worker(deadline):
+        n = 0
+        while time.perf_counter() < deadline:
+            out = oracle.decode(otr, w.c.k, w.emb_np, hid)
+            n += int(out["len"].sum())
+        return n
 
-def config_table(steps: int, warmup: int, cids=("tiny", "product", "product_deep", "structured", "unstructured",
-                                                 "large")):
-    """Every workload: the resident decode's steps/s and tokens/s, gathered
-    bytes per second, the dense+mask step, and the oracle's time for the
-    same batch (the results table of the bench's plan)."""
-    import numpy as np
-    out = {}
-    for cid in cids:
-        _log(f"table: {cid}")
-        w = Workload(cid)
-        r = time_decode(w, steps, warmup)
-        n_rows, n_act, n_uniq = w.legal_profile()
-        gathered = float(((n_rows + n_act) * w.c.hidden * w.esz).sum())
-        unique = float(((n_uniq + n_act) * w.c.hidden * w.esz).sum())
-        sample = None if w.B <= 64 else list(range(0, w.B, w.B // 24))[:24]
-        row = {"B": w.B, "seeds": {"catalog": w.c.cat_seed, "embedding": w.c.emb_seed, "hidden": w.c.hid_seed},
-               "steps_per_s": r["steps_per_s"], "tokens_per_s": r["tokens_per_s"],
-               "ms_per_call": r["ms_per_call"], "gathered_TBps": gathered / (r["gpu_ms"] * 1e-3 / steps) / 1e12,
-               "unique_TBps": unique / (r["gpu_ms"] * 1e-3 / steps) / 1e12,
-               "gathered_bytes_per_call": gathered, "unique_bytes_per_call": unique,
-               "dense_mask_step_us": dense_step_us(w)["us_per_step"],
-               "oracle": cpu_baseline_threads(w, sample)}
-        out[cid] = row
-        _log(f"table: {cid} {row}")
-        w.close()
-    return out
+    def run(threads, secs):
+        t0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(threads) as ex:
+            total = sum(ex.map(worker, [t0 + secs] * threads))
+        return total / (time.perf_counter() - t0)
+
+    single = run(1, max(1.0, seconds / 4))
+    # the threads this process may run on (the box's share of the host)
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    many = run(n, seconds)
+    return {"value": many, "unit": "steps/s", "cores": n, "kind": "oracle",
+            "sample": f"the product decode ({steps_per_answer} steps per answer, B=1) repeated on {n} host threads, "
+                      f"{copies} copies of the sequence per oracle call, for {seconds:.1f} s of wall time "
+                      f"({seconds * n:.0f} thread-seconds); gcc -O2 scalar fp64; single thread: {single:,.0f} steps/s"}
 
 
 def _pmc_traffic(kernel: str, workload: str):
@@ -442,19 +494,41 @@ def _pmc_traffic(kernel: str, workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
+def workload_line(cid: str, steps: int, warmup: int, per_step_graph: bool = True):
+    """Resident-loop rates of one batched workload."""
+    import trie_masked_sparse_amd as tms
+    _log(f"{cid} workload")
+    w = Workload(cid)
+    r = time_answers(w, steps, warmup)
+    prof = w.byte_profile()
+    rates = loop_rates(w, r, prof)
+    d = {"B": w.B, "steps_per_s": r["steps_per_s"], "tokens_per_s": r["tokens_per_s"],
+         "us_per_answer": r["us_per_answer"], "steps_per_call": r["steps_per_call"],
+         "launches_per_answer": r["launches_per_answer"],
+         "path": "fast" if w.info["path"] == tms.PATH_FAST else "global",
+         "root_steps": "grouped" if w.grouped else "per sequence",
+         "unique_frac_of_8TBps": rates["unique_GBps"] / HBM_PEAK_GBPS, **rates,
+         "eager_event_median_us": r["eager_event_median_us"],
+         "seeds": {"catalog": w.c.cat_seed, "embedding": w.c.emb_seed, "hidden": w.c.hid_seed}}
+    if per_step_graph:
+        d["per_step_kernel_graph"] = graph_mode(w, max(5, steps // 5), 2)
+    w.close()
+    _log(f"{cid}: {d['steps_per_s']:.0f} steps/s, {d['us_per_answer']:.1f} us per answer, "
+         f"unique {d['unique_GBps']:.0f} GB/s")
+    return d
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--configs", default="tiny,product,product_deep,structured,unstructured,large",
-                    help="workloads of the --only configs table")
+    ap.add_argument("--cpu-seconds", type=float, default=2.0)
     ap.add_argument("--only", default="",
-                    help="comma list of headline,b64,stress,dense,cpu,copyref,configs (default: all but copyref, configs)")
+                    help="comma list of headline,b64,large,stress,dense,cpu,copyref (default: all but copyref)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}). "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): this build runs on one GPU. "
               "Sequences shard across GPUs with no per-step exchange; run one process per GPU.", file=sys.stderr)
         sys.exit(2)
     only = set(filter(None, args.only.split(",")))
@@ -475,66 +549,60 @@ def main():
     _log("product-scale workload")
     w = Workload("product")
     if want("headline"):
-        r = time_decode(w, args.steps, args.warmup)
-        line.update({"value": r["steps_per_s"], "unit": "steps/s", "ms_per_step": r["ms_per_call"],
+        r = time_answers(w, args.steps, args.warmup)
+        prof = w.byte_profile()
+        rates = loop_rates(w, r, prof)
+        line.update({"value": r["steps_per_s"], "unit": "steps/s",
+                     "ms_per_step": r["us_per_answer"] / r["steps_per_call"] * 1e-3,
                      "tokens_per_s": r["tokens_per_s"]})
         line["config"] = {
             "workload": "product-scale: V=151936, H=2048 bf16 tied embedding (622 MB), 42-tool catalog "
                         f"({w.info['n_nodes']} trie nodes, cap {w.info['cap']}), k=3, B=1; one bench step = "
-                        "state reset + one whole answer from the resident device loop "
-                        f"(up to {w.T} steps); bf16 inputs, fp32 accumulation",
+                        "state reset + one whole answer from the resident device loop (one kernel; "
+                        f"{r['steps_per_call']} steps, {prof['head_steps']} of them head steps); the K answers are "
+                        "captured in one HIP graph and replayed; bf16 inputs, fp32 accumulation",
             "path": "fast" if w.info["path"] == tms.PATH_FAST else "global",
             "steps_per_call": r["steps_per_call"], "tokens_per_call": r["tokens_per_call"],
             "seeds": {"catalog": w.c.cat_seed, "embedding": w.c.emb_seed, "hidden": w.c.hid_seed}}
         _log(f"headline {r}")
-        rf = loop_roofline(w, r, args.steps)
-        line["roofline"] = {"bound": "hbm", "kernel": rf["kernel"], "achieved": rf["achieved_GBps"],
-                            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": rf["achieved_GBps"] / HBM_PEAK_GBPS,
+        line["roofline"] = {"bound": "hbm", "kernel": "loop_kernel", "achieved": rates["unique_GBps"],
+                            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": rates["unique_GBps"] / HBM_PEAK_GBPS,
                             "traffic": _pmc_traffic("loop", "product"),
-                            "alg_bytes_per_launch": rf["alg_bytes_per_launch"],
-                            "avg_launch_us": rf["avg_launch_us"]}
-        also["product_loop_detail"] = rf
-        also["product_graph_mode"] = graph_mode(w, args.steps, args.warmup)
+                            "alg_bytes_per_launch": prof["head_unique"],
+                            "avg_launch_us": r["us_per_answer"]}
+        also["product_answer"] = {**rates, "us_per_answer": r["us_per_answer"],
+                                  "us_per_answer_each_replay": r["us_per_answer_each_replay"],
+                                  "eager_event_median_us": r["eager_event_median_us"],
+                                  "eager_wall_us_per_call": r["eager_wall_us_per_call"],
+                                  "eager_steps_per_s": r["eager_steps_per_s"]}
+        also["product_per_step_kernel_graph"] = graph_mode(w, args.steps, args.warmup)
         also["product_launch_floor"] = launch_floor(w)
-        _log(f"roofline {line['roofline']}; graph {also['product_graph_mode']}")
+        _log(f"roofline {line['roofline']}; per-step graph {also['product_per_step_kernel_graph']}")
+    if want("b64"):
+        for cid in ("structured", "unstructured"):
+            also[f"{cid}_B64"] = workload_line(cid, max(10, args.steps // 2), args.warmup)
+    if want("large"):
+        also["large_B256"] = workload_line("large", max(5, args.steps // 5), 2, per_step_graph=False)
     if want("dense"):
         also["dense_masked_product_B1"] = dense_step_us(w)
-        _log(f"dense {also['dense_masked_product_B1']}")
         wd = Workload("structured")
         also["dense_masked_structured_B64"] = dense_step_us(wd)
-        _log(f"dense B=64 {also['dense_masked_structured_B64']}")
         also["mask_fed_head_structured_B64"] = mask_fed_head_us(wd)
-        _log(f"mask-fed head B=64 {also['mask_fed_head_structured_B64']}")
         wd.close()
+        _log(f"dense {also['dense_masked_product_B1']} / {also['dense_masked_structured_B64']}")
     if want("stress"):
-        for rows in (256, 887):
-            also[f"gather_gemv_stress_64x{rows}"] = stress_gemv(max(3, args.steps // 5), 2, w.emb, w.emb_np, rows)
-            _log(f"stress {also[f'gather_gemv_stress_64x{rows}']}")
-        ref = streaming_read_reference()
+        sizes, ref_sizes = stress_sizes(w.c.vocab, w.c.hidden)
+        ref = streaming_read_reference(w.emb, ref_sizes)
         also["streaming_read_reference"] = ref
-        for rows in (256, 887):
-            d = also[f"gather_gemv_stress_64x{rows}"]
-            d["frac_of_streaming_read"] = d["achieved_GBps"] / ref["GBps"]
+        for R, nb in sizes.items():
+            d = stress_gemv(args.steps, w.emb, w.emb_np, R)
+            d["streaming_read_same_bytes_GBps"] = ref[f"{nb}"]["GBps"]
+            d["frac_of_streaming_read"] = d["achieved_GBps"] / ref[f"{nb}"]["GBps"]
+            also[f"gather_gemv_stress_64x{R}"] = d
+            _log(f"stress {d}")
         _log(f"streaming read {ref}")
     if want("copyref"):
         also["copy_reference"] = copy_reference()
-    if want("b64"):
-        for cid in ("structured", "unstructured"):
-            _log(f"{cid} workload")
-            wb = Workload(cid)
-            nb = max(5, args.steps // 2)
-            rb = time_decode(wb, nb, args.warmup)
-            rfb = loop_roofline(wb, rb, nb)
-            also[f"{cid}_B64"] = {"steps_per_s": rb["steps_per_s"], "tokens_per_s": rb["tokens_per_s"],
-                                  "ms_per_call": rb["ms_per_call"], "steps_per_call": rb["steps_per_call"],
-                                  "path": "fast" if wb.info["path"] == tms.PATH_FAST else "global",
-                                  "root_steps": "grouped" if wb.grouped else "per sequence",
-                                  "loop_kernel": {k: v for k, v in rfb.items() if k != "rows_per_step"},
-                                  "graph_mode": graph_mode(wb, nb, args.warmup)}
-            _log(f"{cid} {also[f'{cid}_B64']['steps_per_s']:.0f} steps/s")
-            wb.close()
-    if args.only and "configs" in args.only.split(","):
-        also["configs"] = config_table(args.steps, args.warmup, tuple(filter(None, args.configs.split(","))))
     if want("cpu"):
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
         _log(f"cpu {line['cpu_baseline']}")

@@ -233,6 +233,18 @@ tms_status tms_gather_gemv(const void* emb, tms_dtype dtype, int32_t V, int32_t 
                            const int32_t* rows, const int32_t* n_rows, int32_t B, int32_t cap,
                            float* out, void* stream);
 
+/* Measurement reference, not part of the decode path: a plain streaming read
+ * of `bytes` (a positive multiple of 16) of device memory at src, the kernel
+ * the sparse head's achieved bandwidth is compared with ("Understanding
+ * Inference for Systems Engineers", Part 9 "Profiling": bandwidth against a
+ * measured plain streaming kernel).  Each wavefront XORs what it read into
+ * one word of out (dev uint32 [1024], caller-owned), so the loads cannot be
+ * dropped.  grid:
+ * workgroups of 256 threads (0: enough for one pass); unroll: loads in flight
+ * per thread, 1, 2, 4 or 8 (0: 4).  Errors: INVALID_ARG, HIP. */
+tms_status tms_read_reference(const void* src, int64_t bytes, uint32_t* out, int32_t grid, int32_t unroll,
+                              void* stream);
+
 /* Negative tests: set live[s][edge] = value on the device. */
 tms_status tms_debug_set_live(tms_state* st, int32_t s, int32_t edge, int32_t value, void* stream);
 

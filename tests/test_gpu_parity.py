@@ -220,6 +220,46 @@ def test_paths_splits_graph_and_shuffle_identical():
     assert np.array_equal(lg, base[1][perm], equal_nan=True)
 
 
+@pytest.mark.parametrize("cid", ["product", "unstructured"])
+def test_resident_loop_in_captured_graph(cid):
+    """The resident decode (one kernel, or grouped root heads plus loop
+    kernels) captured in a caller's HIP graph with the reset inside it:
+    several replays, with the caller's own eager work and synchronisations in
+    between, each equal to the eager answer."""
+    c, otr, T, hid = config_case(cid)
+    trie = tms.Trie(catalog(cid), c.vocab, c.sep, c.stop)
+    st = tms.State(trie, c.batch, c.k, dev_embedding(cid))
+    hd = to_dev(hid)
+    want = run_k_pointers(st, hd)
+    tok = torch.full((c.batch, T), -7, dtype=torch.int32, device="cuda")
+    ln = torch.zeros(c.batch, dtype=torch.int32, device="cuda")
+    ent = torch.zeros((c.batch, c.k), dtype=torch.int32, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        for _ in range(3):
+            st.reset()
+            tms.decode_k_pointers(st, hd, tok, ln, ent, check=False)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        tok.fill_(-7)
+        ln.zero_()
+        ent.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (tok.cpu().numpy(), ln.cpu().numpy(), ent.cpu().numpy())
+        for a, b in zip(got, want):
+            assert np.array_equal(a, b), (cid, rep)
+        assert (st.status() == 0).all()
+        # eager work on the same state between replays
+        st.reset()
+        e = run_k_pointers(st, hd)
+        assert all(np.array_equal(a, b) for a, b in zip(e, want))
+    del g
+    st.close()
+    trie.close()
+
+
 def test_two_tries_no_contamination():
     """Interleaved steps on two tries and two states give the same results as
     running each alone (each grammar owns its store)."""

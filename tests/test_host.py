@@ -101,3 +101,19 @@ def test_state_needs_device_copy(L):
         assert b"device copy" in L.tms_last_error()
     finally:
         tms.trie_free(h)
+
+
+def test_bench_reference_sizes_fit_the_table():
+    """The streaming reference reads slices of the product table: every byte
+    count it is given must fit inside the table."""
+    import bench
+    V, H = CONFIGS["product"].vocab, CONFIGS["product"].hidden
+    sizes, ref = bench.stress_sizes(V, H)
+    assert all(n <= V * H * 2 for n in ref)
+    assert sizes[256] in ref and sizes[887] in ref
+
+
+def test_read_reference_refuses_bytes_past_the_tensor():
+    import torch
+    with pytest.raises(ValueError):
+        tms.read_reference(torch.zeros(16, dtype=torch.int32), torch.zeros(1024, dtype=torch.int32), nbytes=65)

@@ -44,7 +44,7 @@ EXPORTS = (
     "tms_advance_forced", "tms_legal_set", "tms_legal_mask", "tms_mask_to_rows", "tms_gather_gemv",
     "tms_debug_set_live",
     "tms_state_set_split", "tms_state_set_loop", "tms_state_set_norepeat", "tms_state_get_launch",
-    "tms_decode_k_pointers_noalloc", "tms_status_str", "tms_last_error",
+    "tms_decode_k_pointers_noalloc", "tms_read_reference", "tms_status_str", "tms_last_error",
 )
 NOREPEAT_LIVE, NOREPEAT_BITMASK = 0, 1
 NOALLOC_SCRATCH_BYTES = 32 << 20
@@ -96,6 +96,7 @@ def lib():
             "tms_state_set_split": [P, i32],
             "tms_state_set_loop": [P, i32],
             "tms_state_set_norepeat": [P, i32],
+            "tms_read_reference": [P, C.c_int64, P, i32, i32, P],
             "tms_decode_k_pointers_noalloc": [P, P, C.c_int, i32, i32, i32, P, i32, P, P, P, P, P],
             "tms_state_get_launch": [P, P, P],
         }
@@ -359,6 +360,19 @@ def gather_gemv(emb, hidden, rows, n_rows, out, stream=None):
                                  _dev(hidden, _HID, "hidden"), _dev(rows, torch.int32, "rows"),
                                  _dev(n_rows, torch.int32, "n_rows"), B, cap, _dev(out, torch.float32, "out"),
                                  _stream(stream)), "gather_gemv")
+
+
+def read_reference(src, out, grid: int = 0, unroll: int = 0, nbytes: int | None = None, stream=None):
+    """Streaming read of src (a contiguous GPU tensor; nbytes of it, default
+    all) into the XOR words out (int32 [1024]): the bandwidth reference."""
+    have = src.numel() * src.element_size()
+    n = have if nbytes is None else int(nbytes)
+    if n > have:
+        raise ValueError(f"read_reference: {n} bytes asked of a {have}-byte tensor")
+    if out.numel() < 1024:
+        raise ValueError("read_reference: out must hold 1024 words")
+    _check(lib().tms_read_reference(_dev(src, name="src"), n, _dev(out, torch.int32, "out"), grid, unroll,
+                                    _stream(stream)), "read_reference")
 
 
 def debug_set_live(st, s: int, edge: int, value: int, stream=None):

@@ -749,6 +749,17 @@ tms_status tms_gather_gemv(const void* emb, tms_dtype dtype, int32_t V, int32_t 
   return TMS_OK;
 }
 
+tms_status tms_read_reference(const void* src, int64_t bytes, uint32_t* out, int32_t grid, int32_t unroll,
+                              void* stream) {
+  if (!src || !out || !aligned16(src)) return fail(TMS_ERR_INVALID_ARG, "src or out null, or src not 16-byte aligned");
+  if (bytes < 16 || bytes % 16) return fail(TMS_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+  if (grid < 0 || (unroll != 0 && unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8))
+    return fail(TMS_ERR_INVALID_ARG, "grid must be >= 0 and unroll one of 0, 1, 2, 4, 8");
+  TMS_HIP(tms::launch_read_reference(src, bytes, out, grid, unroll, static_cast<hipStream_t>(stream)),
+          "read reference launch");
+  return TMS_OK;
+}
+
 tms_status tms_debug_set_live(tms_state* st, int32_t s, int32_t edge, int32_t value, void* stream) {
   if (!st) return fail(TMS_ERR_INVALID_ARG, "null state");
   if (s < 0 || s >= st->B || edge < 0 || edge >= st->trie->host.n_edges)

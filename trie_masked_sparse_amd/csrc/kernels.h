@@ -162,6 +162,10 @@ hipError_t launch_gather_gemv(const void* emb, int dtype, int32_t V, int32_t H, 
                               const int32_t* rows, const int32_t* n_rows, int32_t B, int32_t cap,
                               float* out, int split, hipStream_t s);
 hipError_t launch_finalize(const DevState& st, int32_t* len, int32_t* entries, hipStream_t s);
+// Streaming read of bytes (a multiple of 16) from src; grid workgroups of 256
+// threads (0: one pass per thread), unroll 1/2/4/8 loads in flight per thread.
+hipError_t launch_read_reference(const void* src, int64_t bytes, uint32_t* out, int grid, int unroll,
+                                 hipStream_t s);
 hipError_t launch_set_live(const DevTrie& tr, const DevState& st, int32_t seq, int32_t edge,
                            int32_t value, hipStream_t s);
 

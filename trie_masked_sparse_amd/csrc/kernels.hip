@@ -2165,6 +2165,38 @@ __global__ __launch_bounds__(kBlock) void gather_gemv_kernel(const uint4* __rest
 }
 
 // ---------------------------------------------------------------------------
+// Streaming-read reference ("Understanding Inference for Systems Engineers",
+// Part 9 "Profiling": an achieved bandwidth is judged against what a plain
+// streaming kernel reaches on the same machine, not only against the data
+// sheet).  Every thread reads 16-byte words of one contiguous buffer in a
+// grid-stride loop with U non-temporal loads in flight, XORs them together,
+// and each wavefront XORs its result into one of 1024 words of out (spread so
+// that the atomics do not queue on one address), so no load is dead code.
+// ---------------------------------------------------------------------------
+
+template <int U>
+__global__ __launch_bounds__(kBlock) void read_ref_kernel(const uint4* __restrict__ src, int64_t n16,
+                                                          uint32_t* out) {
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  uint32_t x = 0u;
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    u32x4_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + i + u * stride));
+#pragma unroll
+    for (int u = 0; u < U; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + i));
+    x ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) x ^= (uint32_t)__shfl_xor((int)x, d);
+  if (__lane_id() == 0) atomicXor(out + ((blockIdx.x * kWavesPerBlock + wave_id()) & 1023u), x);
+}
+
+// ---------------------------------------------------------------------------
 // State maintenance
 // ---------------------------------------------------------------------------
 
@@ -2488,6 +2520,23 @@ hipError_t launch_gather_gemv(const void* emb, int dtype, int32_t V, int32_t H, 
                               int split, hipStream_t s) {
   return dispatch<GemvLaunch>(dtype, chunks_for(dtype, H), emb, V, H, hidden, rows, n_rows, B, cap, out, split,
                               s);
+}
+
+hipError_t launch_read_reference(const void* src, int64_t bytes, uint32_t* out, int grid, int unroll,
+                                 hipStream_t s) {
+  const int64_t n16 = bytes / 16;
+  auto go = [&](auto k, int u) {
+    int64_t g = grid > 0 ? grid : (n16 + (int64_t)kBlock * u - 1) / ((int64_t)kBlock * u);
+    g = g < 1 ? 1 : (g > (1 << 20) ? (1 << 20) : g);
+    hipLaunchKernelGGL(k, dim3((unsigned)g), dim3(kBlock), 0, s, (const uint4*)src, n16, out);
+    return hipGetLastError();
+  };
+  switch (unroll) {
+    case 1: return go(read_ref_kernel<1>, 1);
+    case 2: return go(read_ref_kernel<2>, 2);
+    case 8: return go(read_ref_kernel<8>, 8);
+    default: return go(read_ref_kernel<4>, 4);
+  }
 }
 
 hipError_t launch_finalize(const DevState& st, int32_t* len, int32_t* entries, hipStream_t s) {
