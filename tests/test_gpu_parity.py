@@ -952,6 +952,110 @@ def test_reset_restores_released_paths(mode):
 
 
 # ---------------------------------------------------------------------------
+# The fused step with the root grouped across sequences
+# ---------------------------------------------------------------------------
+
+def _step_answers(st, hd, mode, loop=None):
+    """Host-driven steps (or a loop form) under a root-grouping mode; tokens,
+    winner logits and the exported state."""
+    tms.state_set_step_grouping(st, mode)
+    st.reset()
+    if loop is None:
+        tok, lg = run_step_loop(st, hd)
+    else:
+        tms.state_set_loop(st, loop)
+        tok, _, _ = run_k_pointers(st, hd)
+        lg = None
+        tms.state_set_loop(st, tms.LOOP_RESIDENT)
+    return tok, lg, st.export(live=True)
+
+
+@pytest.mark.parametrize("dtype,H,B", [("bf16", 2048, 64), ("fp32", 256, 37), ("bf16", 8192, 20), ("bf16", 520, 200),
+                                       ("fp32", 4096, 9)])
+def test_step_root_grouping_bit_identical(dtype, H, B):
+    """The grouped step (root rows read once per tile of members) against the
+    per-sequence step: identical tokens, bit-identical winner logits and
+    identical state after every answer, host-driven and in the graph of step
+    kernels; tokens against the oracle.  Batches that leave the last member
+    tile partly filled, hidden sizes that need 1 to 16 chunks per lane."""
+    rng = np.random.Generator(np.random.PCG64(H * 3 + B))
+    V, k = 2000, 3
+    cat = random_catalog(700 + H + B, 400, 5, V - 2, min_len=2)
+    otr = oracle.Trie(cat, V, V - 2, V - 1)
+    b = otr.csr()["begin"]
+    assert b[1] - b[0] >= 64
+    T = k * (otr.max_depth + 1)
+    emb = _rand_table(rng, V, H, dtype)
+    hid = _rand_hidden(rng, T, B, H, dtype)
+    trie = tms.Trie(cat, V, V - 2, V - 1)
+    st = tms.State(trie, B, k, to_dev(emb))
+    hd = to_dev(hid)
+    keys = ("node", "depth", "done", "status", "finished", "n_emitted", "entries", "live")
+    t0, l0, x0 = _step_answers(st, hd, tms.STEP_GROUP_OFF)
+    t1, l1, x1 = _step_answers(st, hd, tms.STEP_GROUP_ROOT)
+    assert np.array_equal(t0, t1) and np.array_equal(l0, l1, equal_nan=True)
+    for key in keys:
+        assert np.array_equal(x0[key], x1[key]), key
+    t2, _, x2 = _step_answers(st, hd, tms.STEP_GROUP_ROOT, loop=tms.LOOP_GRAPH)
+    assert np.array_equal(t2, t0)
+    for key in keys:
+        assert np.array_equal(x2[key], x0[key]), key
+    compare(t1, ref_decode(otr, k, emb, hid), H, l1, where=f"grouped step {dtype} H={H} B={B}")
+    split, grid = tms.state_get_launch(st)
+    assert grid > B * split  # the root workgroups are part of the grid
+    st.close()
+    trie.close()
+
+
+@pytest.mark.parametrize("cid", ["unstructured", "structured"])
+def test_step_root_grouping_workloads(cid):
+    """The batch-64 workloads through the grouped step (forced on for the
+    structured catalog, whose root has 8 edges): the per-sequence step's tokens
+    and logits bit for bit, and the oracle's tokens."""
+    c, otr, T, hid = config_case(cid)
+    trie = tms.Trie(catalog(cid), c.vocab, c.sep, c.stop)
+    st = tms.State(trie, c.batch, c.k, dev_embedding(cid))
+    hd = to_dev(hid)
+    t0, l0, x0 = _step_answers(st, hd, tms.STEP_GROUP_OFF)
+    t1, l1, x1 = _step_answers(st, hd, tms.STEP_GROUP_ROOT)
+    assert np.array_equal(t0, t1) and np.array_equal(l0, l1, equal_nan=True)
+    for key in ("node", "done", "status", "n_emitted", "entries", "live"):
+        assert np.array_equal(x0[key], x1[key]), key
+    compare(t1, ref_decode(otr, c.k, embedding(cid), hid), c.hidden, l1, where=f"{cid}/grouped step")
+    st.close()
+    trie.close()
+
+
+def test_step_root_grouping_empty_mask_isolated():
+    """An empty root mask for one member under the grouped step: that sequence
+    alone gets EMPTY_MASK, the others decode as without it."""
+    rng = np.random.Generator(np.random.PCG64(99))
+    V, H, B, k = 1500, 256, 12, 2
+    cat = random_catalog(4242, 300, 4, V - 2, min_len=2)
+    otr = oracle.Trie(cat, V, V - 2, V - 1)
+    T = k * (otr.max_depth + 1)
+    emb = _rand_table(rng, V, H, "fp32")
+    hid = _rand_hidden(rng, T, B, H, "fp32")
+    trie = tms.Trie(cat, V, V - 2, V - 1)
+    st = tms.State(trie, B, k, to_dev(emb))
+    tms.state_set_step_grouping(st, tms.STEP_GROUP_ROOT)
+    csr = trie.csr()
+    st.reset()
+    st.export()
+    for e in range(csr["begin"][0], csr["begin"][1]):
+        tms.debug_set_live(st, 5, e, 0)
+    tok, lg = run_step_loop(st, to_dev(hid), check=False)
+    status = st.status()
+    assert status[5] == tms.ERR_EMPTY_MASK and (np.delete(status, 5) == 0).all()
+    assert (tok[5] == -1).all()
+    keep = [i for i in range(B) if i != 5]
+    compare(tok[keep], ref_decode(otr, k, emb, np.ascontiguousarray(hid[:, keep])), H, lg[keep],
+            where="grouped step isolated")
+    st.close()
+    trie.close()
+
+
+# ---------------------------------------------------------------------------
 # Root steps grouped across sequences (one phase per pointer)
 # ---------------------------------------------------------------------------
 

@@ -43,10 +43,12 @@ EXPORTS = (
     "tms_decode_step_sparse", "tms_decode_step_dense_masked", "tms_decode_k_pointers",
     "tms_advance_forced", "tms_legal_set", "tms_legal_mask", "tms_mask_to_rows", "tms_gather_gemv",
     "tms_debug_set_live",
-    "tms_state_set_split", "tms_state_set_loop", "tms_state_set_norepeat", "tms_state_get_launch",
+    "tms_state_set_split", "tms_state_set_loop", "tms_state_set_norepeat", "tms_state_set_step_grouping",
+    "tms_state_get_launch",
     "tms_decode_k_pointers_noalloc", "tms_read_reference", "tms_status_str", "tms_last_error",
 )
 NOREPEAT_LIVE, NOREPEAT_BITMASK = 0, 1
+STEP_GROUP_AUTO, STEP_GROUP_OFF, STEP_GROUP_ROOT = 0, 1, 2
 NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
@@ -96,6 +98,7 @@ def lib():
             "tms_state_set_split": [P, i32],
             "tms_state_set_loop": [P, i32],
             "tms_state_set_norepeat": [P, i32],
+            "tms_state_set_step_grouping": [P, i32],
             "tms_read_reference": [P, C.c_int64, P, i32, i32, P],
             "tms_decode_k_pointers_noalloc": [P, P, C.c_int, i32, i32, i32, P, i32, P, P, P, P, P],
             "tms_state_get_launch": [P, P, P],
@@ -251,6 +254,10 @@ def state_set_loop(st, mode: int):
 
 def state_set_norepeat(st, kind: int):
     _check(lib().tms_state_set_norepeat(_handle(st), kind), "state_set_norepeat")
+
+
+def state_set_step_grouping(st, mode: int):
+    _check(lib().tms_state_set_step_grouping(_handle(st), mode), "state_set_step_grouping")
 
 
 def state_get_launch(st):

@@ -51,12 +51,18 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int elem_size(int dtype) { return dtype == TMS_F32 ? 4 : 2; }
 
-int default_split(int B, int cap) {
+// Workgroups per sequence of the fused step: a step is a chain of dependent
+// loads, and combining workgroups costs two device-scope atomics plus a third
+// read on that chain (measured: split 1 against the former 3-4 workgroups per
+// sequence, product 3.5 vs 4.9 us per step, structured B = 64 4.8 vs 8.1), so
+// a sequence gets more than one workgroup only when its widest node needs more
+// than two passes of its wavefronts' rows (4 wavefronts x rows_per_pass rows),
+// and never more than a chip-filling 4096 wavefronts over the batch.
+int default_split(int B, int cap, int rows_per_wg) {
   const int target_waves = 4096;
-  int s = (target_waves + 4 * B - 1) / (4 * B);
-  const int by_cap = std::max(1, (cap + 3) / 4);
-  s = std::min(s, by_cap);
-  return std::max(1, s);
+  const int by_waves = std::max(1, (target_waves + 4 * B - 1) / (4 * B));
+  const int by_cap = std::max(1, (cap + 2 * rows_per_wg - 1) / (2 * rows_per_wg));
+  return std::min(by_waves, by_cap);
 }
 
 // Gather-GEMV workgroups per sequence: 4096 wavefronts for short lists (one
@@ -76,6 +82,16 @@ void destroy_graph(tms_state* st) {
   st->graph = nullptr;
   st->g_hidden = nullptr;
 }
+
+// The root grouping of the fused step, when it applies to this state.
+tms::StepGroup* step_group(tms_state* st) {
+  const bool on = st->step_group_mode == TMS_STEP_GROUP_ROOT ? st->step_group_ok
+                  : st->step_group_mode == TMS_STEP_GROUP_OFF ? false
+                                                              : st->step_group_auto;
+  return on ? &st->grp : nullptr;
+}
+
+const tms::StepGroup* step_group(const tms_state* st) { return step_group(const_cast<tms_state*>(st)); }
 
 tms::StepIO make_io(const tms_state* st, const void* hidden) {
   tms::StepIO io{};
@@ -451,6 +467,7 @@ tms_status tms_state_create(tms_trie* trie, int32_t B, int32_t k, const void* em
   const size_t o_live = c.take<int32_t>(size_t(B) * live_stride);
   const size_t o_spent = c.take<uint32_t>(size_t(B) * spent_words);
   const size_t o_mask = c.take<uint32_t>(size_t(B) * mask_words);
+  const size_t o_snap = c.take<int32_t>(2 * size_t(B));
   hipError_t e = hipMalloc(&st->dmem, c.off);
   if (e != hipSuccess) {
     delete st;
@@ -480,11 +497,30 @@ tms_status tms_state_create(tms_trie* trie, int32_t B, int32_t k, const void* em
   d.live = reinterpret_cast<int32_t*>(base + o_live);
   d.spent = reinterpret_cast<uint32_t*>(base + o_spent);
   d.mask = reinterpret_cast<uint32_t*>(base + o_mask);
-  st->split_default = default_split(B, h.cap);
+  d.snap = reinterpret_cast<int32_t*>(base + o_snap);
+  st->split_default = default_split(B, h.cap, tms::step_group_rows(dtype, H));
   st->split = st->split_default;
+  {
+    // root grouping of the fused step: sequences off the root need only the
+    // widest other node's edges; root workgroups take tiles of root rows x
+    // members, as many members per tile (at most 16) as fit 128 KiB of LDS
+    int cap_rest = 1;
+    for (int32_t n = 1; n < h.n_nodes; ++n) cap_rest = std::max(cap_rest, h.begin[n + 1] - h.begin[n]);
+    const int root_edges = h.begin[1] - h.begin[0];
+    const int nq = H / (dtype == TMS_F32 ? 4 : 8);
+    const int mt = std::max(1, std::min(16, int((128 * 1024 - 64) / (16 * size_t(nq)))));
+    const int rows = tms::step_group_rows(dtype, H);
+    st->grp_split_default = default_split(B, cap_rest, rows);
+    st->grp.split = st->grp_split_default;
+    st->grp.mt = mt;
+    st->grp.mtiles = (B + mt - 1) / mt;
+    st->grp.rt = (root_edges + rows - 1) / rows;
+    st->step_group_ok = root_edges > 0 && tms::step_group_lds(nq, mt) <= 160 * 1024 - 1024;
+    st->step_group_auto = st->step_group_ok && B >= 8 && root_edges >= 64;
+  }
   if (const char* env = std::getenv("TMS_SPLIT")) {
     const int v = std::atoi(env);
-    if (v > 0) st->split = v;
+    if (v > 0) st->split = st->grp.split = v;
   }
   if (const char* env = std::getenv("TMS_DENSE_VECTOR")) st->dense_mfma = std::atoi(env) == 0;
   if (const char* env = std::getenv("TMS_LOOP")) {
@@ -531,6 +567,18 @@ static tms_status flush_reset(tms_state* st, void* stream) {
   TMS_HIP(tms::launch_reset(st->trie->dev, st->dev, reset_kind(st), static_cast<hipStream_t>(stream)),
           "reset launch");
   reset_enqueued(st);
+  st->snap_valid = true;  // the reset kernel put every sequence at the root in half 0
+  st->snap_parity = 0;
+  return TMS_OK;
+}
+
+// The grouped step's snapshot must hold the current nodes in half `parity`
+// before a grouped step reads it; rewrites it from the state when stale.
+static tms_status ensure_snapshot(tms_state* st, int parity, hipStream_t s) {
+  if (st->snap_valid && st->snap_parity == parity) return TMS_OK;
+  TMS_HIP(tms::launch_snapshot(st->dev, parity, s), "snapshot launch");
+  st->snap_valid = true;
+  st->snap_parity = parity;
   return TMS_OK;
 }
 
@@ -603,9 +651,17 @@ tms_status tms_decode_step_sparse(tms_state* st, const void* hidden, int32_t* to
   tms::StepIO io = make_io(st, hidden);
   io.out_tok = tok;
   io.out_logit = logit;
-  TMS_HIP(tms::launch_step_sparse(st->trie->dev, st->dev, io, st->dtype, st->fast, st->split,
-                                  static_cast<hipStream_t>(stream)),
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  tms::StepGroup* g = step_group(st);
+  if (g) {
+    const tms_status rs = ensure_snapshot(st, st->snap_parity, s);
+    if (rs != TMS_OK) return rs;
+    g->parity = st->snap_parity;
+  }
+  TMS_HIP(tms::launch_step_sparse(st->trie->dev, st->dev, io, st->dtype, st->fast, st->split, s, g),
           "sparse step launch");
+  if (g) st->snap_parity ^= 1;  // the step wrote the other half
+  else st->snap_valid = false;
   return TMS_OK;
 }
 
@@ -618,6 +674,7 @@ tms_status tms_decode_step_dense_masked(tms_state* st, const void* hidden, int32
   tms::StepIO io = make_io(st, hidden);
   io.out_tok = tok;
   io.out_logit = logit;
+  st->snap_valid = false;
   TMS_HIP(tms::launch_dense_step(st->trie->dev, st->dev, io, st->dtype, full_logits, 1024, st->dense_mfma,
                                  static_cast<hipStream_t>(stream)),
           "dense step launch");
@@ -648,6 +705,7 @@ tms_status tms_decode_k_pointers(tms_state* st, const void* hidden_seq, int32_t 
     const bool fresh = st->reset_pending;  // every sequence starts at the root
     io.reset = reset_kind(st);             // the kernel resets its sequence first
     const bool bitmask = st->norepeat == TMS_NOREPEAT_BITMASK && !st->live_dirty;
+    st->snap_valid = false;
     TMS_HIP(tms::enqueue_resident(st->trie, st->dev, io, st->dtype, st->fast, st->loop_mode, fresh, bitmask, s),
             "loop launch");
     if (fresh) reset_enqueued(st);
@@ -655,19 +713,35 @@ tms_status tms_decode_k_pointers(tms_state* st, const void* hidden_seq, int32_t 
   }
   TMS_FLUSH_RESET(st, stream);
   const size_t step_bytes = size_t(st->B) * st->H * elem_size(st->dtype);
-  auto enqueue = [&](hipStream_t q) -> hipError_t {
+  tms::StepGroup* grp = step_group(st);
+  // grouped steps alternate the snapshot halves: step t of a call starting at
+  // half p0 reads half (p0 + t) & 1 (the captured graph always starts at 0)
+  auto enqueue = [&](hipStream_t q, int p0) -> hipError_t {
     for (int32_t t = 0; t < T; ++t) {
       tms::StepIO io = make_io(st, static_cast<const char*>(hidden_seq) + step_bytes * t);
       io.tokens_bt = tokens;
       io.T = T;
       io.t = t;
-      hipError_t e = tms::launch_step_sparse(st->trie->dev, st->dev, io, st->dtype, st->fast, st->split, q);
+      tms::StepGroup g{};
+      if (grp) {
+        g = *grp;
+        g.parity = (p0 + t) & 1;
+      }
+      hipError_t e = tms::launch_step_sparse(st->trie->dev, st->dev, io, st->dtype, st->fast, st->split, q,
+                                             grp ? &g : nullptr);
       if (e != hipSuccess) return e;
     }
     return tms::launch_finalize(st->dev, len, entries, q);
   };
   if (st->loop_mode == TMS_LOOP_STREAM) {
-    TMS_HIP(enqueue(s), "step loop launch");
+    const int p0 = st->snap_valid ? st->snap_parity : 0;
+    if (grp) {
+      const tms_status rs = ensure_snapshot(st, p0, s);
+      if (rs != TMS_OK) return rs;
+    }
+    TMS_HIP(enqueue(s, p0), "step loop launch");
+    if (grp) st->snap_parity = (p0 + T) & 1;
+    else st->snap_valid = false;
     return TMS_OK;
   }
   const bool same = st->gexec && st->g_hidden == hidden_seq && st->g_T == T && st->g_tokens == tokens &&
@@ -675,7 +749,7 @@ tms_status tms_decode_k_pointers(tms_state* st, const void* hidden_seq, int32_t 
   if (!same) {
     destroy_graph(st);
     TMS_HIP(hipStreamBeginCapture(st->capture, hipStreamCaptureModeRelaxed), "begin capture");
-    const hipError_t le = enqueue(st->capture);
+    const hipError_t le = enqueue(st->capture, 0);
     hipGraph_t g = nullptr;
     const hipError_t ce = hipStreamEndCapture(st->capture, &g);
     if (le != hipSuccess) {
@@ -691,13 +765,20 @@ tms_status tms_decode_k_pointers(tms_state* st, const void* hidden_seq, int32_t 
     st->g_len = len;
     st->g_entries = entries;
   }
+  if (grp) {
+    const tms_status rs = ensure_snapshot(st, 0, s);
+    if (rs != TMS_OK) return rs;
+  }
   TMS_HIP(hipGraphLaunch(st->gexec, s), "graph launch");
+  if (grp) st->snap_parity = T & 1;
+  else st->snap_valid = false;
   return TMS_OK;
 }
 
 tms_status tms_advance_forced(tms_state* st, const int32_t* tok, void* stream) {
   if (!st || !tok) return fail(TMS_ERR_INVALID_ARG, "null argument");
   TMS_FLUSH_RESET(st, stream);
+  st->snap_valid = false;
   TMS_HIP(tms::launch_forced(st->trie->dev, st->dev, tok, static_cast<hipStream_t>(stream)), "forced launch");
   return TMS_OK;
 }
@@ -775,6 +856,17 @@ tms_status tms_debug_set_live(tms_state* st, int32_t s, int32_t edge, int32_t va
 tms_status tms_state_set_split(tms_state* st, int32_t split) {
   if (!st || split < 0 || split > 4096) return fail(TMS_ERR_INVALID_ARG, "split must be in [0, 4096]");
   st->split = split == 0 ? st->split_default : split;
+  st->grp.split = split == 0 ? st->grp_split_default : split;
+  destroy_graph(st);
+  return TMS_OK;
+}
+
+tms_status tms_state_set_step_grouping(tms_state* st, int32_t mode) {
+  if (!st || mode < TMS_STEP_GROUP_AUTO || mode > TMS_STEP_GROUP_ROOT)
+    return fail(TMS_ERR_INVALID_ARG, "unknown step grouping mode");
+  if (mode == TMS_STEP_GROUP_ROOT && !st->step_group_ok)
+    return fail(TMS_ERR_INVALID_ARG, "root grouping does not fit this state (LDS for the members' vectors)");
+  st->step_group_mode = mode;
   destroy_graph(st);
   return TMS_OK;
 }
@@ -798,8 +890,9 @@ tms_status tms_state_set_norepeat(tms_state* st, int32_t kind) {
 
 tms_status tms_state_get_launch(const tms_state* st, int32_t* split, int32_t* grid) {
   if (!st) return fail(TMS_ERR_INVALID_ARG, "null state");
-  if (split) *split = st->split;
-  if (grid) *grid = st->B * st->split;
+  const tms::StepGroup* g = step_group(st);
+  if (split) *split = g ? g->split : st->split;
+  if (grid) *grid = g ? st->B * g->split + g->rt * g->mtiles : st->B * st->split;
   return TMS_OK;
 }
 

@@ -30,6 +30,17 @@ struct tms_state {
   size_t dbytes = 0;
   tms::DevState dev{};
   int split = 1, split_default = 1;
+  // root grouping of the fused step (TMS_STEP_GROUP_*), its launch shape and
+  // whether the state's trie and batch allow it
+  int step_group_mode = TMS_STEP_GROUP_AUTO;
+  bool step_group_ok = false, step_group_auto = false;
+  tms::StepGroup grp{};
+  int grp_split_default = 1;
+  // the grouped step's snapshot (DevState::snap): the half that holds every
+  // sequence's current node, and whether it is up to date (any other call
+  // that moves sequences makes it stale; the reset kernel rewrites half 0)
+  int snap_parity = 0;
+  bool snap_valid = false;
   bool fast = false;
   int loop_mode = TMS_LOOP_RESIDENT;
   bool dense_mfma = true;  // matrix-core dense head where it applies

@@ -83,6 +83,10 @@ struct DevState {
   int32_t* live;         // [B][live_stride]
   uint32_t* spent;       // [B][spent_words] one bit per catalog entry
   uint32_t* mask;        // [B][mask_words] dense-path vocabulary bitmask
+  // [2][B] each sequence's node at the start of a root-grouped step (-1:
+  // finished or in error), by launch parity: the step reads half p, which no
+  // one writes during it, and writes half 1-p (null where unused)
+  int32_t* snap;
 };
 
 // Per-step inputs and outputs.
@@ -124,8 +128,23 @@ enum { kResetNone = 0, kResetFull = 1, kResetPaths = 2 };
 
 // dtype: 0 fp32, 1 bf16.  Every launcher returns hipGetLastError().
 hipError_t launch_reset(const DevTrie& tr, const DevState& st, int kind, hipStream_t s);
+// Root grouping of the fused step (step_grouped_kernel): split workgroups per
+// sequence not at the root, rt root row tiles of step_group_rows() rows each,
+// mtiles member tiles of mt members (mt <= 16).
+struct StepGroup {
+  int split, rt, mt, mtiles;
+  int parity;  // which half of DevState::snap holds the nodes at the start of this step
+};
+// snap[parity] <- every sequence's node (-1 if finished or in error).
+hipError_t launch_snapshot(const DevState& st, int parity, hipStream_t s);
+// grp null: the plain fused step (step_sparse_kernel, split workgroups per
+// sequence); otherwise the step with the root grouped across sequences.
 hipError_t launch_step_sparse(const DevTrie& tr, const DevState& st, const StepIO& io, int dtype,
-                              bool fast, int split, hipStream_t s);
+                              bool fast, int split, hipStream_t s, const StepGroup* grp = nullptr);
+// LDS bytes of a root workgroup of the grouped step (nq = 16-byte chunks per row).
+size_t step_group_lds(int nq, int mt);
+// Root rows per root workgroup of the grouped step.
+int step_group_rows(int dtype, int H);
 // Variants of the resident loop: trie, live counts and spent bits in LDS
 // (fast path); trie through the scalar cache with live counts in device
 // memory (fast path, too big for LDS); vector edge reads with live counts in

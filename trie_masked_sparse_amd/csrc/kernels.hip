@@ -251,9 +251,10 @@ __device__ __forceinline__ void write_step_out(const StepIO& io, int s, int tok,
 // the winner is not walkable.  Both set a sticky error and stop the sequence.
 // Completing a pointer: its terminal is marked spent, every content edge on
 // its path loses one live pointer, and the catalog index is recorded.
-__device__ void advance(const DevTrie& tr, const DevState& st, const StepIO* io, int s, const Seq& q, int e,
-                        float logit, int lane) {
-  int status = kSeqOk, tok = -1;
+// Returns the sequence's node after the step, -1 once it is finished or in error.
+__device__ int advance(const DevTrie& tr, const DevState& st, const StepIO* io, int s, const Seq& q, int e,
+                       float logit, int lane) {
+  int status = kSeqOk, tok = -1, next = -1;
   int32_t* live = st.live + (int64_t)s * tr.live_stride;
   if (e == -2) {
     status = kSeqEmptyMask;
@@ -269,12 +270,14 @@ __device__ void advance(const DevTrie& tr, const DevState& st, const StepIO* io,
     } else {
       tok = tr.tok[e];
       if (c >= 0) {
+        next = c;
         if (lane == 0) {
           st.path[(int64_t)s * st.path_stride + q.depth] = e;
           st.depth[s] = q.depth + 1;
           st.node[s] = c;
         }
       } else {
+        next = c == kChildStop ? -1 : 0;
         const int ent = tr.entry[q.node];
         const int32_t* path = st.path + (int64_t)s * st.path_stride;
         for (int i = lane; i < q.depth; i += kWave) live[path[i]] -= 1;  // distinct edges
@@ -294,6 +297,7 @@ __device__ void advance(const DevTrie& tr, const DevState& st, const StepIO* io,
     if (status != kSeqOk) st.status[s] = status;
     if (io) write_step_out(*io, s, tok, logit);
   }
+  return status == kSeqOk ? next : -1;
 }
 
 // First edge of the node's range labelled tok, or -1 (one wavefront).
@@ -572,6 +576,243 @@ __global__ __launch_bounds__(kBlock) void step_sparse_kernel(DevTrie tr, DevStat
     __hip_atomic_store(&st.key[s], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&st.arrive[s], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Fused sparse step with the root grouped across sequences (section "The
+// batched engine": the rows one step needs are the union of the sequences'
+// legal sets, and every pointer starts at the root, so at a wide root many
+// sequences need the same rows in the same step).  One launch, fixed grid:
+//   * B * split sequence workgroups: workgroup (s, w) serves sequence s as in
+//     step_sparse_kernel, unless s stands at the root ("member");
+//   * rt * mt root workgroups: workgroup (x, y) reads root rows x*4U ..
+//     x*4U+4U-1 once (U per wavefront) and dots them with the hidden vectors of
+//     members y*mt .. y*mt+mt-1 (ascending sequence order) staged in LDS, in
+//     the per-row order of the other kernels, so every logit and key is the
+//     one step_sparse_kernel computes.  A member's key is the max over the rt
+//     root workgroups of its member tile (atomic max into key[s]); whichever of
+//     them arrives last (arrival counter) advances it.
+// A step in which no sequence is at the root costs the root workgroups one
+// pass over the sequences' nodes.  The root is never a terminal (entries are
+// non-empty), so its edges are content edges only.
+// ---------------------------------------------------------------------------
+template <int DT, int NC, bool FAST>
+__global__ __launch_bounds__(kBlock) void step_grouped_kernel(DevTrie tr, DevState st, StepIO io, int split,
+                                                              int rt, int mt, int parity) {
+  constexpr int EL = DT == 0 ? 4 : 8;
+  constexpr int U = rows_per_pass(NC);
+  constexpr int MPW = 4;  // members staged per wavefront per round
+  const int lane = __lane_id();
+  const int wv = wave_id();
+  const int nq = io.H / EL;
+  const int nseq_wg = st.B * split;
+  // who stands where at the start of the step: read from one half of snap,
+  // which no workgroup writes during this launch (advances happen during it)
+  const int32_t* snap_in = st.snap + (int64_t)parity * st.B;
+  int32_t* snap_out = st.snap + (int64_t)(1 - parity) * st.B;
+  __shared__ unsigned long long s_best[16];
+  __shared__ unsigned long long s_key;
+  __shared__ int s_last;
+  __shared__ int s_cnt[kWavesPerBlock];
+  if ((int)blockIdx.x < nseq_wg) {
+    const int g = blockIdx.x;
+    const int s = g / split;
+    const int w = g - s * split;
+    const int wq = w * kWavesPerBlock + wv;
+    const int W = split * kWavesPerBlock;
+    // the hidden vector first on the scalar-trie path (the edge records come
+    // through the scalar cache and do not queue behind it)
+    uint4 hq[NC];
+    if constexpr (FAST) load_hidden<NC>((const uint4*)io.hidden + (int64_t)s * nq, nq, hq, lane);
+    const int node0 = ((cint_p)snap_in)[s];
+    Seq q;
+    const bool active = load_seq(tr, st, s, q);  // issued with the snapshot read
+    if (node0 == 0) return;  // a member: the root workgroups take its step
+    if (node0 < 0 || !active) {
+      if (w == 0 && threadIdx.x == 0) {
+        write_step_out(io, s, -1, NAN);
+        snap_out[s] = -1;
+      }
+      return;
+    }
+    if constexpr (!FAST) load_hidden<NC>((const uint4*)io.hidden + (int64_t)s * nq, nq, hq, lane);
+    const int32_t* live = st.live + (int64_t)s * tr.live_stride;
+    Cand unused;
+    const TrieView tv{tr.erec, tr.cent, tr.run, tr.run_edge, tr.run_tok, tr.run_land};
+    const unsigned long long best = scan_node<DT, NC, FAST ? kMetaScalar : kMetaVector, kLiveScalar, false>(
+        tr, tv, q, live, (const uint4*)io.emb, nq, hq, wq, W, lane, unused);
+    if (lane == 0) s_best[wv] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      unsigned long long b = s_best[0];
+#pragma unroll
+      for (int i = 1; i < kWavesPerBlock; ++i) b = max(b, s_best[i]);
+      if (split == 1) {
+        s_last = 1;
+        s_key = b;
+      } else {
+        if (b) __hip_atomic_fetch_max(&st.key[s], b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t prev = __hip_atomic_fetch_add(&st.arrive[s], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = prev == (uint32_t)(split - 1);
+        s_last = last;
+        if (last) s_key = __hip_atomic_load(&st.key[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();
+    if (!s_last || threadIdx.x >= kWave) return;
+    const unsigned long long key = s_key;
+    const int next = advance(tr, st, &io, s, q, key ? (int)key_id(key) : -2, key ? key_logit(key) : NAN, lane);
+    if (lane == 0) {
+      snap_out[s] = next;
+      if (split > 1) {
+        __hip_atomic_store(&st.key[s], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&st.arrive[s], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    return;
+  }
+  // root workgroup (x, y); [mt][nq] members' hidden vectors in LDS, then their ids
+  extern __shared__ uint4 sh[];
+  int* s_mem = reinterpret_cast<int*>(sh + (size_t)mt * nq);
+  const int r = (int)blockIdx.x - nseq_wg;
+  const int x = r % rt, y = r / rt;
+  const int m0 = y * mt;
+  if (threadIdx.x < 16) s_best[threadIdx.x] = 0ull;
+  // this wavefront's root edges and their tokens, requested before the member
+  // scan (they do not depend on it)
+  const int r1 = tr.begin[1];
+  const int e0 = tr.begin[0] + (x * kWavesPerBlock + wv) * U;
+  int rows[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) rows[u] = e0 + u < r1 ? tr.tok[e0 + u] : -1;
+  // members of this tile: ranks m0 .. m0+mt-1 among the sequences at the root
+  int n_mem = 0;
+  for (int s0 = 0; s0 < st.B; s0 += kBlock) {
+    const int s = s0 + (int)threadIdx.x;
+    const bool ok = s < st.B && snap_in[s] == 0;
+    const unsigned long long m = __ballot(ok);
+    if (lane == 0) s_cnt[wv] = __popcll(m);
+    lds_barrier();
+    int off = n_mem;
+    for (int i = 0; i < wv; ++i) off += s_cnt[i];
+    if (ok) {
+      const int idx = off + __popcll(m & ((1ull << lane) - 1ull)) - m0;
+      if (idx >= 0 && idx < mt) s_mem[idx] = s;
+    }
+    for (int i = 0; i < kWavesPerBlock; ++i) n_mem += s_cnt[i];
+    lds_barrier();
+  }
+  const int cnt = min(mt, n_mem - m0);
+  if (cnt <= 0) return;  // the same for the whole workgroup
+  uint4 raw[U][NC];
+  issue_rows<NC, U>((const uint4*)io.emb, nq, rows, raw, lane);
+  // lane j reads member j's live counts of the wavefront's edges, requested
+  // with the rows (used after the staging below)
+  int lv[U];
+  {
+    const int32_t* my_live = lane < cnt ? st.live + (int64_t)s_mem[lane] * tr.live_stride : nullptr;
+#pragma unroll
+    for (int u = 0; u < U; ++u) lv[u] = rows[u] >= 0 && lane < cnt ? my_live[e0 + u] : 0;
+  }
+  // stage the members' vectors: every load of a round before its stores
+  const uint4* hid = (const uint4*)io.hidden;
+  for (int jb = wv; jb < cnt; jb += kWavesPerBlock * MPW) {
+    uint4 v[MPW][NC];
+#pragma unroll
+    for (int u = 0; u < MPW; ++u) {
+      const int j = jb + u * kWavesPerBlock;
+      if (j < cnt) load_hidden<NC>(hid + (int64_t)s_mem[j] * nq, nq, v[u], lane);
+    }
+#pragma unroll
+    for (int u = 0; u < MPW; ++u) {
+      const int j = jb + u * kWavesPerBlock;
+      if (j >= cnt) continue;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        if (c * kWave + lane < nq) sh[j * nq + c * kWave + lane] = v[u][c];
+    }
+  }
+  unsigned long long legal[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) legal[u] = __ballot(lv[u] > 0);
+  lds_barrier();  // staged vectors visible
+  // two members per pass: independent accumulation chains side by side
+  for (int j = 0; j < cnt; j += 2) {
+    const int j1 = min(j + 1, cnt - 1);
+    uint4 hq0[NC], hq1[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int i = c * kWave + lane;
+      const int ii = i < nq ? i : 0;
+      hq0[c] = c * kWave < nq ? sh[j * nq + ii] : make_uint4(0, 0, 0, 0);
+      hq1[c] = c * kWave < nq ? sh[j1 * nq + ii] : make_uint4(0, 0, 0, 0);
+    }
+    float l0[U], l1[U];
+    finish_rows<DT, NC, U>(nq, rows, raw, hq0, l0, lane);
+    finish_rows<DT, NC, U>(nq, rows, raw, hq1, l1, lane);
+    unsigned long long b0 = 0ull, b1 = 0ull;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if ((legal[u] >> j) & 1ull) b0 = max(b0, pack_key(l0[u], (uint32_t)(e0 + u)));
+      if ((legal[u] >> j1) & 1ull) b1 = max(b1, pack_key(l1[u], (uint32_t)(e0 + u)));
+    }
+    if (lane == 0) {
+      if (b0) __hip_atomic_fetch_max(&s_best[j], b0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (b1 && j1 != j) __hip_atomic_fetch_max(&s_best[j1], b1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  }
+  lds_barrier();
+  if (wv != 0) return;
+  // combine this tile's best keys into the members' slots; the last of the rt
+  // root workgroups to arrive for a member advances it.  Everything they
+  // exchange goes through device-scope atomics (the key max and the arrival
+  // count), which are performed where they are coherent for the whole device:
+  // waiting for the max to complete before the arrival is issued orders the
+  // two, so the last arrival finds every tile's max in key[s].  A device-scope release and acquire would instead write back and
+  // invalidate this XCD's L2 in each of the rt x mtiles root workgroups.
+  bool last = false;
+  int sm = 0;
+  if (lane < cnt) {
+    sm = s_mem[lane];
+    const unsigned long long b = s_best[lane];
+    if (b) __hip_atomic_fetch_max(&st.key[sm], b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // the max is acknowledged (vector memory counter drained) before the
+  // arrival is issued; no-return atomics count in vmcnt on this part
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (lane < cnt) {
+    const uint32_t prev = __hip_atomic_fetch_add(&st.arrive[sm], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = prev == (uint32_t)(rt - 1);
+  }
+  if (!last) return;
+  // The advance of a member, one lane each (what advance() does for a
+  // sequence at the root: the root has content edges only, so a legal winner
+  // pushes its edge as the path's first and moves to the child; nothing is
+  // released).  Empty mask: EMPTY_MASK; a winner that is not a live root edge:
+  // NOT_WALKABLE.
+  const unsigned long long key = __hip_atomic_load(&st.key[sm], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  int status = kSeqOk, tok = -1, next = -1;
+  if (!key) {
+    status = kSeqEmptyMask;
+  } else {
+    const int e = (int)key_id(key);
+    const int c = e >= tr.begin[0] && e < r1 ? tr.child[e] : -3;
+    if (c < 0 || st.live[(int64_t)sm * tr.live_stride + e] <= 0) {
+      status = kSeqNotWalkable;
+    } else {
+      next = c;
+      tok = tr.tok[e];
+      st.path[(int64_t)sm * st.path_stride] = e;
+      st.depth[sm] = 1;
+      st.node[sm] = c;
+      st.nemit[sm] = st.nemit[sm] + 1;
+    }
+  }
+  if (status != kSeqOk) st.status[sm] = status;
+  snap_out[sm] = next;
+  write_step_out(io, sm, tok, key ? key_logit(key) : NAN);
+  __hip_atomic_store(&st.key[sm], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&st.arrive[sm], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The edges of a node of at most 64 edges, one lane per edge (lane i: edge
@@ -2227,8 +2468,15 @@ __global__ __launch_bounds__(kBlock) void reset_kernel(DevTrie tr, DevState st, 
       st.nemit[s] = 0;
       st.key[s] = 0ull;
       st.arrive[s] = 0u;
+      if (st.snap) st.snap[s] = 0;  // at the root, half 0 of the grouped step's snapshot
     }
   }
+}
+
+__global__ __launch_bounds__(kBlock) void snapshot_kernel(DevState st, int parity) {
+  const int s = blockIdx.x * kBlock + threadIdx.x;
+  if (s >= st.B) return;
+  st.snap[(int64_t)parity * st.B + s] = st.status[s] == kSeqOk && st.finished[s] == 0 ? st.node[s] : -1;
 }
 
 __global__ __launch_bounds__(kBlock) void finalize_kernel(DevState st, int32_t* len, int32_t* entries) {
@@ -2257,13 +2505,25 @@ hipError_t dispatch(int dtype, int nc, A&&... a) {
   return hipErrorInvalidValue;
 }
 
+hipError_t allow_lds(const void* k, size_t lds);
+
 template <int DT, int NC>
 struct StepLaunch {
   static hipError_t run(const DevTrie& tr, const DevState& st, const StepIO& io, bool fast, int split,
-                        hipStream_t s) {
-    const dim3 grid((unsigned)(st.B * split)), block(kBlock);
-    if (fast) hipLaunchKernelGGL((step_sparse_kernel<DT, NC, true>), grid, block, 0, s, tr, st, io, split);
-    else hipLaunchKernelGGL((step_sparse_kernel<DT, NC, false>), grid, block, 0, s, tr, st, io, split);
+                        const StepGroup* grp, hipStream_t s) {
+    const dim3 block(kBlock);
+    if (!grp) {
+      const dim3 grid((unsigned)(st.B * split));
+      if (fast) hipLaunchKernelGGL((step_sparse_kernel<DT, NC, true>), grid, block, 0, s, tr, st, io, split);
+      else hipLaunchKernelGGL((step_sparse_kernel<DT, NC, false>), grid, block, 0, s, tr, st, io, split);
+      return hipGetLastError();
+    }
+    constexpr int EL = DT == 0 ? 4 : 8;
+    const size_t lds = step_group_lds(io.H / EL, grp->mt);
+    auto* k = fast ? &step_grouped_kernel<DT, NC, true> : &step_grouped_kernel<DT, NC, false>;
+    if (hipError_t e = allow_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess) return e;
+    const dim3 grid((unsigned)(st.B * grp->split + grp->rt * grp->mtiles));
+    hipLaunchKernelGGL(k, grid, block, lds, s, tr, st, io, grp->split, grp->rt, grp->mt, grp->parity);
     return hipGetLastError();
   }
 };
@@ -2351,9 +2611,13 @@ hipError_t launch_reset(const DevTrie& tr, const DevState& st, int kind, hipStre
 }
 
 hipError_t launch_step_sparse(const DevTrie& tr, const DevState& st, const StepIO& io, int dtype, bool fast,
-                              int split, hipStream_t s) {
-  return dispatch<StepLaunch>(dtype, chunks_for(dtype, io.H), tr, st, io, fast, split, s);
+                              int split, hipStream_t s, const StepGroup* grp) {
+  return dispatch<StepLaunch>(dtype, chunks_for(dtype, io.H), tr, st, io, fast, split, grp, s);
 }
+
+size_t step_group_lds(int nq, int mt) { return sizeof(uint4) * (size_t)mt * nq + sizeof(int) * (size_t)mt; }
+
+int step_group_rows(int dtype, int H) { return kWavesPerBlock * rows_per_pass(chunks_for(dtype, H)); }
 
 hipError_t launch_loop(const DevTrie& tr, const DevState& st, const LoopIO& io, int dtype, int mode,
                        hipStream_t s) {
@@ -2537,6 +2801,11 @@ hipError_t launch_read_reference(const void* src, int64_t bytes, uint32_t* out, 
     case 8: return go(read_ref_kernel<8>, 8);
     default: return go(read_ref_kernel<4>, 4);
   }
+}
+
+hipError_t launch_snapshot(const DevState& st, int parity, hipStream_t s) {
+  hipLaunchKernelGGL(snapshot_kernel, dim3((st.B + kBlock - 1) / kBlock), dim3(kBlock), 0, s, st, parity);
+  return hipGetLastError();
 }
 
 hipError_t launch_finalize(const DevState& st, int32_t* len, int32_t* entries, hipStream_t s) {
