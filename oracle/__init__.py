@@ -22,7 +22,8 @@ CHILD_SEP, CHILD_STOP = -1, -2
 
 # planted mistakes for negative-control tests
 MUT_NONE, MUT_TIE_HIGHER_ID, MUT_NO_LIVE_DECREMENT, MUT_NO_SPENT_FLAG, MUT_ROW_OFF_BY_ONE, \
-    MUT_SEP_STOP_SWAPPED, MUT_DROP_LAST_TERM, MUT_MARGIN_ZERO, MUT_SUMABS_WINNER, MUT_FOLLOW_IGNORED = range(10)
+    MUT_SEP_STOP_SWAPPED, MUT_DROP_LAST_TERM, MUT_MARGIN_ZERO, MUT_SUMABS_WINNER, MUT_FOLLOW_IGNORED, \
+    MUT_CS_FIRST_BYTE, MUT_CS_STOP_LEAF_ONLY = range(12)
 
 
 def build(force: bool = True) -> str:
@@ -66,6 +67,14 @@ def lib():
         L.orc_decode.argtypes = [P, i32, P, C.c_int, i32, i32, P, i32, i32] + [P] * 9
         L.orc_decode.restype = C.c_int
         L.orc_set_mutant.argtypes = [C.c_int]
+        L.orc_cs_build.argtypes = [P, P, i32, P, P, i32, i32, i32, C.POINTER(P)]
+        L.orc_cs_build.restype = C.c_int
+        L.orc_cs_free.argtypes = [P]
+        L.orc_cs_info.argtypes = [P, P]
+        L.orc_cs_mask.argtypes = [P, P, i64, P]
+        L.orc_cs_mask.restype = i32
+        L.orc_cs_decode.argtypes = [P, P, C.c_int, i32, P, i32, i32] + [P] * 9
+        L.orc_cs_decode.restype = C.c_int
         _lib = L
     return _lib
 
@@ -222,3 +231,72 @@ def decode(trie: Trie, k: int, emb: np.ndarray, hidden: np.ndarray, follow: np.n
     if rc != OK:
         raise OracleError(rc, "decode")
     return out
+
+
+# ---------------------------------------------------------------------------
+# Character-level catalogs (the review of arXiv 2608.12574): one string of a
+# byte-string catalog, spelled by tokens whose byte strings are given.
+# ---------------------------------------------------------------------------
+
+def pack_bytes(items):
+    """list of bytes -> (uint8 concatenation, int64 offsets)."""
+    off = np.zeros(len(items) + 1, np.int64)
+    off[1:] = np.cumsum([len(x) for x in items])
+    buf = np.frombuffer(b"".join(items) or b"\0", np.uint8).copy()
+    return buf, off
+
+
+class CharCatalog:
+    """A catalog of byte strings with a token vocabulary (token v spells
+    vocab[v]; b"" for control and unused tokens)."""
+
+    def __init__(self, strings, vocab, sep: int, stop: int):
+        self.strings = [bytes(x) for x in strings]
+        self.vocab = [bytes(x) for x in vocab]
+        self.V, self.sep, self.stop = len(self.vocab), sep, stop
+        self._sb, self._so = pack_bytes(self.strings)
+        self._tb, self._to = pack_bytes(self.vocab)
+        h = C.c_void_p()
+        rc = lib().orc_cs_build(_ptr(self._sb), _ptr(self._so), len(self.strings), _ptr(self._tb), _ptr(self._to),
+                                self.V, sep, stop, C.byref(h))
+        if rc != OK:
+            raise OracleError(rc, "character catalog")
+        self._h = h
+        info = np.zeros(3, np.int32)
+        lib().orc_cs_info(self._h, _ptr(info))
+        self.max_len, self.max_tok, self.n_content = (int(x) for x in info)
+
+    def __del__(self):
+        if getattr(self, "_h", None) and lib is not None:
+            lib().orc_cs_free(self._h)
+            self._h = None
+
+    def mask(self, prefix: bytes) -> np.ndarray:
+        """Legal token ids (ascending) after the emitted bytes prefix."""
+        out = np.zeros(self.V, np.int32)
+        p = np.frombuffer(bytes(prefix) or b"\0", np.uint8).copy()
+        n = lib().orc_cs_mask(self._h, _ptr(p), len(prefix), _ptr(out))
+        return out[:n].copy()
+
+    def decode(self, emb: np.ndarray, hidden: np.ndarray, follow: np.ndarray | None = None):
+        """Greedy decode (one string) of hidden [T][B][H]; dict of arrays as
+        for decode(), with entry [B] instead of entries."""
+        emb = np.ascontiguousarray(emb)
+        hidden = np.ascontiguousarray(hidden, dtype=emb.dtype)
+        T, B, H = hidden.shape
+        if emb.shape[0] != self.V or emb.shape[1] != H:
+            raise ValueError("table must be [V][H] with the hidden size")
+        if follow is not None:
+            follow = np.ascontiguousarray(follow, dtype=np.int32)
+            if follow.shape != (B, T):
+                raise ValueError("follow must be [B][T]")
+        out = {"tokens": np.full((B, T), -1, np.int32), "len": np.zeros(B, np.int32),
+               "entry": np.full(B, -1, np.int32), "status": np.zeros(B, np.int32),
+               "best": np.zeros((B, T)), "margin": np.zeros((B, T)), "sumabs": np.zeros((B, T)),
+               "nlegal": np.zeros((B, T), np.int32)}
+        rc = lib().orc_cs_decode(self._h, _ptr(emb), _dtype_code(emb), H, _ptr(hidden), B, T, _ptr(follow),
+                                 *(_ptr(out[n]) for n in ("tokens", "len", "entry", "status", "best", "margin",
+                                                          "sumabs", "nlegal")))
+        if rc != OK:
+            raise OracleError(rc, "character decode")
+        return out

@@ -71,6 +71,8 @@ enum {
   MUT_MARGIN_ZERO = 7,      /* the top-two margin is reported as 0 */
   MUT_SUMABS_WINNER = 8,    /* sum|p| is the winner's, not the larger of the top two */
   MUT_FOLLOW_IGNORED = 9,   /* teacher forcing advances by the oracle's own pick */
+  MUT_CS_FIRST_BYTE = 10,   /* character catalogs: a token is legal when its first byte continues a string */
+  MUT_CS_STOP_LEAF_ONLY = 11, /* character catalogs: stop only where no longer string continues */
 };
 static int g_mutant = 0;
 void orc_set_mutant(int m) { g_mutant = m; }
@@ -510,5 +512,270 @@ int orc_decode(const orc_trie* t, int32_t k, const void* emb, int dtype, int32_t
     orc_state_free(s);
   }
   free(scratch);
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Character-level catalogs                                                    */
+/* ------------------------------------------------------------------------- */
+
+/* Source: the review of arXiv 2608.12574 (fields pith_extraction.key_machinery
+ * and core_discovery).  The catalog is a set C of byte strings and the
+ * vocabulary maps each token id v to a byte string b(v); an answer is one
+ * string of C spelled by a sequence of tokens, then the stop token.  By the
+ * next-token mask definition (page "GLRMask", with b as the token-to-bytes
+ * map) the legal set after tokens u is
+ *     Mask(u) = { v : some tokens w make b(u v w) a string of C, v != stop }
+ *               plus stop when b(u) is itself a string of C.
+ * When every byte that occurs in C is also a token of its own (byte-level
+ * vocabularies), every remainder of a string can be spelled, so a content
+ * token v is legal exactly when b(u) b(v) is a prefix of some string of C.
+ * This section computes that set by enumeration: for each catalog string that
+ * starts with b(u), every token spelling the next 1, 2, ... bytes of it.  The
+ * page's trie, Aho-Corasick matcher and precomputed valid[node] sets are the
+ * fast way to the same sets; nothing of them is used here.  Readings: empty
+ * byte strings are control or unused tokens and never content; the sep and
+ * stop ids are never content; duplicate strings are rejected.  One string is
+ * chosen (k = 1): sep is never legal. */
+
+typedef struct {
+  int32_t K, V, sep, stop, max_len, max_tok;
+  uint8_t* bytes;  /* catalog strings, back to back */
+  int64_t* off;    /* [K+1] */
+  int32_t* order;  /* catalog indices in lexicographic byte order */
+  uint8_t* tb;     /* token byte strings, back to back */
+  int64_t* toff;   /* [V+1] */
+  int32_t* torder; /* content token ids ordered by (bytes, id) */
+  int32_t nt;      /* number of content tokens */
+} orc_cs;
+
+static const orc_cs* g_cs_sort; /* context of the two qsort comparators below */
+
+static int cmp_bytes(const uint8_t* a, int64_t la, const uint8_t* b, int64_t lb) {
+  int64_t n = la < lb ? la : lb;
+  int c = n ? memcmp(a, b, (size_t)n) : 0;
+  if (c) return c;
+  return la < lb ? -1 : la > lb ? 1 : 0;
+}
+
+static int cmp_str_idx(const void* x, const void* y) {
+  int32_t i = *(const int32_t*)x, j = *(const int32_t*)y;
+  const orc_cs* c = g_cs_sort;
+  return cmp_bytes(c->bytes + c->off[i], c->off[i + 1] - c->off[i], c->bytes + c->off[j], c->off[j + 1] - c->off[j]);
+}
+
+static int cmp_tok_idx(const void* x, const void* y) {
+  int32_t i = *(const int32_t*)x, j = *(const int32_t*)y;
+  const orc_cs* c = g_cs_sort;
+  int r = cmp_bytes(c->tb + c->toff[i], c->toff[i + 1] - c->toff[i], c->tb + c->toff[j], c->toff[j + 1] - c->toff[j]);
+  return r ? r : (i < j ? -1 : i > j ? 1 : 0);
+}
+
+void orc_cs_free(orc_cs* c) {
+  if (!c) return;
+  free(c->bytes); free(c->off); free(c->order); free(c->tb); free(c->toff); free(c->torder);
+  free(c);
+}
+
+/* Validates and copies a character catalog.  Errors: INVALID_ARG for sizes
+ * and control ids, CATALOG for an empty or duplicate string or a byte of a
+ * string that no single-byte content token spells. */
+int orc_cs_build(const uint8_t* bytes, const int64_t* off, int32_t K, const uint8_t* tbytes,
+                 const int64_t* toff, int32_t V, int32_t sep, int32_t stop, orc_cs** out) {
+  *out = NULL;
+  if (K < 1 || V < 2 || sep < 0 || sep >= V || stop < 0 || stop >= V || sep == stop) return ORC_ERR_INVALID_ARG;
+  if (off[0] != 0 || toff[0] != 0) return ORC_ERR_INVALID_ARG;
+  orc_cs* c = (orc_cs*)calloc(1, sizeof(orc_cs));
+  c->K = K; c->V = V; c->sep = sep; c->stop = stop;
+  c->off = (int64_t*)malloc(sizeof(int64_t) * (K + 1));
+  memcpy(c->off, off, sizeof(int64_t) * (K + 1));
+  c->bytes = (uint8_t*)malloc((size_t)off[K] + 1);
+  memcpy(c->bytes, bytes, (size_t)off[K]);
+  c->toff = (int64_t*)malloc(sizeof(int64_t) * (V + 1));
+  memcpy(c->toff, toff, sizeof(int64_t) * (V + 1));
+  c->tb = (uint8_t*)malloc((size_t)toff[V] + 1);
+  memcpy(c->tb, tbytes, (size_t)toff[V]);
+  int single[256] = {0};
+  c->torder = (int32_t*)malloc(sizeof(int32_t) * V);
+  for (int32_t v = 0; v < V; ++v) {
+    int64_t L = toff[v + 1] - toff[v];
+    if (L < 0) { orc_cs_free(c); return ORC_ERR_INVALID_ARG; }
+    if (L == 0 || v == sep || v == stop) continue;
+    c->torder[c->nt++] = v;
+    if (L > c->max_tok) c->max_tok = (int32_t)L;
+    if (L == 1) single[tbytes[toff[v]]] = 1;
+  }
+  c->order = (int32_t*)malloc(sizeof(int32_t) * K);
+  for (int32_t i = 0; i < K; ++i) {
+    int64_t L = off[i + 1] - off[i];
+    if (L <= 0) { orc_cs_free(c); return ORC_ERR_CATALOG; }
+    if (L > c->max_len) c->max_len = (int32_t)L;
+    for (int64_t j = off[i]; j < off[i + 1]; ++j)
+      if (!single[bytes[j]]) { orc_cs_free(c); return ORC_ERR_CATALOG; }
+    c->order[i] = i;
+  }
+  g_cs_sort = c;
+  qsort(c->order, (size_t)K, sizeof(int32_t), cmp_str_idx);
+  qsort(c->torder, (size_t)c->nt, sizeof(int32_t), cmp_tok_idx);
+  for (int32_t i = 1; i < K; ++i)
+    if (cmp_str_idx(&c->order[i - 1], &c->order[i]) == 0) { orc_cs_free(c); return ORC_ERR_CATALOG; }
+  *out = c;
+  return ORC_OK;
+}
+
+/* max_len, max_tok, number of content tokens */
+void orc_cs_info(const orc_cs* c, int32_t* info) {
+  info[0] = c->max_len; info[1] = c->max_tok; info[2] = c->nt;
+}
+
+/* first position in the sorted catalog whose string is >= p (bytes) */
+static int32_t cs_lower(const orc_cs* c, const uint8_t* p, int64_t n) {
+  int32_t lo = 0, hi = c->K;
+  while (lo < hi) {
+    int32_t mid = (lo + hi) / 2, i = c->order[mid];
+    if (cmp_bytes(c->bytes + c->off[i], c->off[i + 1] - c->off[i], p, n) < 0) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+/* first position in the sorted content tokens whose bytes are >= p */
+static int32_t tok_lower(const orc_cs* c, const uint8_t* p, int64_t n) {
+  int32_t lo = 0, hi = c->nt;
+  while (lo < hi) {
+    int32_t mid = (lo + hi) / 2, v = c->torder[mid];
+    if (cmp_bytes(c->tb + c->toff[v], c->toff[v + 1] - c->toff[v], p, n) < 0) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+/* The legal set after the emitted bytes p[0..n): token ids in ascending
+ * order into out (room for V), stop included when p is a catalog string.
+ * Returns the count (0: empty mask).  mark: scratch of V bytes, zeroed. */
+static int32_t cs_mask(const orc_cs* c, const uint8_t* p, int64_t n, int32_t* out, uint8_t* mark) {
+  int32_t any = 0, stop_ok = 0;
+  for (int32_t pos = cs_lower(c, p, n); pos < c->K; ++pos) {
+    const int32_t i = c->order[pos];
+    const uint8_t* s = c->bytes + c->off[i];
+    const int64_t L = c->off[i + 1] - c->off[i];
+    if (L < n || (n && memcmp(s, p, (size_t)n) != 0)) break; /* past the strings that start with p */
+    if (L == n) {
+      stop_ok = 1;
+      continue;
+    }
+    if (g_mutant == MUT_CS_FIRST_BYTE) {
+      for (int32_t q = 0; q < c->nt; ++q) {
+        const int32_t v = c->torder[q];
+        if (c->tb[c->toff[v]] == s[n] && !mark[v]) { mark[v] = 1; any = 1; }
+      }
+      continue;
+    }
+    /* every token spelling s[n .. n+l), l = 1 .. the bytes left */
+    const int64_t top = L - n < c->max_tok ? L - n : c->max_tok;
+    for (int64_t l = 1; l <= top; ++l) {
+      for (int32_t q = tok_lower(c, s + n, l); q < c->nt; ++q) {
+        const int32_t v = c->torder[q];
+        if (c->toff[v + 1] - c->toff[v] != l || memcmp(c->tb + c->toff[v], s + n, (size_t)l) != 0) break;
+        if (!mark[v]) { mark[v] = 1; any = 1; }
+      }
+    }
+  }
+  if (stop_ok && g_mutant == MUT_CS_STOP_LEAF_ONLY && any) stop_ok = 0;
+  if (stop_ok) mark[c->stop] = 1;
+  int32_t k = 0;
+  for (int32_t v = 0; v < c->V; ++v)
+    if (mark[v]) { out[k++] = v; mark[v] = 0; }
+  return k;
+}
+
+/* Legal set after the byte prefix p[0..n) (ascending token ids into out,
+ * room for V); returns the count. */
+int32_t orc_cs_mask(const orc_cs* c, const uint8_t* p, int64_t n, int32_t* out) {
+  uint8_t* mark = (uint8_t*)calloc((size_t)c->V, 1);
+  int32_t k = cs_mask(c, p, n, out, mark);
+  free(mark);
+  return k;
+}
+
+/* Greedy decode of B sequences over a character catalog (k = 1), hidden
+ * [T][B][H]: at each step the legal set above, one fp64 logit per legal
+ * token (orc_logit), the first maximum in ascending id order, then the
+ * token's bytes appended (stop: the string chosen, sequence done).  follow
+ * ([B][T] or NULL): teacher forcing as in orc_decode.  Outputs as for
+ * orc_decode, with entry [B] the catalog index of the chosen string (-1
+ * when none) and status EMPTY_MASK, NOT_WALKABLE (a forced token outside the
+ * legal set) or NOT_DONE (no stop within T steps). */
+int orc_cs_decode(const orc_cs* c, const void* emb, int dtype, int32_t H, const void* hidden, int32_t B, int32_t T,
+                  const int32_t* follow, int32_t* tokens, int32_t* len, int32_t* entry, int32_t* status,
+                  double* best, double* margin, double* sumabs, int32_t* nlegal) {
+  if (H < 1 || B < 1 || T < 0) return ORC_ERR_INVALID_ARG;
+  const size_t esz = dtype == 0 ? 4 : 2;
+  int32_t* legal = (int32_t*)malloc(sizeof(int32_t) * c->V);
+  uint8_t* mark = (uint8_t*)calloc((size_t)c->V, 1);
+  uint8_t* pre = (uint8_t*)malloc((size_t)c->max_len + 1);
+  for (int32_t b = 0; b < B; ++b) {
+    int64_t n = 0;
+    int32_t st = ORC_OK, fin = 0, emitted = 0, ent = -1;
+    for (int32_t t = 0; t < T; ++t) {
+      const int64_t o = (int64_t)b * T + t;
+      if (tokens) tokens[o] = -1;
+      if (best) best[o] = NAN;
+      if (margin) margin[o] = NAN;
+      if (sumabs) sumabs[o] = NAN;
+      if (nlegal) nlegal[o] = 0;
+      if (fin || st != ORC_OK) continue;
+      const int32_t k = cs_mask(c, pre, n, legal, mark);
+      if (nlegal) nlegal[o] = k;
+      if (k == 0) {
+        st = ORC_ERR_EMPTY_MASK;
+        continue;
+      }
+      const void* h = (const char*)hidden + ((size_t)t * B + b) * (size_t)H * esz;
+      int32_t win = -1;
+      double bl = 0.0, second = -INFINITY, ba = 0.0, sa2 = 0.0;
+      for (int32_t j = 0; j < k; ++j) {
+        double a;
+        const double l = orc_logit(emb, dtype, H, legal[j], h, &a);
+        if (win < 0 || l > bl) {
+          if (win >= 0) { second = bl; sa2 = ba; }
+          win = legal[j]; bl = l; ba = a;
+        } else if (l > second || (l == second && sa2 < a)) {
+          second = l; sa2 = a;
+        }
+      }
+      if (tokens) tokens[o] = win;
+      if (best) best[o] = bl;
+      if (margin) margin[o] = k > 1 ? bl - second : INFINITY;
+      if (sumabs) sumabs[o] = k > 1 && sa2 > ba ? sa2 : ba;
+      int32_t take = win;
+      if (follow && follow[o] >= 0) {
+        take = follow[o];
+        int ok = 0;
+        for (int32_t j = 0; j < k; ++j) ok |= legal[j] == take;
+        if (!ok) {
+          st = ORC_ERR_NOT_WALKABLE;
+          continue;
+        }
+      }
+      emitted++;
+      if (take == c->stop) {
+        fin = 1;
+        const int32_t pos = cs_lower(c, pre, n);
+        ent = c->order[pos]; /* the string equal to the prefix: legal stop guarantees it */
+      } else {
+        const int64_t tl = c->toff[take + 1] - c->toff[take];
+        memcpy(pre + n, c->tb + c->toff[take], (size_t)tl);
+        n += tl;
+      }
+    }
+    if (st == ORC_OK && !fin) st = ORC_ERR_NOT_DONE;
+    if (len) len[b] = emitted;
+    if (entry) entry[b] = fin ? ent : -1;
+    if (status) status[b] = st;
+  }
+  free(legal);
+  free(mark);
+  free(pre);
   return ORC_OK;
 }
