@@ -106,6 +106,31 @@ tms_status tms_trie_build(const int32_t* tokens, const int64_t* offsets, int32_t
 tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_t K, int32_t vocab,
                            int32_t sep, int32_t stop, tms_path path, void* stream, tms_trie** out);
 
+/* Character-level catalogs (the review of arXiv 2608.12574, fields
+ * pith_extraction.key_machinery and core_discovery): the catalog is K byte
+ * strings (bytes [offsets[K]], offsets [K+1], string i = bytes[offsets[i] ..
+ * offsets[i+1])) and the vocabulary gives each of the V token ids a byte
+ * string (token_bytes / token_offsets alike; an empty string marks a control
+ * or unused token).  An answer is one catalog string spelled by tokens,
+ * then stop.  The compiler builds a trie over the strings' bytes and, with
+ * one Aho-Corasick automaton over the vocabulary's byte strings carried along
+ * a walk of the trie, every node's set of tokens whose bytes can be read
+ * downward from it; the result is a trie of the same form as the token
+ * catalogs' (nodes = the byte trie's, breadth first; a node's edges = its
+ * valid tokens in ascending id order, each leading to the node where the
+ * token ends; sep and stop edges where a string ends), decoded by every call
+ * below with k = 1 (TMS_ERR_K otherwise).  Every byte that occurs in a string
+ * must be spelled by a single-byte token (as in byte-level vocabularies), so
+ * that every legal token leaves a remainder that can be spelled.  Errors:
+ * INVALID_ARG (sizes, control ids), CATALOG (empty or duplicate string, a
+ * byte with no single-byte token).  Host arrays, caller-owned. */
+tms_status tms_charset_build(const uint8_t* bytes, const int64_t* offsets, int32_t K, const uint8_t* token_bytes,
+                             const int64_t* token_offsets, int32_t V, int32_t sep, int32_t stop, tms_trie** out);
+/* tms_charset_build plus the device copy, as tms_trie_upload. */
+tms_status tms_charset_upload(const uint8_t* bytes, const int64_t* offsets, int32_t K, const uint8_t* token_bytes,
+                              const int64_t* token_offsets, int32_t V, int32_t sep, int32_t stop, tms_path path,
+                              void* stream, tms_trie** out);
+
 tms_status tms_trie_info_get(const tms_trie* trie, tms_trie_info* info);
 
 /* Copy the canonical CSR to host arrays sized from tms_trie_info:

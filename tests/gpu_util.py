@@ -90,10 +90,24 @@ def run_step_loop(state: tms.State, hid_dev: torch.Tensor, dense: bool = False, 
 
 
 def ref_decode(otr: oracle.Trie, k: int, emb: np.ndarray, hid: np.ndarray):
-    """The oracle's greedy decode, keeping its inputs so that compare() can
+    """The oracle's greedy decode, keeping what compare() needs to
     teacher-force it along the GPU's tokens after a numerical-tie flip."""
     ref = oracle.decode(otr, k, emb, hid)
-    ref["_inputs"] = (otr, k, emb, hid)
+    ref["_emb"], ref["_hid"] = emb, hid
+    ref["_follow"] = lambda b, row: oracle.decode(otr, k, emb, np.ascontiguousarray(hid[:, b:b + 1]),
+                                                  follow=np.ascontiguousarray(row))
+    return ref
+
+
+def ref_decode_chars(cc: oracle.CharCatalog, emb: np.ndarray, hid: np.ndarray):
+    """The same for a character catalog (one string per answer: entries [B][1])."""
+    def as_ref(out):
+        out["entries"] = out["entry"][:, None].copy()
+        return out
+    ref = as_ref(cc.decode(emb, hid))
+    ref["_emb"], ref["_hid"] = emb, hid
+    ref["_follow"] = lambda b, row: as_ref(cc.decode(emb, np.ascontiguousarray(hid[:, b:b + 1]),
+                                                     follow=np.ascontiguousarray(row)))
     return ref
 
 
@@ -113,11 +127,10 @@ def compare(gpu_tokens, ref, H, gpu_logits=None, gpu_len=None, gpu_entries=None,
             g, r = int(gpu_tokens[b, t]), int(cur["tokens"][row, t])
             if g != r:
                 assert r >= 0 and g >= 0, f"{where} seq {b} step {t}: gpu token {g}, oracle {r}"
-                assert "_inputs" in ref, f"{where} seq {b} step {t}: gpu token {g}, oracle {r} (no oracle inputs)"
-                otr, k, emb, hid = ref["_inputs"]
+                assert "_follow" in ref, f"{where} seq {b} step {t}: gpu token {g}, oracle {r} (no oracle inputs)"
+                emb, hid = ref["_emb"], ref["_hid"]
                 if cur is ref:
-                    cur = oracle.decode(otr, k, emb, np.ascontiguousarray(hid[:, b:b + 1]),
-                                        follow=np.ascontiguousarray(gpu_tokens[b:b + 1, :T]))
+                    cur = ref["_follow"](b, gpu_tokens[b:b + 1, :T])
                     row = 0
                     assert int(cur["tokens"][0, t]) == r  # same prefix, same pick
                 lg, ag = oracle.logit(emb, g, hid[t, b])

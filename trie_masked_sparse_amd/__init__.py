@@ -38,7 +38,8 @@ LOOP_RESIDENT, LOOP_GRAPH, LOOP_STREAM, LOOP_RESIDENT_SOLO, LOOP_RESIDENT_GROUPE
 
 # every symbol declared in include/tms.h
 EXPORTS = (
-    "tms_trie_build", "tms_trie_upload", "tms_trie_info_get", "tms_trie_export_csr", "tms_trie_free",
+    "tms_trie_build", "tms_trie_upload", "tms_charset_build", "tms_charset_upload", "tms_trie_info_get",
+    "tms_trie_export_csr", "tms_trie_free",
     "tms_state_create", "tms_state_reset", "tms_state_sync_status", "tms_state_export", "tms_state_free",
     "tms_decode_step_sparse", "tms_decode_step_dense_masked", "tms_decode_k_pointers",
     "tms_advance_forced", "tms_legal_set", "tms_legal_mask", "tms_mask_to_rows", "tms_gather_gemv",
@@ -78,6 +79,8 @@ def lib():
         sig = {
             "tms_trie_build": [P, P, i32, i32, i32, i32, PP],
             "tms_trie_upload": [P, P, i32, i32, i32, i32, C.c_int, P, PP],
+            "tms_charset_build": [P, P, i32, P, P, i32, i32, i32, PP],
+            "tms_charset_upload": [P, P, i32, P, P, i32, i32, i32, C.c_int, P, PP],
             "tms_trie_info_get": [P, C.POINTER(TrieInfo)],
             "tms_trie_export_csr": [P, P, P, P, P, P],
             "tms_trie_free": [P],
@@ -182,6 +185,32 @@ def trie_upload(entries, vocab: int, sep: int, stop: int, path: int = PATH_AUTO,
     h = C.c_void_p()
     _check(lib().tms_trie_upload(toks.ctypes.data, offs.ctypes.data, len(offs) - 1, vocab, sep, stop, path,
                                  _stream(stream), C.byref(h)), "trie_upload")
+    return h
+
+
+def _bytes_arrays(items):
+    off = np.zeros(len(items) + 1, dtype=np.int64)
+    off[1:] = np.cumsum([len(x) for x in items])
+    buf = np.frombuffer(b"".join(bytes(x) for x in items) or b"\0", np.uint8).copy()
+    return buf, off
+
+
+def charset_build(strings, vocab, sep: int, stop: int):
+    """strings: catalog byte strings; vocab: byte string of every token id."""
+    sb, so = _bytes_arrays(strings)
+    tb, to = _bytes_arrays(vocab)
+    h = C.c_void_p()
+    _check(lib().tms_charset_build(sb.ctypes.data, so.ctypes.data, len(strings), tb.ctypes.data, to.ctypes.data,
+                                   len(vocab), sep, stop, C.byref(h)), "charset_build")
+    return h
+
+
+def charset_upload(strings, vocab, sep: int, stop: int, path: int = PATH_AUTO, stream=None):
+    sb, so = _bytes_arrays(strings)
+    tb, to = _bytes_arrays(vocab)
+    h = C.c_void_p()
+    _check(lib().tms_charset_upload(sb.ctypes.data, so.ctypes.data, len(strings), tb.ctypes.data, to.ctypes.data,
+                                    len(vocab), sep, stop, path, _stream(stream), C.byref(h)), "charset_upload")
     return h
 
 
@@ -392,10 +421,22 @@ class Trie:
     """Owning wrapper of a tms_trie handle."""
 
     def __init__(self, entries, vocab: int, sep: int, stop: int, path: int = PATH_AUTO, upload: bool = True,
-                 stream=None):
-        self.h = trie_upload(entries, vocab, sep, stop, path, stream) if upload else \
-            trie_build(entries, vocab, sep, stop)
+                 stream=None, _handle=None):
+        if _handle is not None:
+            self.h = _handle
+        else:
+            self.h = trie_upload(entries, vocab, sep, stop, path, stream) if upload else \
+                trie_build(entries, vocab, sep, stop)
         self.info = trie_info_get(self.h)
+
+    @classmethod
+    def from_charset(cls, strings, vocab, sep: int, stop: int, path: int = PATH_AUTO, upload: bool = True,
+                     stream=None):
+        """A character-level catalog: byte strings and the byte string of
+        every token id (answers pick one string, k = 1)."""
+        h = charset_upload(strings, vocab, sep, stop, path, stream) if upload else \
+            charset_build(strings, vocab, sep, stop)
+        return cls(None, 0, 0, 0, _handle=h)
 
     def csr(self):
         return trie_export_csr(self.h)

@@ -31,7 +31,8 @@ def build(verbose: bool = True) -> str:
     objdir = os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = []
-    for src, lang in (("kernels.hip", "hip"), ("noalloc.hip", "hip"), ("api.cpp", "c++"), ("trie_build.cpp", "c++")):
+    for src, lang in (("kernels.hip", "hip"), ("noalloc.hip", "hip"), ("api.cpp", "c++"), ("trie_build.cpp", "c++"),
+                      ("charset_build.cpp", "c++")):
         obj = os.path.join(objdir, src + ".o")
         cmd = [HIPCC, f"--offload-arch={ARCH}", *COMMON, "-c", "-x", lang, os.path.join(CSRC, src), "-o", obj]
         if lang == "hip":

@@ -12,6 +12,7 @@
 #include <string>
 #include <vector>
 
+#include "charset_build.h"
 #include "handles.h"
 
 namespace {
@@ -185,13 +186,12 @@ tms_status tms_trie_build(const int32_t* tokens, const int64_t* offsets, int32_t
   return TMS_OK;
 }
 
-tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_t K, int32_t vocab, int32_t sep,
-                           int32_t stop, tms_path path, void* stream, tms_trie** out) {
-  if (path != TMS_PATH_AUTO && path != TMS_PATH_FAST && path != TMS_PATH_GLOBAL)
-    return fail(TMS_ERR_INVALID_ARG, "unknown path");
-  tms_trie* t = nullptr;
-  tms_status rc = tms_trie_build(tokens, offsets, K, vocab, sep, stop, &t);
-  if (rc != TMS_OK) return rc;
+// The device copy of a built trie, owned by t (freed with t on failure).
+// tokens/offsets: the token catalog the trie was built from, for the
+// per-entry tables (bitmask state, reset by paths); null for a character
+// catalog, whose entries have no single token path.
+static tms_status upload_host(tms_trie* t, const int32_t* tokens, const int64_t* offsets, int32_t K, tms_path path,
+                              void* stream, tms_trie** out) {
   const tms::HostTrie& h = t->host;
   // hot CSR bytes read by the step: begin, tok, child
   const int64_t hot = 4ll * (h.n_nodes + 1) + 8ll * h.n_edges;
@@ -249,12 +249,12 @@ tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_
   const int32_t n_run = static_cast<int32_t>(run_edge.size());
   // bitmask no-repeat state for catalogs of at most 128 entries: the entries
   // below each content edge (the edges of each entry's root path)
-  const bool with_mask = h.n_entries <= 128;
+  const bool with_mask = tokens && h.n_entries <= 128;
   std::vector<uint32_t> emask(with_mask ? size_t(h.n_edges) * 4 : 0, 0u);
   // each entry's root path, for resets that restore only what completions
   // released (int32 offsets: at most 2^31 - 1 catalog tokens)
-  const int64_t n_path = offsets[K] - offsets[0];
-  const bool with_paths = n_path < (int64_t(1) << 31);
+  const int64_t n_path = tokens ? offsets[K] - offsets[0] : 0;
+  const bool with_paths = tokens && n_path < (int64_t(1) << 31);
   std::vector<int32_t> ent_off(with_paths ? size_t(K) + 1 : 0, 0), ent_path(with_paths ? size_t(n_path) : 0, 0);
   if (with_mask || with_paths) {
     for (int32_t j = 0; j < K; ++j) {
@@ -382,8 +382,50 @@ tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_
   d.stop = h.stop;
   d.vocab = h.vocab;
   d.live_stride = live_stride;
+  d.release = t->charset ? 0 : 1;
   *out = t;
   return TMS_OK;
+}
+
+tms_status tms_trie_upload(const int32_t* tokens, const int64_t* offsets, int32_t K, int32_t vocab, int32_t sep,
+                           int32_t stop, tms_path path, void* stream, tms_trie** out) {
+  if (!out) return fail(TMS_ERR_INVALID_ARG, "out is null");
+  *out = nullptr;
+  if (path != TMS_PATH_AUTO && path != TMS_PATH_FAST && path != TMS_PATH_GLOBAL)
+    return fail(TMS_ERR_INVALID_ARG, "unknown path");
+  tms_trie* t = nullptr;
+  tms_status rc = tms_trie_build(tokens, offsets, K, vocab, sep, stop, &t);
+  if (rc != TMS_OK) return rc;
+  return upload_host(t, tokens, offsets, K, path, stream, out);
+}
+
+tms_status tms_charset_build(const uint8_t* bytes, const int64_t* offsets, int32_t K, const uint8_t* token_bytes,
+                             const int64_t* token_offsets, int32_t V, int32_t sep, int32_t stop, tms_trie** out) {
+  if (!out) return fail(TMS_ERR_INVALID_ARG, "out is null");
+  *out = nullptr;
+  tms_trie* t = new tms_trie();
+  t->charset = true;
+  std::string err;
+  const int rc = tms::build_charset(bytes, offsets, K, token_bytes, token_offsets, V, sep, stop, &t->host, &err);
+  if (rc != 0) {
+    delete t;
+    return fail(static_cast<tms_status>(rc), err);
+  }
+  *out = t;
+  return TMS_OK;
+}
+
+tms_status tms_charset_upload(const uint8_t* bytes, const int64_t* offsets, int32_t K, const uint8_t* token_bytes,
+                              const int64_t* token_offsets, int32_t V, int32_t sep, int32_t stop, tms_path path,
+                              void* stream, tms_trie** out) {
+  if (!out) return fail(TMS_ERR_INVALID_ARG, "out is null");
+  *out = nullptr;
+  if (path != TMS_PATH_AUTO && path != TMS_PATH_FAST && path != TMS_PATH_GLOBAL)
+    return fail(TMS_ERR_INVALID_ARG, "unknown path");
+  tms_trie* t = nullptr;
+  tms_status rc = tms_charset_build(bytes, offsets, K, token_bytes, token_offsets, V, sep, stop, &t);
+  if (rc != TMS_OK) return rc;
+  return upload_host(t, nullptr, nullptr, 0, path, stream, out);
 }
 
 tms_status tms_trie_info_get(const tms_trie* t, tms_trie_info* info) {
@@ -430,6 +472,7 @@ tms_status tms_state_create(tms_trie* trie, int32_t B, int32_t k, const void* em
   if (B < 1 || B > 65535) return fail(TMS_ERR_INVALID_ARG, "B must be in [1, 65535]");
   if (k < 1 || k > trie->host.n_entries)
     return fail(TMS_ERR_K, "k = " + std::to_string(k) + " outside [1, " + std::to_string(trie->host.n_entries) + "]");
+  if (trie->charset && k != 1) return fail(TMS_ERR_K, "a character catalog answers with one string (k = 1)");
   if (dtype != TMS_F32 && dtype != TMS_BF16) return fail(TMS_ERR_INVALID_ARG, "dtype must be fp32 or bf16");
   if (!emb || !aligned16(emb)) return fail(TMS_ERR_INVALID_ARG, "embedding pointer null or not 16-byte aligned");
   if (tms::chunks_for(dtype, H) == 0)
@@ -551,6 +594,7 @@ tms_status tms_state_create(tms_trie* trie, int32_t B, int32_t k, const void* em
 // The kind of reset a pending reset takes.
 static int reset_kind(const tms_state* st) {
   if (!st->reset_pending) return tms::kResetNone;
+  if (!st->trie->dev.release) return st->live_by_paths ? tms::kResetState : tms::kResetFull;
   return st->live_by_paths && st->trie->dev.ent_path ? tms::kResetPaths : tms::kResetFull;
 }
 

@@ -14,6 +14,7 @@
 
 struct tms_trie {
   tms::HostTrie host;
+  bool charset = false;  // built from a character catalog (one string per answer)
   int path = TMS_PATH_AUTO;  // FAST or GLOBAL once uploaded
   int device = -1;
   void* dmem = nullptr;

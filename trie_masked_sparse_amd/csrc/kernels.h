@@ -59,6 +59,10 @@ struct DevTrie {
   int32_t image_words;
   int32_t n_nodes, n_edges, n_entries, cap, max_depth, sep, stop, vocab;
   int32_t live_stride;   // n_edges rounded up to a multiple of 4
+  // 1: a completed pointer releases the live counts on its path (token
+  // catalogs, k pointers); 0: an answer is one string (character catalogs),
+  // so nothing is released and the live rows stay equal to live0
+  int32_t release;
 };
 
 // Struct-of-arrays decode state for B sequences.
@@ -124,7 +128,9 @@ enum { kLoopLater = 1, kLoopExitAtRoot = 2, kLoopRootKey = 4 };
 // relies on the stored live counts differing from live0 only on the root
 // paths of the stored completed entries (what completions release), and
 // restores just those edges and the entries' spent words.
-enum { kResetNone = 0, kResetFull = 1, kResetPaths = 2 };
+// kResetState (tries that never release, see DevTrie::release): the live
+// rows are untouched, only the sequences' state and spent flags are reset.
+enum { kResetNone = 0, kResetFull = 1, kResetPaths = 2, kResetState = 3 };
 
 // dtype: 0 fp32, 1 bf16.  Every launcher returns hipGetLastError().
 hipError_t launch_reset(const DevTrie& tr, const DevState& st, int kind, hipStream_t s);

@@ -280,7 +280,8 @@ __device__ int advance(const DevTrie& tr, const DevState& st, const StepIO* io, 
         next = c == kChildStop ? -1 : 0;
         const int ent = tr.entry[q.node];
         const int32_t* path = st.path + (int64_t)s * st.path_stride;
-        for (int i = lane; i < q.depth; i += kWave) live[path[i]] -= 1;  // distinct edges
+        if (tr.release)
+          for (int i = lane; i < q.depth; i += kWave) live[path[i]] -= 1;  // distinct edges
         if (lane == 0) {
           st.spent[(int64_t)s * st.spent_words + (ent >> 5)] |= 1u << (ent & 31);
           st.entries[(int64_t)s * st.k + q.done] = ent;
@@ -1086,8 +1087,9 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
     restore_paths(tr, st, s, g_live, g_spent, wv, W, lane);
     __syncthreads();  // the stored entries are read before they are cleared below
   } else if (rst) {
-    for (int i = threadIdx.x; i < (int)(ls / 4); i += kLoopBlock)
-      reinterpret_cast<int4*>(g_live)[i] = reinterpret_cast<const int4*>(tr.live0)[i];
+    if (io.reset == kResetFull)
+      for (int i = threadIdx.x; i < (int)(ls / 4); i += kLoopBlock)
+        reinterpret_cast<int4*>(g_live)[i] = reinterpret_cast<const int4*>(tr.live0)[i];
     if (!sreg_ok)
       for (int i = threadIdx.x; i < st.spent_words; i += kLoopBlock) g_spent[i] = 0u;
   }
@@ -1196,10 +1198,11 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
     if (wv == 0) {
       if (lane == 0) tokens[t] = tok;
       if (reg_lists) {
-        if (!MASK && lane < depth) atomicSub(&live[my_path], 1);  // distinct edges; no value returned
+        if (!MASK && lane < depth && tr.release) atomicSub(&live[my_path], 1);  // distinct edges; no value returned
         if (lane == done) my_ent = ent;
       } else {
-        for (int i = lane; i < depth; i += kWave) atomicSub(&live[path[i]], 1);
+        if (tr.release)
+          for (int i = lane; i < depth; i += kWave) atomicSub(&live[path[i]], 1);
         if (lane == 0) entries[done] = ent;
       }
       if (!sreg_ok && lane == 0) spent[ent >> 5] |= 1u << (ent & 31);
@@ -2451,10 +2454,12 @@ __global__ __launch_bounds__(kBlock) void reset_kernel(DevTrie tr, DevState st, 
     restore_paths(tr, st, s, st.live + (int64_t)s * tr.live_stride, sp, wave_id(), kWavesPerBlock, __lane_id());
     __syncthreads();  // the stored entries are read before they are cleared below
   } else {
-    const int q4 = tr.live_stride / 4;
-    const int4* src = (const int4*)tr.live0;
-    int4* dst = (int4*)(st.live + (int64_t)s * tr.live_stride);
-    for (int i = blockIdx.x * kBlock + threadIdx.x; i < q4; i += gridDim.x * kBlock) dst[i] = src[i];
+    if (kind == kResetFull) {
+      const int q4 = tr.live_stride / 4;
+      const int4* src = (const int4*)tr.live0;
+      int4* dst = (int4*)(st.live + (int64_t)s * tr.live_stride);
+      for (int i = blockIdx.x * kBlock + threadIdx.x; i < q4; i += gridDim.x * kBlock) dst[i] = src[i];
+    }
     for (int i = blockIdx.x * kBlock + threadIdx.x; i < st.spent_words; i += gridDim.x * kBlock) sp[i] = 0u;
   }
   if (blockIdx.x == 0) {
@@ -2605,7 +2610,7 @@ int chunks_for(int dtype, int H) {
 hipError_t launch_reset(const DevTrie& tr, const DevState& st, int kind, hipStream_t s) {
   const int q4 = tr.live_stride / 4;
   int gx = (q4 + kBlock * 8 - 1) / (kBlock * 8);
-  gx = kind == kResetPaths || gx < 1 ? 1 : (gx > 256 ? 256 : gx);
+  gx = kind != kResetFull || gx < 1 ? 1 : (gx > 256 ? 256 : gx);
   hipLaunchKernelGGL(reset_kernel, dim3(gx, st.B), dim3(kBlock), 0, s, tr, st, kind);
   return hipGetLastError();
 }

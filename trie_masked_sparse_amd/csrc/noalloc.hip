@@ -95,6 +95,7 @@ extern "C" tms_status tms_decode_k_pointers_noalloc(const tms_trie* trie, const 
   const tms::HostTrie& h = trie->host;
   if (k < 1 || k > h.n_entries)
     return api_fail(TMS_ERR_K, "k = " + std::to_string(k) + " outside [1, " + std::to_string(h.n_entries) + "]");
+  if (trie->charset && k != 1) return api_fail(TMS_ERR_K, "a character catalog answers with one string (k = 1)");
   if (dtype != TMS_F32 && dtype != TMS_BF16) return api_fail(TMS_ERR_INVALID_ARG, "dtype must be fp32 or bf16");
   auto aligned16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
   if (!emb || !aligned16(emb)) return api_fail(TMS_ERR_INVALID_ARG, "embedding pointer null or not 16-byte aligned");
