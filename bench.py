@@ -15,7 +15,8 @@ is reported.
 Also on the same line: the loop kernel's roofline (the unique rows and hidden
 vectors the head steps must read, over the kernel's duration), the batch-64
 and batch-256 workloads (unique-row rates: rows shared by sequences are read
-once), the per-step kernel graph (the form a caller with its own forward pass
+once), the character-level catalogs (host compile time, valid tokens per node
+by depth, decode rates), the per-step kernel graph (the form a caller with its own forward pass
 uses), the gather-GEMV bandwidth stress shapes next to a hand-written
 streaming-read kernel timed on the same byte counts, the dense+mask step, and
 the CPU oracle on every host thread (cpu_baseline, the only place the oracle
@@ -494,11 +495,66 @@ def _pmc_traffic(kernel: str, workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
+class CharWorkload(Workload):
+    """A character-level catalog (byte strings, byte-string vocabulary), one
+    string per answer, rows from the product-scale embedding."""
+
+    def __init__(self, cid):
+        import torch
+
+        import trie_masked_sparse_amd as tms
+        from synth import CHAR_CONFIGS, char_catalog, char_hidden, char_vocab, embedding
+        self.c = c = CHAR_CONFIGS[cid]
+        self.cid = cid
+        self.B = c.batch
+        strings, vocab = char_catalog(cid), char_vocab(cid)
+        t0 = time.perf_counter()
+        h = tms.charset_build(strings, vocab, c.sep, c.stop)  # host compile only, timed
+        self.compile_ms = (time.perf_counter() - t0) * 1e3
+        csr = tms.trie_export_csr(h)
+        tms.trie_free(h)
+        self.valid_by_depth = _valid_by_depth(csr, vocab)
+        self.trie = tms.Trie.from_charset(strings, vocab, c.sep, c.stop)
+        self.info = self.trie.info
+        self.T = self.info["max_depth"] + 1
+        self.emb_np = embedding(c.emb_cid)
+        self.emb = _to_dev(self.emb_np)
+        self.hid_np = char_hidden(cid, self.T)
+        self.hid = _to_dev(self.hid_np)
+        self.state = tms.State(self.trie, self.B, 1, self.emb)
+        self.grouped = self.B >= 8 and int(csr["begin"][1] - csr["begin"][0]) >= 64
+        self.tokens = torch.empty((self.B, self.T), dtype=torch.int32, device="cuda")
+        self.len = torch.empty(self.B, dtype=torch.int32, device="cuda")
+        self.entries = torch.empty((self.B, 1), dtype=torch.int32, device="cuda")
+        self.esz = 2
+
+
+def _valid_by_depth(csr, vocab):
+    """Mean and largest number of valid tokens per trie node, by the node's
+    depth in bytes (the page's measure of how fast the valid sets shrink)."""
+    import numpy as np
+    b = csr["begin"]
+    depth = {0: 0}
+    order = [0]
+    for n in order:
+        for e in range(b[n], b[n + 1]):
+            ch = int(csr["child"][e])
+            if ch >= 0 and ch not in depth:
+                depth[ch] = depth[n] + len(vocab[int(csr["tok"][e])])
+                order.append(ch)
+    sizes = {}
+    for n, d in depth.items():
+        k = int(np.sum(csr["child"][b[n]:b[n + 1]] >= 0))
+        sizes.setdefault(d, []).append(k)
+    return {str(d): {"nodes": len(v), "mean": float(np.mean(v)), "max": int(max(v))}
+            for d, v in sorted(sizes.items()) if d <= 6}
+
+
 def workload_line(cid: str, steps: int, warmup: int, per_step_graph: bool = True):
     """Resident-loop rates of one batched workload."""
     import trie_masked_sparse_amd as tms
     _log(f"{cid} workload")
-    w = Workload(cid)
+    w = CharWorkload(cid) if cid.startswith("charset") else Workload(cid)
     r = time_answers(w, steps, warmup)
     prof = w.byte_profile()
     rates = loop_rates(w, r, prof)
@@ -509,7 +565,11 @@ def workload_line(cid: str, steps: int, warmup: int, per_step_graph: bool = True
          "root_steps": "grouped" if w.grouped else "per sequence",
          "unique_frac_of_8TBps": rates["unique_GBps"] / HBM_PEAK_GBPS, **rates,
          "eager_event_median_us": r["eager_event_median_us"],
-         "seeds": {"catalog": w.c.cat_seed, "embedding": w.c.emb_seed, "hidden": w.c.hid_seed}}
+         "seeds": {"catalog": w.c.cat_seed, "hidden": w.c.hid_seed,
+                   "embedding": getattr(w.c, "emb_seed", None), "vocabulary": getattr(w.c, "voc_seed", None)}}
+    if isinstance(w, CharWorkload):
+        d.update({"host_compile_ms": w.compile_ms, "valid_tokens_by_depth": w.valid_by_depth,
+                  "trie": {k: w.info[k] for k in ("n_nodes", "n_edges", "cap", "max_depth")}})
     if per_step_graph:
         d["per_step_kernel_graph"] = graph_mode(w, max(5, steps // 5), 2)
     w.close()
@@ -525,7 +585,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=2.0)
     ap.add_argument("--only", default="",
-                    help="comma list of headline,b64,large,stress,dense,cpu,copyref (default: all but copyref)")
+                    help="comma list of headline,b64,large,charset,stress,dense,cpu,copyref "
+                         "(default: all but copyref)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): this build runs on one GPU. "
@@ -583,6 +644,9 @@ def main():
             also[f"{cid}_B64"] = workload_line(cid, max(10, args.steps // 2), args.warmup)
     if want("large"):
         also["large_B256"] = workload_line("large", max(5, args.steps // 5), 2, per_step_graph=False)
+    if want("charset"):
+        for cid in ("charset_tools", "charset_hex"):
+            also[f"{cid}_B64"] = workload_line(cid, max(10, args.steps // 2), args.warmup)
     if want("dense"):
         also["dense_masked_product_B1"] = dense_step_us(w)
         wd = Workload("structured")

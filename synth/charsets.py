@@ -35,6 +35,10 @@ class CharConfig:
     emb_cid: str  # the token workload whose embedding table the rows come from
 
     @property
+    def k(self) -> int:
+        return 1  # one string per answer
+
+    @property
     def sep(self) -> int:
         return self.vocab - 2
 
