@@ -495,6 +495,144 @@ def _pmc_traffic(kernel: str, workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
+def _rocprof_rows(folder: str, kind: str):
+    """Rows of the rocprofv3 CSV output (kernel_trace or counter_collection)
+    under folder."""
+    import csv
+    import glob
+    paths = sorted(glob.glob(os.path.join(folder, "**", f"*{kind}.csv"), recursive=True))
+    if not paths:
+        raise FileNotFoundError(f"no *{kind}.csv under {folder}")
+    rows = []
+    for p in paths:
+        with open(p, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _dim(row, key):
+    if row.get(key) not in (None, ""):
+        return int(row[key])
+    return int(row[key + "_X"]) * int(row.get(key + "_Y") or 1) * int(row.get(key + "_Z") or 1)
+
+
+def _kernel_key(row):
+    """(short kernel name, workgroups) of a rocprofv3 dispatch row."""
+    name = row["Kernel_Name"].replace("void ", "").replace("(anonymous namespace)::", "").replace("tms::", "")
+    name = name.split("(")[0].strip()
+    return name, _dim(row, "Grid_Size") // max(1, _dim(row, "Workgroup_Size"))
+
+
+def summarize_trace(folder: str):
+    """Per (kernel, workgroups): dispatches, mean and median duration in
+    microseconds (End - Start of each dispatch)."""
+    groups = {}
+    for r in _rocprof_rows(folder, "kernel_trace"):
+        groups.setdefault(_kernel_key(r), []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    print(f"{'kernel':<48}{'WGs':>6}{'calls':>8}{'mean us':>10}{'median us':>11}")
+    for (k, wg), d in sorted(groups.items()):
+        print(f"{k:<48}{wg:>6}{len(d):>8}{statistics.mean(d):>10.2f}{statistics.median(d):>11.2f}")
+
+
+DECODE_KERNELS = ("loop_kernel", "root_mfma_kernel", "root_head_kernel")
+
+
+def summarize_counters(folder: str, bench_json=None):
+    """HBM bytes per launch from rocprofv3 counter runs, one run per workload
+    and counter in folder/<workload>_<FETCH_SIZE|WRITE_SIZE>/.  Both counters
+    are in KiB per dispatch; each is scaled by what it reads for the 256 MiB
+    device copy of the copyref run (bytes known).  Writes the per-launch
+    traffic of the product loop and of the two stress gathers to profiles/
+    (with the kernel-source hash recorded by the GPU run, which must be the
+    current one) and prints the per-kernel table and the decode kernels'
+    memory fills per answer of every workload."""
+    import glob
+
+    from synth import CHAR_CONFIGS, CONFIGS
+    hash_file = os.path.join(folder, "kernel_hash.txt")
+    run_hash = open(hash_file).read().strip() if os.path.exists(hash_file) else None
+    if run_hash != _kernel_hash():
+        raise SystemExit(f"counters were taken with kernel sources {run_hash}, the tree has {_kernel_hash()}")
+    data = {}  # (workload, counter) -> {(kernel, WGs): [KiB per dispatch]}
+    for d in sorted(glob.glob(os.path.join(folder, "*_*_SIZE"))):
+        wl, ctr = os.path.basename(d).rsplit("_", 2)[0], "_".join(os.path.basename(d).rsplit("_", 2)[1:])
+        g = data.setdefault((wl, ctr), {})
+        for r in _rocprof_rows(d, "counter_collection"):
+            if r["Counter_Name"] == ctr:
+                g.setdefault(_kernel_key(r), []).append(float(r["Counter_Value"]))
+    copy_kib = 256 * 1024.0
+    scale = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        g = data[("copyref", ctr)]
+        big = max((k for k in g if k[0].startswith("__amd_rocclr_copyBuffer")), key=lambda k: k[1])
+        scale[ctr] = copy_kib / statistics.median(g[big])
+    print(f"calibration (256 MiB device copy): FETCH_SIZE x{scale['FETCH_SIZE']:.3f}, "
+          f"WRITE_SIZE x{scale['WRITE_SIZE']:.3f}")
+    print(f"{'workload':<16}{'kernel':<44}{'WGs':>6}{'calls':>7}{'FETCH KiB':>12}{'WRITE KiB':>11}{'MB/launch':>11}")
+    per_launch = {}
+    for wl in sorted({w for w, _ in data}):
+        f, wr = data.get((wl, "FETCH_SIZE"), {}), data.get((wl, "WRITE_SIZE"), {})
+        for key in sorted(set(f) | set(wr)):
+            fk = statistics.mean(f[key]) if key in f else float("nan")
+            wk = statistics.mean(wr[key]) if key in wr else float("nan")
+            mb = (fk * scale["FETCH_SIZE"] + wk * scale["WRITE_SIZE"]) * 1024 / 1e6
+            per_launch[(wl, key)] = (fk, wk, len(f.get(key, [])))
+            print(f"{wl:<16}{key[0]:<44}{key[1]:>6}{len(f.get(key, [])):>7}{fk:>12.1f}{wk:>11.1f}{mb:>11.3f}")
+
+    def hbm_bytes(wl, key):
+        fk, wk, _ = per_launch[(wl, key)]
+        return (fk * scale["FETCH_SIZE"] + wk * scale["WRITE_SIZE"]) * 1024
+
+    def write(kernel, workload, wl, key):
+        out = {"kernel_sources_sha256_16": run_hash, "hbm_bytes_per_launch": hbm_bytes(wl, key),
+               "fetch_bytes_per_launch": per_launch[(wl, key)][0] * scale["FETCH_SIZE"] * 1024,
+               "write_bytes_per_launch": per_launch[(wl, key)][1] * scale["WRITE_SIZE"] * 1024,
+               "dispatches": per_launch[(wl, key)][2], "kernel": key[0], "workgroups": key[1],
+               "fetch_scale": scale["FETCH_SIZE"], "write_scale": scale["WRITE_SIZE"]}
+        with open(os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.json"), "w") as fh:
+            json.dump(out, fh, indent=1)
+            fh.write("\n")
+
+    loops = [k for (wl, k) in per_launch if wl == "headline" and k[0].startswith("loop_kernel") and k[1] == 1]
+    if loops:
+        write("loop", "product", "headline", loops[0])
+    gathers = sorted((k for (wl, k) in per_launch if wl == "stress" and k[0].startswith("gather_gemv_kernel")),
+                     key=lambda k: per_launch[("stress", k)][0])
+    if len(gathers) == 2:  # the 64 x 256 shape reads fewer bytes per launch than 64 x 887
+        write("gather_gemv", "stress64x256", "stress", gathers[0])
+        write("gather_gemv", "stress64x887", "stress", gathers[1])
+    line = json.load(open(bench_json)) if bench_json else None
+    keys = {"headline": ("product_answer", "product"), "structured": ("structured_B64", "structured"),
+            "unstructured": ("unstructured_B64", "unstructured"), "large": ("large_B256", "large"),
+            "charset_tools": ("charset_tools_B64", "charset_tools"), "charset_hex": ("charset_hex_B64", "charset_hex")}
+    print()
+    print("decode kernels (loop_kernel, root heads) per answer:")
+    print(f"{'workload':<16}{'launches':>9}{'us/answer':>11}{'unique MB':>11}{'fills MB':>10}{'writes MB':>11}"
+          f"{'fills/unique':>14}{'U/t TB/s':>10}{'fills/t TB/s':>14}")
+    for wl, (jk, cid) in keys.items():
+        ks = [k for (w, k) in per_launch if w == wl and k[0].split("<")[0] in DECODE_KERNELS]
+        if not ks:
+            continue
+        loop_calls = sum(per_launch[(wl, k)][2] for k in ks if k[0].startswith("loop_kernel"))
+        heads = sum(per_launch[(wl, k)][2] for k in ks if not k[0].startswith("loop_kernel"))
+        c = CONFIGS.get(cid) or CHAR_CONFIGS[cid]
+        answers = loop_calls / c.k if heads else loop_calls
+        fill = sum(per_launch[(wl, k)][0] * per_launch[(wl, k)][2] for k in ks) * scale["FETCH_SIZE"] * 1024 / answers
+        wr = sum(per_launch[(wl, k)][1] * per_launch[(wl, k)][2] for k in ks) * scale["WRITE_SIZE"] * 1024 / answers
+        us = ub = None
+        if line and jk in line.get("also", {}):
+            a = line["also"][jk]
+            us, ub = a["us_per_answer"], a.get("unique_bytes_per_answer")
+        lp = c.k * 2 if heads else 1
+        row = f"{wl:<16}{lp:>9}"
+        row += f"{us:>11.1f}" if us else f"{'':>11}"
+        row += f"{ub / 1e6:>11.2f}" if ub else f"{'':>11}"
+        row += f"{fill / 1e6:>10.2f}{wr / 1e6:>11.2f}"
+        row += f"{fill / ub:>14.2f}" if ub else f"{'':>14}"
+        row += f"{ub / (us * 1e-6) / 1e12:>10.3f}{fill / (us * 1e-6) / 1e12:>14.3f}" if (us and ub) else ""
+        print(row)
+
+
 class CharWorkload(Workload):
     """A character-level catalog (byte strings, byte-string vocabulary), one
     string per answer, rows from the product-scale embedding."""
@@ -585,9 +723,22 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=2.0)
     ap.add_argument("--only", default="",
-                    help="comma list of headline,b64,large,charset,stress,dense,cpu,copyref "
-                         "(default: all but copyref)")
+                    help="comma list of headline,b64,large,charset,stress,dense,cpu,copyref, or single "
+                         "workloads structured,unstructured,charset_tools,charset_hex (default: all but copyref)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print per-kernel durations from a rocprofv3 --kernel-trace run's CSV in DIR; no GPU")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="summarize rocprofv3 FETCH_SIZE / WRITE_SIZE runs under DIR (one subfolder "
+                         "<workload>_<counter> per run) and write profiles/*_pmc.json; no GPU")
+    ap.add_argument("--bench-json", metavar="FILE", help="with --summarize-counters: a bench line of the "
+                    "same kernels, for times and unique bytes per answer")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.bench_json)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): this build runs on one GPU. "
               "Sequences shard across GPUs with no per-step exchange; run one process per GPU.", file=sys.stderr)
@@ -639,13 +790,13 @@ def main():
         also["product_per_step_kernel_graph"] = graph_mode(w, args.steps, args.warmup)
         also["product_launch_floor"] = launch_floor(w)
         _log(f"roofline {line['roofline']}; per-step graph {also['product_per_step_kernel_graph']}")
-    if want("b64"):
-        for cid in ("structured", "unstructured"):
+    for cid in ("structured", "unstructured"):
+        if want("b64") or want(cid):
             also[f"{cid}_B64"] = workload_line(cid, max(10, args.steps // 2), args.warmup)
     if want("large"):
         also["large_B256"] = workload_line("large", max(5, args.steps // 5), 2, per_step_graph=False)
-    if want("charset"):
-        for cid in ("charset_tools", "charset_hex"):
+    for cid in ("charset_tools", "charset_hex"):
+        if want("charset") or want(cid):
             also[f"{cid}_B64"] = workload_line(cid, max(10, args.steps // 2), args.warmup)
     if want("dense"):
         also["dense_masked_product_B1"] = dense_step_us(w)
