@@ -936,7 +936,7 @@ tms_status tms_state_get_launch(const tms_state* st, int32_t* split, int32_t* gr
   if (!st) return fail(TMS_ERR_INVALID_ARG, "null state");
   const tms::StepGroup* g = step_group(st);
   if (split) *split = g ? g->split : st->split;
-  if (grid) *grid = g ? st->B * g->split + g->rt * g->mtiles : st->B * st->split;
+  if (grid) *grid = g ? st->B * g->split + tms::root_tile_grid(g->rt, g->mtiles) : st->B * st->split;
   return TMS_OK;
 }
 

@@ -147,6 +147,10 @@ hipError_t launch_snapshot(const DevState& st, int parity, hipStream_t s);
 // sequence); otherwise the step with the root grouped across sequences.
 hipError_t launch_step_sparse(const DevTrie& tr, const DevState& st, const StepIO& io, int dtype,
                               bool fast, int split, hipStream_t s, const StepGroup* grp = nullptr);
+// Workgroups of a grouped root launch with rt row tiles and mtiles member
+// tiles: rt padded to a multiple of 8, so that the member tiles of a row tile
+// share an XCD (root_tile in the kernels).
+inline int root_tile_grid(int rt, int mtiles) { return (rt + 7) / 8 * 8 * mtiles; }
 // LDS bytes of a root workgroup of the grouped step (nq = 16-byte chunks per row).
 size_t step_group_lds(int nq, int mt);
 // Root rows per root workgroup of the grouped step.

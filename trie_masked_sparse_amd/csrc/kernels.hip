@@ -579,6 +579,20 @@ __global__ __launch_bounds__(kBlock) void step_sparse_kernel(DevTrie tr, DevStat
   }
 }
 
+// Row tile x and member tile y of root workgroup r of a launch with rt row
+// tiles and mtiles member tiles.  Workgroups go to the eight XCDs in launch
+// order, round robin, and each XCD has its own L2; numbering the member tiles
+// of one row tile eight apart puts them on one XCD, whose L2 then fetches the
+// tile's rows once instead of once per member tile.  The row tiles are padded
+// to a multiple of 8 (false: a padding workgroup, which does nothing).
+__device__ __forceinline__ bool root_tile(int r, int rt, int mtiles, int& x, int& y) {
+  const int per = 8 * mtiles;
+  const int q = r / per, rem = r - q * per;
+  y = rem >> 3;
+  x = q * 8 + (rem & 7);
+  return x < rt;
+}
+
 // ---------------------------------------------------------------------------
 // Fused sparse step with the root grouped across sequences (section "The
 // batched engine": the rows one step needs are the union of the sequences'
@@ -586,7 +600,8 @@ __global__ __launch_bounds__(kBlock) void step_sparse_kernel(DevTrie tr, DevStat
 // sequences need the same rows in the same step).  One launch, fixed grid:
 //   * B * split sequence workgroups: workgroup (s, w) serves sequence s as in
 //     step_sparse_kernel, unless s stands at the root ("member");
-//   * rt * mt root workgroups: workgroup (x, y) reads root rows x*4U ..
+//   * rt * mtiles root workgroups (rt padded to a multiple of 8, root_tile):
+//     workgroup (x, y) reads root rows x*4U ..
 //     x*4U+4U-1 once (U per wavefront) and dots them with the hidden vectors of
 //     members y*mt .. y*mt+mt-1 (ascending sequence order) staged in LDS, in
 //     the per-row order of the other kernels, so every logit and key is the
@@ -599,7 +614,7 @@ __global__ __launch_bounds__(kBlock) void step_sparse_kernel(DevTrie tr, DevStat
 // ---------------------------------------------------------------------------
 template <int DT, int NC, bool FAST>
 __global__ __launch_bounds__(kBlock) void step_grouped_kernel(DevTrie tr, DevState st, StepIO io, int split,
-                                                              int rt, int mt, int parity) {
+                                                              int rt, int mt, int mtiles, int parity) {
   constexpr int EL = DT == 0 ? 4 : 8;
   constexpr int U = rows_per_pass(NC);
   constexpr int MPW = 4;  // members staged per wavefront per round
@@ -675,8 +690,8 @@ __global__ __launch_bounds__(kBlock) void step_grouped_kernel(DevTrie tr, DevSta
   // root workgroup (x, y); [mt][nq] members' hidden vectors in LDS, then their ids
   extern __shared__ uint4 sh[];
   int* s_mem = reinterpret_cast<int*>(sh + (size_t)mt * nq);
-  const int r = (int)blockIdx.x - nseq_wg;
-  const int x = r % rt, y = r / rt;
+  int x, y;
+  if (!root_tile((int)blockIdx.x - nseq_wg, rt, mtiles, x, y)) return;
   const int m0 = y * mt;
   if (threadIdx.x < 16) s_best[threadIdx.x] = 0ull;
   // this wavefront's root edges and their tokens, requested before the member
@@ -1447,7 +1462,7 @@ __global__ __launch_bounds__(kLoopBlock) void loop_kernel(DevTrie tr, DevState s
 // and each member's legal edges go into key[s] with an atomic max.
 // ---------------------------------------------------------------------------
 template <int DT, int NC>
-__global__ __launch_bounds__(kBlock) void root_head_kernel(DevTrie tr, DevState st, LoopIO io, int mt) {
+__global__ __launch_bounds__(kBlock) void root_head_kernel(DevTrie tr, DevState st, LoopIO io, int mt, int rt, int mtiles) {
   constexpr int EL = DT == 0 ? 4 : 8;
   constexpr int U = rows_per_pass(NC);
   constexpr int MPW = 4;  // members staged per wavefront per round
@@ -1462,12 +1477,14 @@ __global__ __launch_bounds__(kBlock) void root_head_kernel(DevTrie tr, DevState 
   int* s_mem = reinterpret_cast<int*>(s_off + st.B);
   const bool rst = io.reset != 0;
   const bool later = (io.flags & kLoopLater) != 0;
+  int tx, ty;
+  if (!root_tile((int)blockIdx.x, rt, mtiles, tx, ty)) return;
   if (threadIdx.x < 16) s_best[threadIdx.x] = 0ull;
   // this wavefront's U root edges (the root is not a terminal: content edges
   // only); their rows are requested first, so that the member bookkeeping
   // below overlaps the gathers
   const int r1 = tr.begin[1];
-  const int e0 = tr.begin[0] + ((int)blockIdx.x * kWavesPerBlock + wv) * U;
+  const int e0 = tr.begin[0] + (tx * kWavesPerBlock + wv) * U;
   int rows[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) rows[u] = e0 + u < r1 ? tr.tok[e0 + u] : -1;
@@ -1498,7 +1515,7 @@ __global__ __launch_bounds__(kBlock) void root_head_kernel(DevTrie tr, DevState 
     for (int w = 0; w < kWavesPerBlock; ++w) n_mem += s_cnt[w];
     lds_barrier();
   }
-  const int m0 = (int)blockIdx.y * mt;
+  const int m0 = ty * mt;
   const int cnt = min(mt, n_mem - m0);
   if (cnt <= 0) return;  // the same for the whole workgroup
   // stage the members' vectors: every load of a round before its stores
@@ -1553,7 +1570,7 @@ __global__ __launch_bounds__(kBlock) void root_head_kernel(DevTrie tr, DevState 
   }
   lds_barrier();
   // this tile's best per member (0: none legal); the loop takes the max over tiles
-  if ((int)threadIdx.x < cnt) st.rkey[(int64_t)blockIdx.x * st.B + s_mem[m0 + threadIdx.x]] = s_best[threadIdx.x];
+  if ((int)threadIdx.x < cnt) st.rkey[(int64_t)tx * st.B + s_mem[m0 + threadIdx.x]] = s_best[threadIdx.x];
 }
 
 // ---------------------------------------------------------------------------
@@ -1792,7 +1809,7 @@ __global__ __launch_bounds__(kBlock) void dense_mfma_kernel(DevState st, StepIO 
 // summed in a fixed order ((w0 + w1) + (w2 + w3)), so results do not depend on
 // scheduling, and each member's best legal edge of the tile goes to rkey.
 template <int KS>
-__global__ __launch_bounds__(kBlock) void root_mfma_kernel(DevTrie tr, DevState st, LoopIO io) {
+__global__ __launch_bounds__(kBlock) void root_mfma_kernel(DevTrie tr, DevState st, LoopIO io, int rt, int mtiles) {
   extern __shared__ uint4 sh[];  // [16][nq] members' vectors, then int64 offsets[B], int members[B]
   __shared__ f32x4_t s_part[3][kWave];
   __shared__ int s_cnt[kWavesPerBlock];
@@ -1805,8 +1822,10 @@ __global__ __launch_bounds__(kBlock) void root_mfma_kernel(DevTrie tr, DevState 
   const bool later = (io.flags & kLoopLater) != 0;
   // operand A first: lane l holds row l % 16, elements 8 (l / 16) .. + 8 of each
   // 32-wide step of this wavefront's quarter
+  int tx, ty;
+  if (!root_tile((int)blockIdx.x, rt, mtiles, tx, ty)) return;
   const int r1 = tr.begin[1];
-  const int eb = tr.begin[0] + (int)blockIdx.x * 16;
+  const int eb = tr.begin[0] + tx * 16;
   const int my_e = min(eb + (lane & 15), r1 - 1);
   const uint4* arow = (const uint4*)io.emb + (int64_t)tr.tok[my_e] * nq + wv * (KS * 4) + (lane >> 4);
   u32x4_t a[KS];
@@ -1836,7 +1855,7 @@ __global__ __launch_bounds__(kBlock) void root_mfma_kernel(DevTrie tr, DevState 
     for (int w = 0; w < kWavesPerBlock; ++w) n_mem += s_cnt[w];
     lds_barrier();
   }
-  const int m0 = (int)blockIdx.y * 16;
+  const int m0 = ty * 16;
   const int cnt = min(16, n_mem - m0);
   if (cnt <= 0) return;  // the same for the whole workgroup
   // live counts of this lane's four (row, member) results (wavefront 0 uses them)
@@ -1890,7 +1909,7 @@ __global__ __launch_bounds__(kBlock) void root_mfma_kernel(DevTrie tr, DevState 
     const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(best >> 32), d);
     best = max(best, ((unsigned long long)hi << 32) | lo);
   }
-  if (lane < cnt) st.rkey[(int64_t)blockIdx.x * st.B + s_mem[m0 + lane]] = best;
+  if (lane < cnt) st.rkey[(int64_t)tx * st.B + s_mem[m0 + lane]] = best;
 }
 
 // The same contraction with the K loop outside (H a multiple of 128): each
@@ -2527,8 +2546,8 @@ struct StepLaunch {
     const size_t lds = step_group_lds(io.H / EL, grp->mt);
     auto* k = fast ? &step_grouped_kernel<DT, NC, true> : &step_grouped_kernel<DT, NC, false>;
     if (hipError_t e = allow_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess) return e;
-    const dim3 grid((unsigned)(st.B * grp->split + grp->rt * grp->mtiles));
-    hipLaunchKernelGGL(k, grid, block, lds, s, tr, st, io, grp->split, grp->rt, grp->mt, grp->parity);
+    const dim3 grid((unsigned)(st.B * grp->split + root_tile_grid(grp->rt, grp->mtiles)));
+    hipLaunchKernelGGL(k, grid, block, lds, s, tr, st, io, grp->split, grp->rt, grp->mt, grp->mtiles, grp->parity);
     return hipGetLastError();
   }
 };
@@ -2645,8 +2664,8 @@ hipError_t launch_root_mfma(const DevTrie& tr, const DevState& st, const LoopIO&
   const size_t lds = sizeof(uint4) * (size_t)16 * nq + (sizeof(int64_t) + sizeof(int)) * (size_t)st.B;
   auto* k = &root_mfma_kernel<KS>;
   if (hipError_t e = allow_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess) return e;
-  const dim3 grid((unsigned)((root_edges + 15) / 16), (unsigned)((st.B + 15) / 16));
-  hipLaunchKernelGGL(k, grid, dim3(kBlock), lds, s, tr, st, io);
+  const int rt = (root_edges + 15) / 16, mtiles = (st.B + 15) / 16;
+  hipLaunchKernelGGL(k, dim3((unsigned)root_tile_grid(rt, mtiles)), dim3(kBlock), lds, s, tr, st, io, rt, mtiles);
   return hipGetLastError();
 }
 
@@ -2661,8 +2680,9 @@ struct RootLaunch {
     auto* k = &root_head_kernel<DT, NC>;
     if (hipError_t e = allow_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess) return e;
     const int rows_per_wg = kWavesPerBlock * rows_per_pass(NC);
-    const dim3 grid((unsigned)((root_edges + rows_per_wg - 1) / rows_per_wg), (unsigned)((st.B + mt - 1) / mt));
-    hipLaunchKernelGGL(k, grid, dim3(kBlock), lds, s, tr, st, io, mt);
+    const int rt = (root_edges + rows_per_wg - 1) / rows_per_wg, mtiles = (st.B + mt - 1) / mt;
+    hipLaunchKernelGGL(k, dim3((unsigned)root_tile_grid(rt, mtiles)), dim3(kBlock), lds, s, tr, st, io, mt, rt,
+                       mtiles);
     return hipGetLastError();
   }
 };
