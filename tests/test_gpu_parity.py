@@ -527,6 +527,27 @@ def test_gather_gemv_rows():
     assert o[4, 3] == o[4, 30]
 
 
+@pytest.mark.parametrize("grid,unroll", [(0, 2), (1024, 2), (7, 8), (4096, 4), (3, 1)])
+def test_read_reference_reads_every_byte_once(grid, unroll):
+    """The streaming-read reference kernel behind the bandwidth comparisons:
+    the XOR of its 1024 output words is the XOR of every 32-bit word of the
+    bytes asked for (each read exactly once, none past them), for byte counts
+    that leave ragged passes and a tail, and a prefix of a larger buffer."""
+    rng = np.random.Generator(np.random.PCG64(90 + grid + unroll))
+    data = rng.integers(-2**31, 2**31, size=(3 << 20) + 12, dtype=np.int64).astype(np.int32)
+    src = torch.from_numpy(data).cuda()
+    out = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    for nbytes in (16, 4096 + 16, (1 << 20) + 48, (3 << 20) * 4 - 32, data.nbytes):
+        out.zero_()
+        tms.read_reference(src, out, grid, unroll, nbytes)
+        torch.cuda.synchronize()
+        want = np.bitwise_xor.reduce(data[:nbytes // 4])
+        got = np.bitwise_xor.reduce(out.cpu().numpy())
+        assert got == want, (grid, unroll, nbytes)
+    with pytest.raises(ValueError):
+        tms.read_reference(src, out, grid, unroll, data.nbytes + 16)
+
+
 def test_gather_gemv_stress_shape_sampled():
     """The bandwidth stress shape (64 sequences x 256 distinct rows), sampled."""
     cid = "product"
