@@ -74,17 +74,19 @@ def run_k_pointers(state: tms.State, hid_dev: torch.Tensor, check: bool = True):
     return tokens.cpu().numpy(), ln.cpu().numpy(), ent.cpu().numpy()
 
 
-def run_step_loop(state: tms.State, hid_dev: torch.Tensor, dense: bool = False, full=None, check: bool = True):
-    """T host-driven steps; returns tokens [B][T] and winner logits [B][T]."""
+def run_step_loop(state: tms.State, hid_dev: torch.Tensor, dense: bool = False, full=None, check: bool = True,
+                  logits: bool = True):
+    """T host-driven steps; returns tokens [B][T] and winner logits [B][T]
+    (NaN throughout when logits=False: the steps are asked for tokens only)."""
     T, B = hid_dev.shape[0], hid_dev.shape[1]
     toks = torch.empty((T, B), dtype=torch.int32, device="cuda")
-    lg = torch.empty((T, B), dtype=torch.float32, device="cuda")
+    lg = torch.full((T, B), float("nan"), dtype=torch.float32, device="cuda")
     for t in range(T):
         if dense:
             tms.decode_step_dense_masked(state, hid_dev[t], toks[t], lg[t], None if full is None else full[t],
                                          check=check)
         else:
-            tms.decode_step_sparse(state, hid_dev[t], toks[t], lg[t], check=check)
+            tms.decode_step_sparse(state, hid_dev[t], toks[t], lg[t] if logits else None, check=check)
     torch.cuda.synchronize()
     return toks.cpu().numpy().T.copy(), lg.cpu().numpy().T.copy()
 

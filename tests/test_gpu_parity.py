@@ -398,6 +398,66 @@ def test_teacher_forced_structured():
     _forced_walk(catalog("structured"), c.vocab, c.sep, c.stop, c.k, 16, tms.PATH_AUTO, 5)
 
 
+@pytest.mark.parametrize("cid", ["product", "product_deep", "structured", "unstructured"])
+def test_steps_without_logits_match_steps_with_logits(cid):
+    """Host-driven steps asked for tokens only take the steps a node record
+    decides (a single edge; a leaf terminal's sep or stop) without the head:
+    tokens and the exported state after every step identical to steps that
+    return logits, and the oracle's tokens (fast store, global store, and the
+    root grouped in the step launch on the unstructured catalog)."""
+    c, otr, T, hid = config_case(cid)
+    trie = tms.Trie(catalog(cid), c.vocab, c.sep, c.stop)
+    st = tms.State(trie, c.batch, c.k, dev_embedding(cid))
+    hd = to_dev(hid)
+    keys = ("node", "depth", "done", "status", "finished", "n_emitted", "entries", "live")
+    tok_l, lg = run_step_loop(st, hd)
+    x_l = st.export(live=True)
+    st.reset()
+    tok_n, lg_n = run_step_loop(st, hd, logits=False)
+    x_n = st.export(live=True)
+    assert np.array_equal(tok_l, tok_n)
+    assert np.isnan(lg_n).all()
+    for key in keys:
+        assert np.array_equal(x_l[key], x_n[key]), key
+    compare(tok_n, ref_decode(otr, c.k, embedding(cid), hid), c.hidden, None, where=f"{cid} tokens only")
+    st.close()
+    trie.close()
+
+
+def test_steps_without_logits_empty_and_spent_nodes():
+    """The headless steps' statuses: a single edge whose live count is zero is
+    an empty legal set (EMPTY_MASK), the same as the head reports; and every
+    tiny catalog (prefix pairs, leaf terminals, k = K) stepped with and
+    without logits gives the same tokens and state."""
+    V, H = 16, 64
+    rng = np.random.Generator(np.random.PCG64(77))
+    emb = rng.standard_normal((V, H), dtype=np.float32) * np.float32(0.2)
+    cases = [([[1, 2, 3]], 1), ([[1], [1, 2], [1, 2, 3], [4]], 4), ([[3, 3], [3], [3, 3, 3]], 3),
+             ([[5, 6], [5], [7], [5, 6, 7]], 2)] + [(random_catalog(300 + i, 10, 4, 12), 1 + i % 4) for i in range(10)]
+    keys = ("node", "depth", "done", "status", "finished", "n_emitted", "entries", "live")
+    for i, (cat, k) in enumerate(cases):
+        k = min(k, len(cat))
+        trie = tms.Trie(cat, V, V - 2, V - 1, path=tms.PATH_FAST if i % 2 else tms.PATH_GLOBAL)
+        T = k * (trie.info["max_depth"] + 1)
+        hid = rng.standard_normal((T, 3, H), dtype=np.float32)
+        st = tms.State(trie, 3, k, to_dev(emb))
+        hd = to_dev(hid)
+        out = []
+        for logits in (True, False):
+            st.reset()
+            if i == 0:  # the edge after token 1 (a single-edge node) has no live pointer for sequence 1
+                tms.debug_set_live(st.h, 1, int(trie.csr()["begin"][1]), 0)
+            tok, _ = run_step_loop(st, hd, check=False, logits=logits)
+            out.append((tok, st.export(live=True)))
+        assert np.array_equal(out[0][0], out[1][0]), i
+        for key in keys:
+            assert np.array_equal(out[0][1][key], out[1][1][key]), (i, key)
+        if i == 0:
+            assert list(out[1][1]["status"]) == [0, tms.ERR_EMPTY_MASK, 0]
+        st.close()
+        trie.close()
+
+
 # ---------------------------------------------------------------------------
 # Fail loudly
 # ---------------------------------------------------------------------------

@@ -240,6 +240,20 @@ __device__ __forceinline__ bool edge_ok_bits(int child, int live, const Seq& q) 
   return ((child >= 0) & (live > 0)) | ((child == kChildSep) & q.sep_ok) | ((child == kChildStop) & q.stop_ok);
 }
 
+// The edge a step takes whatever the logits, when the node record decides it
+// (sections "Masked sampling inside the sampler" and "The sparse output
+// layer": the argmax over a single legal token is that token): a node with
+// one edge holds a content edge (terminals carry two control edges), legal iff
+// its live count is positive; a terminal with two edges has no content edge,
+// and of its control edges sep or stop is legal by the exactly-k rule (edges
+// in ascending token order).  -2: nothing is legal; -3: the head decides.
+__device__ __forceinline__ int forced_edge(const DevTrie& tr, const int32_t* live, const Seq& q) {
+  const int f = q.b1 - q.b0;
+  if (f == 1) return ((cint_p)live)[q.b0] > 0 ? q.b0 : -2;
+  if (f == 2 && (q.sep_ok || q.stop_ok)) return q.b0 + (q.sep_ok == (tr.sep < tr.stop) ? 0 : 1);
+  return -3;
+}
+
 __device__ __forceinline__ void write_step_out(const StepIO& io, int s, int tok, float logit) {
   if (io.out_tok) io.out_tok[s] = tok;
   if (io.out_logit) io.out_logit[s] = tok >= 0 ? logit : NAN;
@@ -540,10 +554,18 @@ __global__ __launch_bounds__(kBlock) void step_sparse_kernel(DevTrie tr, DevStat
     if (w == 0 && threadIdx.x == 0) write_step_out(io, s, -1, NAN);
     return;
   }
+  const int32_t* live = st.live + (int64_t)s * tr.live_stride;
+  // no logit asked for: a step the node record decides takes no head
+  if (io.out_logit == nullptr) {
+    const int fe = forced_edge(tr, live, q);
+    if (fe != -3) {
+      if (w == 0 && threadIdx.x < kWave) advance(tr, st, &io, s, q, fe, NAN, lane);
+      return;
+    }
+  }
   const int nq = io.H / EL;
   uint4 hq[NC];
   load_hidden<NC>((const uint4*)io.hidden + (int64_t)s * nq, nq, hq, lane);
-  const int32_t* live = st.live + (int64_t)s * tr.live_stride;
   Cand unused;
   const TrieView tv{tr.erec, tr.cent, tr.run, tr.run_edge, tr.run_tok, tr.run_land};
   const unsigned long long best = scan_node<DT, NC, FAST ? kMetaScalar : kMetaVector, kLiveScalar, false>(
@@ -651,8 +673,19 @@ __global__ __launch_bounds__(kBlock) void step_grouped_kernel(DevTrie tr, DevSta
       }
       return;
     }
-    if constexpr (!FAST) load_hidden<NC>((const uint4*)io.hidden + (int64_t)s * nq, nq, hq, lane);
     const int32_t* live = st.live + (int64_t)s * tr.live_stride;
+    // no logit asked for: a step the node record decides takes no head
+    if (io.out_logit == nullptr) {
+      const int fe = forced_edge(tr, live, q);
+      if (fe != -3) {
+        if (w == 0 && threadIdx.x < kWave) {
+          const int next = advance(tr, st, &io, s, q, fe, NAN, lane);
+          if (lane == 0) snap_out[s] = next;
+        }
+        return;
+      }
+    }
+    if constexpr (!FAST) load_hidden<NC>((const uint4*)io.hidden + (int64_t)s * nq, nq, hq, lane);
     Cand unused;
     const TrieView tv{tr.erec, tr.cent, tr.run, tr.run_edge, tr.run_tok, tr.run_land};
     const unsigned long long best = scan_node<DT, NC, FAST ? kMetaScalar : kMetaVector, kLiveScalar, false>(
