@@ -185,7 +185,12 @@ tms_status tms_state_free(tms_state* st);
  * its node, logit = sum_i hidden[s][i]*emb[v][i] in fp32 for each legal v,
  * argmax with ties to the lower token id, advance.  Outputs: tok dev int32 [B]
  * (the emitted token, -1 if s was inactive or failed), logit dev fp32 [B] or
- * NULL (the winner's logit, NaN when nothing was emitted).
+ * NULL (the winner's logit, NaN when nothing was emitted).  With logit NULL, a
+ * step whose legal set the node alone decides (a node with one edge; a leaf
+ * terminal, where sep or stop is the one legal token) takes that token
+ * without computing logits (sections "Masked sampling inside the sampler"
+ * and "The sparse output layer": the argmax over one legal token is that
+ * token); tokens and state are the same either way.
  * One fused kernel; fixed grid per state, so it can be graph-captured. */
 tms_status tms_decode_step_sparse(tms_state* st, const void* hidden, int32_t* tok, float* logit,
                                   void* stream);
