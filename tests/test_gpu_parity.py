@@ -458,6 +458,84 @@ def test_steps_without_logits_empty_and_spent_nodes():
         trie.close()
 
 
+def _loop_forms(st, hd, check=True):
+    """(name, tokens, len, entries, status) of decode_k_pointers in every
+    loop form on a reset state."""
+    out = []
+    for name, mode in (("resident", tms.LOOP_RESIDENT), ("solo", tms.LOOP_RESIDENT_SOLO),
+                       ("grouped", tms.LOOP_RESIDENT_GROUPED), ("graph", tms.LOOP_GRAPH),
+                       ("stream", tms.LOOP_STREAM)):
+        tms.state_set_loop(st, mode)
+        st.reset()
+        tok, ln, ent = run_k_pointers(st, hd, check=check)
+        out.append((name, tok, ln, ent, st.status().copy()))
+    tms.state_set_loop(st, tms.LOOP_RESIDENT)
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_large_batch_every_loop_form(dtype):
+    """700 sequences: far more workgroups than compute units in every form,
+    175 member tiles of 4 at the grouped root head (its vector form at
+    H = 128) and 44 tiles of 16 in the grouped step, root row tiles padded to
+    a multiple of 8; every loop form, and host-driven steps with and without
+    logits, against the oracle."""
+    rng = np.random.Generator(np.random.PCG64(700 + len(dtype)))
+    V, H, k, B = 3000, 128, 2, 700
+    cat = random_catalog(4242, 600, 6, V - 2, min_len=2)
+    otr = oracle.Trie(cat, V, V - 2, V - 1)
+    b = otr.csr()["begin"]
+    assert b[1] - b[0] >= 64
+    T = k * (otr.max_depth + 1)
+    emb = _rand_table(rng, V, H, dtype)
+    hid = _rand_hidden(rng, T, B, H, dtype)
+    ref = ref_decode(otr, k, emb, hid)
+    assert (ref["status"] == 0).all()
+    trie = tms.Trie(cat, V, V - 2, V - 1)
+    st = tms.State(trie, B, k, to_dev(emb))
+    hd = to_dev(hid)
+    for name, tok, ln, ent, status in _loop_forms(st, hd):
+        compare(tok, ref, H, None, ln, ent, where=f"B={B} {dtype} {name}")
+        assert (status == 0).all(), name
+    st.reset()
+    tok_h, lg_h = run_step_loop(st, hd)
+    compare(tok_h, ref, H, lg_h, where=f"B={B} {dtype} steps")
+    st.reset()
+    tok_n, _ = run_step_loop(st, hd, logits=False)
+    assert np.array_equal(tok_n, tok_h)
+    st.close()
+    trie.close()
+
+
+def test_short_budget_refused_in_every_form():
+    """decode_k_pointers needs T >= k * (max_depth + 1) steps (enough for
+    every answer to stop): every loop form refuses one step less on the host
+    (INVALID_ARG, nothing enqueued), and the state then decodes the full
+    budget to the oracle's answer."""
+    rng = np.random.Generator(np.random.PCG64(31))
+    V, H, k, B = 400, 96, 3, 24
+    cat = random_catalog(31, 120, 7, V - 2, min_len=1)
+    otr = oracle.Trie(cat, V, V - 2, V - 1)
+    emb = _rand_table(rng, V, H, "fp32")
+    T = k * (otr.max_depth + 1)
+    hid = _rand_hidden(rng, T, B, H, "fp32")
+    ref = ref_decode(otr, k, emb, hid)
+    trie = tms.Trie(cat, V, V - 2, V - 1)
+    st = tms.State(trie, B, k, to_dev(emb))
+    hd = to_dev(hid)
+    for mode in (tms.LOOP_RESIDENT, tms.LOOP_RESIDENT_SOLO, tms.LOOP_RESIDENT_GROUPED, tms.LOOP_GRAPH,
+                 tms.LOOP_STREAM):
+        tms.state_set_loop(st, mode)
+        st.reset()
+        with pytest.raises(tms.TmsError) as ei:
+            run_k_pointers(st, hd[:T - 1])
+        assert ei.value.code == tms.ERR_INVALID_ARG
+        tok, ln, ent = run_k_pointers(st, hd)
+        compare(tok, ref, H, None, ln, ent, where=f"after a refused call, loop form {mode}")
+    st.close()
+    trie.close()
+
+
 # ---------------------------------------------------------------------------
 # Fail loudly
 # ---------------------------------------------------------------------------
