@@ -32,7 +32,8 @@
  *     caller.  The library never frees caller memory.
  *   - stream is a hipStream_t (NULL = the legacy default stream).  Decode
  *     calls only enqueue work on it and return; they allocate nothing (the
- *     GRAPH loop form instantiates its graph on its first call).
+ *     GRAPH loop form instantiates its graph on its first call for a step
+ *     count, and waits for the device when it is called with new buffers).
  *   - Device-detected errors (EMPTY_MASK, NOT_WALKABLE, NOT_DONE) are recorded
  *     per sequence and are sticky: that sequence stops, the others continue.
  *     tms_state_sync_status() synchronises the stream and reports them.
@@ -291,8 +292,11 @@ tms_status tms_state_set_split(tms_state* st, int32_t split);
  *   resident loop until each sequence is back at the root (the last phase
  *   runs to the end): 2k launches from a reset state, 2(k+1) otherwise;
  * RESIDENT: GROUPED when B >= 8 and the root has at least 64 edges, else SOLO;
- * GRAPH: a hipGraph of T step kernels (as tms_decode_step_sparse), built on
- *   the first call for a given set of pointers and replayed afterwards;
+ * GRAPH: a hipGraph of T step kernels (as tms_decode_step_sparse), built and
+ *   instantiated on the first call for a given T and replayed afterwards; a
+ *   call with other buffers and the same T updates the instantiated graph's
+ *   kernel arguments in place (after waiting for the device to drain, so
+ *   that no queued replay reads them) instead of instantiating it again;
  * STREAM: the same T step kernels launched directly on the stream.
  * Also read from the TMS_LOOP environment variable (0..4) at create. */
 typedef enum {

@@ -507,6 +507,38 @@ def test_large_batch_every_loop_form(dtype):
     trie.close()
 
 
+def test_graph_loop_alternating_buffers():
+    """The GRAPH loop form called with two sets of buffers in turn, with no
+    synchronisation between the calls (the instantiated graph takes each
+    call's pointers in place), then with a longer step budget (the graph is
+    rebuilt): every answer against the oracle."""
+    rng = np.random.Generator(np.random.PCG64(57))
+    V, H, k, B = 500, 64, 2, 12
+    cat = random_catalog(57, 90, 6, V - 2, min_len=1)
+    otr = oracle.Trie(cat, V, V - 2, V - 1)
+    emb = _rand_table(rng, V, H, "fp32")
+    trie = tms.Trie(cat, V, V - 2, V - 1)
+    st = tms.State(trie, B, k, to_dev(emb))
+    tms.state_set_loop(st, tms.LOOP_GRAPH)
+    T0 = k * (otr.max_depth + 1)
+    for T in (T0, T0 + 3):
+        hids = [_rand_hidden(rng, T, B, H, "fp32") for _ in range(2)]
+        refs = [ref_decode(otr, k, emb, h) for h in hids]
+        devs = [to_dev(h) for h in hids]
+        outs = [(torch.full((B, T), -7, dtype=torch.int32, device="cuda"), torch.zeros(B, dtype=torch.int32, device="cuda"),
+                 torch.zeros((B, k), dtype=torch.int32, device="cuda")) for _ in range(6)]
+        for i, (tok, ln, ent) in enumerate(outs):  # A, B, A, B, ...: no host wait between calls
+            st.reset()
+            tms.decode_k_pointers(st, devs[i % 2], tok, ln, ent, check=False)
+        torch.cuda.synchronize()
+        assert (st.status() == 0).all()
+        for i, (tok, ln, ent) in enumerate(outs):
+            compare(tok.cpu().numpy(), refs[i % 2], H, None, ln.cpu().numpy(), ent.cpu().numpy(),
+                    where=f"graph call {i} T={T}")
+    st.close()
+    trie.close()
+
+
 def test_short_budget_refused_in_every_form():
     """decode_k_pointers needs T >= k * (max_depth + 1) steps (enough for
     every answer to stop): every loop form refuses one step less on the host

@@ -791,7 +791,6 @@ tms_status tms_decode_k_pointers(tms_state* st, const void* hidden_seq, int32_t 
   const bool same = st->gexec && st->g_hidden == hidden_seq && st->g_T == T && st->g_tokens == tokens &&
                     st->g_len == len && st->g_entries == entries;
   if (!same) {
-    destroy_graph(st);
     TMS_HIP(hipStreamBeginCapture(st->capture, hipStreamCaptureModeRelaxed), "begin capture");
     const hipError_t le = enqueue(st->capture, 0);
     hipGraph_t g = nullptr;
@@ -801,8 +800,27 @@ tms_status tms_decode_k_pointers(tms_state* st, const void* hidden_seq, int32_t 
       return hip_fail(le, "capture launch");
     }
     TMS_HIP(ce, "end capture");
-    st->graph = g;
-    TMS_HIP(hipGraphInstantiate(&st->gexec, g, nullptr, nullptr, 0), "graph instantiate");
+    // the same step count keeps the graph's shape: only kernel arguments
+    // (buffer pointers) differ, so the instantiated graph takes them in place;
+    // otherwise (first call, another T, an update refused) it is rebuilt
+    bool updated = false;
+    if (st->gexec && st->g_T == T) {
+      // a launch of the old arguments may still be queued: let it finish first
+      TMS_HIP(hipDeviceSynchronize(), "graph update wait");
+      hipGraphExecUpdateResult ur = hipGraphExecUpdateError;
+      hipGraphNode_t bad = nullptr;
+      updated = hipGraphExecUpdate(st->gexec, g, &bad, &ur) == hipSuccess && ur == hipGraphExecUpdateSuccess;
+      if (!updated) (void)hipGetLastError();  // clear the refused update's error
+    }
+    if (updated) {
+      (void)hipGraphDestroy(st->graph);
+      st->graph = g;
+    } else {
+      if (st->gexec) TMS_HIP(hipDeviceSynchronize(), "graph rebuild wait");
+      destroy_graph(st);
+      st->graph = g;
+      TMS_HIP(hipGraphInstantiate(&st->gexec, g, nullptr, nullptr, 0), "graph instantiate");
+    }
     st->g_hidden = hidden_seq;
     st->g_T = T;
     st->g_tokens = tokens;
