@@ -1843,13 +1843,13 @@ __global__ __launch_bounds__(kBlock) void dense_mfma_kernel(DevState st, StepIO 
 // scheduling, and each member's best legal edge of the tile goes to rkey.
 template <int KS>
 __global__ __launch_bounds__(kBlock) void root_mfma_kernel(DevTrie tr, DevState st, LoopIO io, int rt, int mtiles) {
-  extern __shared__ uint4 sh[];  // [16][nq] members' vectors, then int64 offsets[B], int members[B]
+  extern __shared__ uint4 sh[];  // int64 offsets[B], then int members[B]
   __shared__ f32x4_t s_part[3][kWave];
   __shared__ int s_cnt[kWavesPerBlock];
   const int lane = __lane_id();
   const int wv = wave_id();
   const int nq = io.H / 8;
-  int64_t* s_off = reinterpret_cast<int64_t*>(sh + (size_t)16 * nq);
+  int64_t* s_off = reinterpret_cast<int64_t*>(sh);
   int* s_mem = reinterpret_cast<int*>(s_off + st.B);
   const bool rst = io.reset != 0;
   const bool later = (io.flags & kLoopLater) != 0;
@@ -1902,30 +1902,21 @@ __global__ __launch_bounds__(kBlock) void root_mfma_kernel(DevTrie tr, DevState 
       lv[i] = e < r1 ? live[e] : 0;
     }
   }
-  // stage the members' vectors (missing members as zeros): rounds of 16
-  // loads per thread, all issued before their stores
-  constexpr int NQ = KS * 16;  // uint4 per vector (H / 8)
-  constexpr int SL = 16;
-  const uint4* hid = (const uint4*)io.hidden_seq;
+  // operand B straight from the members' vectors: wavefront wv needs only its
+  // quarter of each, so there is nothing to share through LDS (lane l: member
+  // l % 16, elements 8 (l / 16) .. + 8 of each 32-wide step; missing members
+  // re-read member m0's vector and are zeroed)
+  const bool have = col < cnt;
+  const uint4* bsrc = (const uint4*)io.hidden_seq + s_off[m0 + (have ? col : 0)] + wv * (KS * 4) + (lane >> 4);
+  u32x4_t bq[KS];
 #pragma unroll
-  for (int base = 0; base < 16 * NQ; base += SL * kBlock) {
-    uint4 v[SL];
-#pragma unroll
-    for (int u = 0; u < SL; ++u) {
-      const int i = base + u * kBlock + (int)threadIdx.x;
-      const int j = i / NQ;
-      v[u] = j < cnt ? hid[s_off[m0 + j] + (i - j * NQ)] : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < SL; ++u) sh[base + u * kBlock + threadIdx.x] = v[u];
-  }
-  lds_barrier();
+  for (int j = 0; j < KS; ++j) bq[j] = *reinterpret_cast<const u32x4_t*>(bsrc + j * 4);
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const uint4* brow = sh + col * nq + wv * (KS * 4) + (lane >> 4);
 #pragma unroll
   for (int j = 0; j < KS; ++j) {
-    const bf16x8_t b = __builtin_bit_cast(bf16x8_t, brow[j * 4]);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[j]), b, acc, 0, 0, 0);
+    const u32x4_t bj = have ? bq[j] : u32x4_t{0u, 0u, 0u, 0u};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[j]), __builtin_bit_cast(bf16x8_t, bj),
+                                                  acc, 0, 0, 0);
   }
   if (wv > 0) s_part[wv - 1][lane] = acc;
   lds_barrier();
@@ -2693,8 +2684,7 @@ int root_head_tiles(int dtype, int H, int root_edges) {
 
 template <int KS>
 hipError_t launch_root_mfma(const DevTrie& tr, const DevState& st, const LoopIO& io, int root_edges, hipStream_t s) {
-  const int nq = io.H / 8;
-  const size_t lds = sizeof(uint4) * (size_t)16 * nq + (sizeof(int64_t) + sizeof(int)) * (size_t)st.B;
+  const size_t lds = (sizeof(int64_t) + sizeof(int)) * (size_t)st.B;
   auto* k = &root_mfma_kernel<KS>;
   if (hipError_t e = allow_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess) return e;
   const int rt = (root_edges + 15) / 16, mtiles = (st.B + 15) / 16;
