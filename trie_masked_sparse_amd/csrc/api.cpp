@@ -142,7 +142,8 @@ hipError_t enqueue_resident(const tms_trie* trie, const DevState& dev, LoopIO io
     io.reset = p == 0 ? reset : kResetNone;
     io.flags = (p > 0 ? kLoopLater : 0) | (p + 1 < phases ? kLoopExitAtRoot : 0) | kLoopRootKey;
     io.root_tiles = root_head_tiles(dtype, io.H, root_edges);
-    if (hipError_t e = launch_root_head(trie->dev, dev, io, dtype, root_edges, s); e != hipSuccess) return e;
+    if (hipError_t e = launch_root_head(trie->dev, dev, io, dtype, h.begin[0], root_edges, s); e != hipSuccess)
+      return e;
     if (hipError_t e = launch_loop(trie->dev, dev, io, dtype, mode, s); e != hipSuccess) return e;
   }
   return hipSuccess;

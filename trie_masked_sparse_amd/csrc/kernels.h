@@ -163,9 +163,9 @@ int step_group_rows(int dtype, int H);
 enum { kLoopTrieLds = 0, kLoopFastGlobal = 1, kLoopVectorLds = 2, kLoopVectorGlobal = 3, kLoopTrieMask = 4 };
 // The root step of every sequence at the root (or of all, with io.reset), for
 // the step each is at: per row tile and sequence the best key into st.rkey
-// (root_edges = edges of the root).
-hipError_t launch_root_head(const DevTrie& tr, const DevState& st, const LoopIO& io, int dtype, int root_edges,
-                            hipStream_t s);
+// (the root's edges are [root_b0, root_b0 + root_edges)).
+hipError_t launch_root_head(const DevTrie& tr, const DevState& st, const LoopIO& io, int dtype, int root_b0,
+                            int root_edges, hipStream_t s);
 // Row tiles the grouped root head uses for this hidden size (io.root_tiles).
 int root_head_tiles(int dtype, int H, int root_edges);
 hipError_t launch_loop(const DevTrie& tr, const DevState& st, const LoopIO& io, int dtype, int mode,

@@ -1842,7 +1842,8 @@ __global__ __launch_bounds__(kBlock) void dense_mfma_kernel(DevState st, StepIO 
 // summed in a fixed order ((w0 + w1) + (w2 + w3)), so results do not depend on
 // scheduling, and each member's best legal edge of the tile goes to rkey.
 template <int KS>
-__global__ __launch_bounds__(kBlock) void root_mfma_kernel(DevTrie tr, DevState st, LoopIO io, int rt, int mtiles) {
+__global__ __launch_bounds__(kBlock) void root_mfma_kernel(DevTrie tr, DevState st, LoopIO io, int rb0, int rb1,
+                                                           int rt, int mtiles) {
   extern __shared__ uint4 sh[];  // int64 offsets[B], then int members[B]
   __shared__ f32x4_t s_part[3][kWave];
   __shared__ int s_cnt[kWavesPerBlock];
@@ -1853,28 +1854,35 @@ __global__ __launch_bounds__(kBlock) void root_mfma_kernel(DevTrie tr, DevState 
   int* s_mem = reinterpret_cast<int*>(s_off + st.B);
   const bool rst = io.reset != 0;
   const bool later = (io.flags & kLoopLater) != 0;
-  // operand A first: lane l holds row l % 16, elements 8 (l / 16) .. + 8 of each
-  // 32-wide step of this wavefront's quarter
   int tx, ty;
   if (!root_tile((int)blockIdx.x, rt, mtiles, tx, ty)) return;
-  const int r1 = tr.begin[1];
-  const int eb = tr.begin[0] + tx * 16;
+  const int r1 = rb1;  // the root's edges are [rb0, rb1)
+  const int eb = rb0 + tx * 16;
+  // the states of the member list's first sequences and this lane's root
+  // token, requested together (loads complete in order: the states are not
+  // to wait behind the rows)
+  int f_t = 0, f_stat = 0, f_fin = 1, f_nd = 0, f_dp = 0;
+  if ((int)threadIdx.x < st.B) {
+    f_t = later ? st.tstep[threadIdx.x] : 0;
+    f_stat = st.status[threadIdx.x];
+    f_fin = st.finished[threadIdx.x];
+    f_nd = st.node[threadIdx.x];
+    f_dp = st.depth[threadIdx.x];
+  }
   const int my_e = min(eb + (lane & 15), r1 - 1);
-  const uint4* arow = (const uint4*)io.emb + (int64_t)tr.tok[my_e] * nq + wv * (KS * 4) + (lane >> 4);
+  const int my_tok = tr.tok[my_e];
+  // operand A: lane l holds row l % 16, elements 8 (l / 16) .. + 8 of each
+  // 32-wide step of this wavefront's quarter
+  const uint4* arow = (const uint4*)io.emb + (int64_t)my_tok * nq + wv * (KS * 4) + (lane >> 4);
   u32x4_t a[KS];
 #pragma unroll
   for (int j = 0; j < KS; ++j) a[j] = *reinterpret_cast<const u32x4_t*>(arow + j * 4);
-  // members in ascending sequence order (every workgroup builds the same list)
+  // members in ascending sequence order (every workgroup builds the same
+  // list); the first chunk from the states requested above, outside the loop,
+  // so that no path to it waits for the rows
   int n_mem = 0;
-  for (int s0 = 0; s0 < st.B; s0 += kBlock) {
-    const int s = s0 + (int)threadIdx.x;
-    bool ok = false;
-    int t = 0;
-    if (s < st.B) {
-      t = later ? st.tstep[s] : 0;
-      const int stat = st.status[s], fin = st.finished[s], nd = st.node[s], dp = st.depth[s];
-      ok = t < io.T && (rst || (stat == kSeqOk && fin == 0 && nd == 0 && dp == 0));
-    }
+  auto chunk = [&](int s, int t, int stat, int fin, int nd, int dp) {
+    const bool ok = s < st.B && t < io.T && (rst || (stat == kSeqOk && fin == 0 && nd == 0 && dp == 0));
     const unsigned long long m = __ballot(ok);
     if (lane == 0) s_cnt[wv] = __popcll(m);
     lds_barrier();
@@ -1887,6 +1895,19 @@ __global__ __launch_bounds__(kBlock) void root_mfma_kernel(DevTrie tr, DevState 
     }
     for (int w = 0; w < kWavesPerBlock; ++w) n_mem += s_cnt[w];
     lds_barrier();
+  };
+  chunk((int)threadIdx.x, f_t, f_stat, f_fin, f_nd, f_dp);
+  for (int s0 = kBlock; s0 < st.B; s0 += kBlock) {
+    const int s = s0 + (int)threadIdx.x;
+    int t = 0, stat = 0, fin = 1, nd = 0, dp = 0;
+    if (s < st.B) {
+      t = later ? st.tstep[s] : 0;
+      stat = st.status[s];
+      fin = st.finished[s];
+      nd = st.node[s];
+      dp = st.depth[s];
+    }
+    chunk(s, t, stat, fin, nd, dp);
   }
   const int m0 = ty * 16;
   const int cnt = min(16, n_mem - m0);
@@ -2683,12 +2704,14 @@ int root_head_tiles(int dtype, int H, int root_edges) {
 }
 
 template <int KS>
-hipError_t launch_root_mfma(const DevTrie& tr, const DevState& st, const LoopIO& io, int root_edges, hipStream_t s) {
+hipError_t launch_root_mfma(const DevTrie& tr, const DevState& st, const LoopIO& io, int root_b0, int root_edges,
+                            hipStream_t s) {
   const size_t lds = (sizeof(int64_t) + sizeof(int)) * (size_t)st.B;
   auto* k = &root_mfma_kernel<KS>;
   if (hipError_t e = allow_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess) return e;
   const int rt = (root_edges + 15) / 16, mtiles = (st.B + 15) / 16;
-  hipLaunchKernelGGL(k, dim3((unsigned)root_tile_grid(rt, mtiles)), dim3(kBlock), lds, s, tr, st, io, rt, mtiles);
+  hipLaunchKernelGGL(k, dim3((unsigned)root_tile_grid(rt, mtiles)), dim3(kBlock), lds, s, tr, st, io, root_b0,
+                     root_b0 + root_edges, rt, mtiles);
   return hipGetLastError();
 }
 
@@ -2710,11 +2733,12 @@ struct RootLaunch {
   }
 };
 
-hipError_t launch_root_head(const DevTrie& tr, const DevState& st, const LoopIO& io, int dtype, int root_edges,
-                            hipStream_t s) {
+hipError_t launch_root_head(const DevTrie& tr, const DevState& st, const LoopIO& io, int dtype, int root_b0,
+                            int root_edges, hipStream_t s) {
   if (root_edges <= 0) return hipSuccess;
   if (root_uses_mfma(dtype, io.H))
-    return io.H == 2048 ? launch_root_mfma<16>(tr, st, io, root_edges, s) : launch_root_mfma<32>(tr, st, io, root_edges, s);
+    return io.H == 2048 ? launch_root_mfma<16>(tr, st, io, root_b0, root_edges, s)
+                        : launch_root_mfma<32>(tr, st, io, root_b0, root_edges, s);
   return dispatch<RootLaunch>(dtype, chunks_for(dtype, io.H), tr, st, io, root_edges, s);
 }
 
