@@ -173,6 +173,17 @@ __device__ __forceinline__ void finish_rows(int nq, const int (&rows)[U], const 
   }
 }
 
+// After a pass's dot products every row load of the pass has been consumed.
+// Saying so with an explicit wait (which then waits for nothing) keeps the
+// compiler's wait analysis from carrying loads of a branch it cannot prove
+// consumed (row u issued, its dot product skipped: the same rows[u] < 0 test
+// guards both) around the scan loops, where it otherwise waits for every
+// older load, the hidden vector and the previous row included, before
+// reusing a row's registers.
+// (the builtin, not inline asm: the compiler's wait analysis reads the
+// builtin's counts; 0x0F70 = vmcnt 0, expcnt and lgkmcnt unconstrained)
+__device__ __forceinline__ void rows_consumed() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <int DT, int NC, int U, bool NT = false>
 __device__ __forceinline__ void dot_rows(const uint4* __restrict__ emb, int nq, const int (&rows)[U],
                                          const uint4 (&hq)[NC], float (&out)[U], int lane) {
@@ -463,6 +474,7 @@ __device__ __forceinline__ unsigned long long scan_node(const DevTrie& tr, const
       issue_rows<NC, U>(emb, nq, rows, raw, lane);
       float l[U];
       finish_rows<DT, NC, U>(nq, rows, raw, hq, l, lane);
+      rows_consumed();
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (rows[u] < 0) continue;
@@ -517,6 +529,7 @@ __device__ __forceinline__ unsigned long long scan_node(const DevTrie& tr, const
         }
         float l[U];
         dot_rows<DT, NC, U>(emb, nq, rows, hq, l, lane);
+        rows_consumed();
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           if (rows[u] < 0) continue;
@@ -924,6 +937,7 @@ __device__ __forceinline__ unsigned long long scan_lanes(const Seq& q, const Nod
     issue_rows<NC, U>(emb, nq, rows, raw, lane);
     float l[U];
     finish_rows<DT, NC, U>(nq, rows, raw, hq, l, lane);
+    rows_consumed();
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (rows[u] < 0) continue;
