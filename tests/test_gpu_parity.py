@@ -424,6 +424,52 @@ def test_steps_without_logits_match_steps_with_logits(cid):
     trie.close()
 
 
+@pytest.mark.parametrize("split", [3, 8])
+def test_steps_without_logits_many_workgroups_per_sequence(split):
+    """Headless steps when each sequence has several workgroups and the grid
+    (512 sequences x split) is larger than the chip holds at once, so that
+    some workgroups of a sequence start after others have finished: every
+    workgroup must decide from the same state.  Tokens-only steps equal steps
+    with logits, in the plain and the root-grouped step, and the GRAPH loop
+    (tokens only) equals the resident loop and the oracle."""
+    rng = np.random.Generator(np.random.PCG64(900 + split))
+    V, H, k, B = 4000, 64, 2, 512
+    cat = random_catalog(901, 400, 12, V - 2, min_len=6)  # long single-edge chains below the root
+    otr = oracle.Trie(cat, V, V - 2, V - 1)
+    T = k * (otr.max_depth + 1)
+    emb = _rand_table(rng, V, H, "fp32")
+    hid = _rand_hidden(rng, T, B, H, "fp32")
+    ref = ref_decode(otr, k, emb, hid)
+    trie = tms.Trie(cat, V, V - 2, V - 1)
+    st = tms.State(trie, B, k, to_dev(emb))
+    tms.state_set_split(st, split)
+    hd = to_dev(hid)
+    keys = ("node", "depth", "done", "status", "finished", "n_emitted", "entries", "live")
+    for mode in (tms.STEP_GROUP_OFF, tms.STEP_GROUP_ROOT):
+        tms.state_set_step_grouping(st, mode)
+        st.reset()
+        tok_l, lg = run_step_loop(st, hd)
+        x_l = st.export(live=True)
+        st.reset()
+        tok_n, _ = run_step_loop(st, hd, logits=False)
+        x_n = st.export(live=True)
+        assert np.array_equal(tok_l, tok_n), mode
+        for key in keys:
+            assert np.array_equal(x_l[key], x_n[key]), (mode, key)
+        compare(tok_n, ref, H, None, where=f"split {split} grouping {mode} tokens only")
+        tms.state_set_loop(st, tms.LOOP_GRAPH)
+        st.reset()
+        tok_g, ln_g, ent_g = run_k_pointers(st, hd)
+        tms.state_set_loop(st, tms.LOOP_RESIDENT_SOLO)
+        st.reset()
+        tok_r, ln_r, ent_r = run_k_pointers(st, hd)
+        assert np.array_equal(tok_g, tok_r) and np.array_equal(ent_g, ent_r), mode
+        compare(tok_g, ref, H, None, ln_g, ent_g, where=f"split {split} grouping {mode} graph")
+        tms.state_set_loop(st, tms.LOOP_RESIDENT)
+    st.close()
+    trie.close()
+
+
 def test_steps_without_logits_empty_and_spent_nodes():
     """The headless steps' statuses: a single edge whose live count is zero is
     an empty legal set (EMPTY_MASK), the same as the head reports; and every

@@ -265,6 +265,24 @@ __device__ __forceinline__ int forced_edge(const DevTrie& tr, const int32_t* liv
   return -3;
 }
 
+// A headless step of a sequence served by split workgroups: the advance must
+// wait until every one of them has read the sequence's state (a workgroup
+// that started late would otherwise read the advanced state and decide
+// another step), so each counts itself into arrive[s] and the last one,
+// which clears the counter, advances.  True in that workgroup only.
+__device__ __forceinline__ bool forced_last(const DevState& st, int s, int split) {
+  if (split == 1) return true;
+  __shared__ int s_flast;
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(&st.arrive[s], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = prev == (uint32_t)(split - 1);
+    if (last) __hip_atomic_store(&st.arrive[s], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_flast = last;
+  }
+  __syncthreads();
+  return s_flast != 0;
+}
+
 __device__ __forceinline__ void write_step_out(const StepIO& io, int s, int tok, float logit) {
   if (io.out_tok) io.out_tok[s] = tok;
   if (io.out_logit) io.out_logit[s] = tok >= 0 ? logit : NAN;
@@ -572,7 +590,9 @@ __global__ __launch_bounds__(kBlock) void step_sparse_kernel(DevTrie tr, DevStat
   if (io.out_logit == nullptr) {
     const int fe = forced_edge(tr, live, q);
     if (fe != -3) {
-      if (w == 0 && threadIdx.x < kWave) advance(tr, st, &io, s, q, fe, NAN, lane);
+      if (forced_last(st, s, split)) {
+        if (threadIdx.x < kWave) advance(tr, st, &io, s, q, fe, NAN, lane);
+      }
       return;
     }
   }
@@ -691,7 +711,7 @@ __global__ __launch_bounds__(kBlock) void step_grouped_kernel(DevTrie tr, DevSta
     if (io.out_logit == nullptr) {
       const int fe = forced_edge(tr, live, q);
       if (fe != -3) {
-        if (w == 0 && threadIdx.x < kWave) {
+        if (forced_last(st, s, split) && threadIdx.x < kWave) {
           const int next = advance(tr, st, &io, s, q, fe, NAN, lane);
           if (lane == 0) snap_out[s] = next;
         }
