@@ -117,3 +117,57 @@ def test_read_reference_refuses_bytes_past_the_tensor():
     import torch
     with pytest.raises(ValueError):
         tms.read_reference(torch.zeros(16, dtype=torch.int32), torch.zeros(1024, dtype=torch.int32), nbytes=65)
+
+
+def _write_csv(path, header, rows):
+    import csv
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_profile_summaries_from_rocprof_csv(tmp_path, capsys, monkeypatch):
+    """bench.py's --summarize-trace and --summarize-counters on small
+    synthetic rocprofv3 outputs: durations per (kernel, workgroups), the copy
+    calibration of FETCH_SIZE / WRITE_SIZE, the traffic JSON it writes, and
+    the refusal of counters taken with other kernel sources."""
+    import json
+
+    import bench
+    trace_hdr = ["Kind", "Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X", "Grid_Size_Y",
+                 "Grid_Size_Z", "Workgroup_Size_X", "Workgroup_Size_Y", "Workgroup_Size_Z"]
+    loop = "void tms::(anonymous namespace)::loop_kernel<1, 4, 1, true, true, false>(tms::DevTrie, tms::DevState)"
+    _write_csv(str(tmp_path / "trace" / "run_kernel_trace.csv"), trace_hdr,
+               [["KERNEL_DISPATCH", loop, 1000, 15000, 512, 1, 1, 512, 1, 1],
+                ["KERNEL_DISPATCH", loop, 20000, 33000, 512, 1, 1, 512, 1, 1],
+                ["KERNEL_DISPATCH", loop, 40000, 52000, 512 * 64, 1, 1, 512, 1, 1]])
+    bench.summarize_trace(str(tmp_path / "trace"))
+    out = capsys.readouterr().out
+    lines = [l for l in out.splitlines() if l.startswith("loop_kernel")]
+    assert len(lines) == 2
+    one = [l for l in lines if l.split()[-4] == "1"][0].split()
+    assert one[-3] == "2" and float(one[-2]) == 13.5  # two dispatches of 14 and 13 us
+    # counters: a copy of 256 MiB reading FETCH 131072 KiB (scale 2) and writing 262144 KiB (scale 1)
+    ctr_hdr = ["Kernel_Name", "Grid_Size", "Workgroup_Size", "Counter_Name", "Counter_Value"]
+    pmc = tmp_path / "pmc"
+    for w, ctr, rows_ in (
+            ("copyref", "FETCH_SIZE", [["__amd_rocclr_copyBuffer", 256 * 512, 512, "FETCH_SIZE", 131072.0]]),
+            ("copyref", "WRITE_SIZE", [["__amd_rocclr_copyBuffer", 256 * 512, 512, "WRITE_SIZE", 262144.0]]),
+            ("headline", "FETCH_SIZE", [[loop, 512, 512, "FETCH_SIZE", 50.0], [loop, 512, 512, "FETCH_SIZE", 70.0]]),
+            ("headline", "WRITE_SIZE", [[loop, 512, 512, "WRITE_SIZE", 1.5], [loop, 512, 512, "WRITE_SIZE", 1.5]])):
+        _write_csv(str(pmc / f"{w}_{ctr}" / "run_counter_collection.csv"), ctr_hdr, rows_)
+    (pmc / "kernel_hash.txt").write_text("not-the-tree\n")
+    with pytest.raises(SystemExit):
+        bench.summarize_counters(str(pmc))
+    tree = bench._kernel_hash()
+    (pmc / "kernel_hash.txt").write_text(tree + "\n")
+    monkeypatch.setattr(bench, "_kernel_hash", lambda: tree)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))  # the JSON goes to tmp_path/profiles
+    os.makedirs(tmp_path / "profiles")
+    bench.summarize_counters(str(pmc))
+    d = json.loads((tmp_path / "profiles" / "loop_product_pmc.json").read_text())
+    assert d["fetch_scale"] == 2.0 and d["write_scale"] == 1.0
+    assert d["hbm_bytes_per_launch"] == (60.0 * 2.0 + 1.5) * 1024
+    assert d["dispatches"] == 2 and d["workgroups"] == 1
