@@ -740,7 +740,7 @@ def main():
         summarize_counters(args.summarize_counters, args.bench_json)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): this build runs on one GPU. "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the library runs on one GPU. "
               "Sequences shard across GPUs with no per-step exchange; run one process per GPU.", file=sys.stderr)
         sys.exit(2)
     only = set(filter(None, args.only.split(",")))
