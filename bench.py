@@ -142,10 +142,12 @@ class Workload:
         legal = torch.empty((self.B, cap), dtype=torch.int32, device="cuda")
         nleg = torch.empty(self.B, dtype=torch.int32, device="cuda")
         tok = torch.empty(self.B, dtype=torch.int32, device="cuda")
+        loop_tokens = self.tokens.cpu().numpy().copy()  # the resident loop's last answer
         self.state.reset()
         row = self.c.hidden * self.esz
         g_head = u_head = g_all = 0
         head_steps = rows_head = 0
+        walk = np.full((self.B, self.T), -1, np.int32)
         for t in range(self.T):
             tms.legal_set(self.state, legal, nleg)
             lg, nl = legal.cpu().numpy(), nleg.cpu().numpy()
@@ -160,9 +162,16 @@ class Workload:
             u_head += len(u) + len(head)
             head_steps += len(head)
             tms.decode_step_sparse(self.state, self.hid[t], tok, check=False)
+            walk[:, t] = tok.cpu().numpy()
         torch.cuda.synchronize()
+        # the per-step walk and the resident loop decode the same answers (a
+        # cheap consistency check outside the timed region, reported, not
+        # asserted: a root step on the matrix cores may resolve a numerical
+        # tie differently)
+        same = bool(np.array_equal(walk, loop_tokens[:, :self.T]))
         return {"head_gathered": g_head * row, "head_unique": u_head * row, "sec8d_gathered": g_all * row,
-                "head_steps": head_steps, "head_rows": rows_head, "flops": 2 * self.c.hidden * rows_head}
+                "head_steps": head_steps, "head_rows": rows_head, "flops": 2 * self.c.hidden * rows_head,
+                "step_walk_matches_loop": same}
 
     def close(self):
         self.state.close()
@@ -214,7 +223,7 @@ def loop_rates(w: Workload, r: dict, prof: dict):
     return {"unique_GBps": prof["head_unique"] / t / 1e9, "gathered_GBps": prof["head_gathered"] / t / 1e9,
             "unique_bytes_per_answer": prof["head_unique"], "gathered_bytes_per_answer": prof["head_gathered"],
             "sec8d_gathered_bytes_per_answer": prof["sec8d_gathered"], "head_steps_per_answer": prof["head_steps"],
-            "flops_per_answer": prof["flops"]}
+            "flops_per_answer": prof["flops"], "step_walk_matches_loop": prof["step_walk_matches_loop"]}
 
 
 def graph_mode(w: Workload, steps: int, warmup: int):
