@@ -732,8 +732,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=2.0)
     ap.add_argument("--only", default="",
-                    help="comma list of headline,b64,large,charset,stress,dense,cpu,copyref, or single "
-                         "workloads structured,unstructured,charset_tools,charset_hex (default: all but copyref)")
+                    help="comma list of headline,b64,large,charset,stress,dense,cpu, or single workloads "
+                         "structured,unstructured,charset_tools,charset_hex; copyref (the counter calibration) and "
+                         "dense_large (the dense step at B=256, H=4096) run only when named (default: all others)")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="print per-kernel durations from a rocprofv3 --kernel-trace run's CSV in DIR; no GPU")
     ap.add_argument("--summarize-counters", metavar="DIR",
@@ -754,8 +755,8 @@ def main():
         sys.exit(2)
     only = set(filter(None, args.only.split(",")))
 
-    def want(x):
-        return (not only and x != "copyref") or x in only
+    def want(x):  # copyref and dense_large (profiling aids) only when asked for
+        return (not only and x not in ("copyref", "dense_large")) or x in only
 
     import torch
 
@@ -814,6 +815,11 @@ def main():
         also["mask_fed_head_structured_B64"] = mask_fed_head_us(wd)
         wd.close()
         _log(f"dense {also['dense_masked_product_B1']} / {also['dense_masked_structured_B64']}")
+    if want("dense_large"):
+        wl = Workload("large")
+        also["dense_masked_large_B256"] = dense_step_us(wl)
+        wl.close()
+        _log(f"dense large {also['dense_masked_large_B256']}")
     if want("stress"):
         sizes, ref_sizes = stress_sizes(w.c.vocab, w.c.hidden)
         ref = streaming_read_reference(w.emb, ref_sizes)
