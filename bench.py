@@ -130,10 +130,12 @@ class Workload:
         materialiser over host-driven steps.  Per step and sequence with legal
         set L: a head step (|L| >= 2) reads |L| rows and one hidden vector; a
         forced step (|L| = 1) reads nothing (its token is determined).
-        head_gathered: every sequence reads its own rows; head_unique: a row
-        needed by several sequences in the same step counted once (the union of
-        the legal sets, the least that must come from memory); sec8d_gathered:
-        every step counted, forced ones included."""
+        head_gathered: every sequence reads its own rows; head_node_grouped: the
+        sequences standing at the same node share its rows (what the node-grouped
+        step requests: the union of their legal sets, per node); head_unique: a
+        row needed by several sequences in the same step counted once (the union
+        of the legal sets, the least that must come from memory);
+        sec8d_gathered: every step counted, forced ones included."""
         import numpy as np
         import torch
 
@@ -145,7 +147,7 @@ class Workload:
         loop_tokens = self.tokens.cpu().numpy().copy()  # the resident loop's last answer
         self.state.reset()
         row = self.c.hidden * self.esz
-        g_head = u_head = g_all = 0
+        g_head = u_head = g_all = n_head = 0
         head_steps = rows_head = 0
         walk = np.full((self.B, self.T), -1, np.int32)
         for t in range(self.T):
@@ -154,9 +156,12 @@ class Workload:
             act = nl >= 0
             g_all += int(nl[act].sum()) + int(act.sum())
             head = np.nonzero(nl >= 2)[0]
-            u = set()
+            node = self.state.export()["node"]
+            u, by_node = set(), {}
             for b in head:
                 u.update(lg[b, :nl[b]].tolist())
+                by_node.setdefault(int(node[b]), set()).update(lg[b, :nl[b]].tolist())
+            n_head += sum(len(x) for x in by_node.values()) + len(head)
             g_head += int(nl[head].sum()) + len(head)
             rows_head += int(nl[head].sum())
             u_head += len(u) + len(head)
@@ -169,7 +174,8 @@ class Workload:
         # asserted: a root step on the matrix cores may resolve a numerical
         # tie differently)
         same = bool(np.array_equal(walk, loop_tokens[:, :self.T]))
-        return {"head_gathered": g_head * row, "head_unique": u_head * row, "sec8d_gathered": g_all * row,
+        return {"head_gathered": g_head * row, "head_node_grouped": n_head * row, "head_unique": u_head * row,
+                "sec8d_gathered": g_all * row,
                 "head_steps": head_steps, "head_rows": rows_head, "flops": 2 * self.c.hidden * rows_head,
                 "step_walk_matches_loop": same}
 
@@ -222,6 +228,7 @@ def loop_rates(w: Workload, r: dict, prof: dict):
     t = r["us_per_answer"] * 1e-6
     return {"unique_GBps": prof["head_unique"] / t / 1e9, "gathered_GBps": prof["head_gathered"] / t / 1e9,
             "unique_bytes_per_answer": prof["head_unique"], "gathered_bytes_per_answer": prof["head_gathered"],
+            "node_grouped_bytes_per_answer": prof["head_node_grouped"],
             "sec8d_gathered_bytes_per_answer": prof["sec8d_gathered"], "head_steps_per_answer": prof["head_steps"],
             "flops_per_answer": prof["flops"], "step_walk_matches_loop": prof["step_walk_matches_loop"]}
 
@@ -719,6 +726,12 @@ def workload_line(cid: str, steps: int, warmup: int, per_step_graph: bool = True
                   "trie": {k: w.info[k] for k in ("n_nodes", "n_edges", "cap", "max_depth")}})
     if per_step_graph:
         d["per_step_kernel_graph"] = graph_mode(w, max(5, steps // 5), 2)
+        if w.B > 1:
+            # the same graph with every shared node grouped (requests
+            # node_grouped_bytes_per_answer of rows instead of gathered)
+            tms.state_set_step_grouping(w.state, tms.STEP_GROUP_NODES)
+            d["per_step_kernel_graph_node_grouped"] = graph_mode(w, max(5, steps // 5), 2)
+            tms.state_set_step_grouping(w.state, tms.STEP_GROUP_AUTO)
     w.close()
     _log(f"{cid}: {d['steps_per_s']:.0f} steps/s, {d['us_per_answer']:.1f} us per answer, "
          f"unique {d['unique_GBps']:.0f} GB/s")

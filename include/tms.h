@@ -322,17 +322,27 @@ tms_status tms_state_set_loop(tms_state* st, int32_t mode);
 typedef enum { TMS_NOREPEAT_LIVE = 0, TMS_NOREPEAT_BITMASK = 1 } tms_norepeat;
 tms_status tms_state_set_norepeat(tms_state* st, int32_t kind);
 
-/* Root grouping of the fused step (tms_decode_step_sparse and the GRAPH and
+/* Node grouping of the fused step (tms_decode_step_sparse and the GRAPH and
  * STREAM loop forms; page "Constraint made cheaper than no constraint",
- * section "The batched engine": the rows a step needs are the union of the
- * sequences' legal sets).  ROOT: the sequences standing at the root in a
- * step are served together in the same launch: each root row is read once per
- * tile of up to 16 of them and dotted with each one's hidden vector, with the
- * same per-row arithmetic, so tokens, logits and state are bit-identical to
- * OFF (every sequence reads its own node's rows).  AUTO: ROOT when B >= 8 and
- * the root has at least 64 edges.  Always available for the hidden sizes the
- * library accepts (one member's vector, at most 16 KiB, fits the LDS). */
-typedef enum { TMS_STEP_GROUP_AUTO = 0, TMS_STEP_GROUP_OFF = 1, TMS_STEP_GROUP_ROOT = 2 } tms_step_group;
+ * sections "The sparse output layer" and "The batched engine": the rows a
+ * step needs are the union of the sequences' legal sets).  ROOT: the
+ * sequences standing at the root in a step are served together in the same
+ * launch: each root row is read once per tile of up to 16 of them and dotted
+ * with each one's hidden vector.  NODES: as ROOT, and the sequences that
+ * stand together at any other node are served by the workgroups of the
+ * lowest of them: each row legal for any of them is read once and dotted
+ * with each one's vector; a sequence alone at its node takes its own step.
+ * Both keep the per-row arithmetic, so tokens, logits and state are
+ * bit-identical to OFF (every sequence reads its own node's rows).  AUTO:
+ * ROOT when B >= 8 and the root has at least 64 edges.  Always available for
+ * the hidden sizes the library accepts (one member's vector, at most 16 KiB,
+ * fits the LDS). */
+typedef enum {
+  TMS_STEP_GROUP_AUTO = 0,
+  TMS_STEP_GROUP_OFF = 1,
+  TMS_STEP_GROUP_ROOT = 2,
+  TMS_STEP_GROUP_NODES = 3
+} tms_step_group;
 tms_status tms_state_set_step_grouping(tms_state* st, int32_t mode);
 
 /* Workgroups per sequence used by the fused step (per sequence off the root

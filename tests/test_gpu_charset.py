@@ -56,6 +56,18 @@ def test_charset_workload_parity(cid):
     st.reset()
     tok_h, lg_h = run_step_loop(st, hd)
     compare(tok_h, ref, c.hidden, lg_h, where=cid + "/step")
+    # every shared node grouped (wide nodes of hundreds of valid tokens, read
+    # once per step for the sequences standing there): bit for bit the same,
+    # host-driven and in the graph of step kernels
+    tms.state_set_step_grouping(st, tms.STEP_GROUP_NODES)
+    st.reset()
+    tok_g, lg_g = run_step_loop(st, hd)
+    assert np.array_equal(tok_g, tok_h) and np.array_equal(lg_g, lg_h, equal_nan=True)
+    tms.state_set_loop(st, tms.LOOP_GRAPH)
+    st.reset()
+    tok_gg, ln_gg, ent_gg = run_k_pointers(st, hd)
+    assert np.array_equal(tok_gg, tok_h) and np.array_equal(ent_gg, ent)
+    tms.state_set_loop(st, tms.LOOP_RESIDENT)
     # every answer is a catalog string, spelled by its tokens
     for b in range(c.batch):
         spelled = b"".join(vocab[t] for t in tok_h[b] if t >= 0 and t != c.stop)

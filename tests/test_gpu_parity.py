@@ -445,7 +445,7 @@ def test_steps_without_logits_many_workgroups_per_sequence(split):
     tms.state_set_split(st, split)
     hd = to_dev(hid)
     keys = ("node", "depth", "done", "status", "finished", "n_emitted", "entries", "live")
-    for mode in (tms.STEP_GROUP_OFF, tms.STEP_GROUP_ROOT):
+    for mode in (tms.STEP_GROUP_OFF, tms.STEP_GROUP_ROOT, tms.STEP_GROUP_NODES):
         tms.state_set_step_grouping(st, mode)
         st.reset()
         tok_l, lg = run_step_loop(st, hd)
@@ -1237,6 +1237,15 @@ def test_step_root_grouping_bit_identical(dtype, H, B):
     assert np.array_equal(t2, t0)
     for key in keys:
         assert np.array_equal(x2[key], x0[key]), key
+    # every shared node grouped, host-driven and in the graph
+    t3, l3, x3 = _step_answers(st, hd, tms.STEP_GROUP_NODES)
+    assert np.array_equal(t0, t3) and np.array_equal(l0, l3, equal_nan=True)
+    for key in keys:
+        assert np.array_equal(x0[key], x3[key]), key
+    t4, _, x4 = _step_answers(st, hd, tms.STEP_GROUP_NODES, loop=tms.LOOP_GRAPH)
+    assert np.array_equal(t4, t0)
+    for key in keys:
+        assert np.array_equal(x4[key], x0[key]), key
     compare(t1, ref_decode(otr, k, emb, hid), H, l1, where=f"grouped step {dtype} H={H} B={B}")
     split, grid = tms.state_get_launch(st)
     assert grid > B * split  # the root workgroups are part of the grid
@@ -1246,18 +1255,20 @@ def test_step_root_grouping_bit_identical(dtype, H, B):
 
 @pytest.mark.parametrize("cid", ["unstructured", "structured"])
 def test_step_root_grouping_workloads(cid):
-    """The batch-64 workloads through the grouped step (forced on for the
-    structured catalog, whose root has 8 edges): the per-sequence step's tokens
-    and logits bit for bit, and the oracle's tokens."""
+    """The batch-64 workloads through the grouped step, root only and at
+    every shared node (forced on for the structured catalog, whose root has 8
+    edges): the per-sequence step's tokens and logits bit for bit, and the
+    oracle's tokens."""
     c, otr, T, hid = config_case(cid)
     trie = tms.Trie(catalog(cid), c.vocab, c.sep, c.stop)
     st = tms.State(trie, c.batch, c.k, dev_embedding(cid))
     hd = to_dev(hid)
     t0, l0, x0 = _step_answers(st, hd, tms.STEP_GROUP_OFF)
-    t1, l1, x1 = _step_answers(st, hd, tms.STEP_GROUP_ROOT)
-    assert np.array_equal(t0, t1) and np.array_equal(l0, l1, equal_nan=True)
-    for key in ("node", "done", "status", "n_emitted", "entries", "live"):
-        assert np.array_equal(x0[key], x1[key]), key
+    for mode in (tms.STEP_GROUP_ROOT, tms.STEP_GROUP_NODES):
+        t1, l1, x1 = _step_answers(st, hd, mode)
+        assert np.array_equal(t0, t1) and np.array_equal(l0, l1, equal_nan=True), mode
+        for key in ("node", "done", "status", "n_emitted", "entries", "live"):
+            assert np.array_equal(x0[key], x1[key]), (mode, key)
     compare(t1, ref_decode(otr, c.k, embedding(cid), hid), c.hidden, l1, where=f"{cid}/grouped step")
     st.close()
     trie.close()
@@ -1288,6 +1299,78 @@ def test_step_root_grouping_empty_mask_isolated():
     keep = [i for i in range(B) if i != 5]
     compare(tok[keep], ref_decode(otr, k, emb, np.ascontiguousarray(hid[:, keep])), H, lg[keep],
             where="grouped step isolated")
+    st.close()
+    trie.close()
+
+
+def _two_prefix_catalog(seed, K, max_len, V, prefixes):
+    """Entries that all start with one of a few tokens, so that after the
+    first step whole blocks of sequences stand at the same node."""
+    rest = random_catalog(seed, K, max_len, V - 2 - len(prefixes), min_len=1)
+    return [[prefixes[i % len(prefixes)]] + [x + len(prefixes) for x in r] for i, r in enumerate(rest)]
+
+
+@pytest.mark.parametrize("split", [1, 3])
+def test_step_node_grouping_large_groups(split):
+    """Groups of more than 64 sequences at one node (150 sequences over a root
+    of two edges, so member blocks of 64 and a partial one), served by one and
+    by three workgroups: the per-sequence step's tokens, logits and state bit
+    for bit, host-driven and in the graph; tokens against the oracle."""
+    rng = np.random.Generator(np.random.PCG64(515 + split))
+    V, H, B, k = 3000, 128, 150, 2
+    cat = _two_prefix_catalog(516, 120, 5, V, [0, 1])
+    otr = oracle.Trie(cat, V, V - 2, V - 1)
+    assert otr.csr()["begin"][1] - otr.csr()["begin"][0] == 2
+    T = k * (otr.max_depth + 1)
+    emb = _rand_table(rng, V, H, "fp32")
+    hid = _rand_hidden(rng, T, B, H, "fp32")
+    trie = tms.Trie(cat, V, V - 2, V - 1)
+    st = tms.State(trie, B, k, to_dev(emb))
+    tms.state_set_split(st, split)
+    hd = to_dev(hid)
+    keys = ("node", "depth", "done", "status", "finished", "n_emitted", "entries", "live")
+    t0, l0, x0 = _step_answers(st, hd, tms.STEP_GROUP_OFF)
+    t1, l1, x1 = _step_answers(st, hd, tms.STEP_GROUP_NODES)
+    assert np.array_equal(t0, t1) and np.array_equal(l0, l1, equal_nan=True)
+    for key in keys:
+        assert np.array_equal(x0[key], x1[key]), key
+    t2, _, x2 = _step_answers(st, hd, tms.STEP_GROUP_NODES, loop=tms.LOOP_GRAPH)
+    assert np.array_equal(t2, t0)
+    for key in keys:
+        assert np.array_equal(x2[key], x0[key]), key
+    compare(t1, ref_decode(otr, k, emb, hid), H, l1, where=f"node groups > 64, split {split}")
+    st.close()
+    trie.close()
+
+
+def test_step_node_grouping_empty_mask_isolated():
+    """Every sequence at the root's only child after the first step; one of
+    them has every edge there emptied: under node grouping that sequence alone
+    gets EMPTY_MASK at its second step, the others decode as without it."""
+    rng = np.random.Generator(np.random.PCG64(77))
+    V, H, B, k = 1500, 256, 12, 2
+    cat = _two_prefix_catalog(4343, 200, 4, V, [0])
+    otr = oracle.Trie(cat, V, V - 2, V - 1)
+    csr = otr.csr()
+    assert csr["begin"][1] - csr["begin"][0] == 1
+    c1 = int(csr["child"][csr["begin"][0]])
+    T = k * (otr.max_depth + 1)
+    emb = _rand_table(rng, V, H, "fp32")
+    hid = _rand_hidden(rng, T, B, H, "fp32")
+    trie = tms.Trie(cat, V, V - 2, V - 1)
+    st = tms.State(trie, B, k, to_dev(emb))
+    tms.state_set_step_grouping(st, tms.STEP_GROUP_NODES)
+    st.reset()
+    st.export()
+    for e in range(int(csr["begin"][c1]), int(csr["begin"][c1 + 1])):
+        tms.debug_set_live(st, 5, e, 0)
+    tok, lg = run_step_loop(st, to_dev(hid), check=False)
+    status = st.status()
+    assert status[5] == tms.ERR_EMPTY_MASK and (np.delete(status, 5) == 0).all()
+    assert tok[5, 0] == cat[0][0] and (tok[5, 1:] == -1).all()
+    keep = [i for i in range(B) if i != 5]
+    compare(tok[keep], ref_decode(otr, k, emb, np.ascontiguousarray(hid[:, keep])), H, lg[keep],
+            where="node-grouped step isolated")
     st.close()
     trie.close()
 

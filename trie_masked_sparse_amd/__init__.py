@@ -49,7 +49,7 @@ EXPORTS = (
     "tms_decode_k_pointers_noalloc", "tms_read_reference", "tms_status_str", "tms_last_error",
 )
 NOREPEAT_LIVE, NOREPEAT_BITMASK = 0, 1
-STEP_GROUP_AUTO, STEP_GROUP_OFF, STEP_GROUP_ROOT = 0, 1, 2
+STEP_GROUP_AUTO, STEP_GROUP_OFF, STEP_GROUP_ROOT, STEP_GROUP_NODES = 0, 1, 2, 3
 NOALLOC_SCRATCH_BYTES = 32 << 20
 
 

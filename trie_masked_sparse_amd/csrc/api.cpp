@@ -86,9 +86,11 @@ void destroy_graph(tms_state* st) {
 
 // The root grouping of the fused step, when it applies to this state.
 tms::StepGroup* step_group(tms_state* st) {
-  const bool on = st->step_group_mode == TMS_STEP_GROUP_ROOT ? st->step_group_ok
-                  : st->step_group_mode == TMS_STEP_GROUP_OFF ? false
-                                                              : st->step_group_auto;
+  const int mode = st->step_group_mode;
+  const bool on = mode == TMS_STEP_GROUP_ROOT || mode == TMS_STEP_GROUP_NODES ? st->step_group_ok
+                  : mode == TMS_STEP_GROUP_OFF                               ? false
+                                                                             : st->step_group_auto;
+  st->grp.nodes = mode == TMS_STEP_GROUP_NODES ? 1 : 0;
   return on ? &st->grp : nullptr;
 }
 
@@ -925,10 +927,10 @@ tms_status tms_state_set_split(tms_state* st, int32_t split) {
 }
 
 tms_status tms_state_set_step_grouping(tms_state* st, int32_t mode) {
-  if (!st || mode < TMS_STEP_GROUP_AUTO || mode > TMS_STEP_GROUP_ROOT)
+  if (!st || mode < TMS_STEP_GROUP_AUTO || mode > TMS_STEP_GROUP_NODES)
     return fail(TMS_ERR_INVALID_ARG, "unknown step grouping mode");
-  if (mode == TMS_STEP_GROUP_ROOT && !st->step_group_ok)
-    return fail(TMS_ERR_INVALID_ARG, "root grouping does not fit this state (LDS for the members' vectors)");
+  if ((mode == TMS_STEP_GROUP_ROOT || mode == TMS_STEP_GROUP_NODES) && !st->step_group_ok)
+    return fail(TMS_ERR_INVALID_ARG, "step grouping does not fit this state (LDS for the members' vectors)");
   st->step_group_mode = mode;
   destroy_graph(st);
   return TMS_OK;

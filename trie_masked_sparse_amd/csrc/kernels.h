@@ -140,6 +140,7 @@ hipError_t launch_reset(const DevTrie& tr, const DevState& st, int kind, hipStre
 struct StepGroup {
   int split, rt, mt, mtiles;
   int parity;  // which half of DevState::snap holds the nodes at the start of this step
+  int nodes;   // also group the sequences that share any other node
 };
 // snap[parity] <- every sequence's node (-1 if finished or in error).
 hipError_t launch_snapshot(const DevState& st, int parity, hipStream_t s);
