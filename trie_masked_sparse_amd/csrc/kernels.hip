@@ -664,10 +664,12 @@ __device__ __forceinline__ bool root_tile(int r, int rt, int mtiles, int& x, int
 // (split 1) or in key[] with an arrival count on the leader, whose last
 // workgroup advances every member.
 // ---------------------------------------------------------------------------
+// mask0: with B <= 64, bit q set where sequence q is a member (the caller's
+// ballot over the snapshot), so the member list needs no second read of it.
 template <int DT, int NC>
 __device__ void node_group_step(const DevTrie& tr, const DevState& st, const StepIO& io, int node, int leader,
-                                int n_mem, int split, int w, const int32_t* snap_in, int32_t* snap_out, uint4* sh,
-                                int mt) {
+                                int n_mem, unsigned long long mask0, int split, int w, const int32_t* snap_in,
+                                int32_t* snap_out, uint4* sh, int mt) {
   constexpr int EL = DT == 0 ? 4 : 8;
   constexpr int U = rows_per_pass(NC);
   constexpr int MPW = 4;  // members staged per wavefront per round
@@ -694,7 +696,7 @@ __device__ void node_group_step(const DevTrie& tr, const DevState& st, const Ste
     int rank = 0;
     for (int c = 0; c < st.B; c += kWave) {
       const int q = c + lane;
-      const bool in = q < st.B && snap_in[q] == node;
+      const bool in = st.B <= kWave ? ((mask0 >> lane) & 1ull) != 0ull : q < st.B && snap_in[q] == node;
       const unsigned long long m = __ballot(in);
       const int r = rank + __popcll(m & ((1ull << lane) - 1ull)) - blk * kWave;
       if (in && r >= 0 && r < kWave) s_gm[r] = q;
@@ -723,6 +725,7 @@ __device__ void node_group_step(const DevTrie& tr, const DevState& st, const Ste
     // member j's control edges here: terminal, entry not spent, exactly-k rule
     Seq qj{node, 0, 0, rec.b0, rec.b1, false, false};
     if (mj >= 0) {
+      qj.depth = st.depth[mj];
       qj.done = st.done[mj];
       bool ctl = false;
       if (rec.ent >= 0)
@@ -799,7 +802,15 @@ __device__ void node_group_step(const DevTrie& tr, const DevState& st, const Ste
     }
     __syncthreads();  // this block's keys are complete
     if (split == 1) {
-      for (int j = wv; j < cnt; j += kWavesPerBlock) take(s_gm[j], s_gbest[j]);
+      // each member's record from its lane (read above, unchanged since)
+      for (int j = wv; j < cnt; j += kWavesPerBlock) {
+        const Seq q{node, __builtin_amdgcn_readlane(qj.depth, j), __builtin_amdgcn_readlane(qj.done, j), rec.b0, rec.b1,
+                    __builtin_amdgcn_readlane((int)qj.sep_ok, j) != 0, __builtin_amdgcn_readlane((int)qj.stop_ok, j) != 0};
+        const int m = __builtin_amdgcn_readlane(mj, j);
+        const unsigned long long key = s_gbest[j];
+        const int next = advance(tr, st, &io, m, q, key ? (int)key_id(key) : -2, key ? key_logit(key) : NAN, lane);
+        if (lane == 0) snap_out[m] = next;
+      }
     } else if (wv == 0 && lane < cnt && s_gbest[lane]) {
       __hip_atomic_fetch_max(&st.key[mj], s_gbest[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -876,9 +887,11 @@ __global__ __launch_bounds__(kBlock) void step_grouped_kernel(DevTrie tr, DevSta
     const int wq = w * kWavesPerBlock + wv;
     const int W = split * kWavesPerBlock;
     // the hidden vector first on the scalar-trie path (the edge records come
-    // through the scalar cache and do not queue behind it)
+    // through the scalar cache and do not queue behind it), unless steps
+    // without a head are possible: their advance would wait behind it
     uint4 hq[NC];
-    if constexpr (FAST) load_hidden<NC>((const uint4*)io.hidden + (int64_t)s * nq, nq, hq, lane);
+    const bool early = FAST && io.out_logit != nullptr;
+    if (early) load_hidden<NC>((const uint4*)io.hidden + (int64_t)s * nq, nq, hq, lane);
     const int node0 = ((cint_p)snap_in)[s];
     Seq q;
     const bool active = load_seq(tr, st, s, q);  // issued with the snapshot read
@@ -888,15 +901,18 @@ __global__ __launch_bounds__(kBlock) void step_grouped_kernel(DevTrie tr, DevSta
       // step of all of them.  Decided from the snapshot alone, before this
       // sequence's own state: the leader may already be advancing it
       int n_mem = 0, leader = s;
+      unsigned long long mask0 = 0ull;
       for (int c = 0; node0 > 0 && c < st.B; c += kWave) {
         const int q2 = c + lane;
         const unsigned long long m = __ballot(q2 < st.B && snap_in[q2] == node0);
         if (n_mem == 0 && m) leader = c + (int)__builtin_ctzll(m);
+        if (c == 0) mask0 = m;
         n_mem += __popcll(m);
       }
       if (n_mem > 1) {
         extern __shared__ uint4 sh_g[];
-        if (s == leader) node_group_step<DT, NC>(tr, st, io, node0, leader, n_mem, split, w, snap_in, snap_out, sh_g, mt);
+        if (s == leader)
+          node_group_step<DT, NC>(tr, st, io, node0, leader, n_mem, mask0, split, w, snap_in, snap_out, sh_g, mt);
         return;
       }
     }
@@ -919,7 +935,7 @@ __global__ __launch_bounds__(kBlock) void step_grouped_kernel(DevTrie tr, DevSta
         return;
       }
     }
-    if constexpr (!FAST) load_hidden<NC>((const uint4*)io.hidden + (int64_t)s * nq, nq, hq, lane);
+    if (!early) load_hidden<NC>((const uint4*)io.hidden + (int64_t)s * nq, nq, hq, lane);
     Cand unused;
     const TrieView tv{tr.erec, tr.cent, tr.run, tr.run_edge, tr.run_tok, tr.run_land};
     const unsigned long long best = scan_node<DT, NC, FAST ? kMetaScalar : kMetaVector, kLiveScalar, false>(
