@@ -1315,7 +1315,8 @@ def test_step_node_grouping_large_groups(split):
     """Groups of more than 64 sequences at one node (150 sequences over a root
     of two edges, so member blocks of 64 and a partial one), served by one and
     by three workgroups: the per-sequence step's tokens, logits and state bit
-    for bit, host-driven and in the graph; tokens against the oracle."""
+    for bit, host-driven, in the graph and in the stream of step launches;
+    tokens against the oracle."""
     rng = np.random.Generator(np.random.PCG64(515 + split))
     V, H, B, k = 3000, 128, 150, 2
     cat = _two_prefix_catalog(516, 120, 5, V, [0, 1])
@@ -1334,10 +1335,11 @@ def test_step_node_grouping_large_groups(split):
     assert np.array_equal(t0, t1) and np.array_equal(l0, l1, equal_nan=True)
     for key in keys:
         assert np.array_equal(x0[key], x1[key]), key
-    t2, _, x2 = _step_answers(st, hd, tms.STEP_GROUP_NODES, loop=tms.LOOP_GRAPH)
-    assert np.array_equal(t2, t0)
-    for key in keys:
-        assert np.array_equal(x2[key], x0[key]), key
+    for loop in (tms.LOOP_GRAPH, tms.LOOP_STREAM):
+        t2, _, x2 = _step_answers(st, hd, tms.STEP_GROUP_NODES, loop=loop)
+        assert np.array_equal(t2, t0), loop
+        for key in keys:
+            assert np.array_equal(x2[key], x0[key]), (loop, key)
     compare(t1, ref_decode(otr, k, emb, hid), H, l1, where=f"node groups > 64, split {split}")
     st.close()
     trie.close()
