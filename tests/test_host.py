@@ -33,6 +33,21 @@ def test_header_symbols_exported(L):
         assert hasattr(L, name), name
 
 
+def test_binding_constants_match_header():
+    """Every enumerator and the no-allocation limit that include/tms.h
+    defines has the same value in the Python binding (TMS_X -> tms.X)."""
+    hdr = open(os.path.join(os.path.dirname(tms.__file__), os.pardir, "include", "tms.h")).read()
+    seen = 0
+    for body in re.findall(r"typedef enum\s*\{(.*?)\}", hdr, re.S):
+        body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+        for name, value in re.findall(r"TMS_([A-Z0-9_]+)\s*=\s*(\d+)", body):
+            assert getattr(tms, name) == int(value), name
+            seen += 1
+    assert seen == 27  # status 11, dtype 2, path 3, loop 5, no-repeat 2, step grouping 4
+    m = re.search(r"#define TMS_NOALLOC_SCRATCH_BYTES \((\d+)ll << (\d+)\)", hdr)
+    assert tms.NOALLOC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
+
+
 def test_status_strings(L):
     for code in range(11):
         assert tms.status_str(code) not in ("", "unknown status")
