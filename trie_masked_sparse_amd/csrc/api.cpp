@@ -722,7 +722,7 @@ tms_status tms_decode_step_dense_masked(tms_state* st, const void* hidden, int32
   io.out_tok = tok;
   io.out_logit = logit;
   st->snap_valid = false;
-  TMS_HIP(tms::launch_dense_step(st->trie->dev, st->dev, io, st->dtype, full_logits, 1024, st->dense_mfma,
+  TMS_HIP(tms::launch_dense_step(st->trie->dev, st->dev, io, st->dtype, full_logits, 0, st->dense_mfma,
                                  static_cast<hipStream_t>(stream)),
           "dense step launch");
   return TMS_OK;

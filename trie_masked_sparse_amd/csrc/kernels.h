@@ -176,7 +176,8 @@ hipError_t launch_loop(const DevTrie& tr, const DevState& st, const LoopIO& io, 
 size_t loop_lds_bytes(const DevTrie& tr, const DevState& st, bool trie);
 // Dense step: bitmask, all-V head, masked argmax, advance.  With mfma and a
 // bf16 table, 2 <= B <= 256 and H % 32 == 0 the head runs on the matrix cores;
-// otherwise on the vector units with the sparse head's per-row arithmetic.
+// otherwise on the vector units with the sparse head's per-row arithmetic
+// (grid workgroups; 0: sized from V).
 hipError_t launch_dense_step(const DevTrie& tr, const DevState& st, const StepIO& io, int dtype,
                              float* full_logits, int grid, bool mfma, hipStream_t s);
 bool dense_uses_mfma(int dtype, int B, int H);
