@@ -33,7 +33,7 @@ void orc_dense_logits(const void*, int, int32_t, int32_t, const void*, double*);
 int orc_decode(const orc_trie*, int32_t, const void*, int, int32_t, int32_t, const void*, int32_t, int32_t,
                const int32_t*, int32_t*, int32_t*, int32_t*, int32_t*, double*, double*, double*, int32_t*);
 
-/* xorshift64* generator: the driver's own seeded draws */
+/* xorshift64* generator: this test program's own seeded draws */
 static uint64_t g_rng = 88172645463325252ull;
 static uint64_t rnd(void) {
   g_rng ^= g_rng >> 12;

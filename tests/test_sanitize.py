@@ -6,7 +6,7 @@ and run to completion: tests/sanitize/oracle_driver.c over the CPU oracle
 library's host-side catalog compiler (trie_masked_sparse_amd/csrc/
 trie_build.cpp).  They are built separately: the oracle and the library
 share no code.  Any out-of-bounds access, leak or undefined operation makes
-the driver exit non-zero with the sanitizer's report.
+the test program exit non-zero with the sanitizer's report.
 """
 import os
 import shutil
