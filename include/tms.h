@@ -334,7 +334,7 @@ tms_status tms_state_set_norepeat(tms_state* st, int32_t kind);
  * with each one's vector; a sequence alone at its node takes its own step.
  * Both keep the per-row arithmetic, so tokens, logits and state are
  * bit-identical to OFF (every sequence reads its own node's rows).  AUTO:
- * ROOT when B >= 8 and the root has at least 64 edges.  Always available for
+ * ROOT when B >= 8 and the root has at least 256 edges.  Always available for
  * the hidden sizes the library accepts (one member's vector, at most 16 KiB,
  * fits the LDS). */
 typedef enum {

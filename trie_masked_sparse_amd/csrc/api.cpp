@@ -91,6 +91,8 @@ tms::StepGroup* step_group(tms_state* st) {
                   : mode == TMS_STEP_GROUP_OFF                               ? false
                                                                              : st->step_group_auto;
   st->grp.nodes = mode == TMS_STEP_GROUP_NODES ? 1 : 0;
+  st->grp.mt = st->grp.nodes ? st->grp_mt_nodes : st->grp_mt_root;
+  st->grp.mtiles = (st->B + st->grp.mt - 1) / st->grp.mt;
   return on ? &st->grp : nullptr;
 }
 
@@ -558,11 +560,27 @@ tms_status tms_state_create(tms_trie* trie, int32_t B, int32_t k, const void* em
     const int rows = tms::step_group_rows(dtype, H);
     st->grp_split_default = default_split(B, cap_rest, rows);
     st->grp.split = st->grp_split_default;
-    st->grp.mt = mt;
-    st->grp.mtiles = (B + mt - 1) / mt;
     st->grp.rt = (root_edges + rows - 1) / rows;
+    // members per root tile: the fewest (shorter chains of member pairs per
+    // workgroup) that keep the root tiles within about five workgroups per
+    // compute unit; node groups (NODES) stage as many as fit.  Per-step graph,
+    // B = 64, 16 / 8 / 4 members: unstructured 7.25 / 7.00 / 6.47 us,
+    // charset_tools 6.36 / 5.95 / 5.91, charset_hex (160 row tiles) 10.79 /
+    // 10.00 / 10.97.
+    st->grp_mt_nodes = mt;
+    st->grp_mt_root = mt;
+    for (int m = 4; m < mt; m *= 2)
+      if (size_t(tms::root_tile_grid(st->grp.rt, (B + m - 1) / m)) <= 1280) {
+        st->grp_mt_root = m;
+        break;
+      }
+    st->grp.mt = st->grp_mt_root;
+    st->grp.mtiles = (B + st->grp.mt - 1) / st->grp.mt;
     st->step_group_ok = root_edges > 0 && tms::step_group_lds(nq, mt) <= 160 * 1024 - 1024;
-    st->step_group_auto = st->step_group_ok && B >= 8 && root_edges >= 64;
+    // automatic for wide roots: per-step graph at B = 64, per sequence / root
+    // grouped, unstructured (884 root edges) 19.3 / 6.6 us, charset_hex (2470)
+    // 12.8 / 10.0, charset_tools (191) 5.5 / 5.8
+    st->step_group_auto = st->step_group_ok && B >= 8 && root_edges >= 256;
   }
   if (const char* env = std::getenv("TMS_SPLIT")) {
     const int v = std::atoi(env);
