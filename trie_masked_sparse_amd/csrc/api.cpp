@@ -59,11 +59,17 @@ int elem_size(int dtype) { return dtype == TMS_F32 ? 4 : 2; }
 // a sequence gets more than one workgroup only when its widest node needs more
 // than two passes of its wavefronts' rows (4 wavefronts x rows_per_pass rows),
 // and never more than a chip-filling 4096 wavefronts over the batch.
-int default_split(int B, int cap, int rows_per_wg) {
-  const int target_waves = 4096;
-  const int by_waves = std::max(1, (target_waves + 4 * B - 1) / (4 * B));
-  const int by_cap = std::max(1, (cap + 2 * rows_per_wg - 1) / (2 * rows_per_wg));
-  return std::min(by_waves, by_cap);
+// Workgroups per sequence of the fused step: enough for one pass over the
+// widest node's rows, but only while the grid stays within one workgroup per
+// free compute unit (wgs_free): beyond that the extra workgroups share compute
+// units and their key exchange costs more than the passes they save.  Per-step
+// graph, old rule -> this one: large B = 256 (split 3 -> 1) 21.5 -> 9.3 us,
+// charset_tools B = 64 (11 -> 4) 5.6 -> 4.0, charset_hex root-grouped (9 -> 1)
+// 10.1 -> 5.6; structured and unstructured keep 1.
+int default_split(int B, int cap, int rows_per_wg, int wgs_free) {
+  const int by_cus = std::max(1, wgs_free / B);
+  const int by_cap = std::max(1, (cap + rows_per_wg - 1) / rows_per_wg);
+  return std::min(by_cus, by_cap);
 }
 
 // Gather-GEMV workgroups per sequence: 4096 wavefronts for short lists (one
@@ -486,6 +492,9 @@ tms_status tms_state_create(tms_trie* trie, int32_t B, int32_t k, const void* em
   int dev = -1;
   TMS_HIP(hipGetDevice(&dev), "hipGetDevice");
   if (dev != trie->device) return fail(TMS_ERR_INVALID_ARG, "trie was uploaded on another device");
+  int cus = 0;
+  TMS_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev), "compute unit count");
+  cus = std::max(cus, 1);
 
   tms_state* st = new tms_state();
   st->trie = trie;
@@ -546,7 +555,7 @@ tms_status tms_state_create(tms_trie* trie, int32_t B, int32_t k, const void* em
   d.spent = reinterpret_cast<uint32_t*>(base + o_spent);
   d.mask = reinterpret_cast<uint32_t*>(base + o_mask);
   d.snap = reinterpret_cast<int32_t*>(base + o_snap);
-  st->split_default = default_split(B, h.cap, tms::step_group_rows(dtype, H));
+  st->split_default = default_split(B, h.cap, tms::step_group_rows(dtype, H), cus);
   st->split = st->split_default;
   {
     // root grouping of the fused step: sequences off the root need only the
@@ -558,8 +567,6 @@ tms_status tms_state_create(tms_trie* trie, int32_t B, int32_t k, const void* em
     const int nq = H / (dtype == TMS_F32 ? 4 : 8);
     const int mt = std::max(1, std::min(16, int((128 * 1024 - 64) / (16 * size_t(nq)))));
     const int rows = tms::step_group_rows(dtype, H);
-    st->grp_split_default = default_split(B, cap_rest, rows);
-    st->grp.split = st->grp_split_default;
     st->grp.rt = (root_edges + rows - 1) / rows;
     // members per root tile: the fewest (shorter chains of member pairs per
     // workgroup) that keep the root tiles within about five workgroups per
@@ -570,12 +577,16 @@ tms_status tms_state_create(tms_trie* trie, int32_t B, int32_t k, const void* em
     st->grp_mt_nodes = mt;
     st->grp_mt_root = mt;
     for (int m = 4; m < mt; m *= 2)
-      if (size_t(tms::root_tile_grid(st->grp.rt, (B + m - 1) / m)) <= 1280) {
+      if (tms::root_tile_grid(st->grp.rt, (B + m - 1) / m) <= 5 * cus) {
         st->grp_mt_root = m;
         break;
       }
     st->grp.mt = st->grp_mt_root;
     st->grp.mtiles = (B + st->grp.mt - 1) / st->grp.mt;
+    // the sequences off the root split over the compute units the root tiles leave
+    const int root_wgs = tms::root_tile_grid(st->grp.rt, st->grp.mtiles);
+    st->grp_split_default = default_split(B, cap_rest, rows, std::max(cus - root_wgs, 0));
+    st->grp.split = st->grp_split_default;
     st->step_group_ok = root_edges > 0 && tms::step_group_lds(nq, mt) <= 160 * 1024 - 1024;
     // automatic for wide roots: per-step graph at B = 64, per sequence / root
     // grouped, unstructured (884 root edges) 19.3 / 6.6 us, charset_hex (2470)
