@@ -329,9 +329,9 @@ tms_status tms_state_set_norepeat(tms_state* st, int32_t kind);
  * sequences standing at the root in a step are served together in the same
  * launch: each root row is read once per tile of up to 16 of them and dotted
  * with each one's hidden vector.  NODES: as ROOT, and the sequences that
- * stand together at any other node are served by the workgroups of the
- * lowest of them: each row legal for any of them is read once and dotted
- * with each one's vector; a sequence alone at its node takes its own step.
+ * stand together at any other node share their workgroups: each row legal
+ * for any of them is read once per tile of up to 4 of them and dotted with
+ * each one's vector; a sequence alone at its node takes its own step.
  * Both keep the per-row arithmetic, so tokens, logits and state are
  * bit-identical to OFF (every sequence reads its own node's rows).  AUTO:
  * ROOT when B >= 8 and the root has at least 256 edges.  Always available for

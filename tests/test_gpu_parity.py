@@ -1313,10 +1313,12 @@ def _two_prefix_catalog(seed, K, max_len, V, prefixes):
 @pytest.mark.parametrize("split", [1, 3])
 def test_step_node_grouping_large_groups(split):
     """Groups of more than 64 sequences at one node (150 sequences over a root
-    of two edges, so member blocks of 64 and a partial one), served by one and
-    by three workgroups: the per-sequence step's tokens, logits and state bit
-    for bit, host-driven, in the graph and in the stream of step launches;
-    tokens against the oracle."""
+    of two edges, whose children have about 60 edges each: many member tiles,
+    each over several row tiles whose keys meet in device memory, and below
+    them nodes of one row tile), with one and three workgroups per sequence:
+    the per-sequence step's tokens, logits and state bit for bit, host-driven,
+    in the graph and in the stream of step launches; tokens against the
+    oracle."""
     rng = np.random.Generator(np.random.PCG64(515 + split))
     V, H, B, k = 3000, 128, 150, 2
     cat = _two_prefix_catalog(516, 120, 5, V, [0, 1])

@@ -97,8 +97,7 @@ tms::StepGroup* step_group(tms_state* st) {
                   : mode == TMS_STEP_GROUP_OFF                               ? false
                                                                              : st->step_group_auto;
   st->grp.nodes = mode == TMS_STEP_GROUP_NODES ? 1 : 0;
-  st->grp.mt = st->grp.nodes ? st->grp_mt_nodes : st->grp_mt_root;
-  st->grp.mtiles = (st->B + st->grp.mt - 1) / st->grp.mt;
+  st->grp.gmt = st->grp_mt_nodes;
   return on ? &st->grp : nullptr;
 }
 
@@ -570,11 +569,13 @@ tms_status tms_state_create(tms_trie* trie, int32_t B, int32_t k, const void* em
     st->grp.rt = (root_edges + rows - 1) / rows;
     // members per root tile: the fewest (shorter chains of member pairs per
     // workgroup) that keep the root tiles within about five workgroups per
-    // compute unit; node groups (NODES) stage as many as fit.  Per-step graph,
-    // B = 64, 16 / 8 / 4 members: unstructured 7.25 / 7.00 / 6.47 us,
-    // charset_tools 6.36 / 5.95 / 5.91, charset_hex (160 row tiles) 10.79 /
-    // 10.00 / 10.97.
-    st->grp_mt_nodes = mt;
+    // compute unit.  Per-step graph, B = 64, 16 / 8 / 4 members: unstructured
+    // 7.25 / 7.00 / 6.47 us, charset_tools 6.36 / 5.95 / 5.91, charset_hex (160
+    // row tiles) 10.79 / 10.00 / 10.97.  Node groups (NODES) take 4 members per
+    // tile: per-step graph with 16 / 4 / 2 (1), structured 9.11 / 8.48 / 8.07,
+    // large (B = 256) 14.77 / 14.75 / (19.94); unstructured and the catalogs
+    // within 1 % of each other.
+    st->grp_mt_nodes = std::min(mt, 4);
     st->grp_mt_root = mt;
     for (int m = 4; m < mt; m *= 2)
       if (tms::root_tile_grid(st->grp.rt, (B + m - 1) / m) <= 5 * cus) {

@@ -37,7 +37,7 @@ struct tms_state {
   bool step_group_ok = false, step_group_auto = false;
   tms::StepGroup grp{};
   int grp_split_default = 1;
-  int grp_mt_root = 16, grp_mt_nodes = 16;  // members per root tile; per node-group staging round
+  int grp_mt_root = 16, grp_mt_nodes = 4;  // members per root tile; per node-group tile
   // the grouped step's snapshot (DevState::snap): the half that holds every
   // sequence's current node, and whether it is up to date (any other call
   // that moves sequences makes it stale; the reset kernel rewrites half 0)

@@ -141,6 +141,7 @@ struct StepGroup {
   int split, rt, mt, mtiles;
   int parity;  // which half of DevState::snap holds the nodes at the start of this step
   int nodes;   // also group the sequences that share any other node
+  int gmt;     // members per tile of those node groups
 };
 // snap[parity] <- every sequence's node (-1 if finished or in error).
 hipError_t launch_snapshot(const DevState& st, int parity, hipStream_t s);

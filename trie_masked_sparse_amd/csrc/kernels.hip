@@ -652,80 +652,65 @@ __device__ __forceinline__ bool root_tile(int r, int rt, int mtiles, int& x, int
 // Node-grouped head below the root (sections "The batched engine" and "The
 // sparse output layer": the rows a batch needs are the union of the legal
 // sets, so a row legal for several sequences standing at the same node is
-// read once for all of them).  The n_mem sequences at `node` (ascending ids;
-// the lowest, `leader`, owns the group) are served by the leader's split
-// workgroups; the others' workgroups return.  Workgroup w takes the node's
-// edges b0 + w*8+wv + u*W (W = split*8 wavefronts), as scan_node does, holds
-// their rows in registers and dots them with each member's hidden vector
-// staged in LDS (mt at a time), with the per-row arithmetic of the other
-// kernels, so every logit, key and token is the one step_sparse_kernel
-// computes.  Members go in blocks of 64 (lane j: member j of the block), so
-// an edge's legality for all of them is one ballot.  Their keys meet in LDS
-// (split 1) or in key[] with an arrival count on the leader, whose last
-// workgroup advances every member.
+// read once for all of them).  The n_mem sequences at `node` (ranked by id)
+// share the work of their split workgroups each: the node's edges in row
+// tiles of one pass of the workgroup's rows (U per wavefront) times the
+// members in tiles of mt, tile i taken by the group's workgroup i mod
+// (n_mem * split).  A tile stages its members' hidden vectors in LDS, reads
+// its rows once, and dots every (row, member) pair with the per-row
+// arithmetic of the other kernels, so every logit, key and token is the one
+// step_sparse_kernel computes; an edge's legality for the tile's members is
+// one ballot (lane j: member j).  With one row tile the workgroup that takes a
+// member tile holds its members' keys and advances them; with more, the keys
+// meet in key[] with an atomic max and the last row tile of a member tile to
+// arrive advances its members.
 // ---------------------------------------------------------------------------
-// mask0: with B <= 64, bit q set where sequence q is a member (the caller's
-// ballot over the snapshot), so the member list needs no second read of it.
+// rank: the rank of this workgroup's sequence among the members; mask0: with
+// B <= 64, bit q set where sequence q is a member (the caller's ballot over
+// the snapshot), so member lists need no second read of it.
 template <int DT, int NC>
-__device__ void node_group_step(const DevTrie& tr, const DevState& st, const StepIO& io, int node, int leader,
-                                int n_mem, unsigned long long mask0, int split, int w, const int32_t* snap_in,
-                                int32_t* snap_out, uint4* sh, int mt) {
+__device__ void node_group_step(const DevTrie& tr, const DevState& st, const StepIO& io, int node, int n_mem,
+                                int rank, unsigned long long mask0, int split, int w,
+                                const int32_t* snap_in, int32_t* snap_out, uint4* sh, int mt) {
   constexpr int EL = DT == 0 ? 4 : 8;
   constexpr int U = rows_per_pass(NC);
   constexpr int MPW = 4;  // members staged per wavefront per round
+  constexpr int RT = U * kWavesPerBlock;  // rows per tile
   const int lane = __lane_id();
   const int wv = wave_id();
   const int nq = io.H / EL;
-  const int W = split * kWavesPerBlock;
-  const int wq = w * kWavesPerBlock + wv;
   const NodeRec rec = rec_scalar(tr.node_rec, node);
   const int f = rec.b1 - rec.b0;
-  // passes over the node's edges: one count for the whole workgroup (the
-  // staging barriers), from its first wavefront's share
-  const int first = w * kWavesPerBlock;
-  const int npass = f > first ? (f - first + U * W - 1) / (U * W) : 0;
-  const int nblk = (n_mem + kWave - 1) / kWave;
+  const int nrt = max(1, (f + RT - 1) / RT), nmt = (n_mem + mt - 1) / mt;
+  const int n_wg = n_mem * split, me = rank * split + w;
   __shared__ int s_gm[kWave];
   __shared__ unsigned long long s_gbest[kWave];
   __shared__ int s_glast;
-  // s_gm <- the ids of members blk*64 .. blk*64+63, s_gbest <- 0 (wavefront
-  // 0; the caller's barrier publishes them)
-  auto members = [&](int blk) {
+  // s_gm <- the ids of members r0 .. r0+cnt-1 (cnt <= 64), s_gbest <- 0
+  // (wavefront 0; the caller's barrier publishes them)
+  auto members = [&](int r0, int cnt) {
     if (wv != 0) return;
     s_gbest[lane] = 0ull;
-    int rank = 0;
+    int rk = 0;
     for (int c = 0; c < st.B; c += kWave) {
       const int q = c + lane;
       const bool in = st.B <= kWave ? ((mask0 >> lane) & 1ull) != 0ull : q < st.B && snap_in[q] == node;
       const unsigned long long m = __ballot(in);
-      const int r = rank + __popcll(m & ((1ull << lane) - 1ull)) - blk * kWave;
-      if (in && r >= 0 && r < kWave) s_gm[r] = q;
-      rank += __popcll(m);
+      const int r = rk + __popcll(m & ((1ull << lane) - 1ull)) - r0;
+      if (in && r >= 0 && r < cnt) s_gm[r] = q;
+      rk += __popcll(m);
     }
-  };
-  // one member's advance with its key (one wavefront)
-  auto take = [&](int m, unsigned long long key) {
-    Seq q;
-    if (!load_seq(tr, st, m, q)) {  // not expected: it stood at the node when the step began
-      if (lane == 0) {
-        write_step_out(io, m, -1, NAN);
-        snap_out[m] = -1;
-      }
-      return;
-    }
-    const int next = advance(tr, st, &io, m, q, key ? (int)key_id(key) : -2, key ? key_logit(key) : NAN, lane);
-    if (lane == 0) snap_out[m] = next;
   };
   const uint4* hid = (const uint4*)io.hidden;
-  for (int blk = 0; blk < nblk; ++blk) {
-    members(blk);
+  for (int i = me; i < nrt * nmt; i += n_wg) {
+    const int xr = i % nrt, m0 = (i / nrt) * mt;
+    const int tc = min(mt, n_mem - m0);
+    members(m0, tc);
     __syncthreads();
-    const int cnt = min(kWave, n_mem - blk * kWave);
-    const int mj = lane < cnt ? s_gm[lane] : -1;
+    const int mj = lane < tc ? s_gm[lane] : -1;
     // member j's control edges here: terminal, entry not spent, exactly-k rule
     Seq qj{node, 0, 0, rec.b0, rec.b1, false, false};
     if (mj >= 0) {
-      qj.depth = st.depth[mj];
       qj.done = st.done[mj];
       bool ctl = false;
       if (rec.ent >= 0)
@@ -735,136 +720,109 @@ __device__ void node_group_step(const DevTrie& tr, const DevState& st, const Ste
       qj.stop_ok = ctl && !more;
     }
     const int32_t* mlive = st.live + (int64_t)(mj >= 0 ? mj : 0) * tr.live_stride;
-    for (int p = 0; p < npass; ++p) {
-      const int e0 = rec.b0 + wq + p * U * W;
-      int rows[U];
-      unsigned long long legal[U];  // bit j: legal for member j of the block
+    const int e0 = rec.b0 + xr * RT + wv;
+    int rows[U];
+    unsigned long long legal[U];  // bit j: legal for member j of the tile
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = e0 + u * kWavesPerBlock;
+      const bool in = e < rec.b1;
+      const EdgeRec r = erec_uniform<kMetaScalar>(tr.erec, in ? e : rec.b0);
+      const int lv = (in && mj >= 0) ? mlive[e] : 0;  // control edges hold 0
+      legal[u] = __ballot(in && mj >= 0 && edge_ok_bits(r.child, lv, qj));
+      rows[u] = legal[u] ? r.tok : -1;  // the union over the tile's members
+    }
+    uint4 raw[U][NC];
+    issue_rows<NC, U>((const uint4*)io.emb, nq, rows, raw, lane);
+    for (int jb = wv; jb < tc; jb += kWavesPerBlock * MPW) {
+      uint4 v[MPW][NC];
+#pragma unroll
+      for (int u = 0; u < MPW; ++u) {
+        const int j = jb + u * kWavesPerBlock;
+        if (j < tc) load_hidden<NC>(hid + (int64_t)s_gm[j] * nq, nq, v[u], lane);
+      }
+#pragma unroll
+      for (int u = 0; u < MPW; ++u) {
+        const int j = jb + u * kWavesPerBlock;
+        if (j >= tc) continue;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          if (c * kWave + lane < nq) sh[j * nq + c * kWave + lane] = v[u][c];
+      }
+    }
+    __syncthreads();  // staged vectors visible
+    // two members per pass: independent accumulation chains side by side
+    for (int j = 0; j < tc; j += 2) {
+      const int j1 = min(j + 1, tc - 1);
+      uint4 hq0[NC], hq1[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int ii = c * kWave + lane < nq ? c * kWave + lane : 0;
+        hq0[c] = c * kWave < nq ? sh[j * nq + ii] : make_uint4(0, 0, 0, 0);
+        hq1[c] = c * kWave < nq ? sh[j1 * nq + ii] : make_uint4(0, 0, 0, 0);
+      }
+      float l0[U], l1[U];
+      finish_rows<DT, NC, U>(nq, rows, raw, hq0, l0, lane);
+      finish_rows<DT, NC, U>(nq, rows, raw, hq1, l1, lane);
+      unsigned long long k0 = 0ull, k1 = 0ull;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int e = e0 + u * W;
-        const bool in = e < rec.b1;
-        const EdgeRec r = erec_uniform<kMetaScalar>(tr.erec, in ? e : rec.b0);
-        const int lv = (in && mj >= 0) ? mlive[e] : 0;  // control edges hold 0
-        legal[u] = __ballot(in && mj >= 0 && edge_ok_bits(r.child, lv, qj));
-        rows[u] = legal[u] ? r.tok : -1;  // the union over the members
+        const uint32_t e = (uint32_t)(e0 + u * kWavesPerBlock);
+        if ((legal[u] >> j) & 1ull) k0 = max(k0, pack_key(l0[u], e));
+        if ((legal[u] >> j1) & 1ull) k1 = max(k1, pack_key(l1[u], e));
       }
-      uint4 raw[U][NC];
-      issue_rows<NC, U>((const uint4*)io.emb, nq, rows, raw, lane);
-      for (int t0 = 0; t0 < cnt; t0 += mt) {
-        const int tc = min(mt, cnt - t0);
-        __syncthreads();  // the previous tile's vectors are no longer read
-        for (int jb = wv; jb < tc; jb += kWavesPerBlock * MPW) {
-          uint4 v[MPW][NC];
-#pragma unroll
-          for (int u = 0; u < MPW; ++u) {
-            const int j = jb + u * kWavesPerBlock;
-            if (j < tc) load_hidden<NC>(hid + (int64_t)s_gm[t0 + j] * nq, nq, v[u], lane);
-          }
-#pragma unroll
-          for (int u = 0; u < MPW; ++u) {
-            const int j = jb + u * kWavesPerBlock;
-            if (j >= tc) continue;
-#pragma unroll
-            for (int c = 0; c < NC; ++c)
-              if (c * kWave + lane < nq) sh[j * nq + c * kWave + lane] = v[u][c];
-          }
-        }
-        __syncthreads();  // staged vectors visible
-        // two members per pass: independent accumulation chains side by side
-        for (int j = 0; j < tc; j += 2) {
-          const int j1 = min(j + 1, tc - 1);
-          uint4 hq0[NC], hq1[NC];
-#pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            const int i = c * kWave + lane;
-            const int ii = i < nq ? i : 0;
-            hq0[c] = c * kWave < nq ? sh[j * nq + ii] : make_uint4(0, 0, 0, 0);
-            hq1[c] = c * kWave < nq ? sh[j1 * nq + ii] : make_uint4(0, 0, 0, 0);
-          }
-          float l0[U], l1[U];
-          finish_rows<DT, NC, U>(nq, rows, raw, hq0, l0, lane);
-          finish_rows<DT, NC, U>(nq, rows, raw, hq1, l1, lane);
-          unsigned long long k0 = 0ull, k1 = 0ull;
-#pragma unroll
-          for (int u = 0; u < U; ++u) {
-            const uint32_t e = (uint32_t)(e0 + u * W);
-            if ((legal[u] >> (t0 + j)) & 1ull) k0 = max(k0, pack_key(l0[u], e));
-            if ((legal[u] >> (t0 + j1)) & 1ull) k1 = max(k1, pack_key(l1[u], e));
-          }
+      if (lane == 0) {
+        if (k0) __hip_atomic_fetch_max(&s_gbest[j], k0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (k1 && j1 != j) __hip_atomic_fetch_max(&s_gbest[j1], k1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    }
+    rows_consumed();
+    __syncthreads();  // the tile's keys are complete
+    bool last = true;  // one row tile: this workgroup holds the members' final keys
+    if (nrt > 1) {
+      // the member tile's keys meet in key[]; the last of its nrt row tiles
+      // to arrive (counted in the arrival slot of its first member) advances
+      // its members.  The maxima are acknowledged (no-return atomics count in
+      // vmcnt) before the arrival is issued.
+      if (wv == 0 && lane < tc && s_gbest[lane])
+        __hip_atomic_fetch_max(&st.key[mj], s_gbest[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (threadIdx.x == 0) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const uint32_t prev = __hip_atomic_fetch_add(&st.arrive[s_gm[0]], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_glast = prev == (uint32_t)(nrt - 1);
+      }
+      __syncthreads();
+      last = s_glast;
+    }
+    if (last) {
+      for (int j = wv; j < tc; j += kWavesPerBlock) {
+        const int m = s_gm[j];
+        const unsigned long long key =
+            nrt > 1 ? __hip_atomic_load(&st.key[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : s_gbest[j];
+        Seq q;
+        if (!load_seq(tr, st, m, q)) {  // not expected: it stood at the node when the step began
           if (lane == 0) {
-            if (k0) __hip_atomic_fetch_max(&s_gbest[t0 + j], k0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            if (k1 && j1 != j)
-              __hip_atomic_fetch_max(&s_gbest[t0 + j1], k1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            write_step_out(io, m, -1, NAN);
+            snap_out[m] = -1;
           }
+        } else {
+          const int next = advance(tr, st, &io, m, q, key ? (int)key_id(key) : -2, key ? key_logit(key) : NAN, lane);
+          if (lane == 0) snap_out[m] = next;
         }
+        if (nrt > 1 && lane == 0) __hip_atomic_store(&st.key[m], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      rows_consumed();
+      if (nrt > 1 && threadIdx.x == 0)
+        __hip_atomic_store(&st.arrive[s_gm[0]], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __syncthreads();  // this block's keys are complete
-    if (split == 1) {
-      // each member's record from its lane (read above, unchanged since)
-      for (int j = wv; j < cnt; j += kWavesPerBlock) {
-        const Seq q{node, __builtin_amdgcn_readlane(qj.depth, j), __builtin_amdgcn_readlane(qj.done, j), rec.b0, rec.b1,
-                    __builtin_amdgcn_readlane((int)qj.sep_ok, j) != 0, __builtin_amdgcn_readlane((int)qj.stop_ok, j) != 0};
-        const int m = __builtin_amdgcn_readlane(mj, j);
-        const unsigned long long key = s_gbest[j];
-        const int next = advance(tr, st, &io, m, q, key ? (int)key_id(key) : -2, key ? key_logit(key) : NAN, lane);
-        if (lane == 0) snap_out[m] = next;
-      }
-    } else if (wv == 0 && lane < cnt && s_gbest[lane]) {
-      __hip_atomic_fetch_max(&st.key[mj], s_gbest[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();  // before the next block rewrites s_gm and s_gbest
+    __syncthreads();  // before the next tile rewrites s_gm, s_gbest and the staged vectors
   }
-  if (split == 1) return;
-  // the maxima are acknowledged (no-return atomics count in vmcnt) before the
-  // arrival is issued, so the last arrival finds every workgroup's in key[]
-  if (threadIdx.x == 0) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    const uint32_t prev = __hip_atomic_fetch_add(&st.arrive[leader], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_glast = prev == (uint32_t)(split - 1);
-  }
-  __syncthreads();
-  if (!s_glast) return;
-  for (int blk = 0; blk < nblk; ++blk) {
-    members(blk);
-    __syncthreads();
-    const int cnt = min(kWave, n_mem - blk * kWave);
-    for (int j = wv; j < cnt; j += kWavesPerBlock) {
-      const int m = s_gm[j];
-      const unsigned long long key = __hip_atomic_load(&st.key[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      take(m, key);
-      if (lane == 0) __hip_atomic_store(&st.key[m], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) __hip_atomic_store(&st.arrive[leader], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// ---------------------------------------------------------------------------
-// Fused sparse step with the root grouped across sequences (section "The
-// batched engine": the rows one step needs are the union of the sequences'
-// legal sets, and every pointer starts at the root, so at a wide root many
-// sequences need the same rows in the same step).  One launch, fixed grid:
-//   * B * split sequence workgroups: workgroup (s, w) serves sequence s as in
-//     step_sparse_kernel, unless s stands at the root ("member");
-//   * rt * mtiles root workgroups (rt padded to a multiple of 8, root_tile):
-//     workgroup (x, y) reads root rows x*4U ..
-//     x*4U+4U-1 once (U per wavefront) and dots them with the hidden vectors of
-//     members y*mt .. y*mt+mt-1 (ascending sequence order) staged in LDS, in
-//     the per-row order of the other kernels, so every logit and key is the
-//     one step_sparse_kernel computes.  A member's key is the max over the rt
-//     root workgroups of its member tile (atomic max into key[s]); whichever of
-//     them arrives last (arrival counter) advances it.
-// A step in which no sequence is at the root costs the root workgroups one
-// pass over the sequences' nodes.  The root is never a terminal (entries are
-// non-empty), so its edges are content edges only.
-// ---------------------------------------------------------------------------
 // NODES: sequences standing together at any other node are grouped as well
 // (node_group_step); a sequence alone at its node takes its own step.
 template <int DT, int NC, bool FAST, bool NODES = false>
 __global__ __launch_bounds__(kBlock) void step_grouped_kernel(DevTrie tr, DevState st, StepIO io, int split,
-                                                              int rt, int mt, int mtiles, int parity) {
+                                                              int rt, int mt, int mtiles, int parity, int gmt) {
   constexpr int EL = DT == 0 ? 4 : 8;
   constexpr int U = rows_per_pass(NC);
   constexpr int MPW = 4;  // members staged per wavefront per round
@@ -897,22 +855,23 @@ __global__ __launch_bounds__(kBlock) void step_grouped_kernel(DevTrie tr, DevSta
     const bool active = load_seq(tr, st, s, q);  // issued with the snapshot read
     if (node0 == 0) return;  // a member: the root workgroups take its step
     if constexpr (NODES) {
-      // the sequences at the same node: the lowest one's workgroups take the
-      // step of all of them.  Decided from the snapshot alone, before this
-      // sequence's own state: the leader may already be advancing it
-      int n_mem = 0, leader = s;
+      // the sequences at the same node take their steps together (the
+      // workgroups of all of them share the work).  Decided from the snapshot
+      // alone, before this sequence's own state: the group's last workgroup
+      // may already be advancing it
+      int n_mem = 0, rank = 0;
       unsigned long long mask0 = 0ull;
       for (int c = 0; node0 > 0 && c < st.B; c += kWave) {
         const int q2 = c + lane;
         const unsigned long long m = __ballot(q2 < st.B && snap_in[q2] == node0);
-        if (n_mem == 0 && m) leader = c + (int)__builtin_ctzll(m);
         if (c == 0) mask0 = m;
+        if (c + kWave <= s) rank += __popcll(m);
+        else if (c <= s) rank += __popcll(m & ((1ull << (s - c)) - 1ull));
         n_mem += __popcll(m);
       }
       if (n_mem > 1) {
         extern __shared__ uint4 sh_g[];
-        if (s == leader)
-          node_group_step<DT, NC>(tr, st, io, node0, leader, n_mem, mask0, split, w, snap_in, snap_out, sh_g, mt);
+        node_group_step<DT, NC>(tr, st, io, node0, n_mem, rank, mask0, split, w, snap_in, snap_out, sh_g, gmt);
         return;
       }
     }
@@ -2839,12 +2798,13 @@ struct StepLaunch {
       return hipGetLastError();
     }
     constexpr int EL = DT == 0 ? 4 : 8;
-    const size_t lds = step_group_lds(io.H / EL, grp->mt);
+    const size_t lds = step_group_lds(io.H / EL, grp->nodes ? max(grp->mt, grp->gmt) : grp->mt);
     auto* k = grp->nodes ? (fast ? &step_grouped_kernel<DT, NC, true, true> : &step_grouped_kernel<DT, NC, false, true>)
                          : (fast ? &step_grouped_kernel<DT, NC, true> : &step_grouped_kernel<DT, NC, false>);
     if (hipError_t e = allow_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess) return e;
     const dim3 grid((unsigned)(st.B * grp->split + root_tile_grid(grp->rt, grp->mtiles)));
-    hipLaunchKernelGGL(k, grid, block, lds, s, tr, st, io, grp->split, grp->rt, grp->mt, grp->mtiles, grp->parity);
+    hipLaunchKernelGGL(k, grid, block, lds, s, tr, st, io, grp->split, grp->rt, grp->mt, grp->mtiles, grp->parity,
+                       grp->gmt);
     return hipGetLastError();
   }
 };
