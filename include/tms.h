@@ -192,7 +192,10 @@ tms_status tms_state_free(tms_state* st);
  * without computing logits (sections "Masked sampling inside the sampler"
  * and "The sparse output layer": the argmax over one legal token is that
  * token); tokens and state are the same either way.
- * One fused kernel; fixed grid per state, so it can be graph-captured. */
+ * One fused kernel; fixed grid per state, so it can be graph-captured.  With
+ * the root or node grouping on, a step recorded into a caller's graph is
+ * preceded by a snapshot kernel of the sequences' nodes, so that each replay
+ * reads the nodes it starts from. */
 tms_status tms_decode_step_sparse(tms_state* st, const void* hidden, int32_t* tok, float* logit,
                                   void* stream);
 
@@ -297,6 +300,8 @@ tms_status tms_state_set_split(tms_state* st, int32_t split);
  *   call with other buffers and the same T updates the instantiated graph's
  *   kernel arguments in place (after waiting for the device to drain, so
  *   that no queued replay reads them) instead of instantiating it again;
+ *   while the caller records the stream into a graph, the step kernels are
+ *   recorded as STREAM launches them;
  * STREAM: the same T step kernels launched directly on the stream.
  * Also read from the TMS_LOOP environment variable (0..4) at create. */
 typedef enum {

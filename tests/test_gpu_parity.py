@@ -260,6 +260,93 @@ def test_resident_loop_in_captured_graph(cid):
     trie.close()
 
 
+@pytest.mark.parametrize("loop", [tms.LOOP_GRAPH, tms.LOOP_STREAM])
+def test_step_loops_in_captured_graph(loop):
+    """The step-kernel forms of the whole decode (the library's own graph of
+    step kernels, or the launches one by one) recorded in a caller's graph,
+    root grouped (the unstructured catalog's wide root), reset inside it:
+    the kernels are recorded themselves, each grouped step after a snapshot
+    of its own, so that several replays, with the caller's eager work and a
+    fresh eager decode in between, each give the eager answer."""
+    cid = "unstructured"
+    c, otr, T, hid = config_case(cid)
+    trie = tms.Trie(catalog(cid), c.vocab, c.sep, c.stop)
+    st = tms.State(trie, c.batch, c.k, dev_embedding(cid))
+    tms.state_set_loop(st, loop)
+    hd = to_dev(hid)
+    want = run_k_pointers(st, hd)
+    compare(want[0], ref_decode(otr, c.k, embedding(cid), hid), c.hidden, where=f"{cid} eager, loop {loop}")
+    tok = torch.full((c.batch, T), -7, dtype=torch.int32, device="cuda")
+    ln = torch.zeros(c.batch, dtype=torch.int32, device="cuda")
+    ent = torch.zeros((c.batch, c.k), dtype=torch.int32, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        st.reset()
+        tms.decode_k_pointers(st, hd, tok, ln, ent, check=False)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        tok.fill_(-7)
+        ln.zero_()
+        ent.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (tok.cpu().numpy(), ln.cpu().numpy(), ent.cpu().numpy())
+        for a, b in zip(got, want):
+            assert np.array_equal(a, b), (loop, rep)
+        assert (st.status() == 0).all()
+        st.reset()
+        e = run_k_pointers(st, hd)
+        assert all(np.array_equal(a, b) for a, b in zip(e, want)), (loop, rep)
+    del g
+    st.close()
+    trie.close()
+
+
+@pytest.mark.parametrize("mode", [tms.STEP_GROUP_ROOT, tms.STEP_GROUP_NODES])
+def test_grouped_step_recorded_once_replayed_per_token(mode):
+    """One grouped step recorded in a caller's graph and replayed once per
+    token, the hidden vectors copied into its input between replays (a
+    serving loop's pattern): each replay snapshots the nodes it starts from,
+    so every step's tokens and logits equal the eager steps', bit for bit;
+    and an eager step right after the recording (before any replay) still
+    reads a current snapshot."""
+    cid = "unstructured"
+    c, otr, T, hid = config_case(cid)
+    trie = tms.Trie(catalog(cid), c.vocab, c.sep, c.stop)
+    st = tms.State(trie, c.batch, c.k, dev_embedding(cid))
+    tms.state_set_step_grouping(st, mode)
+    hd = to_dev(hid)
+    st.reset()
+    want_t, want_l = (a.T for a in run_step_loop(st, hd))  # [T][B]
+    h_in = torch.empty_like(hd[0])
+    tok = torch.empty(c.batch, dtype=torch.int32, device="cuda")
+    lg = torch.empty(c.batch, dtype=torch.float32, device="cuda")
+    st.reset()
+    st.status()  # the pending reset runs now, outside the recording
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        tms.decode_step_sparse(st, h_in, tok, lg, check=False)
+    torch.cuda.synchronize()
+    # nothing recorded has run: an eager first step reads a fresh snapshot
+    t0 = torch.empty_like(tok)
+    l0 = torch.empty_like(lg)
+    tms.decode_step_sparse(st, hd[0], t0, l0)
+    torch.cuda.synchronize()
+    assert np.array_equal(t0.cpu().numpy(), want_t[0]) and np.array_equal(l0.cpu().numpy(), want_l[0], equal_nan=True)
+    for t in range(1, T):
+        h_in.copy_(hd[t])
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(tok.cpu().numpy(), want_t[t]), (mode, t)
+        assert np.array_equal(lg.cpu().numpy(), want_l[t], equal_nan=True), (mode, t)
+    assert (st.status() == 0).all()
+    del g
+    st.close()
+    trie.close()
+
+
 def test_two_tries_no_contamination():
     """Interleaved steps on two tries and two states give the same results as
     running each alone (each grammar owns its store)."""

@@ -649,10 +649,21 @@ static tms_status flush_reset(tms_state* st, void* stream) {
   return TMS_OK;
 }
 
+// Whether the caller is recording stream s into a graph.  Recorded work runs
+// at each replay, not now, so what the host tracks about the device (the
+// snapshot below) does not hold for it.
+static bool is_capturing(hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(s, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone;
+}
+
 // The grouped step's snapshot must hold the current nodes in half `parity`
-// before a grouped step reads it; rewrites it from the state when stale.
+// before a grouped step reads it; rewrites it from the state when stale, and
+// always when recorded into a graph, so that every replay starts from a
+// snapshot of its own (the callers then mark it stale for the eager calls
+// that follow the recording).
 static tms_status ensure_snapshot(tms_state* st, int parity, hipStream_t s) {
-  if (st->snap_valid && st->snap_parity == parity) return TMS_OK;
+  if (st->snap_valid && st->snap_parity == parity && !is_capturing(s)) return TMS_OK;
   TMS_HIP(tms::launch_snapshot(st->dev, parity, s), "snapshot launch");
   st->snap_valid = true;
   st->snap_parity = parity;
@@ -729,6 +740,7 @@ tms_status tms_decode_step_sparse(tms_state* st, const void* hidden, int32_t* to
   io.out_tok = tok;
   io.out_logit = logit;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool cap = is_capturing(s);
   tms::StepGroup* g = step_group(st);
   if (g) {
     const tms_status rs = ensure_snapshot(st, st->snap_parity, s);
@@ -737,7 +749,7 @@ tms_status tms_decode_step_sparse(tms_state* st, const void* hidden, int32_t* to
   }
   TMS_HIP(tms::launch_step_sparse(st->trie->dev, st->dev, io, st->dtype, st->fast, st->split, s, g),
           "sparse step launch");
-  if (g) st->snap_parity ^= 1;  // the step wrote the other half
+  if (g && !cap) st->snap_parity ^= 1;  // the step wrote the other half
   else st->snap_valid = false;
   return TMS_OK;
 }
@@ -810,14 +822,17 @@ tms_status tms_decode_k_pointers(tms_state* st, const void* hidden_seq, int32_t 
     }
     return tms::launch_finalize(st->dev, len, entries, q);
   };
-  if (st->loop_mode == TMS_LOOP_STREAM) {
+  // a caller recording the stream into a graph records the step kernels
+  // themselves (the library's own graph is not launched into a recording)
+  const bool cap = is_capturing(s);
+  if (st->loop_mode == TMS_LOOP_STREAM || cap) {
     const int p0 = st->snap_valid ? st->snap_parity : 0;
     if (grp) {
       const tms_status rs = ensure_snapshot(st, p0, s);
       if (rs != TMS_OK) return rs;
     }
     TMS_HIP(enqueue(s, p0), "step loop launch");
-    if (grp) st->snap_parity = (p0 + T) & 1;
+    if (grp && !cap) st->snap_parity = (p0 + T) & 1;
     else st->snap_valid = false;
     return TMS_OK;
   }
