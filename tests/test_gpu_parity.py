@@ -303,6 +303,37 @@ def test_step_loops_in_captured_graph(loop):
     trie.close()
 
 
+@pytest.mark.filterwarnings("ignore:The CUDA Graph is empty")
+def test_check_refused_while_recording():
+    """The fail-loud check synchronises, which a stream being recorded into a
+    graph cannot do: every checked call refuses before recording anything,
+    and the state then decodes as if nothing had happened."""
+    cid = "tiny"
+    c, otr, T, hid = config_case(cid, B=4)
+    trie = tms.Trie(catalog(cid), c.vocab, c.sep, c.stop)
+    st = tms.State(trie, 4, c.k, dev_embedding(cid))
+    hd = to_dev(hid)
+    tok = torch.empty(4, dtype=torch.int32, device="cuda")
+    toks = torch.empty((4, T), dtype=torch.int32, device="cuda")
+    calls = [lambda: tms.decode_step_sparse(st, hd[0], tok),
+             lambda: tms.decode_step_dense_masked(st, hd[0], tok),
+             lambda: tms.decode_k_pointers(st, hd, toks),
+             lambda: tms.advance_forced(st, tok)]
+    for call in calls:
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with pytest.raises(tms.TmsError, match="recorded"):
+            with torch.cuda.graph(g, capture_error_mode="relaxed"):
+                call()
+        del g
+        torch.cuda.synchronize()
+    got = run_k_pointers(st, hd)
+    ref = ref_decode(otr, c.k, embedding(cid), hid)
+    compare(got[0], ref, c.hidden, gpu_len=got[1], gpu_entries=got[2], where="after refused recordings")
+    st.close()
+    trie.close()
+
+
 @pytest.mark.parametrize("mode", [tms.STEP_GROUP_ROOT, tms.STEP_GROUP_NODES])
 def test_grouped_step_recorded_once_replayed_per_token(mode):
     """One grouped step recorded in a caller's graph and replayed once per

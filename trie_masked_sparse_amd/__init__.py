@@ -304,6 +304,25 @@ def _handle(st):
     return st.h if isinstance(st, State) else st
 
 
+def _recording(stream) -> bool:
+    """Whether the stream (default: the current one) is being recorded into a
+    graph; False for a raw handle, which torch cannot ask about."""
+    if stream is None:
+        return torch.cuda.is_current_stream_capturing()
+    if isinstance(stream, torch.cuda.Stream):
+        with torch.cuda.stream(stream):
+            return torch.cuda.is_current_stream_capturing()
+    return False
+
+
+def _refuse_check_while_recording(check: bool, stream, where: str):
+    """check=True synchronises the stream, which a recording cannot do: refuse
+    before anything is recorded, with what to do instead."""
+    if check and _recording(stream):
+        raise TmsError(ERR_INVALID_ARG, where, "check=True synchronises the stream, which is being recorded into a "
+                       "graph: pass check=False and read State.status() after a replay")
+
+
 def _raise_device_errors(st, stream, where: str):
     """Synchronise the stream and raise TmsError if any sequence of st holds a
     device error; the message names the first such sequence and, for a State,
@@ -320,6 +339,7 @@ def _raise_device_errors(st, stream, where: str):
 
 
 def decode_step_sparse(st, hidden, tok, logit=None, stream=None, check: bool = True):
+    _refuse_check_while_recording(check, stream, "decode_step_sparse")
     _check(lib().tms_decode_step_sparse(_handle(st), _dev(hidden, _HID, "hidden"), _dev(tok, torch.int32, "tok"),
                                         _dev(logit, torch.float32, "logit"), _stream(stream)),
            "decode_step_sparse")
@@ -328,6 +348,7 @@ def decode_step_sparse(st, hidden, tok, logit=None, stream=None, check: bool = T
 
 
 def decode_step_dense_masked(st, hidden, tok, logit=None, full_logits=None, stream=None, check: bool = True):
+    _refuse_check_while_recording(check, stream, "decode_step_dense_masked")
     _check(lib().tms_decode_step_dense_masked(_handle(st), _dev(hidden, _HID, "hidden"),
                                               _dev(tok, torch.int32, "tok"), _dev(logit, torch.float32, "logit"),
                                               _dev(full_logits, torch.float32, "full_logits"), _stream(stream)),
@@ -337,6 +358,7 @@ def decode_step_dense_masked(st, hidden, tok, logit=None, full_logits=None, stre
 
 
 def decode_k_pointers(st, hidden_seq, tokens, len=None, entries=None, stream=None, check: bool = True):  # noqa: A002
+    _refuse_check_while_recording(check, stream, "decode_k_pointers")
     T = hidden_seq.shape[0]
     _check(lib().tms_decode_k_pointers(_handle(st), _dev(hidden_seq, _HID, "hidden_seq"), T,
                                        _dev(tokens, torch.int32, "tokens"), _dev(len, torch.int32, "len"),
@@ -354,6 +376,7 @@ def decode_k_pointers_noalloc(trie, emb, k: int, hidden_seq, tokens, status, len
     T, B, H = hidden_seq.shape
     if emb.dim() != 2 or emb.shape[1] != H:
         raise ValueError("emb must be [V][H] with the hidden size of hidden_seq")
+    _refuse_check_while_recording(check, stream, "decode_k_pointers_noalloc")
     _check(lib().tms_decode_k_pointers_noalloc(trie.h if isinstance(trie, Trie) else trie, _dev(emb, name="emb"),
                                                _dtype_code(emb), H, B, k, _dev(hidden_seq, _HID, "hidden_seq"), T,
                                                _dev(tokens, torch.int32, "tokens"), _dev(len, torch.int32, "len"),
@@ -370,6 +393,7 @@ def decode_k_pointers_noalloc(trie, emb, k: int, hidden_seq, tokens, status, len
 
 
 def advance_forced(st, tok, stream=None, check: bool = True):
+    _refuse_check_while_recording(check, stream, "advance_forced")
     _check(lib().tms_advance_forced(_handle(st), _dev(tok, torch.int32, "tok"), _stream(stream)), "advance_forced")
     if check:
         _raise_device_errors(st, stream, "advance_forced")
