@@ -300,6 +300,7 @@ tms_status tms_state_set_split(tms_state* st, int32_t split);
  *   call with other buffers and the same T updates the instantiated graph's
  *   kernel arguments in place (after waiting for the device to drain, so
  *   that no queued replay reads them) instead of instantiating it again;
+ *   a grouping or split set since the last call records the graph again;
  *   while the caller records the stream into a graph, the step kernels are
  *   recorded as STREAM launches them;
  * STREAM: the same T step kernels launched directly on the stream.

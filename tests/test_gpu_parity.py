@@ -303,6 +303,43 @@ def test_step_loops_in_captured_graph(loop):
     trie.close()
 
 
+def test_graph_loop_follows_grouping_and_split_changes():
+    """The graph form with the same buffers on every call, the grouping and
+    the split changed between calls: each change records the graph again
+    (another kernel or grid in the same shape), and every answer equals the
+    first, with the exported state."""
+    cid = "unstructured"
+    c, otr, T, hid = config_case(cid)
+    trie = tms.Trie(catalog(cid), c.vocab, c.sep, c.stop)
+    st = tms.State(trie, c.batch, c.k, dev_embedding(cid))
+    tms.state_set_loop(st, tms.LOOP_GRAPH)
+    hd = to_dev(hid)
+    tok = torch.empty((c.batch, T), dtype=torch.int32, device="cuda")
+    ln = torch.empty(c.batch, dtype=torch.int32, device="cuda")
+    ent = torch.empty((c.batch, c.k), dtype=torch.int32, device="cuda")
+    keys = ("node", "depth", "done", "status", "finished", "n_emitted", "entries", "live")
+    first = None
+    for mode, split in ((tms.STEP_GROUP_OFF, 0), (tms.STEP_GROUP_ROOT, 0), (tms.STEP_GROUP_ROOT, 3),
+                        (tms.STEP_GROUP_NODES, 3), (tms.STEP_GROUP_OFF, 2), (tms.STEP_GROUP_NODES, 0)):
+        tms.state_set_step_grouping(st, mode)
+        tms.state_set_split(st, split)
+        for _ in range(2):
+            st.reset()
+            tms.decode_k_pointers(st, hd, tok, ln, ent)
+            torch.cuda.synchronize()
+            got = (tok.cpu().numpy(), ln.cpu().numpy(), ent.cpu().numpy(), st.export(live=True))
+            if first is None:
+                first = got
+                compare(got[0], ref_decode(otr, c.k, embedding(cid), hid), c.hidden, gpu_len=got[1],
+                        gpu_entries=got[2], where="graph form, grouping off")
+            for a, b in zip(got[:3], first[:3]):
+                assert np.array_equal(a, b), (mode, split)
+            for key in keys:
+                assert np.array_equal(got[3][key], first[3][key]), (mode, split, key)
+    st.close()
+    trie.close()
+
+
 @pytest.mark.filterwarnings("ignore:The CUDA Graph is empty")
 def test_check_refused_while_recording():
     """The fail-loud check synchronises, which a stream being recorded into a
