@@ -83,7 +83,12 @@ int gemv_split(int B, int cap) {
 }
 
 void destroy_graph(tms_state* st) {
-  if (st->gexec) (void)hipGraphExecDestroy(st->gexec);
+  // a replay may still be queued (a setter called without a synchronisation):
+  // it finishes before its graph goes
+  if (st->gexec) {
+    (void)hipDeviceSynchronize();
+    (void)hipGraphExecDestroy(st->gexec);
+  }
   if (st->graph) (void)hipGraphDestroy(st->graph);
   st->gexec = nullptr;
   st->graph = nullptr;
@@ -836,11 +841,8 @@ tms_status tms_decode_k_pointers(tms_state* st, const void* hidden_seq, int32_t 
     else st->snap_valid = false;
     return TMS_OK;
   }
-  // a grouping or split set since the graph was recorded takes effect: the
-  // graph is recorded again (a grouped graph also needs the snapshot kept)
-  const int64_t launch = grp ? (int64_t(1 + grp->nodes) << 40) | (int64_t(grp->split) << 20) | st->split : st->split;
   const bool same = st->gexec && st->g_hidden == hidden_seq && st->g_T == T && st->g_tokens == tokens &&
-                    st->g_len == len && st->g_entries == entries && st->g_launch == launch;
+                    st->g_len == len && st->g_entries == entries;
   if (!same) {
     TMS_HIP(hipStreamBeginCapture(st->capture, hipStreamCaptureModeRelaxed), "begin capture");
     const hipError_t le = enqueue(st->capture, 0);
@@ -874,7 +876,6 @@ tms_status tms_decode_k_pointers(tms_state* st, const void* hidden_seq, int32_t 
     }
     st->g_hidden = hidden_seq;
     st->g_T = T;
-    st->g_launch = launch;
     st->g_tokens = tokens;
     st->g_len = len;
     st->g_entries = entries;

@@ -65,7 +65,6 @@ struct tms_state {
   const void* g_hidden = nullptr;
   int32_t g_T = 0;
   int32_t *g_tokens = nullptr, *g_len = nullptr, *g_entries = nullptr;
-  int64_t g_launch = -1;  // the grouping and split the graph's step kernels were recorded with
   std::vector<int32_t> host_status;
 };
 
