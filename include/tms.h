@@ -342,7 +342,8 @@ tms_status tms_state_set_norepeat(tms_state* st, int32_t kind);
  * bit-identical to OFF (every sequence reads its own node's rows).  AUTO:
  * ROOT when B >= 8 and the root has at least 256 edges.  Always available for
  * the hidden sizes the library accepts (one member's vector, at most 16 KiB,
- * fits the LDS). */
+ * fits the LDS).  Also read from the TMS_STEP_GROUP environment variable
+ * (0..3) at create. */
 typedef enum {
   TMS_STEP_GROUP_AUTO = 0,
   TMS_STEP_GROUP_OFF = 1,

@@ -608,6 +608,12 @@ tms_status tms_state_create(tms_trie* trie, int32_t B, int32_t k, const void* em
     const int v = std::atoi(env);
     if (v >= TMS_LOOP_RESIDENT && v <= TMS_LOOP_RESIDENT_GROUPED) st->loop_mode = v;
   }
+  if (const char* env = std::getenv("TMS_STEP_GROUP")) {
+    const int v = std::atoi(env);
+    const bool needs_fit = v == TMS_STEP_GROUP_ROOT || v == TMS_STEP_GROUP_NODES;
+    if (v >= TMS_STEP_GROUP_AUTO && v <= TMS_STEP_GROUP_NODES && (!needs_fit || st->step_group_ok))
+      st->step_group_mode = v;
+  }
   if (const char* env = std::getenv("TMS_BITMASK"))
     if (env[0] == '1' && trie->dev.emask) st->norepeat = TMS_NOREPEAT_BITMASK;
   st->host_status.assign(B, 0);
