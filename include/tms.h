@@ -283,7 +283,10 @@ tms_status tms_read_reference(const void* src, int64_t bytes, uint32_t* out, int
 tms_status tms_debug_set_live(tms_state* st, int32_t s, int32_t edge, int32_t value, void* stream);
 
 /* Tuning knob (also read from the TMS_SPLIT environment variable at create):
- * workgroups per sequence in the fused step; 0 restores the default. */
+ * workgroups per sequence in the fused step; 0 restores the default.
+ * This setter, tms_state_set_loop and tms_state_set_step_grouping discard the
+ * GRAPH form's instantiated graph, if there is one, after waiting for the
+ * device to finish (a replay of it may still be queued). */
 tms_status tms_state_set_split(tms_state* st, int32_t split);
 
 /* How tms_decode_k_pointers runs its T steps (all bit-identical, up to the
