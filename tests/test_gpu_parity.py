@@ -438,6 +438,39 @@ def test_two_tries_no_contamination():
     assert np.array_equal(toks["b"].cpu().numpy().T, pb[0])
 
 
+def test_states_on_concurrent_streams():
+    """Four states on four streams with their work in flight at once: the
+    resident loop (one kernel, and grouped root heads with loop phases) and
+    the root-grouped step kernels, each decoding repeatedly from resets, with
+    no synchronisation between the streams.  Every answer equals the one the
+    same state gives alone: states share nothing on the device."""
+    jobs = []
+    for cid, loop in (("product", tms.LOOP_RESIDENT), ("unstructured", tms.LOOP_RESIDENT),
+                      ("structured", tms.LOOP_STREAM), ("unstructured", tms.LOOP_GRAPH)):
+        c, otr, T, hid = config_case(cid)
+        trie = tms.Trie(catalog(cid), c.vocab, c.sep, c.stop)
+        st = tms.State(trie, c.batch, c.k, dev_embedding(cid))
+        tms.state_set_loop(st, loop)
+        hd = to_dev(hid)
+        want = run_k_pointers(st, hd)
+        outs = [tuple(torch.full(a.shape, -7, dtype=torch.int32, device="cuda") for a in want) for _ in range(3)]
+        jobs.append((cid, loop, trie, st, hd, want, outs, torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for cid, loop, trie, st, hd, want, outs, stream in jobs:
+            with torch.cuda.stream(stream):
+                st.reset(stream)
+                tms.decode_k_pointers(st, hd, *outs[rep], stream=stream, check=False)
+    torch.cuda.synchronize()
+    for cid, loop, trie, st, hd, want, outs, stream in jobs:
+        for rep in range(3):
+            for a, b in zip(outs[rep], want):
+                assert np.array_equal(a.cpu().numpy(), b), (cid, loop, rep)
+        assert (st.status() == 0).all(), (cid, loop)
+        st.close()
+        trie.close()
+
+
 # ---------------------------------------------------------------------------
 # Dense + mask cross-check
 # ---------------------------------------------------------------------------
